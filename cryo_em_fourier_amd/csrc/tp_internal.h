@@ -1,0 +1,38 @@
+// Host-side interface between the C ABI (tp_api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+
+// Everything a kernel needs for one call; passed by value.
+struct OpParams {
+  const float2* ref;      // reference [B, N, N, N/2+1] or [B, N, N/2+1] (forward, gradient)
+  float2* ref_out;        // adjoint output, same shape
+  const float2* img;      // projections [B, P, No, No/2+1] (adjoint input, gradient's G)
+  float2* img_out;        // forward output
+  const float* rot;       // [B_rot, P, d, d]
+  const float* shift;     // [B_shift, P, 2] or nullptr
+  float* grad_rot;        // [B_rot, P, d, d] or nullptr
+  float* grad_shift;      // [B_shift, P, 2] or nullptr
+  int B, P, N, No, Wo, B_rot, B_shift, ndim;
+  float os;
+  long long cut2;         // keep kx^2+ky^2 <= cut2; -1: keep everything
+  uint32_t ref_bytes;     // bytes of one reference entry
+  long long ref_elems;    // complex elements of one reference entry
+  double inv_no;          // 1 / No
+  int tiles_x, tiles_y, tiles_per_pose;
+  uint32_t nblocks;
+};
+
+// Output tile of one workgroup: TX kx-columns x TY ky-rows.
+constexpr int kTileX = 16;
+constexpr int kTileY = 16;
+
+hipError_t launch_project(const OpParams& p, int interp, hipStream_t s);
+hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s);
+hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s);
+hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
+
+}  // namespace tp

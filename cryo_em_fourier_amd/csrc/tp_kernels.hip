@@ -1,0 +1,282 @@
+// Projector kernels for gfx950: forward gather, adjoint scatter, pose
+// gradients; 2D and 3D references; linear and Catmull-Rom interpolation.
+//
+// One thread per output frequency.  A 256-thread workgroup covers a 16x16
+// tile (kx, ky-row) of one projection; the grid enumerates (batch, pose, tile)
+// pose-major and is remapped so each XCD walks contiguous tiles of the same
+// pose.  The rotation and shift of a pose are wave-uniform (kernel-argument
+// derived addresses -> scalar loads).
+#include "tp_internal.h"
+#include "tp_stencil.h"
+
+namespace tp {
+
+namespace {
+
+struct Out {
+  int b, n, kx, iy, ky;
+  bool in;    // inside the output array
+  bool keep;  // inside the cutoff
+};
+
+__device__ __forceinline__ Out locate(const OpParams& p) {
+  Out o;
+  const uint32_t g = xcd_remap(blockIdx.x, gridDim.x);
+  const uint32_t tile = g % (uint32_t)p.tiles_per_pose;
+  const uint32_t bn = g / (uint32_t)p.tiles_per_pose;
+  o.n = (int)(bn % (uint32_t)p.P);
+  o.b = (int)(bn / (uint32_t)p.P);
+  o.kx = (int)(tile % (uint32_t)p.tiles_x) * kTileX + (int)(threadIdx.x % kTileX);
+  o.iy = (int)(tile / (uint32_t)p.tiles_x) * kTileY + (int)(threadIdx.x / kTileX);
+  o.in = o.kx < p.Wo && o.iy < p.No;
+  o.ky = signed_row(o.iy, p.No);
+  const long long k2 = (long long)o.kx * o.kx + (long long)o.ky * o.ky;
+  o.keep = o.in && (p.cut2 < 0 || k2 <= p.cut2);
+  return o;
+}
+
+__device__ __forceinline__ RefGeom ref_geom(const OpParams& p) {
+  RefGeom g;
+  g.N = p.N;
+  g.xmax = p.N / 2;
+  g.lo = -(p.N / 2);
+  g.hi = (p.N + 1) / 2 - 1;
+  g.row = (uint32_t)(p.N / 2 + 1) * 8u;
+  g.plane = (uint32_t)p.N * g.row;
+  return g;
+}
+
+// p = os * (kx R[0,:] + ky R[1,:]) in fp64; false if a component is not finite
+// or beyond +-2^30 (such samples read 0).
+template <int NDIM>
+__device__ __forceinline__ bool sample_point(const OpParams& p, const Out& o, double* q) {
+  const float* R = p.rot + ((size_t)(p.B_rot == 1 ? 0 : o.b) * p.P + o.n) * (NDIM * NDIM);
+  const double os = (double)p.os;
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < NDIM; ++j) {
+    q[j] = os * ((double)o.kx * (double)R[j] + (double)o.ky * (double)R[NDIM + j]);
+    ok = ok && (fabs(q[j]) <= kCoordLimit);
+  }
+  return ok;
+}
+
+__device__ __forceinline__ float2 pose_shift(const OpParams& p, const Out& o) {
+  if (!p.shift) return make_float2(0.f, 0.f);
+  const float* s = p.shift + ((size_t)(p.B_shift == 1 ? 0 : o.b) * p.P + o.n) * 2;
+  return make_float2(s[0], s[1]);
+}
+
+__device__ __forceinline__ size_t img_index(const OpParams& p, const Out& o) {
+  return ((size_t)((size_t)o.b * p.P + o.n) * p.No + o.iy) * p.Wo + o.kx;
+}
+
+template <int NDIM, int INTERP>
+__device__ __forceinline__ float2 gather(rsrc_t rs, const RefGeom& g, const double* q, int xmin) {
+  if constexpr (NDIM == 3) return gather3<INTERP>(rs, g, q[0], q[1], q[2], xmin);
+  else return gather2<INTERP>(rs, g, q[0], q[1], xmin);
+}
+
+template <int NDIM, int INTERP>
+__device__ __forceinline__ void gather_grad(rsrc_t rs, const RefGeom& g, const double* q, int xmin,
+                                            float2* out) {
+  if constexpr (NDIM == 3) gather3_grad<INTERP>(rs, g, q[0], q[1], q[2], xmin, out);
+  else gather2_grad<INTERP>(rs, g, q[0], q[1], xmin, out);
+}
+
+template <int NDIM, int INTERP>
+__device__ __forceinline__ void scatter(float2* base, const RefGeom& g, const double* q, int xmin,
+                                        float2 v) {
+  if constexpr (NDIM == 3) scatter3<INTERP>(base, g, q[0], q[1], q[2], xmin, v);
+  else scatter2<INTERP>(base, g, q[0], q[1], xmin, v);
+}
+
+// ------------------------------------------------------------------ forward
+
+template <int NDIM, int INTERP>
+__global__ __launch_bounds__(kBlock) void k_project(OpParams p) {
+  const Out o = locate(p);
+  if (!o.in) return;
+  float2 res = make_float2(0.f, 0.f);
+  double q[NDIM];
+  if (o.keep && sample_point<NDIM>(p, o, q)) {
+    const RefGeom g = ref_geom(p);
+    const rsrc_t rs = make_rsrc(p.ref + (size_t)o.b * p.ref_elems, p.ref_bytes);
+    const bool c = q[0] < 0.0;
+    double m[NDIM], mneg[NDIM];
+#pragma unroll
+    for (int j = 0; j < NDIM; ++j) {
+      m[j] = c ? -q[j] : q[j];
+      mneg[j] = -m[j];
+    }
+    const int xmin1 = c ? 1 : 0, xmin2 = c ? 0 : 1;
+    const float2 mv = gather<NDIM, INTERP>(rs, g, m, xmin1);
+    float2 sv = make_float2(0.f, 0.f);
+    if (needs_secondary<INTERP>(m[0], xmin2)) sv = gather<NDIM, INTERP>(rs, g, mneg, xmin2);
+    res = c ? make_float2(mv.x + sv.x, sv.y - mv.y) : make_float2(mv.x + sv.x, mv.y - sv.y);
+    if (p.shift) {
+      const float2 s = pose_shift(p, o);
+      res = cmul(shift_phase(o.kx, o.ky, s.x, s.y, p.inv_no), res);
+    }
+  }
+  p.img_out[img_index(p, o)] = res;
+}
+
+// ------------------------------------------------------------------ adjoint
+
+template <int NDIM, int INTERP>
+__global__ __launch_bounds__(kBlock) void k_backproject(OpParams p) {
+  const Out o = locate(p);
+  if (!o.keep) return;
+  double q[NDIM];
+  if (!sample_point<NDIM>(p, o, q)) return;
+  float2 cv = p.img[img_index(p, o)];
+  if (p.shift) {
+    const float2 s = pose_shift(p, o);
+    cv = cmul(conjf2(shift_phase(o.kx, o.ky, s.x, s.y, p.inv_no)), cv);
+  }
+  const RefGeom g = ref_geom(p);
+  float2* base = p.ref_out + (size_t)o.b * p.ref_elems;
+  const bool c = q[0] < 0.0;
+  double m[NDIM], mneg[NDIM];
+#pragma unroll
+  for (int j = 0; j < NDIM; ++j) {
+    m[j] = c ? -q[j] : q[j];
+    mneg[j] = -m[j];
+  }
+  const int xmin1 = c ? 1 : 0, xmin2 = c ? 0 : 1;
+  scatter<NDIM, INTERP>(base, g, m, xmin1, c ? conjf2(cv) : cv);
+  if (needs_secondary<INTERP>(m[0], xmin2)) scatter<NDIM, INTERP>(base, g, mneg, xmin2, c ? cv : conjf2(cv));
+}
+
+// ----------------------------------------------------------- pose gradients
+
+template <int NDIM, int INTERP>
+__global__ __launch_bounds__(kBlock) void k_grad_pose(OpParams p) {
+  constexpr int NV = 2 * NDIM + 2;  // dR rows 0 and 1, then ds_x, ds_y
+  const Out o = locate(p);
+  double acc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = 0.0;
+  double q[NDIM];
+  if (o.keep && sample_point<NDIM>(p, o, q)) {
+    const RefGeom g = ref_geom(p);
+    const rsrc_t rs = make_rsrc(p.ref + (size_t)o.b * p.ref_elems, p.ref_bytes);
+    const bool c = q[0] < 0.0;
+    double m[NDIM], mneg[NDIM];
+#pragma unroll
+    for (int j = 0; j < NDIM; ++j) {
+      m[j] = c ? -q[j] : q[j];
+      mneg[j] = -m[j];
+    }
+    const int xmin1 = c ? 1 : 0, xmin2 = c ? 0 : 1;
+    float2 mv[NDIM + 1], sv[NDIM + 1];
+    gather_grad<NDIM, INTERP>(rs, g, m, xmin1, mv);
+#pragma unroll
+    for (int j = 0; j <= NDIM; ++j) sv[j] = make_float2(0.f, 0.f);
+    if (needs_secondary<INTERP>(m[0], xmin2)) gather_grad<NDIM, INTERP>(rs, g, mneg, xmin2, sv);
+    // S and dS/dp (chain rule through m = +-p, see tp_device.h)
+    float2 S, dS[NDIM];
+    if (c) {
+      S = make_float2(mv[0].x + sv[0].x, sv[0].y - mv[0].y);
+#pragma unroll
+      for (int j = 0; j < NDIM; ++j) dS[j] = make_float2(sv[j + 1].x - mv[j + 1].x, sv[j + 1].y + mv[j + 1].y);
+    } else {
+      S = make_float2(mv[0].x + sv[0].x, mv[0].y - sv[0].y);
+#pragma unroll
+      for (int j = 0; j < NDIM; ++j) dS[j] = make_float2(mv[j + 1].x - sv[j + 1].x, mv[j + 1].y + sv[j + 1].y);
+    }
+    const float2 G = p.img[img_index(p, o)];
+    float2 gph = conjf2(G);  // conj(G) * phase
+    if (p.shift) {
+      const float2 s = pose_shift(p, o);
+      gph = cmul(gph, shift_phase(o.kx, o.ky, s.x, s.y, p.inv_no));
+    }
+    const double os = (double)p.os;
+#pragma unroll
+    for (int j = 0; j < NDIM; ++j) {
+      const double dldp = (double)gph.x * dS[j].x - (double)gph.y * dS[j].y;  // Re(g dS_j)
+      acc[j] = os * o.kx * dldp;
+      acc[NDIM + j] = os * o.ky * dldp;
+    }
+    const double im_gs = (double)gph.x * S.y + (double)gph.y * S.x;  // Im(g S)
+    const double two_pi_over_n = 6.283185307179586476925 * p.inv_no;
+    acc[2 * NDIM] = two_pi_over_n * o.kx * im_gs;
+    acc[2 * NDIM + 1] = two_pi_over_n * o.ky * im_gs;
+  }
+  // workgroup reduction in fp64: wave shuffles, then LDS across the 4 waves
+  __shared__ double red[kBlock / 64][NV];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    double v = acc[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) red[wave][i] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < NV) {
+    const int i = threadIdx.x;
+    double v = 0.0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) v += red[w][i];
+    const uint32_t g = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t bn = g / (uint32_t)p.tiles_per_pose;
+    const int n = (int)(bn % (uint32_t)p.P), b = (int)(bn / (uint32_t)p.P);
+    if (i < 2 * NDIM) {
+      if (p.grad_rot) {
+        const int row = i / NDIM, col = i % NDIM;
+        const size_t br = p.B_rot == 1 ? 0 : (size_t)b;
+        unsafeAtomicAdd(p.grad_rot + ((br * p.P + n) * NDIM + row) * NDIM + col, (float)v);
+      }
+    } else if (p.grad_shift) {
+      const size_t bs = p.B_shift == 1 ? 0 : (size_t)b;
+      unsafeAtomicAdd(p.grad_shift + (bs * p.P + n) * 2 + (i - 2 * NDIM), (float)v);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_zero(uint32_t* ptr, size_t words) {
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < words; i += stride) ptr[i] = 0u;
+}
+
+}  // namespace
+
+#define TP_DISPATCH(KERNEL, p, interp, s)                                                  \
+  do {                                                                                     \
+    const dim3 grid((p).nblocks), block(kBlock);                                           \
+    if ((p).ndim == 3) {                                                                   \
+      if (interp) hipLaunchKernelGGL((KERNEL<3, 1>), grid, block, 0, s, p);                 \
+      else hipLaunchKernelGGL((KERNEL<3, 0>), grid, block, 0, s, p);                        \
+    } else {                                                                               \
+      if (interp) hipLaunchKernelGGL((KERNEL<2, 1>), grid, block, 0, s, p);                 \
+      else hipLaunchKernelGGL((KERNEL<2, 0>), grid, block, 0, s, p);                        \
+    }                                                                                      \
+  } while (0)
+
+hipError_t launch_project(const OpParams& p, int interp, hipStream_t s) {
+  TP_DISPATCH(k_project, p, interp, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s) {
+  TP_DISPATCH(k_backproject, p, interp, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s) {
+  TP_DISPATCH(k_grad_pose, p, interp, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  size_t blocks = (words + kBlock - 1) / kBlock;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(kBlock), 0, s, (uint32_t*)ptr, words);
+  return hipGetLastError();
+}
+
+}  // namespace tp

@@ -1,0 +1,275 @@
+// Separable stencils of the projector: gather (forward), gather with the
+// kernel derivative (pose gradients) and scatter (adjoint), for 2D and 3D
+// references, linear or Catmull-Rom.  See tp_device.h for the main/secondary
+// split that keeps every tap at x >= 0.
+#pragma once
+
+#include "tp_device.h"
+
+namespace tp {
+
+// x axis: weights (zeroed outside [xmin, xmax]) and the byte offset of the
+// first loaded tap, which is moved to x >= 0 by shifting the weights.
+template <int INTERP, bool GRAD>
+__device__ __forceinline__ uint32_t setup_x(const RefGeom& g, double q, int xmin, float* w, float* dw) {
+  using K = Kern<INTERP>;
+  constexpr int T = K::T;
+  const AxisPos a = axis_pos(q, K::OFF);
+  K::w(a.f, w);
+  if (GRAD) K::dw(a.f, dw);
+#pragma unroll
+  for (int d = 0; d < T; ++d) {
+    const int t = a.x0 + d;
+    if (t < xmin || t > g.xmax) {
+      w[d] = 0.f;
+      if (GRAD) dw[d] = 0.f;
+    }
+  }
+  int start = a.x0;
+  if (start < 0) {
+    const int sh = -start;
+    if (sh >= T) {
+#pragma unroll
+      for (int d = 0; d < T; ++d) { w[d] = 0.f; if (GRAD) dw[d] = 0.f; }
+    } else {
+      shift_left<T>(w, sh);
+      if (GRAD) shift_left<T>(dw, sh);
+    }
+    start = 0;
+  }
+  return (uint32_t)start * 8u;
+}
+
+// y or z axis: weights and byte offsets (kBig for taps outside the stored range).
+template <int INTERP, bool GRAD>
+__device__ __forceinline__ void setup_yz(const RefGeom& g, double q, uint32_t stride, float* w,
+                                         float* dw, uint32_t* off) {
+  using K = Kern<INTERP>;
+  const AxisPos a = axis_pos(q, K::OFF);
+  K::w(a.f, w);
+  if (GRAD) K::dw(a.f, dw);
+#pragma unroll
+  for (int d = 0; d < K::T; ++d) off[d] = axis_off(a.x0 + d, g, stride);
+}
+
+// ---------------------------------------------------------------- gather
+
+// Sum over taps with x >= xmin of w * V[t] at q (3D).
+template <int INTERP>
+__device__ __forceinline__ float2 gather3(rsrc_t rs, const RefGeom& g, double qx, double qy,
+                                          double qz, int xmin) {
+  constexpr int T = Kern<INTERP>::T;
+  float wx[T], wy[T], wz[T];
+  uint32_t yb[T], zb[T];
+  const uint32_t xo = setup_x<INTERP, false>(g, qx, xmin, wx, nullptr);
+  setup_yz<INTERP, false>(g, qy, g.row, wy, nullptr, yb);
+  setup_yz<INTERP, false>(g, qz, g.plane, wz, nullptr, zb);
+#pragma unroll
+  for (int d = 0; d < T; ++d) yb[d] = yb[d] == kBig ? kBig : yb[d] + xo;
+  float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int dz = 0; dz < T; ++dz) {
+    float2 pl = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int dy = 0; dy < T; ++dy) {
+      const uint32_t ro = zb[dz] + yb[dy];
+      float2 r = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int dx = 0; dx < T; ++dx) {
+        const float2 v = load_c64(rs, ro + 8u * dx);
+        r.x = fmaf(wx[dx], v.x, r.x);
+        r.y = fmaf(wx[dx], v.y, r.y);
+      }
+      pl.x = fmaf(wy[dy], r.x, pl.x);
+      pl.y = fmaf(wy[dy], r.y, pl.y);
+    }
+    acc.x = fmaf(wz[dz], pl.x, acc.x);
+    acc.y = fmaf(wz[dz], pl.y, acc.y);
+  }
+  return acc;
+}
+
+template <int INTERP>
+__device__ __forceinline__ float2 gather2(rsrc_t rs, const RefGeom& g, double qx, double qy,
+                                          int xmin) {
+  constexpr int T = Kern<INTERP>::T;
+  float wx[T], wy[T];
+  uint32_t yb[T];
+  const uint32_t xo = setup_x<INTERP, false>(g, qx, xmin, wx, nullptr);
+  setup_yz<INTERP, false>(g, qy, g.row, wy, nullptr, yb);
+  float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int dy = 0; dy < T; ++dy) {
+    const uint32_t ro = yb[dy] == kBig ? kBig : yb[dy] + xo;
+    float2 r = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int dx = 0; dx < T; ++dx) {
+      const float2 v = load_c64(rs, ro + 8u * dx);
+      r.x = fmaf(wx[dx], v.x, r.x);
+      r.y = fmaf(wx[dx], v.y, r.y);
+    }
+    acc.x = fmaf(wy[dy], r.x, acc.x);
+    acc.y = fmaf(wy[dy], r.y, acc.y);
+  }
+  return acc;
+}
+
+// Value and gradient w.r.t. the sample point: out[0] = S, out[1 + j] = dS/dq_j.
+template <int INTERP>
+__device__ __forceinline__ void gather3_grad(rsrc_t rs, const RefGeom& g, double qx, double qy,
+                                             double qz, int xmin, float2* out) {
+  constexpr int T = Kern<INTERP>::T;
+  float wx[T], wy[T], wz[T], dwx[T], dwy[T], dwz[T];
+  uint32_t yb[T], zb[T];
+  const uint32_t xo = setup_x<INTERP, true>(g, qx, xmin, wx, dwx);
+  setup_yz<INTERP, true>(g, qy, g.row, wy, dwy, yb);
+  setup_yz<INTERP, true>(g, qz, g.plane, wz, dwz, zb);
+#pragma unroll
+  for (int d = 0; d < T; ++d) yb[d] = yb[d] == kBig ? kBig : yb[d] + xo;
+  float2 s = make_float2(0.f, 0.f), sx = s, sy = s, sz = s;
+#pragma unroll
+  for (int dz = 0; dz < T; ++dz) {
+    float2 p0 = make_float2(0.f, 0.f), px = p0, py = p0;  // plane sums: w, dx-w, dy-w
+#pragma unroll
+    for (int dy = 0; dy < T; ++dy) {
+      const uint32_t ro = zb[dz] + yb[dy];
+      float2 r = make_float2(0.f, 0.f), rd = r;
+#pragma unroll
+      for (int dx = 0; dx < T; ++dx) {
+        const float2 v = load_c64(rs, ro + 8u * dx);
+        r.x = fmaf(wx[dx], v.x, r.x);
+        r.y = fmaf(wx[dx], v.y, r.y);
+        rd.x = fmaf(dwx[dx], v.x, rd.x);
+        rd.y = fmaf(dwx[dx], v.y, rd.y);
+      }
+      p0.x = fmaf(wy[dy], r.x, p0.x);
+      p0.y = fmaf(wy[dy], r.y, p0.y);
+      px.x = fmaf(wy[dy], rd.x, px.x);
+      px.y = fmaf(wy[dy], rd.y, px.y);
+      py.x = fmaf(dwy[dy], r.x, py.x);
+      py.y = fmaf(dwy[dy], r.y, py.y);
+    }
+    s.x = fmaf(wz[dz], p0.x, s.x);
+    s.y = fmaf(wz[dz], p0.y, s.y);
+    sx.x = fmaf(wz[dz], px.x, sx.x);
+    sx.y = fmaf(wz[dz], px.y, sx.y);
+    sy.x = fmaf(wz[dz], py.x, sy.x);
+    sy.y = fmaf(wz[dz], py.y, sy.y);
+    sz.x = fmaf(dwz[dz], p0.x, sz.x);
+    sz.y = fmaf(dwz[dz], p0.y, sz.y);
+  }
+  out[0] = s;
+  out[1] = sx;
+  out[2] = sy;
+  out[3] = sz;
+}
+
+template <int INTERP>
+__device__ __forceinline__ void gather2_grad(rsrc_t rs, const RefGeom& g, double qx, double qy,
+                                             int xmin, float2* out) {
+  constexpr int T = Kern<INTERP>::T;
+  float wx[T], wy[T], dwx[T], dwy[T];
+  uint32_t yb[T];
+  const uint32_t xo = setup_x<INTERP, true>(g, qx, xmin, wx, dwx);
+  setup_yz<INTERP, true>(g, qy, g.row, wy, dwy, yb);
+  float2 s = make_float2(0.f, 0.f), sx = s, sy = s;
+#pragma unroll
+  for (int dy = 0; dy < T; ++dy) {
+    const uint32_t ro = yb[dy] == kBig ? kBig : yb[dy] + xo;
+    float2 r = make_float2(0.f, 0.f), rd = r;
+#pragma unroll
+    for (int dx = 0; dx < T; ++dx) {
+      const float2 v = load_c64(rs, ro + 8u * dx);
+      r.x = fmaf(wx[dx], v.x, r.x);
+      r.y = fmaf(wx[dx], v.y, r.y);
+      rd.x = fmaf(dwx[dx], v.x, rd.x);
+      rd.y = fmaf(dwx[dx], v.y, rd.y);
+    }
+    s.x = fmaf(wy[dy], r.x, s.x);
+    s.y = fmaf(wy[dy], r.y, s.y);
+    sx.x = fmaf(wy[dy], rd.x, sx.x);
+    sx.y = fmaf(wy[dy], rd.y, sx.y);
+    sy.x = fmaf(dwy[dy], r.x, sy.x);
+    sy.y = fmaf(dwy[dy], r.y, sy.y);
+  }
+  out[0] = s;
+  out[1] = sx;
+  out[2] = sy;
+}
+
+// ---------------------------------------------------------------- scatter
+
+// Adjoint of gather3 / gather2: every tap with x in [xmin, xmax] and y, z in
+// the stored range receives w * val (float atomics, element pointer math).
+template <int INTERP>
+__device__ __forceinline__ void scatter3(float2* base, const RefGeom& g, double qx, double qy,
+                                         double qz, int xmin, float2 val) {
+  using K = Kern<INTERP>;
+  constexpr int T = K::T;
+  const AxisPos ax = axis_pos(qx, K::OFF), ay = axis_pos(qy, K::OFF), az = axis_pos(qz, K::OFF);
+  float wx[T], wy[T], wz[T];
+  K::w(ax.f, wx);
+  K::w(ay.f, wy);
+  K::w(az.f, wz);
+  const long long rowe = g.xmax + 1, planee = (long long)g.N * rowe;
+#pragma unroll
+  for (int dz = 0; dz < T; ++dz) {
+    const int tz = az.x0 + dz;
+    if (tz < g.lo || tz > g.hi) continue;
+    const long long zo = (long long)(tz < 0 ? tz + g.N : tz) * planee;
+#pragma unroll
+    for (int dy = 0; dy < T; ++dy) {
+      const int ty = ay.x0 + dy;
+      if (ty < g.lo || ty > g.hi) continue;
+      const long long yo = zo + (long long)(ty < 0 ? ty + g.N : ty) * rowe;
+      const float wyz = wy[dy] * wz[dz];
+#pragma unroll
+      for (int dx = 0; dx < T; ++dx) {
+        const int tx = ax.x0 + dx;
+        if (tx < xmin || tx > g.xmax) continue;
+        const float w = wx[dx] * wyz;
+        if (w == 0.f) continue;
+        float* dst = reinterpret_cast<float*>(base + yo + tx);
+        unsafeAtomicAdd(dst, w * val.x);
+        unsafeAtomicAdd(dst + 1, w * val.y);
+      }
+    }
+  }
+}
+
+template <int INTERP>
+__device__ __forceinline__ void scatter2(float2* base, const RefGeom& g, double qx, double qy,
+                                         int xmin, float2 val) {
+  using K = Kern<INTERP>;
+  constexpr int T = K::T;
+  const AxisPos ax = axis_pos(qx, K::OFF), ay = axis_pos(qy, K::OFF);
+  float wx[T], wy[T];
+  K::w(ax.f, wx);
+  K::w(ay.f, wy);
+  const long long rowe = g.xmax + 1;
+#pragma unroll
+  for (int dy = 0; dy < T; ++dy) {
+    const int ty = ay.x0 + dy;
+    if (ty < g.lo || ty > g.hi) continue;
+    const long long yo = (long long)(ty < 0 ? ty + g.N : ty) * rowe;
+#pragma unroll
+    for (int dx = 0; dx < T; ++dx) {
+      const int tx = ax.x0 + dx;
+      if (tx < xmin || tx > g.xmax) continue;
+      const float w = wx[dx] * wy[dy];
+      if (w == 0.f) continue;
+      float* dst = reinterpret_cast<float*>(base + yo + tx);
+      unsafeAtomicAdd(dst, w * val.x);
+      unsafeAtomicAdd(dst + 1, w * val.y);
+    }
+  }
+}
+
+// Does the secondary sum at -m (x-taps >= xmin2) have any tap in range?
+template <int INTERP>
+__device__ __forceinline__ bool needs_secondary(double mx, int xmin2) {
+  using K = Kern<INTERP>;
+  return (int)floor(-mx) + K::OFF + K::T - 1 >= xmin2;
+}
+
+}  // namespace tp

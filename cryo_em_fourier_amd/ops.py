@@ -1,0 +1,194 @@
+"""PyTorch-facing binding of the projector.
+
+``tp_project_3d``, ``tp_backproject_3d``, ``tp_project_2d``,
+``tp_backproject_2d`` and ``tp_grad_pose`` mirror the C ABI of the same names
+(include/tp.h) on device tensors: they check shapes, allocate outputs with
+torch and pass raw pointers and the current HIP stream.  ``project_3d`` and
+``project_2d`` are the differentiable forms (torch.autograd.Function): the
+backward calls the adjoint for the reference gradient and ``tp_grad_pose`` for
+the rotation and shift gradients, each only when needed (pages, tech. section
+2: autograd functions wrapping the native ops).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_INTERP = {"linear": _lib.TP_LINEAR, "cubic": _lib.TP_CUBIC,
+           _lib.TP_LINEAR: _lib.TP_LINEAR, _lib.TP_CUBIC: _lib.TP_CUBIC}
+
+
+def _interp(x) -> int:
+    try:
+        return _INTERP[x]
+    except KeyError:
+        raise ValueError(f"interp must be 'linear' or 'cubic', got {x!r}") from None
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ref_dims(ref: torch.Tensor, ndim: int, name: str):
+    _need(ref, name, torch.complex64, ndim + 1)
+    B, N = ref.shape[0], ref.shape[1]
+    want = (B,) + (N,) * (ndim - 1) + (N // 2 + 1,)
+    if tuple(ref.shape) != want:
+        raise ValueError(f"{name} must be a square/cubic rfft half-spectrum {want}, got {tuple(ref.shape)}")
+    return B, N
+
+
+def _pose_dims(rot, shift, ndim, B, dev):
+    _need(rot, "rot", torch.float32, 4)
+    B_rot, P = rot.shape[0], rot.shape[1]
+    if tuple(rot.shape[2:]) != (ndim, ndim):
+        raise ValueError(f"rot must be [B_rot, P, {ndim}, {ndim}], got {tuple(rot.shape)}")
+    if B_rot not in (1, B):
+        raise ValueError(f"rot batch {B_rot} must be 1 or {B}")
+    if rot.device != dev:
+        raise ValueError("rot is on another device")
+    B_shift = 1
+    if shift is not None:
+        _need(shift, "shift", torch.float32, 3)
+        B_shift = shift.shape[0]
+        if tuple(shift.shape[1:]) != (P, 2) or B_shift not in (1, B):
+            raise ValueError(f"shift must be [1 or {B}, {P}, 2], got {tuple(shift.shape)}")
+        if shift.device != dev:
+            raise ValueError("shift is on another device")
+    return B_rot, P, B_shift
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _project(ndim, ref, rot, shift, n_out, interp, oversampling, cutoff):
+    B, N = _ref_dims(ref, ndim, "reference")
+    B_rot, P, B_shift = _pose_dims(rot, shift, ndim, B, ref.device)
+    if n_out is None:
+        n_out = int(round(N / float(oversampling)))
+    out = torch.empty((B, P, n_out, n_out // 2 + 1), dtype=torch.complex64, device=ref.device)
+    fn = _lib.lib().tp_project_3d if ndim == 3 else _lib.lib().tp_project_2d
+    st = fn(ref.data_ptr(), B, N, rot.data_ptr(), B_rot, P, _ptr(shift), B_shift, n_out,
+            _interp(interp), float(oversampling), float(cutoff), out.data_ptr(), _stream(ref.device))
+    _lib.check(st, f"tp_project_{ndim}d")
+    return out
+
+
+def _backproject(ndim, proj, rot, shift, N, interp, oversampling, cutoff):
+    _need(proj, "proj", torch.complex64, 4)
+    B, P, n_out = proj.shape[0], proj.shape[1], proj.shape[2]
+    if proj.shape[3] != n_out // 2 + 1:
+        raise ValueError(f"proj must be [B, P, n, n//2+1], got {tuple(proj.shape)}")
+    B_rot, P2, B_shift = _pose_dims(rot, shift, ndim, B, proj.device)
+    if P2 != P:
+        raise ValueError(f"rot has {P2} poses, proj has {P}")
+    shape = (B,) + (N,) * (ndim - 1) + (N // 2 + 1,)
+    out = torch.empty(shape, dtype=torch.complex64, device=proj.device)
+    fn = _lib.lib().tp_backproject_3d if ndim == 3 else _lib.lib().tp_backproject_2d
+    st = fn(proj.data_ptr(), B, P, n_out, rot.data_ptr(), B_rot, _ptr(shift), B_shift, N,
+            _interp(interp), float(oversampling), float(cutoff), out.data_ptr(), _stream(proj.device))
+    _lib.check(st, f"tp_backproject_{ndim}d")
+    return out
+
+
+def tp_project_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """vol [B,N,N,N//2+1] c64, rot [B_rot,P,3,3] f32, shift [B_shift,P,2] f32 or None
+    -> [B,P,n_out,n_out//2+1] c64 (n_out defaults to round(N / oversampling))."""
+    return _project(3, vol, rot, shift, n_out, interp, oversampling, cutoff)
+
+
+def tp_project_2d(img, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """img [B,N,N//2+1] c64, rot [B_rot,P,2,2] f32 -> [B,P,n_out,n_out//2+1] c64."""
+    return _project(2, img, rot, shift, n_out, interp, oversampling, cutoff)
+
+
+def tp_backproject_3d(proj, rot, shift=None, N=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """Adjoint of tp_project_3d: proj [B,P,n,n//2+1] -> [B,N,N,N//2+1]."""
+    if N is None:
+        N = int(round(proj.shape[2] * float(oversampling)))
+    return _backproject(3, proj, rot, shift, N, interp, oversampling, cutoff)
+
+
+def tp_backproject_2d(proj, rot, shift=None, N=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """Adjoint of tp_project_2d: proj [B,P,n,n//2+1] -> [B,N,N//2+1]."""
+    if N is None:
+        N = int(round(proj.shape[2] * float(oversampling)))
+    return _backproject(2, proj, rot, shift, N, interp, oversampling, cutoff)
+
+
+def tp_grad_pose(ref, grad_out, rot, shift=None, interp="cubic", oversampling=1.0, cutoff=-1.0,
+                 want_rot=True, want_shift=True, B_shift=None):
+    """Rotation and shift gradients of Re sum conj(grad_out) * project(ref, rot, shift).
+
+    Returns (grad_rot or None, grad_shift or None); grad_rot has rot's shape,
+    grad_shift has shift's shape (or [B_shift, P, 2] when shift is None)."""
+    ndim = rot.shape[-1] if isinstance(rot, torch.Tensor) else 0
+    if ndim not in (2, 3):
+        raise ValueError("rot must be [B_rot, P, d, d] with d = 2 or 3")
+    B, N = _ref_dims(ref, ndim, "reference")
+    B_rot, P, Bs = _pose_dims(rot, shift, ndim, B, ref.device)
+    _need(grad_out, "grad_out", torch.complex64, 4)
+    if grad_out.shape[0] != B or grad_out.shape[1] != P or grad_out.shape[3] != grad_out.shape[2] // 2 + 1:
+        raise ValueError(f"grad_out must be [{B}, {P}, n, n//2+1], got {tuple(grad_out.shape)}")
+    n_out = grad_out.shape[2]
+    if shift is None:
+        Bs = 1 if B_shift is None else int(B_shift)
+    gr = torch.empty_like(rot) if want_rot else None
+    gs = torch.empty((Bs, P, 2), dtype=torch.float32, device=ref.device) if want_shift else None
+    st = _lib.lib().tp_grad_pose(ndim, ref.data_ptr(), B, N, grad_out.data_ptr(), rot.data_ptr(),
+                                 B_rot, P, _ptr(shift), Bs, n_out, _interp(interp),
+                                 float(oversampling), float(cutoff), _ptr(gr), _ptr(gs),
+                                 _stream(ref.device))
+    _lib.check(st, "tp_grad_pose")
+    return gr, gs
+
+
+class _Project(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, ref, rot, shift, ndim, n_out, interp, oversampling, cutoff):
+        out = _project(ndim, ref, rot, shift, n_out, interp, oversampling, cutoff)
+        ctx.save_for_backward(ref, rot, shift)
+        ctx.cfg = (ndim, interp, oversampling, cutoff)
+        return out
+
+    @staticmethod
+    def backward(ctx, g):
+        ref, rot, shift = ctx.saved_tensors
+        ndim, interp, oversampling, cutoff = ctx.cfg
+        g = g.contiguous()
+        if g.dtype != torch.complex64:
+            g = g.to(torch.complex64)
+        d_ref = d_rot = d_shift = None
+        if ctx.needs_input_grad[0]:
+            d_ref = _backproject(ndim, g, rot, shift, ref.shape[1], interp, oversampling, cutoff)
+        want_rot = ctx.needs_input_grad[1]
+        want_shift = shift is not None and ctx.needs_input_grad[2]
+        if want_rot or want_shift:
+            d_rot, d_shift = tp_grad_pose(ref, g, rot, shift, interp, oversampling, cutoff,
+                                          want_rot=want_rot, want_shift=want_shift)
+        return d_ref, d_rot, d_shift, None, None, None, None, None
+
+
+def project_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """Differentiable 3D->2D projection (gradients to vol, rot and shift)."""
+    return _Project.apply(vol, rot, shift, 3, n_out, interp, oversampling, cutoff)
+
+
+def project_2d(img, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """Differentiable 2D->2D projection (gradients to img, rot and shift)."""
+    return _Project.apply(img, rot, shift, 2, n_out, interp, oversampling, cutoff)

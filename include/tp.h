@@ -1,0 +1,165 @@
+/*
+ * tp.h -- C ABI of the MI355X differentiable Fourier-space slice projector.
+ *
+ * The operations follow the technical summaries of "torch-projectors: A
+ * High-Performance Differentiable Projection Library for PyTorch"
+ * (gist.science pages in it/de/ja/ko/ar):
+ *   - forward projection 3D->2D and 2D->2D: every output frequency of a 2D
+ *     rfft image is rotated into the reference's rfft half-spectrum,
+ *     interpolated there and multiplied by a shift phase (tech. section 2 of
+ *     every page; Fourier slice theorem, tech. section 1);
+ *   - backprojection: the exact adjoint of the forward (ko page tech. section
+ *     2), which is also the gradient w.r.t. the reference;
+ *   - analytic gradients w.r.t. the rotation matrices and shift vectors (ar
+ *     page tech. section 2, de page tech. section 3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  Complex tensors are interleaved float pairs (re, im), i.e. the
+ *   memory of a contiguous torch.complex64 tensor, in PyTorch/FFTW rfft layout
+ *   (pages, tech. section 2: the RFFT format is kept through every op):
+ *     3D reference  [B, N, N, N/2+1]  (z, y, x), x = halved last axis
+ *     2D reference  [B, N, N/2+1]     (y, x)
+ *     projections   [B, P, N_out, N_out/2+1]
+ *   Index i of a full axis of length n holds the signed frequency
+ *   i if i <= (n-1)/2 else i-n; the halved axis holds 0..n/2.
+ * Poses.  rot is float32 [B_rot, P, d, d] (d = 3 or 2), row-major, with
+ *   B_rot in {1, B} (1 = the same P poses for every batch entry).  An output
+ *   frequency (kx, ky) samples the reference at
+ *     p = oversampling * (kx * rot[0,:] + ky * rot[1,:])   (x, y[, z] order),
+ *   i.e. p = os * R^T (kx, ky[, 0]): the reference rotated by R is projected
+ *   along z (ko page tech. section 2: coordinates through the inverse of the
+ *   rotation).  Rows beyond the first two are not read.
+ *   shift is float32 [B_shift, P, 2] = (s_x, s_y) in output pixels, or NULL
+ *   for no shift; B_shift in {1, B}.  The output is multiplied by
+ *   exp(-2 pi i (kx s_x + ky s_y) / N_out) (de/ar pages tech. section 2).
+ * Friedel.  A tap with x < 0 reads conj(ref[-t]) (F(-k) = conj F(k), every
+ *   page tech. section 2).  Taps with x = 0 read the stored entry as it is.
+ *   Taps outside the stored range read 0.  Sample points with a component
+ *   beyond +-2^30 or not finite read 0.
+ * Interpolation.  interp = TP_LINEAR (2 taps per axis: 4 in 2D, 8 in 3D) or
+ *   TP_CUBIC (Catmull-Rom / Keys a = -0.5, 4 taps per axis: 16 in 2D, 64 in
+ *   3D) (every page tech. section 2).
+ * Oversampling.  oversampling > 0 scales p; the reference spectrum is that of
+ *   a box zero-padded by the caller to os*N_out (centred, then ifftshift,
+ *   then rfftn).  The library does no padding and no FFT.
+ * Cutoff.  Outputs with kx^2 + ky^2 > cutoff^2 are 0 and take no part in the
+ *   adjoint or the gradients; cutoff < 0 disables it.
+ * Ownership.  Every pointer is a device pointer owned by the caller; inputs
+ *   must be 8-byte aligned, contiguous and must not alias outputs.  The
+ *   library allocates nothing and keeps no state between calls.
+ * Writes.  Outputs are overwritten (the adjoint and the gradients clear their
+ *   outputs on the stream before accumulating into them).
+ * Streams.  stream is a hipStream_t (NULL = default stream); every call is
+ *   asynchronous on it and may be issued from several host threads.
+ * Errors.  Arguments are checked before anything is launched:
+ *   TP_EINVAL        null pointer, non-positive size, misaligned pointer,
+ *                    bad interp, oversampling <= 0 or not finite, cutoff NaN,
+ *                    B_rot or B_shift not in {1, B}, ndim not in {2, 3};
+ *   TP_EUNSUPPORTED  a reference entry larger than 2^31 - 4096 bytes, a box
+ *                    above 65535, or a launch grid above 2^31 - 1 blocks;
+ *   TP_EHIP          the HIP runtime reported an error at launch.
+ *   Nothing is thrown across the ABI.
+ * Results.  Forward and pose gradients are deterministic.  The adjoint
+ *   accumulates with float atomics, so its last bits may differ between runs.
+ */
+#ifndef TP_H
+#define TP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct { float re, im; } tp_c64; /* == torch.complex64 */
+
+typedef enum { TP_LINEAR = 0, TP_CUBIC = 1 } tp_interp;
+
+typedef enum {
+  TP_OK = 0,
+  TP_EINVAL = -1,
+  TP_EUNSUPPORTED = -2,
+  TP_EHIP = -3
+} tp_status;
+
+/* ABI version of this header (major * 100 + minor). */
+#define TP_ABI_VERSION 100
+int tp_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* tp_status_str(int status);
+
+/*
+ * Forward 3D -> 2D (central slice).
+ *   vol    [B, N, N, N/2+1] complex64, input
+ *   rot    [B_rot, P, 3, 3] float32, input
+ *   shift  [B_shift, P, 2] float32 or NULL, input
+ *   out    [B, P, N_out, N_out/2+1] complex64, overwritten
+ */
+tp_status tp_project_3d(const tp_c64* vol, int64_t B, int64_t N,
+                        const float* rot, int64_t B_rot, int64_t P,
+                        const float* shift, int64_t B_shift,
+                        int64_t N_out, int interp, float oversampling, float cutoff,
+                        tp_c64* out, void* stream);
+
+/*
+ * Adjoint of tp_project_3d for the real inner product Re sum conj(a) b
+ * (2D -> 3D backprojection): every kept output c = conj(phase) * proj is
+ * spread with the forward's interpolation weights onto the taps it was read
+ * from; a folded tap (x < 0) receives conj(w c) at -t.
+ *   proj     [B, P, N_out, N_out/2+1] complex64, input
+ *   vol_out  [B, N, N, N/2+1] complex64, overwritten
+ */
+tp_status tp_backproject_3d(const tp_c64* proj, int64_t B, int64_t P, int64_t N_out,
+                            const float* rot, int64_t B_rot,
+                            const float* shift, int64_t B_shift,
+                            int64_t N, int interp, float oversampling, float cutoff,
+                            tp_c64* vol_out, void* stream);
+
+/*
+ * Forward 2D -> 2D (rotated, shifted copy of a 2D reference).
+ *   img    [B, N, N/2+1] complex64, input
+ *   rot    [B_rot, P, 2, 2] float32, input
+ *   out    [B, P, N_out, N_out/2+1] complex64, overwritten
+ */
+tp_status tp_project_2d(const tp_c64* img, int64_t B, int64_t N,
+                        const float* rot, int64_t B_rot, int64_t P,
+                        const float* shift, int64_t B_shift,
+                        int64_t N_out, int interp, float oversampling, float cutoff,
+                        tp_c64* out, void* stream);
+
+/* Adjoint of tp_project_2d; img_out [B, N, N/2+1] is overwritten. */
+tp_status tp_backproject_2d(const tp_c64* proj, int64_t B, int64_t P, int64_t N_out,
+                            const float* rot, int64_t B_rot,
+                            const float* shift, int64_t B_shift,
+                            int64_t N, int interp, float oversampling, float cutoff,
+                            tp_c64* img_out, void* stream);
+
+/*
+ * Gradients of L = Re sum conj(grad_out) * project(ref, rot, shift) w.r.t.
+ * the rotations and the shifts (ndim = 3: tp_project_3d, ndim = 2:
+ * tp_project_2d), by the chain rule through the interpolation kernel's
+ * derivative (ar page tech. section 2):
+ *   dL/dR[i][j] = os * sum_k k_i Re(conj(G) phase dS/dp_j)   (i = 0: kx, 1: ky)
+ *   dL/ds_j     = sum_k Re(conj(G) (-2 pi i k_j / N_out) phase S)
+ * The last row of dL/dR is 0 in 3D.  With B_rot = 1 (or B_shift = 1) and
+ * B > 1 the gradient is summed over the batch.
+ *   ref       [B, N, N, N/2+1] (3D) or [B, N, N/2+1] (2D) complex64, input
+ *   grad_out  [B, P, N_out, N_out/2+1] complex64, input
+ *   grad_rot  [B_rot, P, ndim, ndim] float32, overwritten, or NULL to skip
+ *   grad_shift[B_shift, P, 2] float32, overwritten, or NULL to skip
+ *             (with shift == NULL the shift is 0 and grad_shift still has
+ *             B_shift rows, B_shift in {1, B})
+ */
+tp_status tp_grad_pose(int ndim, const tp_c64* ref, int64_t B, int64_t N,
+                       const tp_c64* grad_out, const float* rot, int64_t B_rot, int64_t P,
+                       const float* shift, int64_t B_shift,
+                       int64_t N_out, int interp, float oversampling, float cutoff,
+                       float* grad_rot, float* grad_shift, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_H */

@@ -186,15 +186,12 @@ def _scatter(Aflat, N: int, p: np.ndarray, c: np.ndarray, interp: int):
     w*conj(c) at -t when the tap was folded."""
     ndim = p.shape[1]
     base = np.floor(p).astype(np.int64)
-    size = Aflat.shape[0]
     for d in itertools.product(tap_offsets(interp), repeat=ndim):
         t = base + np.asarray(d, np.int64)[None, :]
         w = np.prod(kernel(interp, p - t), axis=1)
         valid, idx, conj = resolve_taps(t, N)
         val = w * np.where(conj, np.conj(c), c)
-        idx, val = idx[valid], val[valid]
-        Aflat += np.bincount(idx, weights=val.real, minlength=size)
-        Aflat += 1j * np.bincount(idx, weights=val.imag, minlength=size)
+        np.add.at(Aflat, idx[valid], val[valid])
 
 
 # ---------------------------------------------------------------- public ops

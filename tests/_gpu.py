@@ -1,0 +1,45 @@
+"""Shared helpers of the GPU parity tests (not collected by pytest)."""
+import sys
+
+import numpy as np
+
+# Tolerances of the parity bar: relative L2 error and max-abs error relative
+# to the reference's largest magnitude (fp32 kernels vs the fp64 oracle).
+REL_L2 = 1e-5
+MAX_ABS = 1e-4
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dtype=None):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def rel_errors(got, ref):
+    got = np.asarray(got, np.complex128 if np.iscomplexobj(got) or np.iscomplexobj(ref) else np.float64)
+    ref = np.asarray(ref)
+    diff = got - ref
+    nref = np.linalg.norm(ref.ravel())
+    rel = np.linalg.norm(diff.ravel()) / nref if nref > 0 else np.linalg.norm(diff.ravel())
+    mref = np.abs(ref).max() if ref.size else 0.0
+    mabs = np.abs(diff).max() / mref if mref > 0 else np.abs(diff).max()
+    return float(rel), float(mabs)
+
+
+def assert_parity(got, ref, what: str, rel_tol: float = REL_L2, abs_tol: float = MAX_ABS):
+    rel, mabs = rel_errors(got, ref)
+    log(f"  parity {what}: rel-L2 {rel:.2e}  max-abs/max {mabs:.2e}")
+    assert rel <= rel_tol and mabs <= abs_tol, (
+        f"{what}: rel-L2 {rel:.3e} (tol {rel_tol:.0e}), max-abs/max {mabs:.3e} (tol {abs_tol:.0e})")
+
+
+def complex_normal(rng, shape):
+    return (rng.standard_normal(shape) + 1j * rng.standard_normal(shape)).astype(np.complex64) * np.float32(np.sqrt(0.5))

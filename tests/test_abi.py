@@ -1,0 +1,119 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, and rejects invalid arguments before launching anything."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from cryo_em_fourier_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp.h")
+
+FAKE = 0x10000          # 64 KiB-aligned fake device address: never dereferenced
+FAKE_ODD = 0x10004      # 4- but not 8-byte aligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ("tp_project_3d", "tp_backproject_3d", "tp_project_2d", "tp_backproject_2d", "tp_grad_pose"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(_lib.EXPORTS)
+    assert L.tp_abi_version() == 100
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for code in (0, -1, -2, -3, 7):
+        assert L.tp_status_str(code)
+
+
+def proj3(**kw):
+    a = dict(vol=FAKE, B=1, N=32, rot=FAKE, B_rot=1, P=4, shift=None, B_shift=1, N_out=32,
+             interp=1, os=1.0, cutoff=16.0, out=FAKE, stream=None)
+    a.update(kw)
+    return _lib.lib().tp_project_3d(*a.values())
+
+
+def back3(**kw):
+    a = dict(proj=FAKE, B=1, P=4, N_out=32, rot=FAKE, B_rot=1, shift=None, B_shift=1, N=32,
+             interp=1, os=1.0, cutoff=16.0, out=FAKE, stream=None)
+    a.update(kw)
+    return _lib.lib().tp_backproject_3d(*a.values())
+
+
+def grad(**kw):
+    a = dict(ndim=3, ref=FAKE, B=1, N=32, g=FAKE, rot=FAKE, B_rot=1, P=4, shift=None, B_shift=1,
+             N_out=32, interp=1, os=1.0, cutoff=16.0, gr=FAKE, gs=None, stream=None)
+    a.update(kw)
+    return _lib.lib().tp_grad_pose(*a.values())
+
+
+EINVAL, EUNSUP = _lib.TP_EINVAL, _lib.TP_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(vol=None), EINVAL), (dict(out=None), EINVAL), (dict(rot=None), EINVAL),
+    (dict(vol=FAKE_ODD), EINVAL), (dict(out=FAKE_ODD), EINVAL),
+    (dict(B=0), EINVAL), (dict(N=0), EINVAL), (dict(P=0), EINVAL), (dict(N_out=-3), EINVAL),
+    (dict(interp=2), EINVAL), (dict(interp=-1), EINVAL),
+    (dict(os=0.0), EINVAL), (dict(os=-1.0), EINVAL), (dict(os=math.inf), EINVAL), (dict(os=math.nan), EINVAL),
+    (dict(cutoff=math.nan), EINVAL),
+    (dict(B=2, B_rot=3), EINVAL), (dict(B=2, shift=FAKE, B_shift=3), EINVAL),
+    (dict(N=70000), EUNSUP), (dict(N_out=70000), EUNSUP),
+    (dict(N=1024), EUNSUP),                 # 1024^2 * 513 * 8 bytes > 2 GiB
+    (dict(B=1 << 20, B_rot=1 << 20, P=1 << 20), EUNSUP),  # grid too large
+])
+def test_project_3d_argument_checks(kw, code):
+    assert proj3(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(proj=None), EINVAL), (dict(out=None), EINVAL), (dict(interp=5), EINVAL),
+    (dict(os=0.0), EINVAL), (dict(B=3, B_rot=2), EINVAL), (dict(N=2000), EUNSUP),
+])
+def test_backproject_3d_argument_checks(kw, code):
+    assert back3(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ndim=4), EINVAL), (dict(ndim=1), EINVAL), (dict(ref=None), EINVAL), (dict(g=None), EINVAL),
+    (dict(gr=FAKE + 2), EINVAL), (dict(gs=FAKE, B=2, B_rot=2, B_shift=3), EINVAL),
+    (dict(cutoff=math.nan), EINVAL),
+])
+def test_grad_pose_argument_checks(kw, code):
+    assert grad(**kw) == code
+
+
+def test_2d_entry_points_check_arguments():
+    L = _lib.lib()
+    assert L.tp_project_2d(None, 1, 32, FAKE, 1, 4, None, 1, 32, 1, 1.0, -1.0, FAKE, None) == EINVAL
+    assert L.tp_project_2d(FAKE, 1, 32, FAKE, 1, 4, None, 1, 32, 3, 1.0, -1.0, FAKE, None) == EINVAL
+    assert L.tp_backproject_2d(FAKE, 1, 4, 32, FAKE, 1, None, 1, 32, 1, -2.0, -1.0, FAKE, None) == EINVAL
+    # 2D references are limited by the same 2 GiB per entry
+    assert L.tp_project_2d(FAKE, 1, 60000, FAKE, 1, 4, None, 1, 32, 1, 1.0, -1.0, FAKE, None) == EUNSUP
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    from cryo_em_fourier_amd import tp_project_3d
+
+    vol = torch.zeros((1, 8, 8, 5), dtype=torch.complex64)
+    rot = torch.eye(3).reshape(1, 1, 3, 3)
+    with pytest.raises(ValueError, match="GPU"):
+        tp_project_3d(vol, rot)
