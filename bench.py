@@ -1,0 +1,263 @@
+"""Throughput of the Fourier-slice projector's hot path on one MI355X.
+
+One step = the whole path on one batch: forward projection (tp_project_3d),
+then the backward of a loss on its output: the adjoint for the reference
+gradient (tp_backproject_3d) and the rotation + shift gradients
+(tp_grad_pose).  Default workload (``c4``): a 256^3 blob phantom (rfft
+half-spectrum 256x256x129 complex64), 4096 uniform SO(3) poses, shifts
+U[-10,10] px, Catmull-Rom cubic, oversampling 1, cutoff 128.
+
+Prints one JSON line:  value = projections/s forward+backward; the forward
+rate, per-kernel times, the roofline of the dominant kernel and the CPU
+baseline (the fp64 oracle on a bounded pose sample, timed on the host before
+the GPU is touched) ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from cryo_em_fourier_amd import synth  # noqa: E402
+
+METRIC = "projections/sec fwd and fwd+bwd, box 256 cubic; % of HBM/L2 roofline"
+
+# MI355X published peaks
+HBM_PEAK_GBS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def in_cutoff_count(n_out: int, cutoff: float) -> int:
+    kx = np.arange(n_out // 2 + 1)[None, :]
+    iy = np.arange(n_out)[:, None]
+    ky = np.where(iy <= (n_out - 1) // 2, iy, iy - n_out)
+    if cutoff < 0:
+        return n_out * (n_out // 2 + 1)
+    return int(np.count_nonzero(kx * kx + ky * ky <= cutoff * cutoff))
+
+
+# ------------------------------------------------------------- CPU baseline
+
+_CPU = {}
+
+
+def _oracle_worker(idx):
+    import oracle
+
+    c = _CPU
+    R = c["R"][:, idx]
+    s = c["s"][:, idx]
+    G = c["G"][:, idx]
+    t0 = time.perf_counter()
+    oracle.project(c["V"], R, s, c["n_out"], c["interp"], c["os"], c["cutoff"])
+    t1 = time.perf_counter()
+    oracle.backproject(G, R, s, c["N"], c["interp"], c["os"], c["cutoff"])
+    oracle.grad_pose(c["V"], G, R, s, c["n_out"], c["interp"], c["os"], c["cutoff"])
+    t2 = time.perf_counter()
+    return len(idx), t1 - t0, t2 - t1
+
+
+def cpu_baseline(V, R, s, w: synth.Workload, N: int, os_: float, poses_per_worker: int):
+    """Time the oracle on a bounded pose sample with a fork pool (no GPU yet)."""
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    workers = max(1, min(16, ncpu))
+    rng = np.random.default_rng(12345)
+    sample = rng.choice(w.P, size=workers * poses_per_worker, replace=False)
+    G = synth.make_upstream(w, poses=sample)
+    _CPU.update(V=V, R=R[:, sample], s=s[:, sample], G=G, n_out=w.N_out, N=N,
+                interp=w.interp, os=os_, cutoff=w.cutoff)
+    chunks = [list(range(i * poses_per_worker, (i + 1) * poses_per_worker)) for i in range(workers)]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        res = pool.map(_oracle_worker, chunks)
+    wall = time.perf_counter() - t0
+    n = sum(r[0] for r in res)
+    fwd = sum(r[1] for r in res)
+    bwd = sum(r[2] for r in res)
+    # throughput of the pool: poses per wall second, split by the measured work
+    rate_total = n / wall
+    return {
+        "value": rate_total,
+        "unit": "projections/s fwd+bwd",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{n} of {w.P} poses (seeded), {workers} single-threaded workers, fork pool",
+        "fwd_proj_per_s": n / (fwd / workers) if fwd > 0 else None,
+        "wall_s": wall,
+    }
+
+
+# -------------------------------------------------------------------- GPU
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c4", choices=["c3", "c4", "c5"])
+    ap.add_argument("--oversampling", type=int, default=1, choices=[1, 2])
+    ap.add_argument("--poses", type=int, default=0, help="override the pose count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-poses-per-worker", type=int, default=10)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the projector is single-GPU; sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    w = synth.WORKLOADS[args.config]
+    if args.poses:
+        w = synth.Workload(**{**w.__dict__, "P": args.poses})
+    os_ = float(args.oversampling)
+    N = w.N * args.oversampling
+    t0 = time.perf_counter()
+    V = synth.make_reference(w, pad_to=N if args.oversampling != 1 else None)
+    R = synth.make_rotations(w)
+    s = synth.make_shifts(w)
+    print(f"# inputs: reference {V.shape} rot {R.shape} ({time.perf_counter() - t0:.1f}s)",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(V, R, s, w, N, os_, args.cpu_poses_per_worker)
+        print(f"# cpu baseline: {cpu['value']:.3f} proj/s on {cpu['cores']} cores "
+              f"({cpu['wall_s']:.1f}s)", file=sys.stderr, flush=True)
+
+    import torch
+
+    from cryo_em_fourier_amd import _lib
+
+    L = _lib.lib()
+    dev = torch.device("cuda:0")
+    Wo = w.N_out // 2 + 1
+    Vd = torch.from_numpy(V).to(dev)
+    Rd = torch.from_numpy(R).to(dev)
+    sd = torch.from_numpy(s).to(dev)
+    G = synth.make_upstream(w)
+    Gd = torch.from_numpy(G).to(dev)
+    del G
+    out = torch.empty((w.B, w.P, w.N_out, Wo), dtype=torch.complex64, device=dev)
+    dV = torch.empty_like(Vd)
+    dR = torch.empty_like(Rd)
+    ds = torch.empty_like(sd)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    B, P = w.B, w.P
+
+    def fwd():
+        _lib.check(L.tp_project_3d(Vd.data_ptr(), B, N, Rd.data_ptr(), R.shape[0], P, sd.data_ptr(),
+                                   s.shape[0], w.N_out, w.interp, os_, w.cutoff, out.data_ptr(), sh),
+                   "tp_project_3d")
+
+    def adj():
+        _lib.check(L.tp_backproject_3d(Gd.data_ptr(), B, P, w.N_out, Rd.data_ptr(), R.shape[0],
+                                       sd.data_ptr(), s.shape[0], N, w.interp, os_, w.cutoff,
+                                       dV.data_ptr(), sh), "tp_backproject_3d")
+
+    def grad():
+        _lib.check(L.tp_grad_pose(3, Vd.data_ptr(), B, N, Gd.data_ptr(), Rd.data_ptr(), R.shape[0], P,
+                                  sd.data_ptr(), s.shape[0], w.N_out, w.interp, os_, w.cutoff,
+                                  dR.data_ptr(), ds.data_ptr(), sh), "tp_grad_pose")
+
+    kernels = [("project", fwd), ("backproject", adj), ("grad_pose", grad)]
+    for i in range(args.warmup):
+        for _, f in kernels:
+            f()
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        for j, (_, f) in enumerate(kernels):
+            f()
+            ev[k][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per_kernel = {name: [] for name, _ in kernels}
+    step_ms = []
+    for k in range(args.steps):
+        for j, (name, _) in enumerate(kernels):
+            per_kernel[name].append(ev[k][j].elapsed_time(ev[k][j + 1]))
+        step_ms.append(ev[k][0].elapsed_time(ev[k][-1]))
+    avg = {n: float(np.mean(v)) for n, v in per_kernel.items()}
+    med = {n: float(np.median(v)) for n, v in per_kernel.items()}
+    ms_step = float(np.mean(step_ms))
+    fwd_bwd_rate = B * P / (ms_step * 1e-3)
+    fwd_rate = B * P / (avg["project"] * 1e-3)
+
+    # algorithmic traffic / work per launch
+    n_c = in_cutoff_count(w.N_out, w.cutoff)
+    taps = 64 if w.interp == synth.CUBIC else 8
+    units = B * P * n_c                        # in-cutoff output frequencies per launch
+    ref_bytes = V.nbytes
+    img_bytes = B * P * w.N_out * Wo * 8
+    pose_bytes = R.nbytes + s.nbytes
+    hbm = {  # compulsory HBM bytes per launch
+        "project": ref_bytes + img_bytes + pose_bytes,
+        "backproject": units * 8 + 2 * ref_bytes + pose_bytes,
+        "grad_pose": ref_bytes + units * 8 + pose_bytes + dR.numel() * 4 + ds.numel() * 4,
+    }
+    tap_bytes = {"project": units * taps * 8, "backproject": units * taps * 8,
+                 "grad_pose": units * taps * 8}
+    dom = max(avg, key=avg.get)
+    achieved = hbm[dom] / (avg[dom] * 1e-3) / 1e9
+    roof = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": None,
+        "algorithmic_bytes_per_launch": hbm[dom],
+        "tap_bytes_per_launch": tap_bytes[dom],
+        "tap_rate_GBs": round(tap_bytes[dom] / (avg[dom] * 1e-3) / 1e9, 1),
+    }
+    res = {
+        "metric": METRIC,
+        "value": round(fwd_bwd_rate, 1),
+        "unit": "projections/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: 3D->2D forward+backward, box {w.N}, {P} poses, cubic, "
+                        f"oversampling {args.oversampling}, cutoff {w.cutoff:g}, shifts U[-{w.shift_max:g},{w.shift_max:g}]",
+            "box": w.N, "spectrum_box": N, "poses": P, "batch": B, "interp": "cubic" if w.interp else "linear",
+            "oversampling": args.oversampling, "cutoff": w.cutoff, "in_cutoff_outputs_per_pose": n_c,
+        },
+        "fwd_proj_per_s": round(fwd_rate, 1),
+        "kernel_ms_mean": {k: round(v, 4) for k, v in avg.items()},
+        "kernel_ms_median": {k: round(v, 4) for k, v in med.items()},
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -39,9 +39,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
                                            0x00020000);
 }
 
+// 8-byte complex load.  The whole 2 x i32 result is bit-cast at once: taking
+// its elements one by one lets this compiler narrow the load to one dword and
+// return the real part twice.
 __device__ __forceinline__ float2 load_c64(rsrc_t r, uint32_t off) {
-  auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-  return make_float2(__builtin_bit_cast(float, v[0]), __builtin_bit_cast(float, v[1]));
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 
 // Round-robin dispatch sends workgroup g to XCD g % 8.  Remap so that each

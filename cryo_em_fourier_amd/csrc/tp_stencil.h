@@ -265,11 +265,18 @@ __device__ __forceinline__ void scatter2(float2* base, const RefGeom& g, double 
   }
 }
 
-// Does the secondary sum at -m (x-taps >= xmin2) have any tap in range?
+// Does the secondary sum at -m (x-taps >= xmin2) have a tap of nonzero
+// weight?  For the cubic kernel a tap of zero weight still has a nonzero
+// derivative (K'(+-1) = -+0.5), so any tap in range counts.  For the linear
+// kernel the only candidate tap, floor(-m_x) + 1, has weight frac(-m_x); at an
+// integer -m_x it carries no value and is skipped, which keeps the gradient a
+// one-sided derivative at the kink.
 template <int INTERP>
 __device__ __forceinline__ bool needs_secondary(double mx, int xmin2) {
   using K = Kern<INTERP>;
-  return (int)floor(-mx) + K::OFF + K::T - 1 >= xmin2;
+  const double q = -mx, fl = floor(q);
+  if (INTERP == 0) return (int)fl + 1 >= xmin2 && q > fl;
+  return (int)fl + K::OFF + K::T - 1 >= xmin2;
 }
 
 }  // namespace tp

@@ -28,7 +28,7 @@ def adversarial_rotations(rng):
     cyc = np.array([[0.0, 1, 0], [0, 0, 1], [1, 0, 0]])       # slice plane = the x = 0 plane
     Rz90 = np.array([[0.0, -1, 0], [1, 0, 0], [0, 0, 1]])
     Rx90 = np.array([[1.0, 0, 0], [0, 0, -1], [0, 1, 0]])
-    near = synth.axis_angle(np.array([0.0, 0.0, 1.0]), 1e-3) @ cyc
+    near = cyc @ synth.axis_angle(np.array([0.36, 0.48, 0.8]), 1e-3)   # slightly off the x = 0 plane
     tilt_p = synth.axis_angle(np.array([0.0, 1.0, 0.0]), math.radians(60))
     tilt_m = synth.axis_angle(np.array([0.6, 0.8, 0.0]), math.radians(-60))
     mats = [I, cyc, Rz90, Rx90, near, tilt_p, tilt_m, -np.diag([1.0, 1.0, -1.0])]
@@ -117,9 +117,13 @@ def test_grad_pose_3d_matches_oracle(name):
     gr, gs = tp_grad_pose(V, G, R, s, c["interp"], float(c["os"]), float(c["cutoff"]))
     dR, ds = oracle.grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
     if name == "adv-linear":
-        # on-grid samples sit on the kinks of the linear kernel, where the
-        # one-sided derivative is a convention; compare off-grid poses only
-        keep = [4, 5, 6]
+        # The linear kernel has kinks at integer coordinates, where the
+        # gradient is a one-sided derivative by convention: the oracle takes
+        # the right derivative in p, the kernels the right derivative in the
+        # evaluation point +-p (folded samples: the left one in p).  Poses
+        # whose samples sit on kinks with p_x < 0 (Rz90, Rx90, the 180 degree
+        # turn) are left out; identity and the x = 0 plane agree.
+        keep = [0, 1, 4, 5, 6]
         gr, dR = gr[:, keep], dR[:, keep]
         gs, ds = gs[:, keep], ds[:, keep]
     assert_parity(gr.cpu().numpy(), dR, f"grad_rot {name}")
@@ -290,3 +294,29 @@ def test_nonfinite_rotation_reads_zero():
     ref = oracle.project(c["V"], R, None, 12, CUBIC, 1.0, -1.0)
     assert np.all(np.isfinite(out))
     assert_parity(out, ref, "non-finite rotations")
+
+
+@pytest.mark.parametrize("N", [8, 9, 16])
+@pytest.mark.parametrize("interp", [LINEAR, CUBIC])
+def test_taps_at_the_end_of_the_reference(N, interp):
+    """Sample points on the last stored row (y = z = -1) next to x = N/2,
+    whose tap windows reach past the end of the reference buffer."""
+    from cryo_em_fourier_amd import tp_project_2d, tp_project_3d
+
+    rng = np.random.default_rng(N * 10 + interp)
+    xm = N // 2
+    pts = [(xm - 0.5, -1.0, -1.0), (xm + 0.0, -1.0, -1.0), (xm - 0.25, -1.0, -1.0), (xm - 1.0, -1.0, -1.0),
+           (-(xm - 0.5), 1.0, 1.0), (xm - 0.5, -1.5, -1.0)]
+    R = np.zeros((1, len(pts), 3, 3), np.float32)
+    for i, p in enumerate(pts):
+        R[0, i, 0] = p                       # output (kx=1, ky=0) samples p
+        R[0, i, 1] = (p[0] * 0.5, p[1], p[2])  # output (kx=0, ky=1) samples this
+    V = complex_normal(rng, (1, N, N, N // 2 + 1))
+    out = tp_project_3d(to_dev(V), to_dev(R), None, 4, interp, 1.0, -1.0).cpu().numpy()
+    ref = oracle.project(V, R, None, 4, interp, 1.0, -1.0)
+    assert_parity(out, ref, f"end-of-buffer 3D N={N}")
+    R2 = np.ascontiguousarray(R[:, :, :2, :2])
+    V2 = complex_normal(rng, (1, N, N // 2 + 1))
+    out = tp_project_2d(to_dev(V2), to_dev(R2), None, 4, interp, 1.0, -1.0).cpu().numpy()
+    ref = oracle.project(V2, R2, None, 4, interp, 1.0, -1.0)
+    assert_parity(out, ref, f"end-of-buffer 2D N={N}")
