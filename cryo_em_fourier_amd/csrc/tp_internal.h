@@ -26,6 +26,16 @@ struct OpParams {
   uint32_t nblocks;
 };
 
+// Brick decomposition of the adjoint (tp_adjoint.hip).
+struct BrickParams {
+  int nb[3];          // bricks along x, y, z
+  int nbricks;
+  int near_lo[3];     // box of bricks next to the origin, split over pose chunks
+  int near_ext[3];
+  int near_count;
+  int chunks;         // pose chunks of a near brick
+};
+
 // Output tile of one workgroup: TX kx-columns x TY ky-rows.
 constexpr int kTileX = 16;
 constexpr int kTileY = 16;
@@ -34,5 +44,6 @@ hipError_t launch_project(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
+uint64_t adjoint_blocks(const OpParams& p);
 
 }  // namespace tp

@@ -1,5 +1,6 @@
-// Projector kernels for gfx950: forward gather, adjoint scatter, pose
-// gradients; 2D and 3D references; linear and Catmull-Rom interpolation.
+// Projector kernels for gfx950: forward gather and pose gradients (the
+// adjoint lives in tp_adjoint.hip); 2D and 3D references; linear and
+// Catmull-Rom interpolation.
 //
 // One thread per output frequency.  A 256-thread workgroup covers a 16x16
 // tile (kx, ky-row) of one projection; the grid enumerates (batch, pose, tile)
@@ -84,13 +85,6 @@ __device__ __forceinline__ void gather_grad(rsrc_t rs, const RefGeom& g, const d
   else gather2_grad<INTERP>(rs, g, q[0], q[1], xmin, out);
 }
 
-template <int NDIM, int INTERP>
-__device__ __forceinline__ void scatter(float2* base, const RefGeom& g, const double* q, int xmin,
-                                        float2 v) {
-  if constexpr (NDIM == 3) scatter3<INTERP>(base, g, q[0], q[1], q[2], xmin, v);
-  else scatter2<INTERP>(base, g, q[0], q[1], xmin, v);
-}
-
 // ------------------------------------------------------------------ forward
 
 template <int NDIM, int INTERP>
@@ -120,33 +114,6 @@ __global__ __launch_bounds__(kBlock) void k_project(OpParams p) {
     }
   }
   p.img_out[img_index(p, o)] = res;
-}
-
-// ------------------------------------------------------------------ adjoint
-
-template <int NDIM, int INTERP>
-__global__ __launch_bounds__(kBlock) void k_backproject(OpParams p) {
-  const Out o = locate(p);
-  if (!o.keep) return;
-  double q[NDIM];
-  if (!sample_point<NDIM>(p, o, q)) return;
-  float2 cv = p.img[img_index(p, o)];
-  if (p.shift) {
-    const float2 s = pose_shift(p, o);
-    cv = cmul(conjf2(shift_phase(o.kx, o.ky, s.x, s.y, p.inv_no)), cv);
-  }
-  const RefGeom g = ref_geom(p);
-  float2* base = p.ref_out + (size_t)o.b * p.ref_elems;
-  const bool c = q[0] < 0.0;
-  double m[NDIM], mneg[NDIM];
-#pragma unroll
-  for (int j = 0; j < NDIM; ++j) {
-    m[j] = c ? -q[j] : q[j];
-    mneg[j] = -m[j];
-  }
-  const int xmin1 = c ? 1 : 0, xmin2 = c ? 0 : 1;
-  scatter<NDIM, INTERP>(base, g, m, xmin1, c ? conjf2(cv) : cv);
-  if (needs_secondary<INTERP>(m[0], xmin2)) scatter<NDIM, INTERP>(base, g, mneg, xmin2, c ? cv : conjf2(cv));
 }
 
 // ----------------------------------------------------------- pose gradients
@@ -257,11 +224,6 @@ __global__ __launch_bounds__(kBlock) void k_zero(uint32_t* ptr, size_t words) {
 
 hipError_t launch_project(const OpParams& p, int interp, hipStream_t s) {
   TP_DISPATCH(k_project, p, interp, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s) {
-  TP_DISPATCH(k_backproject, p, interp, s);
   return hipGetLastError();
 }
 

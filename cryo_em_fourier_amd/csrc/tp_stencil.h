@@ -1,6 +1,6 @@
-// Separable stencils of the projector: gather (forward), gather with the
-// kernel derivative (pose gradients) and scatter (adjoint), for 2D and 3D
-// references, linear or Catmull-Rom.  See tp_device.h for the main/secondary
+// Separable stencils of the projector: gather (forward) and gather with the
+// kernel derivative (pose gradients), for 2D and 3D references, linear or
+// Catmull-Rom.  See tp_device.h for the main/secondary
 // split that keeps every tap at x >= 0.
 #pragma once
 
@@ -195,74 +195,6 @@ __device__ __forceinline__ void gather2_grad(rsrc_t rs, const RefGeom& g, double
   out[0] = s;
   out[1] = sx;
   out[2] = sy;
-}
-
-// ---------------------------------------------------------------- scatter
-
-// Adjoint of gather3 / gather2: every tap with x in [xmin, xmax] and y, z in
-// the stored range receives w * val (float atomics, element pointer math).
-template <int INTERP>
-__device__ __forceinline__ void scatter3(float2* base, const RefGeom& g, double qx, double qy,
-                                         double qz, int xmin, float2 val) {
-  using K = Kern<INTERP>;
-  constexpr int T = K::T;
-  const AxisPos ax = axis_pos(qx, K::OFF), ay = axis_pos(qy, K::OFF), az = axis_pos(qz, K::OFF);
-  float wx[T], wy[T], wz[T];
-  K::w(ax.f, wx);
-  K::w(ay.f, wy);
-  K::w(az.f, wz);
-  const long long rowe = g.xmax + 1, planee = (long long)g.N * rowe;
-#pragma unroll
-  for (int dz = 0; dz < T; ++dz) {
-    const int tz = az.x0 + dz;
-    if (tz < g.lo || tz > g.hi) continue;
-    const long long zo = (long long)(tz < 0 ? tz + g.N : tz) * planee;
-#pragma unroll
-    for (int dy = 0; dy < T; ++dy) {
-      const int ty = ay.x0 + dy;
-      if (ty < g.lo || ty > g.hi) continue;
-      const long long yo = zo + (long long)(ty < 0 ? ty + g.N : ty) * rowe;
-      const float wyz = wy[dy] * wz[dz];
-#pragma unroll
-      for (int dx = 0; dx < T; ++dx) {
-        const int tx = ax.x0 + dx;
-        if (tx < xmin || tx > g.xmax) continue;
-        const float w = wx[dx] * wyz;
-        if (w == 0.f) continue;
-        float* dst = reinterpret_cast<float*>(base + yo + tx);
-        unsafeAtomicAdd(dst, w * val.x);
-        unsafeAtomicAdd(dst + 1, w * val.y);
-      }
-    }
-  }
-}
-
-template <int INTERP>
-__device__ __forceinline__ void scatter2(float2* base, const RefGeom& g, double qx, double qy,
-                                         int xmin, float2 val) {
-  using K = Kern<INTERP>;
-  constexpr int T = K::T;
-  const AxisPos ax = axis_pos(qx, K::OFF), ay = axis_pos(qy, K::OFF);
-  float wx[T], wy[T];
-  K::w(ax.f, wx);
-  K::w(ay.f, wy);
-  const long long rowe = g.xmax + 1;
-#pragma unroll
-  for (int dy = 0; dy < T; ++dy) {
-    const int ty = ay.x0 + dy;
-    if (ty < g.lo || ty > g.hi) continue;
-    const long long yo = (long long)(ty < 0 ? ty + g.N : ty) * rowe;
-#pragma unroll
-    for (int dx = 0; dx < T; ++dx) {
-      const int tx = ax.x0 + dx;
-      if (tx < xmin || tx > g.xmax) continue;
-      const float w = wx[dx] * wy[dy];
-      if (w == 0.f) continue;
-      float* dst = reinterpret_cast<float*>(base + yo + tx);
-      unsafeAtomicAdd(dst, w * val.x);
-      unsafeAtomicAdd(dst + 1, w * val.y);
-    }
-  }
 }
 
 // Does the secondary sum at -m (x-taps >= xmin2) have a tap of nonzero
