@@ -15,9 +15,10 @@
 // part, integer ones are not: contributions are accumulated as int32 fixed
 // point (exact, order independent), with a power-of-two quantum chosen per
 // group of poses from a pre-scan of |G| so the sums cannot overflow, and the
-// group is flushed into fp32 registers.  Bricks near the origin, which every
-// pose crosses, are split over pose chunks and merged with coalesced float
-// atomics; all other bricks are written with plain stores.
+// group is flushed into fp32 registers.  Bricks are split over pose chunks in
+// proportion to the poses expected to cross them (near the origin: all of
+// them); chunks of one brick merge with coalesced float atomics, unsplit
+// bricks are written with plain stores.
 #include "tp_internal.h"
 #include "tp_stencil.h"
 
@@ -27,11 +28,43 @@ namespace {
 
 constexpr int kVox = 4096;          // voxels per brick
 constexpr int kPerThread = kVox / kBlock;
-constexpr int kGroup = 8;           // poses per fixed-point group
+constexpr int kGroupMax = 16;       // poses per fixed-point group
+constexpr int kHitCap = 4096;       // lattice points per group (LDS hit list)
 
 template <int NDIM> struct Brick;
 template <> struct Brick<3> { static constexpr int X = 16, Y = 16, Z = 16; };
 template <> struct Brick<2> { static constexpr int X = 64, Y = 64, Z = 1; };
+
+// LDS slot of brick-local voxel (x, y, z).  Entries are 8 bytes, so only the
+// low 4 bits of the slot pick the bank pair; XOR-ing x with a hash of (y, z)
+// spreads the taps of a wave over the bank pairs.
+template <int NDIM>
+__device__ __forceinline__ int row_hash(int y, int z) {
+  return NDIM == 3 ? ((y + 3 * z) & 15) : ((y * 5) & 63);
+}
+template <int NDIM>
+__device__ __forceinline__ int slot_of(int x, int y, int z) {
+  using BR = Brick<NDIM>;
+  return ((z * BR::Y + y) * BR::X) | (x ^ row_hash<NDIM>(y, z));
+}
+
+// float -> int32, rounding to nearest (ties up): one VALU instruction.
+__device__ __forceinline__ int cvt_rpi(float x) {
+  int r;
+  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// (re, im) int32 pair as one int64, re * 2^32 + im: sums of such values
+// decode uniquely while both component sums stay inside int32.
+__device__ __forceinline__ unsigned long long pack_pair(int re, int im) {
+  const unsigned hi = (unsigned)(re + (im >> 31));
+  return ((unsigned long long)hi << 32) | (unsigned)im;
+}
+__device__ __forceinline__ void unpack_pair(unsigned long long v, int& re, int& im) {
+  im = (int)(unsigned)(v & 0xFFFFFFFFull);
+  re = (int)(long long)((long long)v >> 32) + (im < 0 ? 1 : 0);
+}
 
 struct BrickPos {
   int b;            // batch entry
@@ -42,37 +75,36 @@ struct BrickPos {
   bool valid;
 };
 
+// Pose chunks of a brick.  A random plane through the origin meets a ball of
+// radius rho centred at distance r with probability about rho / r, so bricks
+// near the origin see every pose and outer ones a fraction; each chunk gets
+// about pmax of the poses expected to reach the brick.
+template <int NDIM>
+__device__ __forceinline__ int brick_chunks(const OpParams& p, const BrickParams& bp, int x0, int y0,
+                                            int z0) {
+  using BR = Brick<NDIM>;
+  double frac = 1.0;
+  if (NDIM == 3) {
+    const double cx = x0 + 0.5 * (BR::X - 1), cy = y0 + 0.5 * (BR::Y - 1), cz = z0 + 0.5 * (BR::Z - 1);
+    const double r = sqrt(cx * cx + cy * cy + cz * cz);
+    const double rho = 0.5 * sqrt(3.0) * (BR::X + 4);
+    frac = r > rho ? rho / r : 1.0;
+  }
+  const double c = ceil((double)p.P * frac / (double)bp.pmax);
+  return (int)fmin(fmax(c, 1.0), (double)bp.cmax);
+}
+
 template <int NDIM>
 __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams& bp) {
   using BR = Brick<NDIM>;
   BrickPos r;
-  uint32_t g = xcd_remap(blockIdx.x, gridDim.x);
-  const uint32_t per_b = bp.near_count * bp.chunks + bp.nbricks;
-  r.b = (int)(g / per_b);
-  g %= per_b;
-  int bi, bj, bk;
-  if (g < (uint32_t)(bp.near_count * bp.chunks)) {
-    const int nb = (int)(g / bp.chunks), ch = (int)(g % bp.chunks);
-    bi = bp.near_lo[0] + nb % bp.near_ext[0];
-    bj = bp.near_lo[1] + (nb / bp.near_ext[0]) % bp.near_ext[1];
-    bk = bp.near_lo[2] + nb / (bp.near_ext[0] * bp.near_ext[1]);
-    r.n0 = (int)((long long)p.P * ch / bp.chunks);
-    r.n1 = (int)((long long)p.P * (ch + 1) / bp.chunks);
-    r.chunked = true;
-    r.valid = true;
-  } else {
-    const int f = (int)(g - bp.near_count * bp.chunks);
-    bi = f % bp.nb[0];
-    bj = (f / bp.nb[0]) % bp.nb[1];
-    bk = f / (bp.nb[0] * bp.nb[1]);
-    const bool near = bi >= bp.near_lo[0] && bi < bp.near_lo[0] + bp.near_ext[0] &&
-                      bj >= bp.near_lo[1] && bj < bp.near_lo[1] + bp.near_ext[1] &&
-                      bk >= bp.near_lo[2] && bk < bp.near_lo[2] + bp.near_ext[2];
-    r.valid = !near;
-    r.n0 = 0;
-    r.n1 = p.P;
-    r.chunked = false;
-  }
+  // plain round-robin over the XCDs: consecutive bricks (and the mostly empty
+  // high chunk slots) spread evenly; bricks share little data across XCDs
+  const uint32_t lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int brick = (int)(lin % (uint32_t)bp.nbricks);
+  const int ch = (int)((lin / (uint32_t)bp.nbricks) % (uint32_t)bp.cmax);
+  r.b = (int)(lin / ((uint32_t)bp.nbricks * (uint32_t)bp.cmax));
+  const int bi = brick % bp.nb[0], bj = (brick / bp.nb[0]) % bp.nb[1], bk = brick / (bp.nb[0] * bp.nb[1]);
   const int lo = -(p.N / 2), hi = (p.N + 1) / 2 - 1;
   r.x0 = bi * BR::X;
   r.x1 = min(r.x0 + BR::X - 1, p.N / 2);
@@ -84,17 +116,21 @@ __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams&
   } else {
     r.z0 = r.z1 = 0;
   }
+  const int nch = brick_chunks<NDIM>(p, bp, r.x0, r.y0, r.z0);
+  r.valid = ch < nch;
+  r.chunked = nch > 1;
+  r.n0 = (int)((long long)p.P * ch / nch);
+  r.n1 = (int)((long long)p.P * (ch + 1) / nch);
   return r;
 }
 
 // Everything about one pose that the brick loop needs (uniform values).
 struct PoseView {
   double u[3], v[3];      // p = kx u + ky v
-  double ud[3], vd[3];    // dual basis: kx = p . ud, ky = p . vd (points on the plane)
   float sx, sy;
-  double cell;            // |u x v| (area of the lattice cell), 0 if degenerate
+  float dens;             // max(1, 1 / |u x v|): lattice points per unit area bound
   int kx0, kx1, ky0, ky1; // candidate rectangle (full plane, clipped)
-  bool hit;
+  int hit;
 };
 
 template <int NDIM, int INTERP>
@@ -129,13 +165,14 @@ __device__ __forceinline__ PoseView pose_view(const OpParams& p, const BrickPos&
     pv.kx0 = max(pv.kx0, -c); pv.kx1 = min(pv.kx1, c);
     pv.ky0 = max(pv.ky0, -c); pv.ky1 = min(pv.ky1, c);
   }
-  pv.hit = true;
-  pv.cell = 0.0;
+  pv.hit = 1;
+  pv.dens = 1e30f;
   if (D > 0.0 && isfinite(D)) {
-    pv.cell = sqrt(D);
+    pv.dens = (float)fmax(1.0, 1.0 / sqrt(D));
+    double ud[3], vd[3];  // dual basis: kx = p . ud, ky = p . vd for points on the plane
     for (int j = 0; j < 3; ++j) {
-      pv.ud[j] = (vv * pv.u[j] - uv * pv.v[j]) / D;
-      pv.vd[j] = (uu * pv.v[j] - uv * pv.u[j]) / D;
+      ud[j] = (vv * pv.u[j] - uv * pv.v[j]) / D;
+      vd[j] = (uu * pv.v[j] - uv * pv.u[j]) / D;
     }
     // plane through the origin with normal u x v must cross the box
     double nrm[3] = {pv.u[1] * pv.v[2] - pv.u[2] * pv.v[1], pv.u[2] * pv.v[0] - pv.u[0] * pv.v[2],
@@ -145,74 +182,93 @@ __device__ __forceinline__ PoseView pose_view(const OpParams& p, const BrickPos&
       const double a = lo[j] * nrm[j], b = hi[j] * nrm[j];
       mn += fmin(a, b);
       mx += fmax(a, b);
-      const double xa = lo[j] * pv.ud[j], xb = hi[j] * pv.ud[j];
+      const double xa = lo[j] * ud[j], xb = hi[j] * ud[j];
       kmin[0] += fmin(xa, xb);
       kmax[0] += fmax(xa, xb);
-      const double ya = lo[j] * pv.vd[j], yb = hi[j] * pv.vd[j];
+      const double ya = lo[j] * vd[j], yb = hi[j] * vd[j];
       kmin[1] += fmin(ya, yb);
       kmax[1] += fmax(ya, yb);
     }
     const double slack = 1e-9 * (fabs(mn) + fabs(mx) + 1.0);
-    if (NDIM == 3 && (mn > slack || mx < -slack)) pv.hit = false;
+    if (NDIM == 3 && (mn > slack || mx < -slack)) pv.hit = 0;
     if (fabs(kmin[0]) < 1e9 && fabs(kmax[0]) < 1e9 && fabs(kmin[1]) < 1e9 && fabs(kmax[1]) < 1e9) {
       pv.kx0 = max(pv.kx0, (int)floor(kmin[0]) - 1);
       pv.kx1 = min(pv.kx1, (int)ceil(kmax[0]) + 1);
       pv.ky0 = max(pv.ky0, (int)floor(kmin[1]) - 1);
       pv.ky1 = min(pv.ky1, (int)ceil(kmax[1]) + 1);
     }
-  } else {
-    // degenerate rows: no dual basis; visit the whole clipped plane
-    for (int j = 0; j < 3; ++j) pv.ud[j] = pv.vd[j] = 0.0;
-  }
+  }  // degenerate rows: no dual basis; visit the whole clipped plane
   if (!(isfinite(pv.u[0]) && isfinite(pv.u[1]) && isfinite(pv.u[2]) && isfinite(pv.v[0]) &&
         isfinite(pv.v[1]) && isfinite(pv.v[2])))
-    pv.hit = false;
-  if (pv.kx0 > pv.kx1 || pv.ky0 > pv.ky1) pv.hit = false;
+    pv.hit = 0;
+  if (pv.kx0 > pv.kx1 || pv.ky0 > pv.ky1) pv.hit = 0;
   return pv;
 }
 
-// One lattice point of the full plane: its sample point and the values it
-// spreads (real part on x >= 0, real + mirror on x >= 1).  false if it
-// carries nothing or its stencil misses the brick.
-struct Cand {
-  double q[3];
-  float2 v0;   // value for taps at x = 0
-  float2 v1;   // value for taps at x >= 1
-};
-
-template <int NDIM, int INTERP>
-__device__ __forceinline__ bool candidate(const OpParams& p, const BrickPos& br, const PoseView& pv,
-                                          int n, int kx, int ky, bool want_values, Cand& cd,
-                                          float& amax) {
-  if (p.cut2 >= 0 && (long long)kx * kx + (long long)ky * ky > p.cut2) return false;
+// A lattice point (kx, ky) of the full plane carries the real output (kx, ky)
+// when kx >= 0 and the mirror of the real output (-kx, -ky) when kx <= 0.
+__device__ __forceinline__ void lattice_parts(const OpParams& p, int kx, int ky, bool& real, bool& mirr) {
   const int rlo = -(p.No / 2), rhi = (p.No - 1) / 2;
-  const bool real = kx >= 0 && kx <= p.No / 2 && ky >= rlo && ky <= rhi;
-  const bool mirr = kx <= 0 && -kx <= p.No / 2 && -ky >= rlo && -ky <= rhi;
+  real = kx >= 0 && kx <= p.No / 2 && ky >= rlo && ky <= rhi;
+  mirr = kx <= 0 && -kx <= p.No / 2 && -ky >= rlo && -ky <= rhi;
+}
+
+__device__ __forceinline__ size_t out_index(const OpParams& p, size_t img, int kx, int ky) {
+  return (img * p.No + (ky < 0 ? ky + p.No : ky)) * p.Wo + kx;
+}
+
+// Phase A: does the lattice point reach the brick?  Tracks max |G| read.
+template <int NDIM, int INTERP>
+__device__ __forceinline__ bool lattice_hit(const OpParams& p, const BrickPos& br, const PoseView& pv,
+                                            int n, int kx, int ky, float& amax) {
+  if (p.cut2 >= 0 && (long long)kx * kx + (long long)ky * ky > p.cut2) return false;
+  bool real, mirr;
+  lattice_parts(p, kx, ky, real, mirr);
   if (!real && !mirr) return false;
   constexpr double reach = INTERP ? 2.0 : 1.0;
   const double lo[3] = {br.x0 - reach, br.y0 - reach, br.z0 - reach};
   const double hi[3] = {br.x1 + reach, br.y1 + reach, br.z1 + reach};
-  bool in = true;
 #pragma unroll
   for (int j = 0; j < NDIM; ++j) {
-    cd.q[j] = (double)kx * pv.u[j] + (double)ky * pv.v[j];
-    in = in && cd.q[j] >= lo[j] && cd.q[j] < hi[j];
+    const double q = (double)kx * pv.u[j] + (double)ky * pv.v[j];
+    if (!(q >= lo[j] && q < hi[j])) return false;
   }
-  if (!in) return false;
   const size_t img = (size_t)br.b * p.P + n;
-  float2 gr = make_float2(0.f, 0.f), gm = gr;
-  if (real) gr = p.img[(img * p.No + (ky < 0 ? ky + p.No : ky)) * p.Wo + kx];
-  if (mirr) gm = p.img[(img * p.No + (-ky < 0 ? -ky + p.No : -ky)) * p.Wo + (-kx)];
-  amax = fmaxf(amax, fmaxf(fabsf(gr.x) + fabsf(gr.y), fabsf(gm.x) + fabsf(gm.y)));
-  if (!want_values) return true;
-  float2 cr = gr, cm = gm;
-  if (p.shift) {
-    if (real) cr = cmul(conjf2(shift_phase(kx, ky, pv.sx, pv.sy, p.inv_no)), gr);
-    if (mirr) cm = cmul(conjf2(shift_phase(-kx, -ky, pv.sx, pv.sy, p.inv_no)), gm);
+  if (real) {
+    const float2 g = p.img[out_index(p, img, kx, ky)];
+    amax = fmaxf(amax, fabsf(g.x) + fabsf(g.y));
   }
-  cd.v0 = cr;                                                      // real only
-  cd.v1 = make_float2(cr.x + cm.x, cr.y - cm.y);                   // real + conj(mirror)
+  if (mirr) {
+    const float2 g = p.img[out_index(p, img, -kx, -ky)];
+    amax = fmaxf(amax, fabsf(g.x) + fabsf(g.y));
+  }
   return true;
+}
+
+// Phase B: sample point and the values spread by a lattice point that hit.
+struct Cand {
+  double q[3];
+  float2 v0;   // value for taps at x = 0 (real part only)
+  float2 v1;   // value for taps at x >= 1 (real + conj(mirror))
+};
+
+template <int NDIM>
+__device__ __forceinline__ void lattice_values(const OpParams& p, const BrickPos& br, const PoseView& pv,
+                                               int n, int kx, int ky, Cand& cd) {
+  bool real, mirr;
+  lattice_parts(p, kx, ky, real, mirr);
+#pragma unroll
+  for (int j = 0; j < NDIM; ++j) cd.q[j] = (double)kx * pv.u[j] + (double)ky * pv.v[j];
+  const size_t img = (size_t)br.b * p.P + n;
+  float2 cr = make_float2(0.f, 0.f), cm = cr;
+  if (real) cr = p.img[out_index(p, img, kx, ky)];
+  if (mirr) cm = p.img[out_index(p, img, -kx, -ky)];
+  if (p.shift) {
+    if (real) cr = cmul(conjf2(shift_phase(kx, ky, pv.sx, pv.sy, p.inv_no)), cr);
+    if (mirr) cm = cmul(conjf2(shift_phase(-kx, -ky, pv.sx, pv.sy, p.inv_no)), cm);
+  }
+  cd.v0 = cr;
+  cd.v1 = make_float2(cr.x + cm.x, cr.y - cm.y);
 }
 
 template <int NDIM, int INTERP>
@@ -220,11 +276,14 @@ __global__ __launch_bounds__(kBlock) void k_adjoint_bricks(OpParams p, BrickPara
   using BR = Brick<NDIM>;
   using K = Kern<INTERP>;
   constexpr int T = K::T;
-  __shared__ int acc[2][kVox];
+  __shared__ unsigned long long acc[kVox];
+  __shared__ uint32_t s_hits[kHitCap];
   __shared__ int s_poses[kBlock];
-  __shared__ PoseView s_view[kGroup];
+  __shared__ int s_area[kBlock];
+  __shared__ PoseView s_view[kGroupMax];
   __shared__ int s_wcnt[kBlock / 64];
   __shared__ float s_red[kBlock / 64];
+  __shared__ int s_nhit;
 
   const BrickPos br = decode<NDIM>(p, bp);
   if (!br.valid) return;
@@ -234,15 +293,18 @@ __global__ __launch_bounds__(kBlock) void k_adjoint_bricks(OpParams p, BrickPara
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     fre[i] = fim[i] = 0.f;
-    acc[0][tid + i * kBlock] = 0;
-    acc[1][tid + i * kBlock] = 0;
+    acc[tid + i * kBlock] = 0ull;
   }
-  const int lx = tid % 16, ly = tid / 16;  // 16x16 thread grid over candidate rectangles
 
   for (int w0 = br.n0; w0 < br.n1; w0 += kBlock) {
     // one pose per thread: does its plane reach this brick?  ordered compaction
     const int n = w0 + tid;
-    const bool hit = n < br.n1 && pose_view<NDIM, INTERP>(p, br, n).hit;
+    int area = 0;
+    if (n < br.n1) {
+      const PoseView pv = pose_view<NDIM, INTERP>(p, br, n);
+      if (pv.hit) area = (pv.kx1 - pv.kx0 + 1) * (pv.ky1 - pv.ky0 + 1);
+    }
+    const bool hit = area > 0;
     const unsigned long long m = __ballot(hit);
     __syncthreads();
     if (lane == 0) s_wcnt[wave] = __popcll(m);
@@ -253,28 +315,50 @@ __global__ __launch_bounds__(kBlock) void k_adjoint_bricks(OpParams p, BrickPara
       off += w < wave ? s_wcnt[w] : 0;
       total += s_wcnt[w];
     }
-    if (hit) s_poses[off + __popcll(m & ((1ull << lane) - 1ull))] = n;
+    if (hit) {
+      const int slot = off + __popcll(m & ((1ull << lane) - 1ull));
+      s_poses[slot] = n;
+      s_area[slot] = area;
+    }
     __syncthreads();
 
-    for (int g0 = 0; g0 < total; g0 += kGroup) {
-      const int cnt = min(kGroup, total - g0);
+    // groups: whole poses whose rectangles fit the hit list, or one slice of
+    // a single pose's rectangle
+    int g0 = 0, r0 = 0;
+    while (g0 < total) {
+      int g1 = g0 + 1, f0 = 0, f1;
+      if (r0 > 0 || s_area[g0] > kHitCap) {
+        f0 = r0;
+        f1 = min(r0 + kHitCap, s_area[g0]);
+      } else {
+        int sum = s_area[g0];
+        while (g1 < total && g1 - g0 < kGroupMax && sum + s_area[g1] <= kHitCap) sum += s_area[g1++];
+        f1 = s_area[g0];
+      }
+      const int cnt = g1 - g0;
       if (tid < cnt) s_view[tid] = pose_view<NDIM, INTERP>(p, br, s_poses[g0 + tid]);
+      if (tid == 0) s_nhit = 0;
       __syncthreads();
 
-      // pre-scan: bound on the group's contributions -> fixed-point quantum.
-      // Per pose and voxel, sum |w| over the lattice <= 4 / cell and every
-      // value is <= 2 max|G|.
+      // phase A: compact the lattice points that reach the brick; max |G|
       float amax = 0.f;
-      double dens_sum = 0.0;
+      float dens_sum = 0.f;
       for (int g = 0; g < cnt; ++g) {
         const PoseView& pv = s_view[g];
         const int pn = s_poses[g0 + g];
-        dens_sum += 8.0 * (pv.cell > 0.0 ? fmax(1.0, 1.0 / pv.cell) : 1e30);
-        for (int ky = pv.ky0 + ly; ky <= pv.ky1; ky += 16)
-          for (int kx = pv.kx0 + lx; kx <= pv.kx1; kx += 16) {
-            Cand cd;
-            candidate<NDIM, INTERP>(p, br, pv, pn, kx, ky, false, cd, amax);
+        dens_sum += pv.dens;
+        const int W = pv.kx1 - pv.kx0 + 1;
+        const float invW = 1.f / (float)W;
+        const int a0 = cnt == 1 ? f0 : 0, a1 = cnt == 1 ? f1 : (pv.kx1 - pv.kx0 + 1) * (pv.ky1 - pv.ky0 + 1);
+        for (int i = a0 + tid; i < a1; i += kBlock) {
+          int dky = (int)(((float)i + 0.5f) * invW);
+          int dkx = i - dky * W;
+          if (dkx < 0) { --dky; dkx += W; } else if (dkx >= W) { ++dky; dkx -= W; }
+          if (lattice_hit<NDIM, INTERP>(p, br, pv, pn, pv.kx0 + dkx, pv.ky0 + dky, amax)) {
+            const int slot = atomicAdd(&s_nhit, 1);
+            s_hits[slot] = ((uint32_t)g << 24) | ((uint32_t)dky << 12) | (uint32_t)dkx;
           }
+        }
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
@@ -283,80 +367,89 @@ __global__ __launch_bounds__(kBlock) void k_adjoint_bricks(OpParams p, BrickPara
       float gmax = s_red[0];
 #pragma unroll
       for (int w = 1; w < kBlock / 64; ++w) gmax = fmaxf(gmax, s_red[w]);
-      const float gb = (float)fmin(dens_sum * (double)gmax, 1e30);
-      if (gb > 0.f) {
-        // quantum q = 2^e with |sum| <= gb / q < 2^29
+      const int nh = s_nhit;
+      // per pose and voxel: sum |w| over the lattice <= 4 dens, |value| <= 2 max|G|
+      const float gb = fminf(8.f * dens_sum * gmax, 1e30f);
+      if (nh > 0 && gb > 0.f) {
         int e;
-        frexpf(gb, &e);  // gb < 2^e
+        frexpf(gb, &e);  // gb < 2^e: |sum| <= gb / q < 2^29
         const float inv_q = ldexpf(1.f, 29 - e);
         const float q = ldexpf(1.f, e - 29);
 
-        for (int g = 0; g < cnt; ++g) {
+        // phase B: spread every hit over its taps inside the brick
+        for (int i = tid; i < nh; i += kBlock) {
+          const uint32_t h = s_hits[i];
+          const int g = (int)(h >> 24);
           const PoseView& pv = s_view[g];
-          const int pn = s_poses[g0 + g];
-          for (int ky = pv.ky0 + ly; ky <= pv.ky1; ky += 16)
-            for (int kx = pv.kx0 + lx; kx <= pv.kx1; kx += 16) {
-              Cand cd;
-              float dummy = 0.f;
-              if (!candidate<NDIM, INTERP>(p, br, pv, pn, kx, ky, true, cd, dummy)) continue;
-              const AxisPos ax = axis_pos(cd.q[0], K::OFF), ay = axis_pos(cd.q[1], K::OFF);
-              float wx[T], wy[T], wz[T];
-              K::w(ax.f, wx);
-              K::w(ay.f, wy);
-              int z0 = 0;
-              if (NDIM == 3) {
-                const AxisPos az = axis_pos(cd.q[2], K::OFF);
-                K::w(az.f, wz);
-                z0 = az.x0;
-              } else {
+          Cand cd;
+          lattice_values<NDIM>(p, br, pv, s_poses[g0 + g], pv.kx0 + (int)(h & 0xFFFu),
+                               pv.ky0 + (int)((h >> 12) & 0xFFFu), cd);
+          const AxisPos ax = axis_pos(cd.q[0], K::OFF), ay = axis_pos(cd.q[1], K::OFF);
+          float wx[T], wy[T], wz[T];
+          K::w(ax.f, wx);
+          K::w(ay.f, wy);
+          int z0 = 0;
+          if (NDIM == 3) {
+            const AxisPos az = axis_pos(cd.q[2], K::OFF);
+            K::w(az.f, wz);
+            z0 = az.x0;
+          } else {
 #pragma unroll
-                for (int d = 0; d < T; ++d) wz[d] = d == 0 ? 1.f : 0.f;
-              }
-              // x weights folded with the per-x value (x = 0 takes the real part only)
-              float are[T], aim[T];
+            for (int d = 0; d < T; ++d) wz[d] = d == 0 ? 1.f : 0.f;
+          }
+          // x weights folded with the per-x value (x = 0 takes the real part
+          // only); taps outside the brick get weight 0 and a clamped slot
+          float are[T], aim[T];
+          int xl[T];
 #pragma unroll
-              for (int d = 0; d < T; ++d) {
-                const int tx = ax.x0 + d;
-                const float2 v = tx >= 1 ? cd.v1 : cd.v0;
-                const bool inx = tx >= br.x0 && tx <= br.x1;
-                are[d] = inx ? wx[d] * v.x * inv_q : 0.f;
-                aim[d] = inx ? wx[d] * v.y * inv_q : 0.f;
-              }
+          for (int d = 0; d < T; ++d) {
+            const int tx = ax.x0 + d;
+            const float2 v = tx >= 1 ? cd.v1 : cd.v0;
+            const bool inx = tx >= br.x0 && tx <= br.x1;
+            are[d] = inx ? wx[d] * v.x * inv_q : 0.f;
+            aim[d] = inx ? wx[d] * v.y * inv_q : 0.f;
+            xl[d] = inx ? tx - br.x0 : 0;
+          }
 #pragma unroll
-              for (int dz = 0; dz < (NDIM == 3 ? T : 1); ++dz) {
-                const int tz = z0 + dz;
-                if (NDIM == 3 && (tz < br.z0 || tz > br.z1)) continue;
+          for (int dz = 0; dz < (NDIM == 3 ? T : 1); ++dz) {
+            const int tz = z0 + dz;
+            if (NDIM == 3 && (tz < br.z0 || tz > br.z1)) continue;
 #pragma unroll
-                for (int dy = 0; dy < T; ++dy) {
-                  const int ty = ay.x0 + dy;
-                  if (ty < br.y0 || ty > br.y1) continue;
-                  const float wyz = wy[dy] * wz[dz];
-                  const int base = (((NDIM == 3 ? tz - br.z0 : 0) * BR::Y) + (ty - br.y0)) * BR::X +
-                                   (ax.x0 - br.x0);
+            for (int dy = 0; dy < T; ++dy) {
+              const int ty = ay.x0 + dy;
+              if (ty < br.y0 || ty > br.y1) continue;
+              const float wyz = wy[dy] * wz[dz];
+              const int yl = ty - br.y0, zl = NDIM == 3 ? tz - br.z0 : 0;
+              const int row = (zl * BR::Y + yl) * BR::X, h = row_hash<NDIM>(yl, zl);
 #pragma unroll
-                  for (int dx = 0; dx < T; ++dx) {
-                    const int ir = (int)rintf(are[dx] * wyz), ii = (int)rintf(aim[dx] * wyz);
-                    if ((ir | ii) != 0) {
-                      atomicAdd(&acc[0][base + dx], ir);
-                      atomicAdd(&acc[1][base + dx], ii);
-                    }
-                  }
-                }
+              for (int dx = 0; dx < T; ++dx) {
+                const int ir = cvt_rpi(are[dx] * wyz), ii = cvt_rpi(aim[dx] * wyz);
+                atomicAdd(&acc[row | (xl[dx] ^ h)], pack_pair(ir, ii));
               }
             }
+          }
         }
         // flush the group into fp32 registers
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i) {
           const int v = tid + i * kBlock;
-          fre[i] = fmaf((float)acc[0][v], q, fre[i]);
-          fim[i] = fmaf((float)acc[1][v], q, fim[i]);
-          acc[0][v] = 0;
-          acc[1][v] = 0;
+          const int sl = slot_of<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
+          int ir, ii;
+          unpack_pair(acc[sl], ir, ii);
+          fre[i] = fmaf((float)ir, q, fre[i]);
+          fim[i] = fmaf((float)ii, q, fim[i]);
+          acc[sl] = 0ull;
         }
       }
       __syncthreads();
+      // next group
+      if (cnt == 1 && f1 < s_area[g0]) {
+        r0 = f1;
+      } else {
+        g0 = g1;
+        r0 = 0;
+      }
     }
   }
 
@@ -388,42 +481,24 @@ template <int NDIM>
 static BrickParams brick_params(const OpParams& p) {
   using BR = Brick<NDIM>;
   BrickParams bp{};
-  const int lo = -(p.N / 2);
   bp.nb[0] = (p.N / 2 + 1 + BR::X - 1) / BR::X;
   bp.nb[1] = (p.N + BR::Y - 1) / BR::Y;
   bp.nb[2] = NDIM == 3 ? (p.N + BR::Z - 1) / BR::Z : 1;
   bp.nbricks = bp.nb[0] * bp.nb[1] * bp.nb[2];
-  // bricks next to the origin are crossed by every pose: split their poses
-  const int jo = (0 - lo) / BR::Y;  // brick holding y = 0
-  int nlo[3] = {0, jo - 2, NDIM == 3 ? jo - 2 : 0};
-  int nhi[3] = {2, jo + 2, NDIM == 3 ? jo + 2 : 1};
-  if (NDIM == 2) { nhi[0] = 1; nlo[1] = jo - 1; nhi[1] = jo + 1; }
-  bp.near_count = 1;
-  for (int j = 0; j < 3; ++j) {
-    nlo[j] = nlo[j] < 0 ? 0 : nlo[j];
-    nhi[j] = nhi[j] > bp.nb[j] ? bp.nb[j] : nhi[j];
-    bp.near_lo[j] = nlo[j];
-    bp.near_ext[j] = nhi[j] > nlo[j] ? nhi[j] - nlo[j] : 0;
-    bp.near_count *= bp.near_ext[j];
-  }
-  int chunks = (p.P + 255) / 256;  // about 256 poses per chunk
-  bp.chunks = chunks < 1 ? 1 : (chunks > 32 ? 32 : chunks);
-  if (bp.chunks == 1 || bp.near_count == 0) {  // nothing to split
-    bp.chunks = 1;
-    bp.near_count = 0;
-    for (int j = 0; j < 3; ++j) bp.near_ext[j] = 0;
-  }
+  bp.pmax = 256;
+  const int c = (p.P + bp.pmax - 1) / bp.pmax;
+  bp.cmax = c < 1 ? 1 : (c > 64 ? 64 : c);
   return bp;
 }
 
 uint64_t adjoint_blocks(const OpParams& p) {
   const BrickParams bp = p.ndim == 3 ? brick_params<3>(p) : brick_params<2>(p);
-  return (uint64_t)p.B * ((uint64_t)bp.near_count * bp.chunks + bp.nbricks);
+  return (uint64_t)p.B * (uint64_t)bp.nbricks * (uint64_t)bp.cmax;
 }
 
 hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s) {
   const BrickParams bp = p.ndim == 3 ? brick_params<3>(p) : brick_params<2>(p);
-  const dim3 grid((unsigned)adjoint_blocks(p)), block(kBlock);
+  const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kBlock);
   if (p.ndim == 3) {
     if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1>), grid, block, 0, s, p, bp);
     else hipLaunchKernelGGL((k_adjoint_bricks<3, 0>), grid, block, 0, s, p, bp);

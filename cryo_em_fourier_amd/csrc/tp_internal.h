@@ -30,10 +30,8 @@ struct OpParams {
 struct BrickParams {
   int nb[3];          // bricks along x, y, z
   int nbricks;
-  int near_lo[3];     // box of bricks next to the origin, split over pose chunks
-  int near_ext[3];
-  int near_count;
-  int chunks;         // pose chunks of a near brick
+  int cmax;           // pose-chunk slots per brick (grid y)
+  int pmax;           // target poses per chunk
 };
 
 // Output tile of one workgroup: TX kx-columns x TY ky-rows.

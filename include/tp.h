@@ -57,11 +57,16 @@
  *                    bad interp, oversampling <= 0 or not finite, cutoff NaN,
  *                    B_rot or B_shift not in {1, B}, ndim not in {2, 3};
  *   TP_EUNSUPPORTED  a reference entry larger than 2^31 - 4096 bytes, a box
- *                    above 65535, or a launch grid above 2^31 - 1 blocks;
+ *                    above 65535 (N_out above 4095 for the adjoints), or a
+ *                    launch grid above 2^31 - 1 blocks;
  *   TP_EHIP          the HIP runtime reported an error at launch.
  *   Nothing is thrown across the ABI.
- * Results.  Forward and pose gradients are deterministic.  The adjoint
- *   accumulates with float atomics, so its last bits may differ between runs.
+ * Results.  Forward and pose gradients are deterministic up to the order of
+ *   float atomics that merge per-workgroup partial sums of the pose
+ *   gradients.  The adjoint sums each brick's contributions exactly in
+ *   int32 fixed point (quantum <= 2^-22 of the largest |proj| a group of
+ *   poses reads) and merges a few pose chunks next to the origin with float
+ *   atomics, so its last bits there may differ between runs.
  */
 #ifndef TP_H
 #define TP_H
