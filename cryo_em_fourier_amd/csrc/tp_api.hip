@@ -42,8 +42,9 @@ tp_status check_and_fill(const Common& c, tp::OpParams& p) {
   const uint64_t elems = (c.ndim == 3 ? (uint64_t)c.N * (uint64_t)c.N : (uint64_t)c.N) * wh;
   if (elems * 8ull > kMaxRefBytes) return TP_EUNSUPPORTED;
   const int64_t wo = c.N_out / 2 + 1;
+  const int64_t tile_y = c.ndim == 3 ? tp::kTileYPairs : tp::kTileY;
   const int64_t tx = (wo + tp::kTileX - 1) / tp::kTileX;
-  const int64_t ty = (c.N_out + tp::kTileY - 1) / tp::kTileY;
+  const int64_t ty = (c.N_out + tile_y - 1) / tile_y;
   const uint64_t blocks = (uint64_t)c.B * (uint64_t)c.P * (uint64_t)(tx * ty);
   if (blocks > kMaxBlocks) return TP_EUNSUPPORTED;
 
@@ -71,6 +72,7 @@ tp_status check_and_fill(const Common& c, tp::OpParams& p) {
   p.tiles_x = (int)tx;
   p.tiles_y = (int)ty;
   p.tiles_per_pose = (int)(tx * ty);
+  p.tile_y = (int)tile_y;
   p.nblocks = (uint32_t)blocks;
   return TP_OK;
 }

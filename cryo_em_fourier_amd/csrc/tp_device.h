@@ -143,6 +143,31 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
 }
 __device__ __forceinline__ float2 conjf2(float2 a) { return make_float2(a.x, -a.y); }
 
+// Wave sum of eight doubles by halving: each exchange step sends half of the
+// values still held, so 10 shuffles replace 8 x 6.  On return lane l holds the
+// total of value 4*bit5(l) + 2*bit4(l) + bit3(l).
+__device__ __forceinline__ double wave_sum8(const double* a) {
+  const int lane = threadIdx.x & 63;
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+  double b[4], c[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const double send = b5 ? a[k] : a[k + 4], keep = b5 ? a[k + 4] : a[k];
+    b[k] = keep + __shfl_xor(send, 32, 64);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const double send = b4 ? b[k] : b[k + 2], keep = b4 ? b[k + 2] : b[k];
+    c[k] = keep + __shfl_xor(send, 16, 64);
+  }
+  const double send = b3 ? c[0] : c[1], keep = b3 ? c[1] : c[0];
+  double d = keep + __shfl_xor(send, 8, 64);
+  d += __shfl_xor(d, 4, 64);
+  d += __shfl_xor(d, 2, 64);
+  d += __shfl_xor(d, 1, 64);
+  return d;
+}
+
 // Signed frequency of row index iy of an n-row rfft image.
 __device__ __forceinline__ int signed_row(int iy, int n) { return iy <= (n - 1) / 2 ? iy : iy - n; }
 

@@ -23,6 +23,7 @@ struct OpParams {
   long long ref_elems;    // complex elements of one reference entry
   double inv_no;          // 1 / No
   int tiles_x, tiles_y, tiles_per_pose;
+  int tile_y;             // ky-rows per tile (kTileY, or kTileYPairs for the paired 3D kernels)
   uint32_t nblocks;
 };
 
@@ -34,9 +35,11 @@ struct BrickParams {
   int pmax;           // target poses per chunk
 };
 
-// Output tile of one workgroup: TX kx-columns x TY ky-rows.
+// Output tile of one workgroup: TX kx-columns x TY ky-rows (one lane per
+// output), or TX x kTileYPairs with two lanes per output (3D kernels).
 constexpr int kTileX = 16;
 constexpr int kTileY = 16;
+constexpr int kTileYPairs = 8;
 
 hipError_t launch_project(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s);

@@ -20,6 +20,8 @@ struct Out {
   bool keep;  // inside the cutoff
 };
 
+// PAIRS: two lanes per output (lane pair = output threadIdx.x / 2).
+template <bool PAIRS = false>
 __device__ __forceinline__ Out locate(const OpParams& p) {
   Out o;
   const uint32_t g = xcd_remap(blockIdx.x, gridDim.x);
@@ -27,8 +29,9 @@ __device__ __forceinline__ Out locate(const OpParams& p) {
   const uint32_t bn = g / (uint32_t)p.tiles_per_pose;
   o.n = (int)(bn % (uint32_t)p.P);
   o.b = (int)(bn / (uint32_t)p.P);
-  o.kx = (int)(tile % (uint32_t)p.tiles_x) * kTileX + (int)(threadIdx.x % kTileX);
-  o.iy = (int)(tile / (uint32_t)p.tiles_x) * kTileY + (int)(threadIdx.x / kTileX);
+  const int oi = PAIRS ? (int)(threadIdx.x >> 1) : (int)threadIdx.x;
+  o.kx = (int)(tile % (uint32_t)p.tiles_x) * kTileX + oi % kTileX;
+  o.iy = (int)(tile / (uint32_t)p.tiles_x) * p.tile_y + oi / kTileX;
   o.in = o.kx < p.Wo && o.iy < p.No;
   o.ky = signed_row(o.iy, p.No);
   const long long k2 = (long long)o.kx * o.kx + (long long)o.ky * o.ky;
@@ -172,14 +175,16 @@ __global__ __launch_bounds__(kBlock) void k_grad_pose(OpParams p) {
     acc[2 * NDIM + 1] = two_pi_over_n * o.ky * im_gs;
   }
   // workgroup reduction in fp64: wave shuffles, then LDS across the 4 waves
-  __shared__ double red[kBlock / 64][NV];
+  __shared__ double red[kBlock / 64][8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (__ballot(o.keep) != 0ull) {
+    double a8[8];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    double v = acc[i];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    if (lane == 0) red[wave][i] = v;
+    for (int i = 0; i < 8; ++i) a8[i] = i < NV ? acc[i] : 0.0;
+    const double d = wave_sum8(a8);
+    if ((lane & 7) == 0) red[wave][lane >> 3] = d;
+  } else if (lane < 8) {
+    red[wave][lane] = 0.0;
   }
   __syncthreads();
   if (threadIdx.x < NV) {
@@ -199,6 +204,127 @@ __global__ __launch_bounds__(kBlock) void k_grad_pose(OpParams p) {
     } else if (p.grad_shift) {
       const size_t bs = p.B_shift == 1 ? 0 : (size_t)b;
       unsafeAtomicAdd(p.grad_shift + (bs * p.P + n) * 2 + (i - 2 * NDIM), (float)v);
+    }
+  }
+}
+
+// ------------------------------------------------- 3D with two lanes per output
+
+template <int INTERP>
+__global__ __launch_bounds__(kBlock) void k_project3p(OpParams p) {
+  const Out o = locate<true>(p);
+  const int h = threadIdx.x & 1;
+  double q[3] = {0.0, 0.0, 0.0};
+  const bool active = o.keep && sample_point<3>(p, o, q);
+  float2 res = make_float2(0.f, 0.f);
+  if (active) {
+    const RefGeom g = ref_geom(p);
+    const rsrc_t rs = make_rsrc(p.ref + (size_t)o.b * p.ref_elems, p.ref_bytes);
+    const bool c = q[0] < 0.0;
+    double m[3], mneg[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      m[j] = c ? -q[j] : q[j];
+      mneg[j] = -m[j];
+    }
+    const int xmin1 = c ? 1 : 0, xmin2 = c ? 0 : 1;
+    const float2 mv = gather3_half<INTERP>(rs, g, m[0], m[1], m[2], xmin1, h);
+    float2 sv = make_float2(0.f, 0.f);
+    if (needs_secondary<INTERP>(m[0], xmin2)) sv = gather3_half<INTERP>(rs, g, mneg[0], mneg[1], mneg[2], xmin2, h);
+    res = c ? make_float2(mv.x + sv.x, sv.y - mv.y) : make_float2(mv.x + sv.x, mv.y - sv.y);
+  }
+  res = pair_sum(res);  // both lanes of a pair share `active`
+  if (!o.in || h) return;
+  if (active && p.shift) {
+    const float2 s = pose_shift(p, o);
+    res = cmul(shift_phase(o.kx, o.ky, s.x, s.y, p.inv_no), res);
+  }
+  p.img_out[img_index(p, o)] = res;
+}
+
+template <int INTERP>
+__global__ __launch_bounds__(kBlock) void k_grad3p(OpParams p) {
+  constexpr int NV = 8;  // dR rows 0 and 1, then ds_x, ds_y
+  __shared__ double red[kBlock / 64][NV];
+  const Out o = locate<true>(p);
+  const int h = threadIdx.x & 1;
+  double q[3] = {0.0, 0.0, 0.0};
+  const bool active = o.keep && sample_point<3>(p, o, q);
+  const bool c = active && q[0] < 0.0;
+  float2 S = make_float2(0.f, 0.f), dS[3] = {S, S, S};
+  if (active) {
+    const RefGeom g = ref_geom(p);
+    const rsrc_t rs = make_rsrc(p.ref + (size_t)o.b * p.ref_elems, p.ref_bytes);
+    double m[3], mneg[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      m[j] = c ? -q[j] : q[j];
+      mneg[j] = -m[j];
+    }
+    const int xmin1 = c ? 1 : 0, xmin2 = c ? 0 : 1;
+    float2 mv[4], sv[4];
+    gather3_grad_half<INTERP>(rs, g, m[0], m[1], m[2], xmin1, h, mv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sv[j] = make_float2(0.f, 0.f);
+    if (needs_secondary<INTERP>(m[0], xmin2)) gather3_grad_half<INTERP>(rs, g, mneg[0], mneg[1], mneg[2], xmin2, h, sv);
+    // S and dS/dp (chain rule through m = +-p, see tp_device.h); linear in the halves
+    if (c) {
+      S = make_float2(mv[0].x + sv[0].x, sv[0].y - mv[0].y);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) dS[j] = make_float2(sv[j + 1].x - mv[j + 1].x, sv[j + 1].y + mv[j + 1].y);
+    } else {
+      S = make_float2(mv[0].x + sv[0].x, mv[0].y - sv[0].y);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) dS[j] = make_float2(mv[j + 1].x - sv[j + 1].x, mv[j + 1].y + sv[j + 1].y);
+    }
+  }
+  S = pair_sum(S);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) dS[j] = pair_sum(dS[j]);
+  double acc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = 0.0;
+  if (active && h == 0) {
+    const float2 G = p.img[img_index(p, o)];
+    float2 gph = conjf2(G);
+    if (p.shift) {
+      const float2 s = pose_shift(p, o);
+      gph = cmul(gph, shift_phase(o.kx, o.ky, s.x, s.y, p.inv_no));
+    }
+    const double os = (double)p.os;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const double dldp = (double)gph.x * dS[j].x - (double)gph.y * dS[j].y;
+      acc[j] = os * o.kx * dldp;
+      acc[3 + j] = os * o.ky * dldp;
+    }
+    const double im_gs = (double)gph.x * S.y + (double)gph.y * S.x;
+    const double two_pi_over_n = 6.283185307179586476925 * p.inv_no;
+    acc[6] = two_pi_over_n * o.kx * im_gs;
+    acc[7] = two_pi_over_n * o.ky * im_gs;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (__ballot(active) != 0ull) {
+    const double d = wave_sum8(acc);
+    if ((lane & 7) == 0) red[wave][lane >> 3] = d;
+  } else if (lane < NV) {
+    red[wave][lane] = 0.0;
+  }
+  __syncthreads();
+  if (threadIdx.x < NV) {
+    const int i = threadIdx.x;
+    double v = 0.0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) v += red[w][i];
+    if (v == 0.0) return;
+    if (i < 6) {
+      if (p.grad_rot) {
+        const size_t br = p.B_rot == 1 ? 0 : (size_t)o.b;
+        unsafeAtomicAdd(p.grad_rot + ((br * p.P + o.n) * 3 + i / 3) * 3 + i % 3, (float)v);
+      }
+    } else if (p.grad_shift) {
+      const size_t bs = p.B_shift == 1 ? 0 : (size_t)o.b;
+      unsafeAtomicAdd(p.grad_shift + (bs * p.P + o.n) * 2 + (i - 6), (float)v);
     }
   }
 }
@@ -223,12 +349,26 @@ __global__ __launch_bounds__(kBlock) void k_zero(uint32_t* ptr, size_t words) {
   } while (0)
 
 hipError_t launch_project(const OpParams& p, int interp, hipStream_t s) {
-  TP_DISPATCH(k_project, p, interp, s);
+  const dim3 grid(p.nblocks), block(kBlock);
+  if (p.ndim == 3) {
+    if (interp) hipLaunchKernelGGL((k_project3p<1>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_project3p<0>), grid, block, 0, s, p);
+  } else {
+    if (interp) hipLaunchKernelGGL((k_project<2, 1>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_project<2, 0>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s) {
-  TP_DISPATCH(k_grad_pose, p, interp, s);
+  const dim3 grid(p.nblocks), block(kBlock);
+  if (p.ndim == 3) {
+    if (interp) hipLaunchKernelGGL((k_grad3p<1>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_grad3p<0>), grid, block, 0, s, p);
+  } else {
+    if (interp) hipLaunchKernelGGL((k_grad_pose<2, 1>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_grad_pose<2, 0>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

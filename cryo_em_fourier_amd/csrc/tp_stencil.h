@@ -197,6 +197,117 @@ __device__ __forceinline__ void gather2_grad(rsrc_t rs, const RefGeom& g, double
   out[2] = sy;
 }
 
+// ------------------------------------------------ half stencils (lane pairs)
+//
+// Two lanes share one output: lane half h reads x-taps [h*T/2, (h+1)*T/2) of
+// every row with one load, so a load instruction covers the whole row of 32
+// outputs in adjacent lanes (one cache line each) instead of half-rows of 64.
+
+template <int INTERP>
+__device__ __forceinline__ float2 gather3_half(rsrc_t rs, const RefGeom& g, double qx, double qy,
+                                               double qz, int xmin, int h) {
+  constexpr int T = Kern<INTERP>::T, H = T / 2;
+  float wx[T], wy[T], wz[T];
+  uint32_t yb[T], zb[T];
+  const uint32_t xo = setup_x<INTERP, false>(g, qx, xmin, wx, nullptr) + 8u * H * h;
+  setup_yz<INTERP, false>(g, qy, g.row, wy, nullptr, yb);
+  setup_yz<INTERP, false>(g, qz, g.plane, wz, nullptr, zb);
+  float wh[H];
+#pragma unroll
+  for (int d = 0; d < H; ++d) wh[d] = h ? wx[H + d] : wx[d];
+#pragma unroll
+  for (int d = 0; d < T; ++d) yb[d] = yb[d] == kBig ? kBig : yb[d] + xo;
+  float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int dz = 0; dz < T; ++dz) {
+    float2 pl = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int dy = 0; dy < T; ++dy) {
+      const uint32_t ro = zb[dz] + yb[dy];
+      float2 r;
+      if (H == 2) {
+        const float4 v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)ro, 0, 0));
+        r.x = fmaf(wh[0], v.x, wh[H - 1] * v.z);
+        r.y = fmaf(wh[0], v.y, wh[H - 1] * v.w);
+      } else {
+        const float2 v = load_c64(rs, ro);
+        r.x = wh[0] * v.x;
+        r.y = wh[0] * v.y;
+      }
+      pl.x = fmaf(wy[dy], r.x, pl.x);
+      pl.y = fmaf(wy[dy], r.y, pl.y);
+    }
+    acc.x = fmaf(wz[dz], pl.x, acc.x);
+    acc.y = fmaf(wz[dz], pl.y, acc.y);
+  }
+  return acc;
+}
+
+template <int INTERP>
+__device__ __forceinline__ void gather3_grad_half(rsrc_t rs, const RefGeom& g, double qx, double qy,
+                                                  double qz, int xmin, int h, float2* out) {
+  constexpr int T = Kern<INTERP>::T, H = T / 2;
+  float wx[T], wy[T], wz[T], dwx[T], dwy[T], dwz[T];
+  uint32_t yb[T], zb[T];
+  const uint32_t xo = setup_x<INTERP, true>(g, qx, xmin, wx, dwx) + 8u * H * h;
+  setup_yz<INTERP, true>(g, qy, g.row, wy, dwy, yb);
+  setup_yz<INTERP, true>(g, qz, g.plane, wz, dwz, zb);
+  float wh[H], dh[H];
+#pragma unroll
+  for (int d = 0; d < H; ++d) {
+    wh[d] = h ? wx[H + d] : wx[d];
+    dh[d] = h ? dwx[H + d] : dwx[d];
+  }
+#pragma unroll
+  for (int d = 0; d < T; ++d) yb[d] = yb[d] == kBig ? kBig : yb[d] + xo;
+  float2 s = make_float2(0.f, 0.f), sx = s, sy = s, sz = s;
+#pragma unroll
+  for (int dz = 0; dz < T; ++dz) {
+    float2 p0 = make_float2(0.f, 0.f), px = p0, py = p0;
+#pragma unroll
+    for (int dy = 0; dy < T; ++dy) {
+      const uint32_t ro = zb[dz] + yb[dy];
+      float2 r, rd;
+      if (H == 2) {
+        const float4 v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)ro, 0, 0));
+        r.x = fmaf(wh[0], v.x, wh[H - 1] * v.z);
+        r.y = fmaf(wh[0], v.y, wh[H - 1] * v.w);
+        rd.x = fmaf(dh[0], v.x, dh[H - 1] * v.z);
+        rd.y = fmaf(dh[0], v.y, dh[H - 1] * v.w);
+      } else {
+        const float2 v = load_c64(rs, ro);
+        r.x = wh[0] * v.x;
+        r.y = wh[0] * v.y;
+        rd.x = dh[0] * v.x;
+        rd.y = dh[0] * v.y;
+      }
+      p0.x = fmaf(wy[dy], r.x, p0.x);
+      p0.y = fmaf(wy[dy], r.y, p0.y);
+      px.x = fmaf(wy[dy], rd.x, px.x);
+      px.y = fmaf(wy[dy], rd.y, px.y);
+      py.x = fmaf(dwy[dy], r.x, py.x);
+      py.y = fmaf(dwy[dy], r.y, py.y);
+    }
+    s.x = fmaf(wz[dz], p0.x, s.x);
+    s.y = fmaf(wz[dz], p0.y, s.y);
+    sx.x = fmaf(wz[dz], px.x, sx.x);
+    sx.y = fmaf(wz[dz], px.y, sx.y);
+    sy.x = fmaf(wz[dz], py.x, sy.x);
+    sy.y = fmaf(wz[dz], py.y, sy.y);
+    sz.x = fmaf(dwz[dz], p0.x, sz.x);
+    sz.y = fmaf(dwz[dz], p0.y, sz.y);
+  }
+  out[0] = s;
+  out[1] = sx;
+  out[2] = sy;
+  out[3] = sz;
+}
+
+// Sum of a value over the two lanes of a pair.
+__device__ __forceinline__ float2 pair_sum(float2 v) {
+  return make_float2(v.x + __shfl_xor(v.x, 1, 64), v.y + __shfl_xor(v.y, 1, 64));
+}
+
 // Does the secondary sum at -m (x-taps >= xmin2) have a tap of nonzero
 // weight?  For the cubic kernel a tap of zero weight still has a nonzero
 // derivative (K'(+-1) = -+0.5), so any tap in range counts.  For the linear
