@@ -14,7 +14,8 @@
 // tap contributions to the brick in LDS.  LDS float atomics are slow on this
 // part, integer ones are not: contributions are accumulated as int32 fixed
 // point (exact, order independent), with a power-of-two quantum chosen per
-// group of poses from a pre-scan of |G| so the sums cannot overflow, and the
+// group of poses from a bound on |G| that is checked against the values read
+// (a group that exceeds it is redone), so the sums cannot overflow; each
 // group is flushed into fp32 registers.  Bricks are split over pose chunks in
 // proportion to the poses expected to cross them (near the origin: all of
 // them); chunks of one brick merge with coalesced float atomics, unsplit
@@ -30,6 +31,7 @@ constexpr int kVox = 4096;          // voxels per brick
 constexpr int kPerThread = kVox / kBlock;
 constexpr int kGroupMax = 16;       // poses per fixed-point group
 constexpr int kHitCap = 4096;       // lattice points per group (LDS hit list)
+constexpr int kPrefetch = 4;        // hits whose G values a thread loads at once
 
 template <int NDIM> struct Brick;
 template <> struct Brick<3> { static constexpr int X = 16, Y = 16, Z = 16; };
@@ -217,10 +219,10 @@ __device__ __forceinline__ size_t out_index(const OpParams& p, size_t img, int k
   return (img * p.No + (ky < 0 ? ky + p.No : ky)) * p.Wo + kx;
 }
 
-// Phase A: does the lattice point reach the brick?  Tracks max |G| read.
+// Phase A: does the lattice point reach the brick?  (geometry only)
 template <int NDIM, int INTERP>
 __device__ __forceinline__ bool lattice_hit(const OpParams& p, const BrickPos& br, const PoseView& pv,
-                                            int n, int kx, int ky, float& amax) {
+                                            int kx, int ky) {
   if (p.cut2 >= 0 && (long long)kx * kx + (long long)ky * ky > p.cut2) return false;
   bool real, mirr;
   lattice_parts(p, kx, ky, real, mirr);
@@ -233,16 +235,17 @@ __device__ __forceinline__ bool lattice_hit(const OpParams& p, const BrickPos& b
     const double q = (double)kx * pv.u[j] + (double)ky * pv.v[j];
     if (!(q >= lo[j] && q < hi[j])) return false;
   }
-  const size_t img = (size_t)br.b * p.P + n;
-  if (real) {
-    const float2 g = p.img[out_index(p, img, kx, ky)];
-    amax = fmaxf(amax, fabsf(g.x) + fabsf(g.y));
-  }
-  if (mirr) {
-    const float2 g = p.img[out_index(p, img, -kx, -ky)];
-    amax = fmaxf(amax, fabsf(g.x) + fabsf(g.y));
-  }
   return true;
+}
+
+// G entries of a lattice point: the real output (kx, ky) and the real output
+// (-kx, -ky) whose mirror it carries (zero where absent).
+__device__ __forceinline__ void lattice_load(const OpParams& p, size_t img, int kx, int ky, float2& gr,
+                                             float2& gm) {
+  bool real, mirr;
+  lattice_parts(p, kx, ky, real, mirr);
+  gr = real ? p.img[out_index(p, img, kx, ky)] : make_float2(0.f, 0.f);
+  gm = mirr ? p.img[out_index(p, img, -kx, -ky)] : make_float2(0.f, 0.f);
 }
 
 // Phase B: sample point and the values spread by a lattice point that hit.
@@ -253,26 +256,75 @@ struct Cand {
 };
 
 template <int NDIM>
-__device__ __forceinline__ void lattice_values(const OpParams& p, const BrickPos& br, const PoseView& pv,
-                                               int n, int kx, int ky, Cand& cd) {
-  bool real, mirr;
-  lattice_parts(p, kx, ky, real, mirr);
+__device__ __forceinline__ void lattice_values(const OpParams& p, const PoseView& pv, int kx, int ky,
+                                               float2 gr, float2 gm, Cand& cd) {
 #pragma unroll
   for (int j = 0; j < NDIM; ++j) cd.q[j] = (double)kx * pv.u[j] + (double)ky * pv.v[j];
-  const size_t img = (size_t)br.b * p.P + n;
-  float2 cr = make_float2(0.f, 0.f), cm = cr;
-  if (real) cr = p.img[out_index(p, img, kx, ky)];
-  if (mirr) cm = p.img[out_index(p, img, -kx, -ky)];
+  float2 cr = gr, cm = gm;
   if (p.shift) {
-    if (real) cr = cmul(conjf2(shift_phase(kx, ky, pv.sx, pv.sy, p.inv_no)), cr);
-    if (mirr) cm = cmul(conjf2(shift_phase(-kx, -ky, pv.sx, pv.sy, p.inv_no)), cm);
+    cr = cmul(conjf2(shift_phase(kx, ky, pv.sx, pv.sy, p.inv_no)), gr);
+    cm = cmul(conjf2(shift_phase(-kx, -ky, pv.sx, pv.sy, p.inv_no)), gm);
   }
   cd.v0 = cr;
   cd.v1 = make_float2(cr.x + cm.x, cr.y - cm.y);
 }
 
+// Spread one lattice point over its taps inside the brick (int32 fixed point).
 template <int NDIM, int INTERP>
-__global__ __launch_bounds__(kBlock) void k_adjoint_bricks(OpParams p, BrickParams bp) {
+__device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float inv_q,
+                                       unsigned long long* acc) {
+  using BR = Brick<NDIM>;
+  using K = Kern<INTERP>;
+  constexpr int T = K::T;
+  const AxisPos ax = axis_pos(cd.q[0], K::OFF), ay = axis_pos(cd.q[1], K::OFF);
+  float wx[T], wy[T], wz[T];
+  K::w(ax.f, wx);
+  K::w(ay.f, wy);
+  int z0 = 0;
+  if (NDIM == 3) {
+    const AxisPos az = axis_pos(cd.q[2], K::OFF);
+    K::w(az.f, wz);
+    z0 = az.x0;
+  } else {
+#pragma unroll
+    for (int d = 0; d < T; ++d) wz[d] = d == 0 ? 1.f : 0.f;
+  }
+  // x weights folded with the per-x value (x = 0 takes the real part only);
+  // taps outside the brick get weight 0 and a clamped slot
+  float are[T], aim[T];
+  int xl[T];
+#pragma unroll
+  for (int d = 0; d < T; ++d) {
+    const int tx = ax.x0 + d;
+    const float2 v = tx >= 1 ? cd.v1 : cd.v0;
+    const bool inx = tx >= br.x0 && tx <= br.x1;
+    are[d] = inx ? wx[d] * v.x * inv_q : 0.f;
+    aim[d] = inx ? wx[d] * v.y * inv_q : 0.f;
+    xl[d] = inx ? tx - br.x0 : 0;
+  }
+#pragma unroll
+  for (int dz = 0; dz < (NDIM == 3 ? T : 1); ++dz) {
+    const int tz = z0 + dz;
+    if (NDIM == 3 && (tz < br.z0 || tz > br.z1)) continue;
+#pragma unroll
+    for (int dy = 0; dy < T; ++dy) {
+      const int ty = ay.x0 + dy;
+      if (ty < br.y0 || ty > br.y1) continue;
+      const float wyz = wy[dy] * wz[dz];
+      const int yl = ty - br.y0, zl = NDIM == 3 ? tz - br.z0 : 0;
+      const int row = (zl * BR::Y + yl) * BR::X, h = row_hash<NDIM>(yl, zl);
+#pragma unroll
+      for (int dx = 0; dx < T; ++dx) {
+        const int ir = cvt_rpi(are[dx] * wyz), ii = cvt_rpi(aim[dx] * wyz);
+        atomicAdd(&acc[row | (xl[dx] ^ h)], pack_pair(ir, ii));
+      }
+    }
+  }
+}
+
+template <int NDIM, int INTERP>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_adjoint_bricks(OpParams p,
+                                                                                           BrickParams bp) {
   using BR = Brick<NDIM>;
   using K = Kern<INTERP>;
   constexpr int T = K::T;
@@ -289,6 +341,7 @@ __global__ __launch_bounds__(kBlock) void k_adjoint_bricks(OpParams p, BrickPara
   if (!br.valid) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float m_prev = 0.f;  // max |G| of the previous group (0: none yet)
   float fre[kPerThread], fim[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
@@ -340,12 +393,10 @@ __global__ __launch_bounds__(kBlock) void k_adjoint_bricks(OpParams p, BrickPara
       if (tid == 0) s_nhit = 0;
       __syncthreads();
 
-      // phase A: compact the lattice points that reach the brick; max |G|
-      float amax = 0.f;
+      // phase A: compact the lattice points that reach the brick (geometry)
       float dens_sum = 0.f;
       for (int g = 0; g < cnt; ++g) {
         const PoseView& pv = s_view[g];
-        const int pn = s_poses[g0 + g];
         dens_sum += pv.dens;
         const int W = pv.kx1 - pv.kx0 + 1;
         const float invW = 1.f / (float)W;
@@ -354,93 +405,92 @@ __global__ __launch_bounds__(kBlock) void k_adjoint_bricks(OpParams p, BrickPara
           int dky = (int)(((float)i + 0.5f) * invW);
           int dkx = i - dky * W;
           if (dkx < 0) { --dky; dkx += W; } else if (dkx >= W) { ++dky; dkx -= W; }
-          if (lattice_hit<NDIM, INTERP>(p, br, pv, pn, pv.kx0 + dkx, pv.ky0 + dky, amax)) {
+          if (lattice_hit<NDIM, INTERP>(p, br, pv, pv.kx0 + dkx, pv.ky0 + dky)) {
             const int slot = atomicAdd(&s_nhit, 1);
             s_hits[slot] = ((uint32_t)g << 24) | ((uint32_t)dky << 12) | (uint32_t)dkx;
           }
         }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-      if (lane == 0) s_red[wave] = amax;
       __syncthreads();
-      float gmax = s_red[0];
-#pragma unroll
-      for (int w = 1; w < kBlock / 64; ++w) gmax = fmaxf(gmax, s_red[w]);
       const int nh = s_nhit;
-      // per pose and voxel: sum |w| over the lattice <= 4 dens, |value| <= 2 max|G|
-      const float gb = fminf(8.f * dens_sum * gmax, 1e30f);
-      if (nh > 0 && gb > 0.f) {
-        int e;
-        frexpf(gb, &e);  // gb < 2^e: |sum| <= gb / q < 2^29
-        const float inv_q = ldexpf(1.f, 29 - e);
-        const float q = ldexpf(1.f, e - 29);
 
-        // phase B: spread every hit over its taps inside the brick
-        for (int i = tid; i < nh; i += kBlock) {
-          const uint32_t h = s_hits[i];
-          const int g = (int)(h >> 24);
-          const PoseView& pv = s_view[g];
-          Cand cd;
-          lattice_values<NDIM>(p, br, pv, s_poses[g0 + g], pv.kx0 + (int)(h & 0xFFFu),
-                               pv.ky0 + (int)((h >> 12) & 0xFFFu), cd);
-          const AxisPos ax = axis_pos(cd.q[0], K::OFF), ay = axis_pos(cd.q[1], K::OFF);
-          float wx[T], wy[T], wz[T];
-          K::w(ax.f, wx);
-          K::w(ay.f, wy);
-          int z0 = 0;
-          if (NDIM == 3) {
-            const AxisPos az = axis_pos(cd.q[2], K::OFF);
-            K::w(az.f, wz);
-            z0 = az.x0;
-          } else {
+      // phase B: spread the hits.  The fixed-point quantum assumes the
+      // group's max |G| is at most twice the previous group's; the values
+      // actually read are checked, and a group that exceeds its assumption
+      // is cleared and redone with the measured bound (the first group of a
+      // workgroup only measures).  Per pose and voxel, sum |w| over the
+      // lattice <= 4 dens and |value| <= 2 max|G|, so |sum| < 2^29 q.
+      bool measure_only = m_prev <= 0.f;
+      float m_assume = 2.f * m_prev, q = 0.f;
+      while (nh > 0) {
+        float inv_q = 0.f;
+        if (!measure_only) {
+          int e;
+          frexpf(fminf(8.f * dens_sum * m_assume, 1e30f), &e);
+          inv_q = ldexpf(1.f, 29 - e);
+          q = ldexpf(1.f, e - 29);
+        }
+        float amax = 0.f;
+        for (int i0 = 0; i0 < nh; i0 += kPrefetch * kBlock) {
+          float2 gr[kPrefetch], gm[kPrefetch];
 #pragma unroll
-            for (int d = 0; d < T; ++d) wz[d] = d == 0 ? 1.f : 0.f;
-          }
-          // x weights folded with the per-x value (x = 0 takes the real part
-          // only); taps outside the brick get weight 0 and a clamped slot
-          float are[T], aim[T];
-          int xl[T];
-#pragma unroll
-          for (int d = 0; d < T; ++d) {
-            const int tx = ax.x0 + d;
-            const float2 v = tx >= 1 ? cd.v1 : cd.v0;
-            const bool inx = tx >= br.x0 && tx <= br.x1;
-            are[d] = inx ? wx[d] * v.x * inv_q : 0.f;
-            aim[d] = inx ? wx[d] * v.y * inv_q : 0.f;
-            xl[d] = inx ? tx - br.x0 : 0;
-          }
-#pragma unroll
-          for (int dz = 0; dz < (NDIM == 3 ? T : 1); ++dz) {
-            const int tz = z0 + dz;
-            if (NDIM == 3 && (tz < br.z0 || tz > br.z1)) continue;
-#pragma unroll
-            for (int dy = 0; dy < T; ++dy) {
-              const int ty = ay.x0 + dy;
-              if (ty < br.y0 || ty > br.y1) continue;
-              const float wyz = wy[dy] * wz[dz];
-              const int yl = ty - br.y0, zl = NDIM == 3 ? tz - br.z0 : 0;
-              const int row = (zl * BR::Y + yl) * BR::X, h = row_hash<NDIM>(yl, zl);
-#pragma unroll
-              for (int dx = 0; dx < T; ++dx) {
-                const int ir = cvt_rpi(are[dx] * wyz), ii = cvt_rpi(aim[dx] * wyz);
-                atomicAdd(&acc[row | (xl[dx] ^ h)], pack_pair(ir, ii));
-              }
+          for (int k = 0; k < kPrefetch; ++k) {
+            const int i = i0 + tid + k * kBlock;
+            gr[k] = gm[k] = make_float2(0.f, 0.f);
+            if (i < nh) {
+              const uint32_t h = s_hits[i];
+              const PoseView& pv = s_view[h >> 24];
+              lattice_load(p, (size_t)br.b * p.P + s_poses[g0 + (int)(h >> 24)], pv.kx0 + (int)(h & 0xFFFu),
+                           pv.ky0 + (int)((h >> 12) & 0xFFFu), gr[k], gm[k]);
             }
           }
-        }
-        // flush the group into fp32 registers
-        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-          const int v = tid + i * kBlock;
-          const int sl = slot_of<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
-          int ir, ii;
-          unpack_pair(acc[sl], ir, ii);
-          fre[i] = fmaf((float)ir, q, fre[i]);
-          fim[i] = fmaf((float)ii, q, fim[i]);
-          acc[sl] = 0ull;
+          for (int k = 0; k < kPrefetch; ++k)
+            amax = fmaxf(amax, fmaxf(fabsf(gr[k].x) + fabsf(gr[k].y), fabsf(gm[k].x) + fabsf(gm[k].y)));
+          if (measure_only) continue;
+#pragma unroll
+          for (int k = 0; k < kPrefetch; ++k) {
+            const int i = i0 + tid + k * kBlock;
+            if (i >= nh) continue;
+            const uint32_t h = s_hits[i];
+            const PoseView& pv = s_view[h >> 24];
+            Cand cd;
+            lattice_values<NDIM>(p, pv, pv.kx0 + (int)(h & 0xFFFu), pv.ky0 + (int)((h >> 12) & 0xFFFu), gr[k],
+                                 gm[k], cd);
+            spread<NDIM, INTERP>(br, cd, inv_q, acc);
+          }
         }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        __syncthreads();
+        if (lane == 0) s_red[wave] = amax;
+        __syncthreads();
+        float gmax = s_red[0];
+#pragma unroll
+        for (int w = 1; w < kBlock / 64; ++w) gmax = fmaxf(gmax, s_red[w]);
+        if (!(gmax > 0.f)) break;  // an all-zero group adds nothing
+        if (!measure_only && gmax <= m_assume) {
+          // flush the group into fp32 registers
+#pragma unroll
+          for (int i = 0; i < kPerThread; ++i) {
+            const int v = tid + i * kBlock;
+            const int sl = slot_of<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
+            int ir, ii;
+            unpack_pair(acc[sl], ir, ii);
+            fre[i] = fmaf((float)ir, q, fre[i]);
+            fim[i] = fmaf((float)ii, q, fim[i]);
+            acc[sl] = 0ull;
+          }
+          m_prev = gmax;
+          break;
+        }
+        if (!measure_only) {
+#pragma unroll
+          for (int i = 0; i < kPerThread; ++i) acc[tid + i * kBlock] = 0ull;
+          __syncthreads();
+        }
+        m_assume = gmax;
+        measure_only = false;
       }
       __syncthreads();
       // next group
