@@ -34,6 +34,41 @@ METRIC = "projections/sec fwd and fwd+bwd, box 256 cubic; % of HBM/L2 roofline"
 # MI355X published peaks
 HBM_PEAK_GBS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3
+# L2 read bandwidth derived from unit counts and clock:
+# 8 XCDs x 16 channels x 128 B/clk x 2.4 GHz
+L2_PEAK_GBS = 8 * 16 * 128 * 2.4
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources: counter data is valid only for these."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "cryo_em_fourier_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, copy_bytes: int) -> dict:
+    """Per-launch HBM bytes from the committed counter summary of this
+    workload (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter
+    read for the calibration copy), or {} when there is none or the kernel
+    sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if d.get("kernel_source_sha256") != kernel_source_digest() or d.get("copy_bytes") != copy_bytes:
+        return {}
+    out = {}
+    for k, v in d.get("kernels", {}).items():
+        out[k] = int(round(v["fetch_kib"] * 1024 * d["fetch_scale"] + v["write_kib"] * 1024 * d["write_scale"]))
+    return out
 
 
 def in_cutoff_count(n_out: int, cutoff: float) -> int:
@@ -174,6 +209,15 @@ def main():
                                   dR.data_ptr(), ds.data_ptr(), sh), "tp_grad_pose")
 
     kernels = [("project", fwd), ("backproject", adj), ("grad_pose", grad)]
+
+    # calibration for HBM byte counters: one plain streaming copy (y = x * 1)
+    # of known size, outside the timed region.  A counter run of this same
+    # command reads FETCH_SIZE / WRITE_SIZE for it and for the kernels.
+    cal_src, cal_dst = Gd.view(torch.float32), out.view(torch.float32)
+    torch.mul(cal_src, 1.0, out=cal_dst)
+    torch.cuda.synchronize()
+    copy_bytes = cal_src.numel() * 4
+
     for i in range(args.warmup):
         for _, f in kernels:
             f()
@@ -218,6 +262,8 @@ def main():
                  "grad_pose": units * taps * 8}
     dom = max(avg, key=avg.get)
     achieved = hbm[dom] / (avg[dom] * 1e-3) / 1e9
+    wl_key = f"{w.name}_os{args.oversampling}" + (f"_p{P}" if args.poses else "")
+    traffic = measured_traffic(wl_key, copy_bytes)
     roof = {
         "kernel": dom,
         "bound": "hbm",
@@ -225,11 +271,19 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": None,
+        "traffic": traffic.get(dom),
         "algorithmic_bytes_per_launch": hbm[dom],
-        "tap_bytes_per_launch": tap_bytes[dom],
-        "tap_rate_GBs": round(tap_bytes[dom] / (avg[dom] * 1e-3) / 1e9, 1),
     }
+    # the on-chip term that actually bounds a gather / scatter: tap bytes
+    # (8 B x taps x in-cutoff outputs) against the L2 peak derived from unit
+    # counts and clock (8 XCDs x 16 channels x 128 B/clk x 2.4 GHz)
+    tap_roof = {
+        k: {"achieved": round(tap_bytes[k] / (avg[k] * 1e-3) / 1e9, 1),
+            "frac": round(tap_bytes[k] / (avg[k] * 1e-3) / 1e9 / L2_PEAK_GBS, 4)}
+        for k in avg
+    }
+    roof_tap = {"bound": "l2", "peak": L2_PEAK_GBS, "unit": "GB/s",
+                "tap_bytes_per_launch": tap_bytes[dom], "kernels": tap_roof}
     res = {
         "metric": METRIC,
         "value": round(fwd_bwd_rate, 1),
@@ -254,6 +308,9 @@ def main():
         "kernel_ms_median": {k: round(v, 4) for k, v in med.items()},
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
+        "roofline_tap": roof_tap,
+        "traffic_all": traffic or None,
+        "counter_calibration_copy_bytes": copy_bytes,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

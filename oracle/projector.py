@@ -8,8 +8,8 @@ Projection Library for PyTorch, gist.science summaries in it/de/ja/ko/ar).
 
 What it computes (NumPy, complex128; inputs are upcast from complex64/fp32):
 
-* Layout: PyTorch/FFTW rfft half-spectra kept as they are [tech. §2 of every
-  page, "RFFT format, FFTW conventions, no intermediate format changes"].
+* Layout: PyTorch/FFTW rfft half-spectra kept as they are, with no format
+  conversion anywhere [tech. §2 of every page].
   3D reference ``V[b, z, y, x]`` with x = the halved last axis, 2D reference
   ``V[b, y, x]``.  Index -> signed frequency is ``f_N(i) = i if i <= (N-1)//2
   else i - N``.  Stored: x in [0, N//2], y and z in [-(N//2), (N+1)//2 - 1].
@@ -31,10 +31,10 @@ What it computes (NumPy, complex128; inputs are upcast from complex64/fp32):
 * Pose gradients by the chain rule through the interpolation-kernel
   derivatives [ar tech. §2; de tech. §3 item 4].
 
-Readings where the pages are silent are listed in the module's design notes
-(per-tap fold, zero outside the stored range, right derivative of the linear
-kernel at integers, sample points with a non-finite or |p| > 2**30 component
-read 0).  Every function here is pinned by tests in ``tests/test_oracle_*.py``.
+Where the pages are silent this module takes the plainest reading and says
+so in the function that applies it: per-tap fold, zero outside the stored
+range, right derivative of the linear kernel at integers, sample points with
+a non-finite or |p| > 2**30 component read 0.  Every function here is pinned by tests in ``tests/test_oracle_*.py``.
 """
 from __future__ import annotations
 
