@@ -204,6 +204,10 @@ __device__ __forceinline__ PoseView pose_view(const OpParams& p, const BrickPos&
         isfinite(pv.v[1]) && isfinite(pv.v[2])))
     pv.hit = 0;
   if (pv.kx0 > pv.kx1 || pv.ky0 > pv.ky1) pv.hit = 0;
+  // every weight is at most 1 in magnitude, so a pose adds at most its
+  // rectangle's lattice count of them to a voxel: this caps the density
+  // bound of nearly degenerate rows
+  if (pv.hit) pv.dens = fminf(pv.dens, 0.25f * (float)(pv.kx1 - pv.kx0 + 1) * (float)(pv.ky1 - pv.ky0 + 1) + 1.f);
   return pv;
 }
 
@@ -426,7 +430,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         float inv_q = 0.f;
         if (!measure_only) {
           int e;
-          frexpf(fminf(8.f * dens_sum * m_assume, 1e30f), &e);
+          frexpf(fminf(8.f * dens_sum * m_assume, 3e38f), &e);
+          e = max(e, -90);  // |G| below ~1e-27 gets a coarser quantum than needed
           inv_q = ldexpf(1.f, 29 - e);
           q = ldexpf(1.f, e - 29);
         }
