@@ -129,6 +129,7 @@ __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams&
 // Everything about one pose that the brick loop needs (uniform values).
 struct PoseView {
   double u[3], v[3];      // p = kx u + ky v
+  double iu[3];           // 1 / u (0 where u = 0)
   float sx, sy;
   float dens;             // max(1, 1 / |u x v|): lattice points per unit area bound
   int kx0, kx1, ky0, ky1; // candidate rectangle (full plane, clipped)
@@ -143,6 +144,7 @@ __device__ __forceinline__ PoseView pose_view(const OpParams& p, const BrickPos&
   for (int j = 0; j < 3; ++j) {
     pv.u[j] = j < NDIM ? os * (double)R[j] : 0.0;
     pv.v[j] = j < NDIM ? os * (double)R[NDIM + j] : 0.0;
+    pv.iu[j] = pv.u[j] != 0.0 ? 1.0 / pv.u[j] : 0.0;
   }
   if (p.shift) {
     const float* s = p.shift + ((size_t)(p.B_shift == 1 ? 0 : br.b) * p.P + n) * 2;
@@ -223,23 +225,69 @@ __device__ __forceinline__ size_t out_index(const OpParams& p, size_t img, int k
   return (img * p.No + (ky < 0 ? ky + p.No : ky)) * p.Wo + kx;
 }
 
-// Phase A: does the lattice point reach the brick?  (geometry only)
+// Sample points whose stencil can reach the brick lie in the brick widened
+// by the stencil reach: [x0 - r, x1 + r) per axis (r = 2 cubic, 1 linear);
+// any point outside has all its taps outside the brick.
 template <int NDIM, int INTERP>
-__device__ __forceinline__ bool lattice_hit(const OpParams& p, const BrickPos& br, const PoseView& pv,
-                                            int kx, int ky) {
-  if (p.cut2 >= 0 && (long long)kx * kx + (long long)ky * ky > p.cut2) return false;
-  bool real, mirr;
-  lattice_parts(p, kx, ky, real, mirr);
-  if (!real && !mirr) return false;
+__device__ __forceinline__ bool in_reach(const BrickPos& br, const double* q) {
   constexpr double reach = INTERP ? 2.0 : 1.0;
   const double lo[3] = {br.x0 - reach, br.y0 - reach, br.z0 - reach};
   const double hi[3] = {br.x1 + reach, br.y1 + reach, br.z1 + reach};
+  bool in = true;
+#pragma unroll
+  for (int j = 0; j < NDIM; ++j) in = in && q[j] >= lo[j] && q[j] < hi[j];
+  return in;
+}
+
+// Phase A: the kx range [a, b] of row ky whose sample points fall in the
+// reach box widened by half a voxel (a superset of the points in reach; the
+// margin dwarfs rounding), clipped to the pose's rectangle and to the cutoff
+// disk.  Empty when b < a.
+template <int NDIM, int INTERP>
+__device__ __forceinline__ void row_range(const OpParams& p, const BrickPos& br, const PoseView& pv, int ky,
+                                          int& a, int& b) {
+  constexpr double reach = INTERP ? 2.5 : 1.5;
+  const double lo[3] = {br.x0 - reach, br.y0 - reach, br.z0 - reach};
+  const double hi[3] = {br.x1 + reach, br.y1 + reach, br.z1 + reach};
+  double ta = (double)pv.kx0, tb = (double)pv.kx1;
+  bool empty = false;
 #pragma unroll
   for (int j = 0; j < NDIM; ++j) {
-    const double q = (double)kx * pv.u[j] + (double)ky * pv.v[j];
-    if (!(q >= lo[j] && q < hi[j])) return false;
+    const double c = (double)ky * pv.v[j];
+    if (pv.iu[j] == 0.0) {
+      empty = empty || !(c >= lo[j] && c < hi[j]);
+    } else {
+      const double t0 = (lo[j] - c) * pv.iu[j], t1 = (hi[j] - c) * pv.iu[j];
+      ta = fmax(ta, fmin(t0, t1));
+      tb = fmin(tb, fmax(t0, t1));
+    }
   }
-  return true;
+  if (p.cut2 >= 0) {
+    const long long rem = p.cut2 - (long long)ky * ky;
+    if (rem < 0) {
+      empty = true;
+    } else {
+      long long m = (long long)sqrt((double)rem);
+      while ((m + 1) * (m + 1) <= rem) ++m;
+      while (m * m > rem) --m;
+      ta = fmax(ta, (double)-m);
+      tb = fmin(tb, (double)m);
+    }
+  }
+  a = (int)ceil(ta);
+  b = empty ? a - 1 : (int)floor(tb);
+}
+
+// Lattice points listed for a pose (phase A's row ranges summed).
+template <int NDIM, int INTERP>
+__device__ __forceinline__ int pose_hits(const OpParams& p, const BrickPos& br, const PoseView& pv) {
+  int n = 0;
+  for (int ky = pv.ky0; ky <= pv.ky1; ++ky) {
+    int a, b;
+    row_range<NDIM, INTERP>(p, br, pv, ky, a, b);
+    n += max(0, b - a + 1);
+  }
+  return n;
 }
 
 // G entries of a lattice point: the real output (kx, ky) and the real output
@@ -330,8 +378,6 @@ template <int NDIM, int INTERP>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_adjoint_bricks(OpParams p,
                                                                                            BrickParams bp) {
   using BR = Brick<NDIM>;
-  using K = Kern<INTERP>;
-  constexpr int T = K::T;
   __shared__ unsigned long long acc[kVox];
   __shared__ uint32_t s_hits[kHitCap];
   __shared__ int s_poses[kBlock];
@@ -339,7 +385,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   __shared__ PoseView s_view[kGroupMax];
   __shared__ int s_wcnt[kBlock / 64];
   __shared__ float s_red[kBlock / 64];
-  __shared__ int s_nhit;
 
   const BrickPos br = decode<NDIM>(p, bp);
   if (!br.valid) return;
@@ -359,7 +404,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     int area = 0;
     if (n < br.n1) {
       const PoseView pv = pose_view<NDIM, INTERP>(p, br, n);
-      if (pv.hit) area = (pv.kx1 - pv.kx0 + 1) * (pv.ky1 - pv.ky0 + 1);
+      if (pv.hit) area = pose_hits<NDIM, INTERP>(p, br, pv);
     }
     const bool hit = area > 0;
     const unsigned long long m = __ballot(hit);
@@ -394,29 +439,59 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       }
       const int cnt = g1 - g0;
       if (tid < cnt) s_view[tid] = pose_view<NDIM, INTERP>(p, br, s_poses[g0 + tid]);
-      if (tid == 0) s_nhit = 0;
       __syncthreads();
 
-      // phase A: compact the lattice points that reach the brick (geometry)
+      // phase A: list the group's lattice points that can reach the brick,
+      // row by row; the flat index runs over the rows of pose 0, then pose 1,
+      // ...; a slice of one pose keeps the flat indices [f0, f1)
       float dens_sum = 0.f;
+      int rows_total = 0;
       for (int g = 0; g < cnt; ++g) {
-        const PoseView& pv = s_view[g];
-        dens_sum += pv.dens;
-        const int W = pv.kx1 - pv.kx0 + 1;
-        const float invW = 1.f / (float)W;
-        const int a0 = cnt == 1 ? f0 : 0, a1 = cnt == 1 ? f1 : (pv.kx1 - pv.kx0 + 1) * (pv.ky1 - pv.ky0 + 1);
-        for (int i = a0 + tid; i < a1; i += kBlock) {
-          int dky = (int)(((float)i + 0.5f) * invW);
-          int dkx = i - dky * W;
-          if (dkx < 0) { --dky; dkx += W; } else if (dkx >= W) { ++dky; dkx -= W; }
-          if (lattice_hit<NDIM, INTERP>(p, br, pv, pv.kx0 + dkx, pv.ky0 + dky)) {
-            const int slot = atomicAdd(&s_nhit, 1);
-            s_hits[slot] = ((uint32_t)g << 24) | ((uint32_t)dky << 12) | (uint32_t)dkx;
-          }
-        }
+        dens_sum += s_view[g].dens;
+        rows_total += s_view[g].ky1 - s_view[g].ky0 + 1;
       }
-      __syncthreads();
-      const int nh = s_nhit;
+      const int h0 = cnt == 1 ? f0 : 0, h1 = cnt == 1 ? f1 : 0x7FFFFFFF;
+      int carry = 0;
+      for (int rw = 0; rw < rows_total; rw += kBlock) {
+        const int r = rw + tid;
+        int g = 0, cr = 0, a = 0, dky = 0;
+        if (r < rows_total) {
+          int rb = 0;
+          while (true) {
+            const int H = s_view[g].ky1 - s_view[g].ky0 + 1;
+            if (r < rb + H) break;
+            rb += H;
+            ++g;
+          }
+          const PoseView& pv = s_view[g];
+          dky = r - rb;
+          int b;
+          row_range<NDIM, INTERP>(p, br, pv, pv.ky0 + dky, a, b);
+          cr = max(0, b - a + 1);
+          a -= pv.kx0;
+        }
+        // exclusive block scan of the row counts
+        int incl = cr;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        if (lane == 63) s_wcnt[wave] = incl;
+        __syncthreads();
+        int off = carry + incl - cr, tot = 0;
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) {
+          off += w < wave ? s_wcnt[w] : 0;
+          tot += s_wcnt[w];
+        }
+        const uint32_t tag = ((uint32_t)g << 24) | ((uint32_t)dky << 12);
+        for (int j = max(0, h0 - off); j < cr && off + j < h1; ++j) s_hits[off + j - h0] = tag | (uint32_t)(a + j);
+        carry += tot;
+        __syncthreads();
+      }
+      const int nh = min(carry, h1) - h0;
+
 
       // phase B: spread the hits.  The fixed-point quantum assumes the
       // group's max |G| is at most twice the previous group's; the values
@@ -462,7 +537,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             Cand cd;
             lattice_values<NDIM>(p, pv, pv.kx0 + (int)(h & 0xFFFu), pv.ky0 + (int)((h >> 12) & 0xFFFu), gr[k],
                                  gm[k], cd);
-            spread<NDIM, INTERP>(br, cd, inv_q, acc);
+            if (in_reach<NDIM, INTERP>(br, cd.q)) spread<NDIM, INTERP>(br, cd, inv_q, acc);
           }
         }
 #pragma unroll
