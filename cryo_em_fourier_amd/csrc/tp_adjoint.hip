@@ -31,7 +31,16 @@ constexpr int kVox = 4096;          // voxels per brick
 constexpr int kPerThread = kVox / kBlock;
 constexpr int kGroupMax = 16;       // poses per fixed-point group
 constexpr int kHitCap = 4096;       // lattice points per group (LDS hit list)
-constexpr int kPrefetch = 4;        // hits whose G values a thread loads at once
+constexpr int kPrefetch = 2;        // hits whose G values a thread loads at once
+// Fixed point: per group, |sum| < 2^kQuantumBits q at every voxel, with
+// q = 2^e / 2^kQuantumBits >= 8 sum_poses(dens) max|G| / 2^kQuantumBits.
+// A pose's share of a voxel is at most 2 max|G| (a lattice point carries a
+// real and a mirror value) times the sum of |w| over its lattice points,
+// which is about dens times the plane integral of |kernel|: sampled over
+// 20,000 random poses and voxel offsets it stays below 1.6 dens (Catmull-Rom)
+// and 1.25 dens (linear) for oversampling 0.25 to 2.  The bound takes 4 dens,
+// and 29 bits leave another factor 4 of int32 headroom.
+constexpr int kQuantumBits = 29;
 
 template <int NDIM> struct Brick;
 template <> struct Brick<3> { static constexpr int X = 16, Y = 16, Z = 16; };
@@ -101,10 +110,12 @@ __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams&
   using BR = Brick<NDIM>;
   BrickPos r;
   // plain round-robin over the XCDs: consecutive bricks (and the mostly empty
-  // high chunk slots) spread evenly; bricks share little data across XCDs
+  // high chunk slots) spread evenly; bricks share little data across XCDs.
+  // High chunk slots go first: only the busiest bricks near the origin have
+  // them, so the long workgroups start early and the short ones fill the end.
   const uint32_t lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const int brick = (int)(lin % (uint32_t)bp.nbricks);
-  const int ch = (int)((lin / (uint32_t)bp.nbricks) % (uint32_t)bp.cmax);
+  const int ch = bp.cmax - 1 - (int)((lin / (uint32_t)bp.nbricks) % (uint32_t)bp.cmax);
   r.b = (int)(lin / ((uint32_t)bp.nbricks * (uint32_t)bp.cmax));
   const int bi = brick % bp.nb[0], bj = (brick / bp.nb[0]) % bp.nb[1], bk = brick / (bp.nb[0] * bp.nb[1]);
   const int lo = -(p.N / 2), hi = (p.N + 1) / 2 - 1;
@@ -213,6 +224,52 @@ __device__ __forceinline__ PoseView pose_view(const OpParams& p, const BrickPos&
   return pv;
 }
 
+// Scan test: can pose n's sample plane bring a kept lattice point into reach
+// of the brick?  The plane (through the origin, normal u x v) must cross the
+// reach box, and the box must come within the largest |p| of a kept output
+// (cutoff or the output box, times the largest stretch of the rows).
+template <int NDIM, int INTERP>
+__device__ __forceinline__ bool plane_meets(const OpParams& p, const BrickPos& br, int n) {
+  const float* R = p.rot + ((size_t)(p.B_rot == 1 ? 0 : br.b) * p.P + n) * (NDIM * NDIM);
+  const double os = (double)p.os;
+  double u[3], v[3];
+  for (int j = 0; j < 3; ++j) {
+    u[j] = j < NDIM ? os * (double)R[j] : 0.0;
+    v[j] = j < NDIM ? os * (double)R[NDIM + j] : 0.0;
+  }
+  if (!(isfinite(u[0]) && isfinite(u[1]) && isfinite(u[2]) && isfinite(v[0]) && isfinite(v[1]) &&
+        isfinite(v[2])))
+    return false;
+  constexpr double reach = INTERP ? 2.0 : 1.0;
+  double lo[3] = {br.x0 - reach, br.y0 - reach, br.z0 - reach};
+  double hi[3] = {br.x1 + reach, br.y1 + reach, br.z1 + reach};
+  if (NDIM == 2) { lo[2] = 0.0; hi[2] = 0.0; }
+  if (NDIM == 3) {
+    const double nrm[3] = {u[1] * v[2] - u[2] * v[1], u[2] * v[0] - u[0] * v[2], u[0] * v[1] - u[1] * v[0]};
+    double mn = 0.0, mx = 0.0;
+    for (int j = 0; j < 3; ++j) {
+      const double a = lo[j] * nrm[j], b = hi[j] * nrm[j];
+      mn += fmin(a, b);
+      mx += fmax(a, b);
+    }
+    const double slack = 1e-9 * (fabs(mn) + fabs(mx) + 1.0);
+    if (mn > slack || mx < -slack) return false;
+  }
+  // |p|^2 <= |k|^2 * largest eigenvalue of the rows' Gram matrix
+  const double uu = u[0] * u[0] + u[1] * u[1] + u[2] * u[2];
+  const double vv = v[0] * v[0] + v[1] * v[1] + v[2] * v[2];
+  const double uv = u[0] * v[0] + u[1] * v[1] + u[2] * v[2];
+  const double lmax = 0.5 * (uu + vv) + sqrt(0.25 * (uu - vv) * (uu - vv) + uv * uv);
+  const double h = 0.5 * p.No;
+  const double k2 = p.cut2 >= 0 ? fmin((double)p.cut2, 2.0 * h * h) : 2.0 * h * h;
+  double d2 = 0.0;  // squared distance from the origin to the reach box
+  for (int j = 0; j < NDIM; ++j) {
+    const double d = lo[j] > 0.0 ? lo[j] : (hi[j] < 0.0 ? -hi[j] : 0.0);
+    d2 += d * d;
+  }
+  return d2 <= k2 * lmax * (1.0 + 1e-9) + 1e-9;
+}
+
 // A lattice point (kx, ky) of the full plane carries the real output (kx, ky)
 // when kx >= 0 and the mirror of the real output (-kx, -ky) when kx <= 0.
 __device__ __forceinline__ void lattice_parts(const OpParams& p, int kx, int ky, bool& real, bool& mirr) {
@@ -240,13 +297,14 @@ __device__ __forceinline__ bool in_reach(const BrickPos& br, const double* q) {
 }
 
 // Phase A: the kx range [a, b] of row ky whose sample points fall in the
-// reach box widened by half a voxel (a superset of the points in reach; the
-// margin dwarfs rounding), clipped to the pose's rectangle and to the cutoff
+// reach box widened by 1e-6 (the margin covers the rounding of this fp64
+// arithmetic; a point within rounding of the reach boundary has weight ~0 in
+// the brick either way), clipped to the pose's rectangle and to the cutoff
 // disk.  Empty when b < a.
 template <int NDIM, int INTERP>
 __device__ __forceinline__ void row_range(const OpParams& p, const BrickPos& br, const PoseView& pv, int ky,
                                           int& a, int& b) {
-  constexpr double reach = INTERP ? 2.5 : 1.5;
+  constexpr double reach = (INTERP ? 2.0 : 1.0) + 1e-6;
   const double lo[3] = {br.x0 - reach, br.y0 - reach, br.z0 - reach};
   const double hi[3] = {br.x1 + reach, br.y1 + reach, br.z1 + reach};
   double ta = (double)pv.kx0, tb = (double)pv.kx1;
@@ -276,18 +334,6 @@ __device__ __forceinline__ void row_range(const OpParams& p, const BrickPos& br,
   }
   a = (int)ceil(ta);
   b = empty ? a - 1 : (int)floor(tb);
-}
-
-// Lattice points listed for a pose (phase A's row ranges summed).
-template <int NDIM, int INTERP>
-__device__ __forceinline__ int pose_hits(const OpParams& p, const BrickPos& br, const PoseView& pv) {
-  int n = 0;
-  for (int ky = pv.ky0; ky <= pv.ky1; ++ky) {
-    int a, b;
-    row_range<NDIM, INTERP>(p, br, pv, ky, a, b);
-    n += max(0, b - a + 1);
-  }
-  return n;
 }
 
 // G entries of a lattice point: the real output (kx, ky) and the real output
@@ -381,7 +427,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   __shared__ unsigned long long acc[kVox];
   __shared__ uint32_t s_hits[kHitCap];
   __shared__ int s_poses[kBlock];
-  __shared__ int s_area[kBlock];
   __shared__ PoseView s_view[kGroupMax];
   __shared__ int s_wcnt[kBlock / 64];
   __shared__ float s_red[kBlock / 64];
@@ -399,14 +444,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   }
 
   for (int w0 = br.n0; w0 < br.n1; w0 += kBlock) {
-    // one pose per thread: does its plane reach this brick?  ordered compaction
+    // one pose per thread: can its plane reach this brick?  ordered compaction
     const int n = w0 + tid;
-    int area = 0;
-    if (n < br.n1) {
-      const PoseView pv = pose_view<NDIM, INTERP>(p, br, n);
-      if (pv.hit) area = pose_hits<NDIM, INTERP>(p, br, pv);
-    }
-    const bool hit = area > 0;
+    const bool hit = n < br.n1 && plane_meets<NDIM, INTERP>(p, br, n);
     const unsigned long long m = __ballot(hit);
     __syncthreads();
     if (lane == 0) s_wcnt[wave] = __popcll(m);
@@ -417,168 +457,151 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       off += w < wave ? s_wcnt[w] : 0;
       total += s_wcnt[w];
     }
-    if (hit) {
-      const int slot = off + __popcll(m & ((1ull << lane) - 1ull));
-      s_poses[slot] = n;
-      s_area[slot] = area;
-    }
+    if (hit) s_poses[off + __popcll(m & ((1ull << lane) - 1ull))] = n;
     __syncthreads();
 
-    // groups: whole poses whose rectangles fit the hit list, or one slice of
-    // a single pose's rectangle
-    int g0 = 0, r0 = 0;
-    while (g0 < total) {
-      int g1 = g0 + 1, f0 = 0, f1;
-      if (r0 > 0 || s_area[g0] > kHitCap) {
-        f0 = r0;
-        f1 = min(r0 + kHitCap, s_area[g0]);
-      } else {
-        int sum = s_area[g0];
-        while (g1 < total && g1 - g0 < kGroupMax && sum + s_area[g1] <= kHitCap) sum += s_area[g1++];
-        f1 = s_area[g0];
-      }
-      const int cnt = g1 - g0;
+    // groups of up to kGroupMax poses; a group whose lattice points overflow
+    // the hit list is spread in slices of kHitCap
+    for (int g0 = 0; g0 < total; g0 += kGroupMax) {
+      const int cnt = min(kGroupMax, total - g0);
       if (tid < cnt) s_view[tid] = pose_view<NDIM, INTERP>(p, br, s_poses[g0 + tid]);
       __syncthreads();
-
-      // phase A: list the group's lattice points that can reach the brick,
-      // row by row; the flat index runs over the rows of pose 0, then pose 1,
-      // ...; a slice of one pose keeps the flat indices [f0, f1)
       float dens_sum = 0.f;
       int rows_total = 0;
       for (int g = 0; g < cnt; ++g) {
-        dens_sum += s_view[g].dens;
-        rows_total += s_view[g].ky1 - s_view[g].ky0 + 1;
+        const PoseView& pv = s_view[g];
+        if (!pv.hit) continue;
+        dens_sum += pv.dens;
+        rows_total += pv.ky1 - pv.ky0 + 1;
       }
-      const int h0 = cnt == 1 ? f0 : 0, h1 = cnt == 1 ? f1 : 0x7FFFFFFF;
-      int carry = 0;
-      for (int rw = 0; rw < rows_total; rw += kBlock) {
-        const int r = rw + tid;
-        int g = 0, cr = 0, a = 0, dky = 0;
-        if (r < rows_total) {
-          int rb = 0;
-          while (true) {
-            const int H = s_view[g].ky1 - s_view[g].ky0 + 1;
-            if (r < rb + H) break;
-            rb += H;
-            ++g;
+
+      for (int h0 = 0, hits_total = 1; h0 < hits_total; h0 += kHitCap) {
+        // phase A: list the lattice points that can reach the brick, row by
+        // row; the flat index runs over the rows of pose 0, then pose 1, ...;
+        // this slice keeps the flat indices [h0, h0 + kHitCap)
+        const int h1 = h0 + kHitCap;
+        int carry = 0;
+        for (int rw = 0; rw < rows_total; rw += kBlock) {
+          const int r = rw + tid;
+          int g = 0, cr = 0, a = 0, dky = 0;
+          if (r < rows_total) {
+            int rb = 0;
+            while (true) {
+              const PoseView& pv = s_view[g];
+              const int H = pv.hit ? pv.ky1 - pv.ky0 + 1 : 0;
+              if (r < rb + H) break;
+              rb += H;
+              ++g;
+            }
+            const PoseView& pv = s_view[g];
+            dky = r - rb;
+            int b;
+            row_range<NDIM, INTERP>(p, br, pv, pv.ky0 + dky, a, b);
+            cr = max(0, b - a + 1);
+            a -= pv.kx0;
           }
-          const PoseView& pv = s_view[g];
-          dky = r - rb;
-          int b;
-          row_range<NDIM, INTERP>(p, br, pv, pv.ky0 + dky, a, b);
-          cr = max(0, b - a + 1);
-          a -= pv.kx0;
-        }
-        // exclusive block scan of the row counts
-        int incl = cr;
+          // exclusive block scan of the row counts
+          int incl = cr;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int t = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += t;
-        }
-        if (lane == 63) s_wcnt[wave] = incl;
-        __syncthreads();
-        int off = carry + incl - cr, tot = 0;
+          for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += t;
+          }
+          if (lane == 63) s_wcnt[wave] = incl;
+          __syncthreads();
+          int off = carry + incl - cr, tot = 0;
 #pragma unroll
-        for (int w = 0; w < kBlock / 64; ++w) {
-          off += w < wave ? s_wcnt[w] : 0;
-          tot += s_wcnt[w];
+          for (int w = 0; w < kBlock / 64; ++w) {
+            off += w < wave ? s_wcnt[w] : 0;
+            tot += s_wcnt[w];
+          }
+          const uint32_t tag = ((uint32_t)g << 24) | ((uint32_t)dky << 12);
+          for (int j = max(0, h0 - off); j < cr && off + j < h1; ++j) s_hits[off + j - h0] = tag | (uint32_t)(a + j);
+          carry += tot;
+          __syncthreads();
         }
-        const uint32_t tag = ((uint32_t)g << 24) | ((uint32_t)dky << 12);
-        for (int j = max(0, h0 - off); j < cr && off + j < h1; ++j) s_hits[off + j - h0] = tag | (uint32_t)(a + j);
-        carry += tot;
-        __syncthreads();
-      }
-      const int nh = min(carry, h1) - h0;
+        hits_total = carry;
+        const int nh = max(0, min(carry, h1) - h0);
 
-
-      // phase B: spread the hits.  The fixed-point quantum assumes the
-      // group's max |G| is at most twice the previous group's; the values
-      // actually read are checked, and a group that exceeds its assumption
-      // is cleared and redone with the measured bound (the first group of a
-      // workgroup only measures).  Per pose and voxel, sum |w| over the
-      // lattice <= 4 dens and |value| <= 2 max|G|, so |sum| < 2^29 q.
-      bool measure_only = m_prev <= 0.f;
-      float m_assume = 2.f * m_prev, q = 0.f;
-      while (nh > 0) {
-        float inv_q = 0.f;
-        if (!measure_only) {
-          int e;
-          frexpf(fminf(8.f * dens_sum * m_assume, 3e38f), &e);
-          e = max(e, -90);  // |G| below ~1e-27 gets a coarser quantum than needed
-          inv_q = ldexpf(1.f, 29 - e);
-          q = ldexpf(1.f, e - 29);
-        }
-        float amax = 0.f;
-        for (int i0 = 0; i0 < nh; i0 += kPrefetch * kBlock) {
-          float2 gr[kPrefetch], gm[kPrefetch];
+        // phase B: spread the hits.  The fixed-point quantum assumes the
+        // group's max |G| is at most twice the previous group's; the values
+        // actually read are checked, and a group that exceeds its assumption
+        // is cleared and redone with the measured bound (the first group of a
+        // workgroup only measures).  See the bound at kQuantumBits.
+        bool measure_only = m_prev <= 0.f;
+        float m_assume = 2.f * m_prev, q = 0.f;
+        while (nh > 0) {
+          float inv_q = 0.f;
+          if (!measure_only) {
+            int e;
+            frexpf(fminf(8.f * dens_sum * m_assume, 3e38f), &e);
+            e = max(e, -90);  // |G| below ~1e-27 gets a coarser quantum than needed
+            inv_q = ldexpf(1.f, kQuantumBits - e);
+            q = ldexpf(1.f, e - kQuantumBits);
+          }
+          float amax = 0.f;
+          for (int i0 = 0; i0 < nh; i0 += kPrefetch * kBlock) {
+            float2 gr[kPrefetch], gm[kPrefetch];
 #pragma unroll
-          for (int k = 0; k < kPrefetch; ++k) {
-            const int i = i0 + tid + k * kBlock;
-            gr[k] = gm[k] = make_float2(0.f, 0.f);
-            if (i < nh) {
+            for (int k = 0; k < kPrefetch; ++k) {
+              const int i = i0 + tid + k * kBlock;
+              gr[k] = gm[k] = make_float2(0.f, 0.f);
+              if (i < nh) {
+                const uint32_t h = s_hits[i];
+                const PoseView& pv = s_view[h >> 24];
+                lattice_load(p, (size_t)br.b * p.P + s_poses[g0 + (int)(h >> 24)], pv.kx0 + (int)(h & 0xFFFu),
+                             pv.ky0 + (int)((h >> 12) & 0xFFFu), gr[k], gm[k]);
+              }
+            }
+#pragma unroll
+            for (int k = 0; k < kPrefetch; ++k)
+              amax = fmaxf(amax, fmaxf(fabsf(gr[k].x) + fabsf(gr[k].y), fabsf(gm[k].x) + fabsf(gm[k].y)));
+            if (measure_only) continue;
+#pragma unroll
+            for (int k = 0; k < kPrefetch; ++k) {
+              const int i = i0 + tid + k * kBlock;
+              if (i >= nh) continue;
               const uint32_t h = s_hits[i];
               const PoseView& pv = s_view[h >> 24];
-              lattice_load(p, (size_t)br.b * p.P + s_poses[g0 + (int)(h >> 24)], pv.kx0 + (int)(h & 0xFFFu),
-                           pv.ky0 + (int)((h >> 12) & 0xFFFu), gr[k], gm[k]);
+              Cand cd;
+              lattice_values<NDIM>(p, pv, pv.kx0 + (int)(h & 0xFFFu), pv.ky0 + (int)((h >> 12) & 0xFFFu), gr[k],
+                                   gm[k], cd);
+              if (in_reach<NDIM, INTERP>(br, cd.q)) spread<NDIM, INTERP>(br, cd, inv_q, acc);
             }
           }
 #pragma unroll
-          for (int k = 0; k < kPrefetch; ++k)
-            amax = fmaxf(amax, fmaxf(fabsf(gr[k].x) + fabsf(gr[k].y), fabsf(gm[k].x) + fabsf(gm[k].y)));
-          if (measure_only) continue;
-#pragma unroll
-          for (int k = 0; k < kPrefetch; ++k) {
-            const int i = i0 + tid + k * kBlock;
-            if (i >= nh) continue;
-            const uint32_t h = s_hits[i];
-            const PoseView& pv = s_view[h >> 24];
-            Cand cd;
-            lattice_values<NDIM>(p, pv, pv.kx0 + (int)(h & 0xFFFu), pv.ky0 + (int)((h >> 12) & 0xFFFu), gr[k],
-                                 gm[k], cd);
-            if (in_reach<NDIM, INTERP>(br, cd.q)) spread<NDIM, INTERP>(br, cd, inv_q, acc);
-          }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-        __syncthreads();
-        if (lane == 0) s_red[wave] = amax;
-        __syncthreads();
-        float gmax = s_red[0];
-#pragma unroll
-        for (int w = 1; w < kBlock / 64; ++w) gmax = fmaxf(gmax, s_red[w]);
-        if (!(gmax > 0.f)) break;  // an all-zero group adds nothing
-        if (!measure_only && gmax <= m_assume) {
-          // flush the group into fp32 registers
-#pragma unroll
-          for (int i = 0; i < kPerThread; ++i) {
-            const int v = tid + i * kBlock;
-            const int sl = slot_of<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
-            int ir, ii;
-            unpack_pair(acc[sl], ir, ii);
-            fre[i] = fmaf((float)ir, q, fre[i]);
-            fim[i] = fmaf((float)ii, q, fim[i]);
-            acc[sl] = 0ull;
-          }
-          m_prev = gmax;
-          break;
-        }
-        if (!measure_only) {
-#pragma unroll
-          for (int i = 0; i < kPerThread; ++i) acc[tid + i * kBlock] = 0ull;
+          for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
           __syncthreads();
+          if (lane == 0) s_red[wave] = amax;
+          __syncthreads();
+          float gmax = s_red[0];
+#pragma unroll
+          for (int w = 1; w < kBlock / 64; ++w) gmax = fmaxf(gmax, s_red[w]);
+          if (!(gmax > 0.f)) break;  // an all-zero slice adds nothing
+          if (!measure_only && gmax <= m_assume) {
+            // flush the slice into fp32 registers
+#pragma unroll
+            for (int i = 0; i < kPerThread; ++i) {
+              const int v = tid + i * kBlock;
+              const int sl = slot_of<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
+              int ir, ii;
+              unpack_pair(acc[sl], ir, ii);
+              fre[i] = fmaf((float)ir, q, fre[i]);
+              fim[i] = fmaf((float)ii, q, fim[i]);
+              acc[sl] = 0ull;
+            }
+            m_prev = gmax;
+            break;
+          }
+          if (!measure_only) {
+#pragma unroll
+            for (int i = 0; i < kPerThread; ++i) acc[tid + i * kBlock] = 0ull;
+            __syncthreads();
+          }
+          m_assume = gmax;
+          measure_only = false;
         }
-        m_assume = gmax;
-        measure_only = false;
-      }
-      __syncthreads();
-      // next group
-      if (cnt == 1 && f1 < s_area[g0]) {
-        r0 = f1;
-      } else {
-        g0 = g1;
-        r0 = 0;
+        __syncthreads();
       }
     }
   }
