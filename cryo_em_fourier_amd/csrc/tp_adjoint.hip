@@ -20,6 +20,7 @@
 // proportion to the poses expected to cross them (near the origin: all of
 // them); chunks of one brick merge with coalesced float atomics, unsplit
 // bricks are written with plain stores.
+#include "tp_bricks.h"
 #include "tp_internal.h"
 #include "tp_stencil.h"
 
@@ -137,137 +138,15 @@ __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams&
   return r;
 }
 
-// Everything about one pose that the brick loop needs (uniform values).
-struct PoseView {
-  double u[3], v[3];      // p = kx u + ky v
-  double iu[3];           // 1 / u (0 where u = 0)
-  float sx, sy;
-  float dens;             // max(1, 1 / |u x v|): lattice points per unit area bound
-  int kx0, kx1, ky0, ky1; // candidate rectangle (full plane, clipped)
-  int hit;
-};
-
+// Sample points whose stencil can reach the brick lie in the brick widened
+// by the stencil reach: [x0 - r, x1 + r) per axis (r = 2 cubic, 1 linear);
+// any point outside has all its taps outside the brick.
 template <int NDIM, int INTERP>
-__device__ __forceinline__ PoseView pose_view(const OpParams& p, const BrickPos& br, int n) {
-  PoseView pv;
-  const float* R = p.rot + ((size_t)(p.B_rot == 1 ? 0 : br.b) * p.P + n) * (NDIM * NDIM);
-  const double os = (double)p.os;
-  for (int j = 0; j < 3; ++j) {
-    pv.u[j] = j < NDIM ? os * (double)R[j] : 0.0;
-    pv.v[j] = j < NDIM ? os * (double)R[NDIM + j] : 0.0;
-    pv.iu[j] = pv.u[j] != 0.0 ? 1.0 / pv.u[j] : 0.0;
-  }
-  if (p.shift) {
-    const float* s = p.shift + ((size_t)(p.B_shift == 1 ? 0 : br.b) * p.P + n) * 2;
-    pv.sx = s[0];
-    pv.sy = s[1];
-  } else {
-    pv.sx = pv.sy = 0.f;
-  }
-  // box of sample positions whose stencil reaches the brick: p_j in [t0-R, t1+R)
+__device__ __forceinline__ Box reach_box(const BrickPos& br) {
   constexpr double reach = INTERP ? 2.0 : 1.0;
-  double lo[3] = {br.x0 - reach, br.y0 - reach, br.z0 - reach};
-  double hi[3] = {br.x1 + reach, br.y1 + reach, br.z1 + reach};
-  if (NDIM == 2) { lo[2] = 0.0; hi[2] = 0.0; }
-  const double uu = pv.u[0] * pv.u[0] + pv.u[1] * pv.u[1] + pv.u[2] * pv.u[2];
-  const double vv = pv.v[0] * pv.v[0] + pv.v[1] * pv.v[1] + pv.v[2] * pv.v[2];
-  const double uv = pv.u[0] * pv.v[0] + pv.u[1] * pv.v[1] + pv.u[2] * pv.v[2];
-  const double D = uu * vv - uv * uv;
-  const int kxlim = p.No / 2, kylim = p.No / 2;
-  pv.kx0 = -kxlim; pv.kx1 = kxlim; pv.ky0 = -kylim; pv.ky1 = kylim;
-  if (p.cut2 >= 0) {
-    const int c = (int)floor(sqrt((double)p.cut2));
-    pv.kx0 = max(pv.kx0, -c); pv.kx1 = min(pv.kx1, c);
-    pv.ky0 = max(pv.ky0, -c); pv.ky1 = min(pv.ky1, c);
-  }
-  pv.hit = 1;
-  pv.dens = 1e30f;
-  if (D > 0.0 && isfinite(D)) {
-    pv.dens = (float)fmax(1.0, 1.0 / sqrt(D));
-    double ud[3], vd[3];  // dual basis: kx = p . ud, ky = p . vd for points on the plane
-    for (int j = 0; j < 3; ++j) {
-      ud[j] = (vv * pv.u[j] - uv * pv.v[j]) / D;
-      vd[j] = (uu * pv.v[j] - uv * pv.u[j]) / D;
-    }
-    // plane through the origin with normal u x v must cross the box
-    double nrm[3] = {pv.u[1] * pv.v[2] - pv.u[2] * pv.v[1], pv.u[2] * pv.v[0] - pv.u[0] * pv.v[2],
-                     pv.u[0] * pv.v[1] - pv.u[1] * pv.v[0]};
-    double mn = 0.0, mx = 0.0, kmin[2] = {0.0, 0.0}, kmax[2] = {0.0, 0.0};
-    for (int j = 0; j < 3; ++j) {
-      const double a = lo[j] * nrm[j], b = hi[j] * nrm[j];
-      mn += fmin(a, b);
-      mx += fmax(a, b);
-      const double xa = lo[j] * ud[j], xb = hi[j] * ud[j];
-      kmin[0] += fmin(xa, xb);
-      kmax[0] += fmax(xa, xb);
-      const double ya = lo[j] * vd[j], yb = hi[j] * vd[j];
-      kmin[1] += fmin(ya, yb);
-      kmax[1] += fmax(ya, yb);
-    }
-    const double slack = 1e-9 * (fabs(mn) + fabs(mx) + 1.0);
-    if (NDIM == 3 && (mn > slack || mx < -slack)) pv.hit = 0;
-    if (fabs(kmin[0]) < 1e9 && fabs(kmax[0]) < 1e9 && fabs(kmin[1]) < 1e9 && fabs(kmax[1]) < 1e9) {
-      pv.kx0 = max(pv.kx0, (int)floor(kmin[0]) - 1);
-      pv.kx1 = min(pv.kx1, (int)ceil(kmax[0]) + 1);
-      pv.ky0 = max(pv.ky0, (int)floor(kmin[1]) - 1);
-      pv.ky1 = min(pv.ky1, (int)ceil(kmax[1]) + 1);
-    }
-  }  // degenerate rows: no dual basis; visit the whole clipped plane
-  if (!(isfinite(pv.u[0]) && isfinite(pv.u[1]) && isfinite(pv.u[2]) && isfinite(pv.v[0]) &&
-        isfinite(pv.v[1]) && isfinite(pv.v[2])))
-    pv.hit = 0;
-  if (pv.kx0 > pv.kx1 || pv.ky0 > pv.ky1) pv.hit = 0;
-  // every weight is at most 1 in magnitude, so a pose adds at most its
-  // rectangle's lattice count of them to a voxel: this caps the density
-  // bound of nearly degenerate rows
-  if (pv.hit) pv.dens = fminf(pv.dens, 0.25f * (float)(pv.kx1 - pv.kx0 + 1) * (float)(pv.ky1 - pv.ky0 + 1) + 1.f);
-  return pv;
-}
-
-// Scan test: can pose n's sample plane bring a kept lattice point into reach
-// of the brick?  The plane (through the origin, normal u x v) must cross the
-// reach box, and the box must come within the largest |p| of a kept output
-// (cutoff or the output box, times the largest stretch of the rows).
-template <int NDIM, int INTERP>
-__device__ __forceinline__ bool plane_meets(const OpParams& p, const BrickPos& br, int n) {
-  const float* R = p.rot + ((size_t)(p.B_rot == 1 ? 0 : br.b) * p.P + n) * (NDIM * NDIM);
-  const double os = (double)p.os;
-  double u[3], v[3];
-  for (int j = 0; j < 3; ++j) {
-    u[j] = j < NDIM ? os * (double)R[j] : 0.0;
-    v[j] = j < NDIM ? os * (double)R[NDIM + j] : 0.0;
-  }
-  if (!(isfinite(u[0]) && isfinite(u[1]) && isfinite(u[2]) && isfinite(v[0]) && isfinite(v[1]) &&
-        isfinite(v[2])))
-    return false;
-  constexpr double reach = INTERP ? 2.0 : 1.0;
-  double lo[3] = {br.x0 - reach, br.y0 - reach, br.z0 - reach};
-  double hi[3] = {br.x1 + reach, br.y1 + reach, br.z1 + reach};
-  if (NDIM == 2) { lo[2] = 0.0; hi[2] = 0.0; }
-  if (NDIM == 3) {
-    const double nrm[3] = {u[1] * v[2] - u[2] * v[1], u[2] * v[0] - u[0] * v[2], u[0] * v[1] - u[1] * v[0]};
-    double mn = 0.0, mx = 0.0;
-    for (int j = 0; j < 3; ++j) {
-      const double a = lo[j] * nrm[j], b = hi[j] * nrm[j];
-      mn += fmin(a, b);
-      mx += fmax(a, b);
-    }
-    const double slack = 1e-9 * (fabs(mn) + fabs(mx) + 1.0);
-    if (mn > slack || mx < -slack) return false;
-  }
-  // |p|^2 <= |k|^2 * largest eigenvalue of the rows' Gram matrix
-  const double uu = u[0] * u[0] + u[1] * u[1] + u[2] * u[2];
-  const double vv = v[0] * v[0] + v[1] * v[1] + v[2] * v[2];
-  const double uv = u[0] * v[0] + u[1] * v[1] + u[2] * v[2];
-  const double lmax = 0.5 * (uu + vv) + sqrt(0.25 * (uu - vv) * (uu - vv) + uv * uv);
-  const double h = 0.5 * p.No;
-  const double k2 = p.cut2 >= 0 ? fmin((double)p.cut2, 2.0 * h * h) : 2.0 * h * h;
-  double d2 = 0.0;  // squared distance from the origin to the reach box
-  for (int j = 0; j < NDIM; ++j) {
-    const double d = lo[j] > 0.0 ? lo[j] : (hi[j] < 0.0 ? -hi[j] : 0.0);
-    d2 += d * d;
-  }
-  return d2 <= k2 * lmax * (1.0 + 1e-9) + 1e-9;
+  Box bx = {{br.x0 - reach, br.y0 - reach, br.z0 - reach}, {br.x1 + reach, br.y1 + reach, br.z1 + reach}};
+  if (NDIM == 2) bx.lo[2] = bx.hi[2] = 0.0;
+  return bx;
 }
 
 // A lattice point (kx, ky) of the full plane carries the real output (kx, ky)
@@ -276,64 +155,6 @@ __device__ __forceinline__ void lattice_parts(const OpParams& p, int kx, int ky,
   const int rlo = -(p.No / 2), rhi = (p.No - 1) / 2;
   real = kx >= 0 && kx <= p.No / 2 && ky >= rlo && ky <= rhi;
   mirr = kx <= 0 && -kx <= p.No / 2 && -ky >= rlo && -ky <= rhi;
-}
-
-__device__ __forceinline__ size_t out_index(const OpParams& p, size_t img, int kx, int ky) {
-  return (img * p.No + (ky < 0 ? ky + p.No : ky)) * p.Wo + kx;
-}
-
-// Sample points whose stencil can reach the brick lie in the brick widened
-// by the stencil reach: [x0 - r, x1 + r) per axis (r = 2 cubic, 1 linear);
-// any point outside has all its taps outside the brick.
-template <int NDIM, int INTERP>
-__device__ __forceinline__ bool in_reach(const BrickPos& br, const double* q) {
-  constexpr double reach = INTERP ? 2.0 : 1.0;
-  const double lo[3] = {br.x0 - reach, br.y0 - reach, br.z0 - reach};
-  const double hi[3] = {br.x1 + reach, br.y1 + reach, br.z1 + reach};
-  bool in = true;
-#pragma unroll
-  for (int j = 0; j < NDIM; ++j) in = in && q[j] >= lo[j] && q[j] < hi[j];
-  return in;
-}
-
-// Phase A: the kx range [a, b] of row ky whose sample points fall in the
-// reach box widened by 1e-6 (the margin covers the rounding of this fp64
-// arithmetic; a point within rounding of the reach boundary has weight ~0 in
-// the brick either way), clipped to the pose's rectangle and to the cutoff
-// disk.  Empty when b < a.
-template <int NDIM, int INTERP>
-__device__ __forceinline__ void row_range(const OpParams& p, const BrickPos& br, const PoseView& pv, int ky,
-                                          int& a, int& b) {
-  constexpr double reach = (INTERP ? 2.0 : 1.0) + 1e-6;
-  const double lo[3] = {br.x0 - reach, br.y0 - reach, br.z0 - reach};
-  const double hi[3] = {br.x1 + reach, br.y1 + reach, br.z1 + reach};
-  double ta = (double)pv.kx0, tb = (double)pv.kx1;
-  bool empty = false;
-#pragma unroll
-  for (int j = 0; j < NDIM; ++j) {
-    const double c = (double)ky * pv.v[j];
-    if (pv.iu[j] == 0.0) {
-      empty = empty || !(c >= lo[j] && c < hi[j]);
-    } else {
-      const double t0 = (lo[j] - c) * pv.iu[j], t1 = (hi[j] - c) * pv.iu[j];
-      ta = fmax(ta, fmin(t0, t1));
-      tb = fmin(tb, fmax(t0, t1));
-    }
-  }
-  if (p.cut2 >= 0) {
-    const long long rem = p.cut2 - (long long)ky * ky;
-    if (rem < 0) {
-      empty = true;
-    } else {
-      long long m = (long long)sqrt((double)rem);
-      while ((m + 1) * (m + 1) <= rem) ++m;
-      while (m * m > rem) --m;
-      ta = fmax(ta, (double)-m);
-      tb = fmin(tb, (double)m);
-    }
-  }
-  a = (int)ceil(ta);
-  b = empty ? a - 1 : (int)floor(tb);
 }
 
 // G entries of a lattice point: the real output (kx, ky) and the real output
@@ -443,85 +264,26 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     acc[tid + i * kBlock] = 0ull;
   }
 
+  const Box bx = reach_box<NDIM, INTERP>(br);
   for (int w0 = br.n0; w0 < br.n1; w0 += kBlock) {
-    // one pose per thread: can its plane reach this brick?  ordered compaction
-    const int n = w0 + tid;
-    const bool hit = n < br.n1 && plane_meets<NDIM, INTERP>(p, br, n);
-    const unsigned long long m = __ballot(hit);
-    __syncthreads();
-    if (lane == 0) s_wcnt[wave] = __popcll(m);
-    __syncthreads();
-    int off = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) {
-      off += w < wave ? s_wcnt[w] : 0;
-      total += s_wcnt[w];
-    }
-    if (hit) s_poses[off + __popcll(m & ((1ull << lane) - 1ull))] = n;
-    __syncthreads();
+    // the poses whose plane can reach this brick, in order
+    const int total = scan_poses<NDIM>(p, br.b, bx, w0, br.n1, s_poses, s_wcnt);
 
     // groups of up to kGroupMax poses; a group whose lattice points overflow
     // the hit list is spread in slices of kHitCap
     for (int g0 = 0; g0 < total; g0 += kGroupMax) {
       const int cnt = min(kGroupMax, total - g0);
-      if (tid < cnt) s_view[tid] = pose_view<NDIM, INTERP>(p, br, s_poses[g0 + tid]);
+      if (tid < cnt) s_view[tid] = pose_view<NDIM>(p, br.b, bx, s_poses[g0 + tid], false);
       __syncthreads();
       float dens_sum = 0.f;
-      int rows_total = 0;
-      for (int g = 0; g < cnt; ++g) {
-        const PoseView& pv = s_view[g];
-        if (!pv.hit) continue;
-        dens_sum += pv.dens;
-        rows_total += pv.ky1 - pv.ky0 + 1;
-      }
+      for (int g = 0; g < cnt; ++g)
+        if (s_view[g].hit) dens_sum += s_view[g].dens;
 
       for (int h0 = 0, hits_total = 1; h0 < hits_total; h0 += kHitCap) {
-        // phase A: list the lattice points that can reach the brick, row by
-        // row; the flat index runs over the rows of pose 0, then pose 1, ...;
-        // this slice keeps the flat indices [h0, h0 + kHitCap)
-        const int h1 = h0 + kHitCap;
-        int carry = 0;
-        for (int rw = 0; rw < rows_total; rw += kBlock) {
-          const int r = rw + tid;
-          int g = 0, cr = 0, a = 0, dky = 0;
-          if (r < rows_total) {
-            int rb = 0;
-            while (true) {
-              const PoseView& pv = s_view[g];
-              const int H = pv.hit ? pv.ky1 - pv.ky0 + 1 : 0;
-              if (r < rb + H) break;
-              rb += H;
-              ++g;
-            }
-            const PoseView& pv = s_view[g];
-            dky = r - rb;
-            int b;
-            row_range<NDIM, INTERP>(p, br, pv, pv.ky0 + dky, a, b);
-            cr = max(0, b - a + 1);
-            a -= pv.kx0;
-          }
-          // exclusive block scan of the row counts
-          int incl = cr;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const int t = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += t;
-          }
-          if (lane == 63) s_wcnt[wave] = incl;
-          __syncthreads();
-          int off = carry + incl - cr, tot = 0;
-#pragma unroll
-          for (int w = 0; w < kBlock / 64; ++w) {
-            off += w < wave ? s_wcnt[w] : 0;
-            tot += s_wcnt[w];
-          }
-          const uint32_t tag = ((uint32_t)g << 24) | ((uint32_t)dky << 12);
-          for (int j = max(0, h0 - off); j < cr && off + j < h1; ++j) s_hits[off + j - h0] = tag | (uint32_t)(a + j);
-          carry += tot;
-          __syncthreads();
-        }
-        hits_total = carry;
-        const int nh = max(0, min(carry, h1) - h0);
+        // phase A: list the lattice points that can reach the brick (this
+        // slice keeps the flat indices [h0, h0 + kHitCap))
+        hits_total = list_hits<NDIM, kGroupMax>(p, bx, s_view, cnt, h0, kHitCap, s_hits, s_wcnt);
+        const int nh = max(0, min(hits_total, h0 + kHitCap) - h0);
 
         // phase B: spread the hits.  The fixed-point quantum assumes the
         // group's max |G| is at most twice the previous group's; the values
@@ -548,9 +310,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
               gr[k] = gm[k] = make_float2(0.f, 0.f);
               if (i < nh) {
                 const uint32_t h = s_hits[i];
-                const PoseView& pv = s_view[h >> 24];
-                lattice_load(p, (size_t)br.b * p.P + s_poses[g0 + (int)(h >> 24)], pv.kx0 + (int)(h & 0xFFFu),
-                             pv.ky0 + (int)((h >> 12) & 0xFFFu), gr[k], gm[k]);
+                const PoseView& pv = s_view[hit_pose(h)];
+                lattice_load(p, (size_t)br.b * p.P + s_poses[g0 + hit_pose(h)], hit_kx(h, pv), hit_ky(h, pv), gr[k],
+                             gm[k]);
               }
             }
 #pragma unroll
@@ -562,11 +324,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
               const int i = i0 + tid + k * kBlock;
               if (i >= nh) continue;
               const uint32_t h = s_hits[i];
-              const PoseView& pv = s_view[h >> 24];
+              const PoseView& pv = s_view[hit_pose(h)];
               Cand cd;
-              lattice_values<NDIM>(p, pv, pv.kx0 + (int)(h & 0xFFFu), pv.ky0 + (int)((h >> 12) & 0xFFFu), gr[k],
-                                   gm[k], cd);
-              if (in_reach<NDIM, INTERP>(br, cd.q)) spread<NDIM, INTERP>(br, cd, inv_q, acc);
+              lattice_values<NDIM>(p, pv, hit_kx(h, pv), hit_ky(h, pv), gr[k], gm[k], cd);
+              if (in_box<NDIM>(bx, cd.q)) spread<NDIM, INTERP>(br, cd, inv_q, acc);
             }
           }
 #pragma unroll

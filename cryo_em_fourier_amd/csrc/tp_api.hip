@@ -103,8 +103,8 @@ tp_status backproject(int ndim, const tp_c64* proj, int64_t B, int64_t P, int64_
   const Common c{B, N, P, N_out, B_rot, B_shift, interp, ndim, os, cutoff, rot, shift};
   const tp_status st = check_and_fill(c, p);
   if (st != TP_OK) return st;
-  // the adjoint's lattice lists hold 12-bit offsets within an output image
-  if (N_out > 4095 || B > 65535 || tp::adjoint_blocks(p) > kMaxBlocks) return TP_EUNSUPPORTED;
+  // the brick kernels' lattice lists hold 14-bit offsets within an output image
+  if (N_out > tp::kMaxBrickOut || B > 65535 || tp::adjoint_blocks(p) > kMaxBlocks) return TP_EUNSUPPORTED;
   p.img = reinterpret_cast<const float2*>(proj);
   p.ref_out = reinterpret_cast<float2*>(ref_out);
   const hipStream_t s = (hipStream_t)stream;

@@ -363,6 +363,7 @@ hipError_t launch_project(const OpParams& p, int interp, hipStream_t s) {
 hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s) {
   const dim3 grid(p.nblocks), block(kBlock);
   if (p.ndim == 3) {
+    if (use_grad_bricks(p, interp)) return launch_grad_bricks(p, interp, s);
     if (interp) hipLaunchKernelGGL((k_grad3p<1>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((k_grad3p<0>), grid, block, 0, s, p);
   } else {

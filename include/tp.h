@@ -57,8 +57,8 @@
  *                    bad interp, oversampling <= 0 or not finite, cutoff NaN,
  *                    B_rot or B_shift not in {1, B}, ndim not in {2, 3};
  *   TP_EUNSUPPORTED  a reference entry larger than 2^31 - 4096 bytes, a box
- *                    above 65535 (N_out above 4095 for the adjoints), or a
- *                    launch grid above 2^31 - 1 blocks;
+ *                    above 65535, a launch grid above 2^31 - 1 blocks, or,
+ *                    for the adjoints, N_out above 16383 or B above 65535;
  *   TP_EHIP          the HIP runtime reported an error at launch.
  *   Nothing is thrown across the ABI.
  * Results.  Forward and pose gradients are deterministic up to the order of

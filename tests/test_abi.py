@@ -85,6 +85,8 @@ def test_project_3d_argument_checks(kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(proj=None), EINVAL), (dict(out=None), EINVAL), (dict(interp=5), EINVAL),
     (dict(os=0.0), EINVAL), (dict(B=3, B_rot=2), EINVAL), (dict(N=2000), EUNSUP),
+    (dict(N_out=16384), EUNSUP),            # 14-bit lattice offsets in the hit lists
+    (dict(B=70000, B_rot=1), EUNSUP),       # the batch is a grid dimension
 ])
 def test_backproject_3d_argument_checks(kw, code):
     assert back3(**kw) == code

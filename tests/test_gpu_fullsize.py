@@ -221,3 +221,41 @@ def test_largest_adjoint_output_box():
     assert_parity(out, oracle.project(V, R, s, n_out, 0, os_, cutoff), "forward N_out=4095")
     got = tp_backproject_3d(to_dev(G), Rd, sd, N, 0, float(os_), float(cutoff)).cpu().numpy()
     assert_parity(got, oracle.backproject(G, R, s, N, 0, os_, cutoff), "adjoint N_out=4095")
+
+
+# ------------------------------------------- brick gather of the pose gradients
+
+@pytest.mark.parametrize("interp,os_,batch", [(1, 1.0, 1), (0, 1.0, 1), (1, 1.2, 2), (0, 1.25, 1)])
+def test_grad_bricks_against_oracle(interp, os_, batch):
+    """Box >= 192, >= 256 poses, oversampling <= 1.25: the sizes where the
+    gradients run as the LDS brick gather.  Every pose is processed; the
+    upstream gradient is nonzero on a sample that includes on-grid and
+    x = 0-plane poses (linear kinks at integer coordinates: both sides take the
+    right derivative in p)."""
+    import torch
+
+    from cryo_em_fourier_amd import tp_grad_pose
+    from test_gpu_parity import adversarial_rotations
+
+    N, P = 200, 260
+    n_out = int(round(N / os_))
+    rng = np.random.default_rng(200 + interp + 10 * batch)
+    V = np.stack([synth.rfft_spectrum(synth.blob_volume(rng, int(N / os_) if os_ != 1.0 else N, 60), 3,
+                                      pad_to=N if os_ != 1.0 else None) for _ in range(batch)]).astype(np.complex64)
+    R = np.stack([synth.uniform_rotations(rng, P) for _ in range(batch)])
+    R[:, :8] = adversarial_rotations(rng)
+    s = rng.uniform(-6, 6, (batch, P, 2)).astype(np.float32)
+    cutoff = np.float32(n_out // 2 - 1)
+    idx = np.array([0, 1, 2, 3, 4, 7, 100, 259])
+    G_sub = ((rng.standard_normal((batch, len(idx), n_out, n_out // 2 + 1))
+              + 1j * rng.standard_normal((batch, len(idx), n_out, n_out // 2 + 1))) * np.sqrt(0.5)).astype(np.complex64)
+    log(f"[grad bricks] N={N} P={P} B={batch} interp={interp} os={os_} n_out={n_out}")
+    G = torch.zeros((batch, P, n_out, n_out // 2 + 1), dtype=torch.complex64, device="cuda")
+    G[:, torch.from_numpy(idx).cuda()] = to_dev(G_sub)
+    gr, gs = tp_grad_pose(to_dev(V), G, to_dev(R), to_dev(s), interp, os_, float(cutoff))
+    gr, gs = gr.cpu().numpy(), gs.cpu().numpy()
+    dR, ds = oracle.grad_pose(V, G_sub, R[:, idx], s[:, idx], n_out, interp, np.float32(os_), cutoff)
+    assert_parity(gr[:, idx], dR, f"grad_rot bricks interp={interp} os={os_}")
+    assert_parity(gs[:, idx], ds, f"grad_shift bricks interp={interp} os={os_}")
+    rest = np.setdiff1d(np.arange(P), idx)
+    assert not gr[:, rest].any() and not gs[:, rest].any()
