@@ -181,8 +181,11 @@ __device__ __forceinline__ void lattice_values(const OpParams& p, const PoseView
   for (int j = 0; j < NDIM; ++j) cd.q[j] = (double)kx * pv.u[j] + (double)ky * pv.v[j];
   float2 cr = gr, cm = gm;
   if (p.shift) {
-    cr = cmul(conjf2(shift_phase(kx, ky, pv.sx, pv.sy, p.inv_no)), gr);
-    cm = cmul(conjf2(shift_phase(-kx, -ky, pv.sx, pv.sy, p.inv_no)), gm);
+    // conj(phase(k)) G(k), and for the mirror conj(phase(-k)) G(-k) =
+    // phase(k) G(-k): one phase per lattice point
+    const float2 ph = shift_phase(kx, ky, pv.sx, pv.sy, p.inv_no);
+    cr = cmul(conjf2(ph), gr);
+    cm = cmul(ph, gm);
   }
   cd.v0 = cr;
   cd.v1 = make_float2(cr.x + cm.x, cr.y - cm.y);
@@ -219,8 +222,9 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
     const bool inx = tx >= br.x0 && tx <= br.x1;
     are[d] = inx ? wx[d] * v.x * inv_q : 0.f;
     aim[d] = inx ? wx[d] * v.y * inv_q : 0.f;
-    xl[d] = inx ? tx - br.x0 : 0;
+    xl[d] = (inx ? tx - br.x0 : 0) * (int)sizeof(unsigned long long);  // byte offset in the row
   }
+  char* accb = reinterpret_cast<char*>(acc);
 #pragma unroll
   for (int dz = 0; dz < (NDIM == 3 ? T : 1); ++dz) {
     const int tz = z0 + dz;
@@ -231,11 +235,13 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
       if (ty < br.y0 || ty > br.y1) continue;
       const float wyz = wy[dy] * wz[dz];
       const int yl = ty - br.y0, zl = NDIM == 3 ? tz - br.z0 : 0;
-      const int row = (zl * BR::Y + yl) * BR::X, h = row_hash<NDIM>(yl, zl);
+      // slot_of() in bytes: the shift distributes over | and ^
+      constexpr int E = (int)sizeof(unsigned long long);
+      const int row = (zl * BR::Y + yl) * BR::X * E, h = row_hash<NDIM>(yl, zl) * E;
 #pragma unroll
       for (int dx = 0; dx < T; ++dx) {
         const int ir = cvt_rpi(are[dx] * wyz), ii = cvt_rpi(aim[dx] * wyz);
-        atomicAdd(&acc[row | (xl[dx] ^ h)], pack_pair(ir, ii));
+        atomicAdd(reinterpret_cast<unsigned long long*>(accb + (row | (xl[dx] ^ h))), pack_pair(ir, ii));
       }
     }
   }
