@@ -4,21 +4,35 @@ The HIP library (libtp.so, C ABI in include/tp.h) is loaded on first use;
 importing the package does not touch the GPU.
 """
 from .ops import (  # noqa: F401
+    backproject_2d,
+    backproject_3d,
+    backproject_weights_2d,
+    backproject_weights_3d,
     project_2d,
     project_3d,
     tp_backproject_2d,
     tp_backproject_3d,
+    tp_backproject_weights_2d,
+    tp_backproject_weights_3d,
     tp_grad_pose,
     tp_project_2d,
     tp_project_3d,
+    tp_symmetrize_x0,
 )
 
 __all__ = [
+    "backproject_2d",
+    "backproject_3d",
+    "backproject_weights_2d",
+    "backproject_weights_3d",
     "project_2d",
     "project_3d",
     "tp_backproject_2d",
     "tp_backproject_3d",
+    "tp_backproject_weights_2d",
+    "tp_backproject_weights_3d",
     "tp_grad_pose",
     "tp_project_2d",
     "tp_project_3d",
+    "tp_symmetrize_x0",
 ]

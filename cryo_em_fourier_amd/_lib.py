@@ -23,6 +23,9 @@ EXPORTS = (
     "tp_project_2d",
     "tp_backproject_2d",
     "tp_grad_pose",
+    "tp_backproject_weights_3d",
+    "tp_backproject_weights_2d",
+    "tp_symmetrize_x0",
 )
 
 _vp = ctypes.c_void_p
@@ -43,6 +46,11 @@ _SIGS = {
     # grad_rot, grad_shift, stream
     "tp_grad_pose": ([_int, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32,
                       _vp, _vp, _vp], _int),
+    # weights, B, P, N_out, rot, B_rot, N, interp, os, cutoff, wref_out, stream
+    "tp_backproject_weights_3d": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp], _int),
+    "tp_backproject_weights_2d": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp], _int),
+    # ndim, ref, B, N, stream
+    "tp_symmetrize_x0": ([_int, _vp, _i64, _i64, _vp], _int),
 }
 
 _lib = None

@@ -159,12 +159,19 @@ __device__ __forceinline__ void lattice_parts(const OpParams& p, int kx, int ky,
 
 // G entries of a lattice point: the real output (kx, ky) and the real output
 // (-kx, -ky) whose mirror it carries (zero where absent).
+// (WEIGHTS: real weights, as (w, 0).)
+template <bool WEIGHTS>
 __device__ __forceinline__ void lattice_load(const OpParams& p, size_t img, int kx, int ky, float2& gr,
                                              float2& gm) {
   bool real, mirr;
   lattice_parts(p, kx, ky, real, mirr);
-  gr = real ? p.img[out_index(p, img, kx, ky)] : make_float2(0.f, 0.f);
-  gm = mirr ? p.img[out_index(p, img, -kx, -ky)] : make_float2(0.f, 0.f);
+  if (WEIGHTS) {
+    gr = make_float2(real ? p.wimg[out_index(p, img, kx, ky)] : 0.f, 0.f);
+    gm = make_float2(mirr ? p.wimg[out_index(p, img, -kx, -ky)] : 0.f, 0.f);
+  } else {
+    gr = real ? p.img[out_index(p, img, kx, ky)] : make_float2(0.f, 0.f);
+    gm = mirr ? p.img[out_index(p, img, -kx, -ky)] : make_float2(0.f, 0.f);
+  }
 }
 
 // Phase B: sample point and the values spread by a lattice point that hit.
@@ -247,7 +254,7 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
   }
 }
 
-template <int NDIM, int INTERP>
+template <int NDIM, int INTERP, bool WEIGHTS>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_adjoint_bricks(OpParams p,
                                                                                            BrickParams bp) {
   using BR = Brick<NDIM>;
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
               if (i < nh) {
                 const uint32_t h = s_hits[i];
                 const PoseView& pv = s_view[hit_pose(h)];
-                lattice_load(p, (size_t)br.b * p.P + s_poses[g0 + hit_pose(h)], hit_kx(h, pv), hit_ky(h, pv), gr[k],
+                lattice_load<WEIGHTS>(p, (size_t)br.b * p.P + s_poses[g0 + hit_pose(h)], hit_kx(h, pv), hit_ky(h, pv), gr[k],
                              gm[k]);
               }
             }
@@ -375,6 +382,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 
   // write the brick: plain stores, or float atomics for pose-chunked bricks
   float2* out = p.ref_out + (size_t)br.b * p.ref_elems;
+  float* wout = p.wref_out + (size_t)br.b * p.ref_elems;
   const int wh = p.N / 2 + 1;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
@@ -385,6 +393,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     if (x > br.x1 || y > br.y1 || (NDIM == 3 && z > br.z1)) continue;
     const size_t row = NDIM == 3 ? (size_t)(z < 0 ? z + p.N : z) * p.N + (y < 0 ? y + p.N : y)
                                  : (size_t)(y < 0 ? y + p.N : y);
+    if (WEIGHTS) {
+      float* wdst = wout + row * wh + x;
+      if (br.chunked) {
+        if (fre[i] != 0.f) unsafeAtomicAdd(wdst, fre[i]);
+      } else {
+        *wdst = fre[i];
+      }
+      continue;
+    }
     float2* dst = out + row * wh + x;
     if (br.chunked) {
       if (fre[i] != 0.f) unsafeAtomicAdd(&dst->x, fre[i]);
@@ -420,11 +437,24 @@ hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s) {
   const BrickParams bp = p.ndim == 3 ? brick_params<3>(p) : brick_params<2>(p);
   const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kBlock);
   if (p.ndim == 3) {
-    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1>), grid, block, 0, s, p, bp);
-    else hipLaunchKernelGGL((k_adjoint_bricks<3, 0>), grid, block, 0, s, p, bp);
+    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, false>), grid, block, 0, s, p, bp);
+    else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, false>), grid, block, 0, s, p, bp);
   } else {
-    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<2, 1>), grid, block, 0, s, p, bp);
-    else hipLaunchKernelGGL((k_adjoint_bricks<2, 0>), grid, block, 0, s, p, bp);
+    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<2, 1, false>), grid, block, 0, s, p, bp);
+    else hipLaunchKernelGGL((k_adjoint_bricks<2, 0, false>), grid, block, 0, s, p, bp);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backproject_weights(const OpParams& p, int interp, hipStream_t s) {
+  const BrickParams bp = p.ndim == 3 ? brick_params<3>(p) : brick_params<2>(p);
+  const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kBlock);
+  if (p.ndim == 3) {
+    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, true>), grid, block, 0, s, p, bp);
+    else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, true>), grid, block, 0, s, p, bp);
+  } else {
+    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<2, 1, true>), grid, block, 0, s, p, bp);
+    else hipLaunchKernelGGL((k_adjoint_bricks<2, 0, true>), grid, block, 0, s, p, bp);
   }
   return hipGetLastError();
 }

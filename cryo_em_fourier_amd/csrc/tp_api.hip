@@ -113,6 +113,23 @@ tp_status backproject(int ndim, const tp_c64* proj, int64_t B, int64_t P, int64_
   return hip_status(tp::launch_backproject(p, interp, s));
 }
 
+tp_status backproject_weights(int ndim, const float* w, int64_t B, int64_t P, int64_t N_out,
+                              const float* rot, int64_t B_rot, int64_t N, int interp, float os,
+                              float cutoff, float* wref_out, void* stream) {
+  if (!w || !wref_out || !aligned4(w) || !aligned4(wref_out)) return TP_EINVAL;
+  tp::OpParams p;
+  const Common c{B, N, P, N_out, B_rot, 1, interp, ndim, os, cutoff, rot, nullptr};
+  const tp_status st = check_and_fill(c, p);
+  if (st != TP_OK) return st;
+  if (N_out > tp::kMaxBrickOut || B > 65535 || tp::adjoint_blocks(p) > kMaxBlocks) return TP_EUNSUPPORTED;
+  p.wimg = w;
+  p.wref_out = wref_out;
+  const hipStream_t s = (hipStream_t)stream;
+  if (tp::launch_zero(wref_out, (size_t)p.B * (size_t)p.ref_elems * sizeof(float), s) != hipSuccess)
+    return TP_EHIP;
+  return hip_status(tp::launch_backproject_weights(p, interp, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -157,6 +174,30 @@ tp_status tp_backproject_2d(const tp_c64* proj, int64_t B, int64_t P, int64_t N_
                             tp_c64* img_out, void* stream) {
   return backproject(2, proj, B, P, N_out, rot, B_rot, shift, B_shift, N, interp, oversampling,
                      cutoff, img_out, stream);
+}
+
+tp_status tp_backproject_weights_3d(const float* weights, int64_t B, int64_t P, int64_t N_out,
+                                    const float* rot, int64_t B_rot, int64_t N, int interp,
+                                    float oversampling, float cutoff, float* wvol_out, void* stream) {
+  return backproject_weights(3, weights, B, P, N_out, rot, B_rot, N, interp, oversampling, cutoff, wvol_out,
+                             stream);
+}
+
+tp_status tp_backproject_weights_2d(const float* weights, int64_t B, int64_t P, int64_t N_out,
+                                    const float* rot, int64_t B_rot, int64_t N, int interp,
+                                    float oversampling, float cutoff, float* wimg_out, void* stream) {
+  return backproject_weights(2, weights, B, P, N_out, rot, B_rot, N, interp, oversampling, cutoff, wimg_out,
+                             stream);
+}
+
+tp_status tp_symmetrize_x0(int ndim, tp_c64* ref, int64_t B, int64_t N, void* stream) {
+  if (ndim != 2 && ndim != 3) return TP_EINVAL;
+  if (!ref || !aligned8(ref) || B <= 0 || N <= 0) return TP_EINVAL;
+  if (N > kMaxBox || B > 0x7FFFFFFF) return TP_EUNSUPPORTED;
+  const uint64_t rows = (uint64_t)B * (uint64_t)N * (uint64_t)(ndim == 3 ? N : 1);
+  if ((rows + 255) / 256 > kMaxBlocks) return TP_EUNSUPPORTED;
+  return hip_status(tp::launch_symmetrize_x0(reinterpret_cast<float2*>(ref), ndim, (int)B, (int)N,
+                                             (hipStream_t)stream));
 }
 
 tp_status tp_grad_pose(int ndim, const tp_c64* ref, int64_t B, int64_t N, const tp_c64* grad_out,

@@ -16,6 +16,8 @@ struct OpParams {
   const float* shift;     // [B_shift, P, 2] or nullptr
   float* grad_rot;        // [B_rot, P, d, d] or nullptr
   float* grad_shift;      // [B_shift, P, 2] or nullptr
+  const float* wimg;      // real weights [B, P, No, No/2+1] (weight backprojection)
+  float* wref_out;        // real weight volume, the reference's shape
   int B, P, N, No, Wo, B_rot, B_shift, ndim;
   float os;
   long long cut2;         // keep kx^2+ky^2 <= cut2; -1: keep everything
@@ -43,6 +45,8 @@ constexpr int kTileYPairs = 8;
 
 hipError_t launch_project(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s);
+hipError_t launch_backproject_weights(const OpParams& p, int interp, hipStream_t s);
+hipError_t launch_symmetrize_x0(float2* ref, int ndim, int B, int N, hipStream_t s);
 hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
 uint64_t adjoint_blocks(const OpParams& p);

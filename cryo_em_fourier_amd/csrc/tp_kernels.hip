@@ -329,6 +329,30 @@ __global__ __launch_bounds__(kBlock) void k_grad3p(OpParams p) {
   }
 }
 
+// Hermitian symmetry of the x = 0 plane: V(0, y, z) <- (V(0, y, z) +
+// conj V(0, -y, -z)) / 2, indices mod N (self-mirrored entries keep their
+// real part).  One thread per mirror pair, so the update is in place.
+template <int NDIM>
+__global__ __launch_bounds__(kBlock) void k_symmetrize_x0(float2* ref, int B, int N) {
+  const long long per = NDIM == 3 ? (long long)N * N : (long long)N;
+  const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= per * B) return;
+  const int b = (int)(i / per);
+  const int r = (int)(i % per);
+  const int iy = r % N, iz = NDIM == 3 ? r / N : 0;
+  const int my = (N - iy) % N, mz = NDIM == 3 ? (N - iz) % N : 0;
+  const int mr = mz * N + my;
+  if (mr < r) return;  // the pair's other thread does it
+  const size_t wh = (size_t)(N / 2 + 1);
+  float2* base = ref + (size_t)b * (size_t)per * wh;
+  float2* a = base + (size_t)r * wh;
+  float2* c = base + (size_t)mr * wh;
+  const float2 va = *a, vc = *c;
+  const float2 h = make_float2(0.5f * (va.x + vc.x), 0.5f * (va.y - vc.y));
+  *a = h;
+  *c = make_float2(h.x, -h.y);
+}
+
 __global__ __launch_bounds__(kBlock) void k_zero(uint32_t* ptr, size_t words) {
   const size_t stride = (size_t)gridDim.x * kBlock;
   for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < words; i += stride) ptr[i] = 0u;
@@ -370,6 +394,14 @@ hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s) {
     if (interp) hipLaunchKernelGGL((k_grad_pose<2, 1>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((k_grad_pose<2, 0>), grid, block, 0, s, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_symmetrize_x0(float2* ref, int ndim, int B, int N, hipStream_t s) {
+  const long long n = (long long)B * N * (ndim == 3 ? N : 1);
+  const dim3 grid((unsigned)((n + kBlock - 1) / kBlock)), block(kBlock);
+  if (ndim == 3) hipLaunchKernelGGL((k_symmetrize_x0<3>), grid, block, 0, s, ref, B, N);
+  else hipLaunchKernelGGL((k_symmetrize_x0<2>), grid, block, 0, s, ref, B, N);
   return hipGetLastError();
 }
 

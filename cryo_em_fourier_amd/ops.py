@@ -1,13 +1,26 @@
 """PyTorch-facing binding of the projector.
 
 ``tp_project_3d``, ``tp_backproject_3d``, ``tp_project_2d``,
-``tp_backproject_2d`` and ``tp_grad_pose`` mirror the C ABI of the same names
-(include/tp.h) on device tensors: they check shapes, allocate outputs with
-torch and pass raw pointers and the current HIP stream.  ``project_3d`` and
-``project_2d`` are the differentiable forms (torch.autograd.Function): the
-backward calls the adjoint for the reference gradient and ``tp_grad_pose`` for
-the rotation and shift gradients, each only when needed (pages, tech. section
-2: autograd functions wrapping the native ops).
+``tp_backproject_2d``, ``tp_grad_pose``, ``tp_backproject_weights_3d``,
+``tp_backproject_weights_2d`` and ``tp_symmetrize_x0`` mirror the C ABI of
+the same names (include/tp.h) on device tensors: they check shapes, allocate
+outputs with torch and pass raw pointers and the current HIP stream.
+
+Differentiable forms (torch.autograd.Function; pages, tech. section 2:
+autograd functions wrapping the native ops):
+
+* ``project_3d`` / ``project_2d``: the backward calls the adjoint for the
+  reference gradient and ``tp_grad_pose`` for the rotation and shift
+  gradients, each only when needed.
+* ``backproject_3d`` / ``backproject_2d``: backprojection as an op of its
+  own (2D -> 3D; it page tech. section 2, list of operations), optionally
+  with the x = 0 plane symmetrised.  Its backward is the forward projection
+  (gradient to the projections) and ``tp_grad_pose`` with the reference and
+  upstream roles swapped (Re<Y, P^T G> = Re<P Y, G>).
+* ``backproject_weights_3d`` / ``backproject_weights_2d``: the real weight
+  volume of a dual-volume reconstruction, with gradients to the weights
+  (the real forward projection) and to the rotations (ar page tech. section
+  2: optional gradients through the weight components).
 """
 from __future__ import annotations
 
@@ -192,3 +205,136 @@ def project_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.
 def project_2d(img, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
     """Differentiable 2D->2D projection (gradients to img, rot and shift)."""
     return _Project.apply(img, rot, shift, 2, n_out, interp, oversampling, cutoff)
+
+
+# --------------------------------------------------- weights and x = 0 plane
+
+def _backproject_weights(ndim, weights, rot, N, interp, oversampling, cutoff):
+    _need(weights, "weights", torch.float32, 4)
+    B, P, n_out = weights.shape[0], weights.shape[1], weights.shape[2]
+    if weights.shape[3] != n_out // 2 + 1:
+        raise ValueError(f"weights must be [B, P, n, n//2+1], got {tuple(weights.shape)}")
+    B_rot, P2, _ = _pose_dims(rot, None, ndim, B, weights.device)
+    if P2 != P:
+        raise ValueError(f"rot has {P2} poses, weights has {P}")
+    shape = (B,) + (N,) * (ndim - 1) + (N // 2 + 1,)
+    out = torch.empty(shape, dtype=torch.float32, device=weights.device)
+    fn = _lib.lib().tp_backproject_weights_3d if ndim == 3 else _lib.lib().tp_backproject_weights_2d
+    st = fn(weights.data_ptr(), B, P, n_out, rot.data_ptr(), B_rot, N, _interp(interp), float(oversampling),
+            float(cutoff), out.data_ptr(), _stream(weights.device))
+    _lib.check(st, f"tp_backproject_weights_{ndim}d")
+    return out
+
+
+def tp_backproject_weights_3d(weights, rot, N=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """Real weights [B,P,n,n//2+1] f32 spread like the adjoint (no phase)
+    -> real weight volume [B,N,N,N//2+1] f32."""
+    if N is None:
+        N = int(round(weights.shape[2] * float(oversampling)))
+    return _backproject_weights(3, weights, rot, N, interp, oversampling, cutoff)
+
+
+def tp_backproject_weights_2d(weights, rot, N=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """2D form of tp_backproject_weights_3d -> [B,N,N//2+1] f32."""
+    if N is None:
+        N = int(round(weights.shape[2] * float(oversampling)))
+    return _backproject_weights(2, weights, rot, N, interp, oversampling, cutoff)
+
+
+def tp_symmetrize_x0(ref):
+    """Hermitian symmetrisation of the x = 0 plane of a complex64 rfft
+    half-spectrum [B,N,N,N//2+1] or [B,N,N//2+1], in place; returns ref."""
+    if not isinstance(ref, torch.Tensor) or ref.dim() not in (3, 4):
+        raise ValueError("ref must be [B,N,N//2+1] or [B,N,N,N//2+1]")
+    ndim = ref.dim() - 1
+    B, N = _ref_dims(ref, ndim, "ref")
+    _lib.check(_lib.lib().tp_symmetrize_x0(ndim, ref.data_ptr(), B, N, _stream(ref.device)), "tp_symmetrize_x0")
+    return ref
+
+
+def _as_c64(x):
+    return torch.complex(x, torch.zeros_like(x))
+
+
+class _Backproject(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, proj, rot, shift, ndim, N, interp, oversampling, cutoff, symmetrize):
+        out = _backproject(ndim, proj, rot, shift, N, interp, oversampling, cutoff)
+        if symmetrize:
+            tp_symmetrize_x0(out)
+        ctx.save_for_backward(proj, rot, shift)
+        ctx.cfg = (ndim, interp, oversampling, cutoff, symmetrize)
+        return out
+
+    @staticmethod
+    def backward(ctx, g):
+        proj, rot, shift = ctx.saved_tensors
+        ndim, interp, oversampling, cutoff, symmetrize = ctx.cfg
+        g = g.contiguous()
+        if g.dtype != torch.complex64:
+            g = g.to(torch.complex64)
+        if symmetrize:  # the symmetrisation is self-adjoint
+            g = tp_symmetrize_x0(g.clone())
+        d_proj = d_rot = d_shift = None
+        if ctx.needs_input_grad[0]:
+            d_proj = _project(ndim, g, rot, shift, proj.shape[2], interp, oversampling, cutoff)
+        want_rot = ctx.needs_input_grad[1]
+        want_shift = shift is not None and ctx.needs_input_grad[2]
+        if want_rot or want_shift:
+            d_rot, d_shift = tp_grad_pose(g, proj, rot, shift, interp, oversampling, cutoff,
+                                          want_rot=want_rot, want_shift=want_shift)
+        return d_proj, d_rot, d_shift, None, None, None, None, None, None
+
+
+def backproject_3d(proj, rot, shift=None, N=None, interp="cubic", oversampling=1.0, cutoff=-1.0,
+                   symmetrize=False):
+    """Differentiable 2D->3D backprojection (gradients to proj, rot and shift)."""
+    if N is None:
+        N = int(round(proj.shape[2] * float(oversampling)))
+    return _Backproject.apply(proj, rot, shift, 3, N, interp, oversampling, cutoff, symmetrize)
+
+
+def backproject_2d(proj, rot, shift=None, N=None, interp="cubic", oversampling=1.0, cutoff=-1.0,
+                   symmetrize=False):
+    """Differentiable 2D->2D backprojection (gradients to proj, rot and shift)."""
+    if N is None:
+        N = int(round(proj.shape[2] * float(oversampling)))
+    return _Backproject.apply(proj, rot, shift, 2, N, interp, oversampling, cutoff, symmetrize)
+
+
+class _BackprojectWeights(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, weights, rot, ndim, N, interp, oversampling, cutoff):
+        out = _backproject_weights(ndim, weights, rot, N, interp, oversampling, cutoff)
+        ctx.save_for_backward(weights, rot)
+        ctx.cfg = (ndim, interp, oversampling, cutoff)
+        return out
+
+    @staticmethod
+    def backward(ctx, g):
+        weights, rot = ctx.saved_tensors
+        ndim, interp, oversampling, cutoff = ctx.cfg
+        gc = _as_c64(g.contiguous().to(torch.float32))
+        d_w = d_rot = None
+        if ctx.needs_input_grad[0]:
+            # the real forward: a real reference's projection has no imaginary part
+            d_w = _project(ndim, gc, rot, None, weights.shape[2], interp, oversampling, cutoff).real.contiguous()
+        if ctx.needs_input_grad[1]:
+            d_rot, _ = tp_grad_pose(gc, _as_c64(weights.contiguous()), rot, None, interp, oversampling, cutoff,
+                                    want_rot=True, want_shift=False)
+        return d_w, d_rot, None, None, None, None, None
+
+
+def backproject_weights_3d(weights, rot, N=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """Differentiable weight backprojection (gradients to weights and rot)."""
+    if N is None:
+        N = int(round(weights.shape[2] * float(oversampling)))
+    return _BackprojectWeights.apply(weights, rot, 3, N, interp, oversampling, cutoff)
+
+
+def backproject_weights_2d(weights, rot, N=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """Differentiable 2D weight backprojection (gradients to weights and rot)."""
+    if N is None:
+        N = int(round(weights.shape[2] * float(oversampling)))
+    return _BackprojectWeights.apply(weights, rot, 2, N, interp, oversampling, cutoff)
+

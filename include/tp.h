@@ -144,6 +144,41 @@ tp_status tp_backproject_2d(const tp_c64* proj, int64_t B, int64_t P, int64_t N_
                             tp_c64* img_out, void* stream);
 
 /*
+ * Weight backprojection (the second, real volume of a dual-volume
+ * reconstruction: per-frequency weights such as CTF^2 spread with the same
+ * interpolation weights as the adjoint, for normalisation or Wiener-style
+ * deconvolution; it/de/ar pages tech. section 2).  Real weights carry no
+ * phase, so there is no shift; a folded tap (x < 0) adds w * weight at -t.
+ * It is the adjoint of the real-valued forward (interpolation of a real
+ * volume at the sample points, folded taps unconjugated).
+ *   weights  [B, P, N_out, N_out/2+1] float32, input
+ *   rot      [B_rot, P, 3, 3] (3D) or [B_rot, P, 2, 2] (2D) float32
+ *   wvol_out [B, N, N, N/2+1] (3D) or wimg_out [B, N, N/2+1] (2D) float32,
+ *            overwritten
+ * Limits and errors as tp_backproject_3d; pointers need 4-byte alignment.
+ */
+tp_status tp_backproject_weights_3d(const float* weights, int64_t B, int64_t P, int64_t N_out,
+                                    const float* rot, int64_t B_rot, int64_t N, int interp,
+                                    float oversampling, float cutoff, float* wvol_out, void* stream);
+tp_status tp_backproject_weights_2d(const float* weights, int64_t B, int64_t P, int64_t N_out,
+                                    const float* rot, int64_t B_rot, int64_t N, int interp,
+                                    float oversampling, float cutoff, float* wimg_out, void* stream);
+
+/*
+ * Hermitian symmetrisation of the x = 0 plane of an rfft half-spectrum, in
+ * place: V(0, y, z) <- (V(0, y, z) + conj V(0, -y, -z)) / 2 with indices mod
+ * N (entries that are their own mirror keep their real part); other planes
+ * are untouched.  The alternative treatment of the zero-frequency axis in
+ * the backward pass (de page tech. section 2: no double counting on that
+ * axis; ar page tech. section 2: symmetric accumulation there), offered as a
+ * step after tp_backproject_*.  It is R-linear and self-adjoint.
+ *   ref  [B, N, N, N/2+1] (ndim 3) or [B, N, N/2+1] (ndim 2) complex64
+ * Errors: TP_EINVAL for ndim not in {2, 3}, a null or misaligned pointer or
+ * a non-positive size; TP_EUNSUPPORTED for N above 65535.
+ */
+tp_status tp_symmetrize_x0(int ndim, tp_c64* ref, int64_t B, int64_t N, void* stream);
+
+/*
  * Gradients of L = Re sum conj(grad_out) * project(ref, rot, shift) w.r.t.
  * the rotations and the shifts (ndim = 3: tp_project_3d, ndim = 2:
  * tp_project_2d), by the chain rule through the interpolation kernel's

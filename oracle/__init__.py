@@ -3,6 +3,7 @@ from .projector import (  # noqa: F401
     CUBIC,
     LINEAR,
     backproject,
+    backproject_weights,
     grad_pose,
     kernel,
     kernel_deriv,
@@ -11,5 +12,6 @@ from .projector import (  # noqa: F401
     project,
     resolve_taps,
     signed_freq,
+    symmetrize_x0,
     tap_offsets,
 )

@@ -290,3 +290,66 @@ def grad_pose(V, G, R, s, n_out: int, interp: int, os: float = 1.0, cutoff: floa
             for j, kj in enumerate((kxk, kyk)):
                 ds[bs, n, j] += np.sum(np.real(g * (-2j * np.pi * kj / n_out) * S))
     return dR, ds
+
+
+# --------------------------------------------- dual-volume weights, x = 0 plane
+
+def backproject_weights(W, R, N: int, interp: int, os: float = 1.0, cutoff: float = -1.0):
+    """Second (real) volume of a dual-volume reconstruction: every in-cutoff
+    output's real weight W (e.g. CTF^2) is spread with the same
+    interpolation weights as the adjoint; no phase; a folded tap (x < 0)
+    adds to -t (real, so nothing to conjugate) [it tech. §2: optional
+    weight accumulation for CTF correction; de tech. §2: dual-volume
+    approach, second tensor for weights; ar tech. §2: dual-volume weighting].
+
+    W [B, P, n_out, n_out//2+1] real -> [B, N, N, N//2+1] (3D) or
+    [B, N, N//2+1] (2D) real.
+    """
+    W = np.asarray(W, np.float64)
+    R = np.asarray(R, np.float64)
+    ndim = R.shape[-1]
+    B, P, n_out = W.shape[0], W.shape[1], W.shape[2]
+    kx, ky, keep = output_grid(n_out, cutoff)
+    kxk, kyk = kx[keep], ky[keep]
+    A = np.zeros((B,) + (N,) * (ndim - 1) + (N // 2 + 1,), np.float64)
+    for b in range(B):
+        Aflat = np.zeros(A[b].size, np.float64)
+        for n in range(P):
+            p, ok = _sample_points(kxk, kyk, R[_bidx(R.shape[0], b), n], os)
+            c = np.where(ok, W[b, n][keep], 0.0)
+            base = np.floor(p).astype(np.int64)
+            for d in itertools.product(tap_offsets(interp), repeat=ndim):
+                t = base + np.asarray(d, np.int64)[None, :]
+                w = np.prod(kernel(interp, p - t), axis=1)
+                valid, idx, _ = resolve_taps(t, N)
+                np.add.at(Aflat, idx[valid], (w * c)[valid])
+        A[b] = Aflat.reshape(A[b].shape)
+    return A
+
+
+def symmetrize_x0(V):
+    """Hermitian symmetrisation of the x = 0 plane of an rfft half-spectrum:
+    V(0, y, z) <- (V(0, y, z) + conj V(0, -y, -z)) / 2, indices taken mod N
+    (the periodic mirror of the DFT); every other plane is unchanged [de
+    tech. §2: the zero-frequency axis is treated so that nothing is counted
+    twice; ar tech. §2: symmetric accumulation on that axis].
+
+    V [B, N, N, N//2+1] (3D) or [B, N, N//2+1] (2D), complex -> same shape.
+    Plain loops over the plane.
+    """
+    V = np.array(V, np.complex128)
+    N = V.shape[1]
+    out = V.copy()
+    if V.ndim == 4:
+        for b in range(V.shape[0]):
+            for iz in range(N):
+                for iy in range(N):
+                    mz, my = (-iz) % N, (-iy) % N
+                    out[b, iz, iy, 0] = 0.5 * (V[b, iz, iy, 0] + np.conj(V[b, mz, my, 0]))
+    else:
+        for b in range(V.shape[0]):
+            for iy in range(N):
+                my = (-iy) % N
+                out[b, iy, 0] = 0.5 * (V[b, iy, 0] + np.conj(V[b, my, 0]))
+    return out
+

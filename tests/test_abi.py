@@ -119,3 +119,21 @@ def test_python_binding_rejects_cpu_tensors():
     rot = torch.eye(3).reshape(1, 1, 3, 3)
     with pytest.raises(ValueError, match="GPU"):
         tp_project_3d(vol, rot)
+
+
+def test_weights_and_symmetrize_check_arguments():
+    L = _lib.lib()
+    # weights, B, P, N_out, rot, B_rot, N, interp, os, cutoff, out, stream
+    assert L.tp_backproject_weights_3d(None, 1, 4, 32, FAKE, 1, 32, 1, 1.0, -1.0, FAKE, None) == EINVAL
+    assert L.tp_backproject_weights_3d(FAKE, 1, 4, 32, FAKE, 1, 32, 1, 1.0, -1.0, None, None) == EINVAL
+    assert L.tp_backproject_weights_3d(FAKE, 1, 4, 32, FAKE, 1, 32, 7, 1.0, -1.0, FAKE, None) == EINVAL
+    assert L.tp_backproject_weights_3d(FAKE, 2, 4, 32, FAKE, 3, 32, 1, 1.0, -1.0, FAKE, None) == EINVAL
+    assert L.tp_backproject_weights_3d(FAKE, 1, 4, 16384, FAKE, 1, 32, 1, 1.0, -1.0, FAKE, None) == EUNSUP
+    assert L.tp_backproject_weights_2d(FAKE, 1, 4, 32, FAKE, 1, 32, 1, 0.0, -1.0, FAKE, None) == EINVAL
+    assert L.tp_backproject_weights_2d(FAKE + 2, 1, 4, 32, FAKE, 1, 32, 1, 1.0, -1.0, FAKE, None) == EINVAL
+    # ndim, ref, B, N, stream
+    assert L.tp_symmetrize_x0(4, FAKE, 1, 8, None) == EINVAL
+    assert L.tp_symmetrize_x0(3, None, 1, 8, None) == EINVAL
+    assert L.tp_symmetrize_x0(3, FAKE_ODD, 1, 8, None) == EINVAL
+    assert L.tp_symmetrize_x0(2, FAKE, 0, 8, None) == EINVAL
+    assert L.tp_symmetrize_x0(2, FAKE, 1, 70000, None) == EUNSUP

@@ -36,6 +36,14 @@ MUTATIONS = [
      "c = _phase(kxk, kyk, sv, n_out) * G[b, n][keep]"),
     ("folded index sign", "idx = idx * N + np.mod(tt[..., j], N)", "idx = idx * N + np.mod(-tt[..., j], N)"),
     ("cutoff exclusive", "<= float(cutoff) ** 2", "< float(cutoff) ** 2"),
+    ("weights without interpolation weight", "np.add.at(Aflat, idx[valid], (w * c)[valid])",
+     "np.add.at(Aflat, idx[valid], c[valid])"),
+    ("weights stencil from round", "            base = np.floor(p).astype(np.int64)\n            for d",
+     "            base = np.round(p).astype(np.int64)\n            for d"),
+    ("symmetrize mirror off by one", "mz, my = (-iz) % N, (-iy) % N", "mz, my = (N - 1 - iz) % N, (N - 1 - iy) % N"),
+    ("symmetrize without conjugate", "0.5 * (V[b, iz, iy, 0] + np.conj(V[b, mz, my, 0]))",
+     "0.5 * (V[b, iz, iy, 0] + V[b, mz, my, 0])"),
+    ("symmetrize not halved 2D", "0.5 * (V[b, iy, 0] + np.conj(V[b, my, 0]))", "(V[b, iy, 0] + np.conj(V[b, my, 0]))"),
 ]
 
 
@@ -54,6 +62,6 @@ def test_pins_catch_planted_mistake(name, old, new, tmp_path):
     env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run(
         [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-         "tests/test_oracle_kernels.py", "tests/test_oracle_projector.py"],
+         "tests/test_oracle_kernels.py", "tests/test_oracle_projector.py", "tests/test_oracle_extras.py"],
         cwd=tmp_path, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch: {name}\n{r.stdout[-2000:]}"
