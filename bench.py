@@ -137,6 +137,36 @@ def cpu_baseline(V, R, s, w: synth.Workload, N: int, os_: float, poses_per_worke
 
 # -------------------------------------------------------------------- GPU
 
+def time_extras(L, _lib, torch, stream, Gd, Rd, R, dV, w, N, os_, B, P, reps=5):
+    """Per-launch times of the dual-volume weight backprojection (weights
+    |G|^2 on the same poses) and of the x = 0 symmetrisation of the adjoint's
+    output, HIP events on the launch stream."""
+    sh = stream.cuda_stream
+    Wd = Gd.abs().square().contiguous()
+    wV = torch.empty(dV.shape, dtype=torch.float32, device=dV.device)
+
+    def weights():
+        _lib.check(L.tp_backproject_weights_3d(Wd.data_ptr(), B, P, w.N_out, Rd.data_ptr(), R.shape[0], N,
+                                               w.interp, os_, w.cutoff, wV.data_ptr(), sh),
+                   "tp_backproject_weights_3d")
+
+    def sym():
+        _lib.check(L.tp_symmetrize_x0(3, dV.data_ptr(), B, N, sh), "tp_symmetrize_x0")
+
+    out = {}
+    for name, f in (("backproject_weights", weights), ("symmetrize_x0", sym)):
+        f()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            f()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        out[name + "_ms"] = round(float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])), 4)
+    del Wd, wV
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +264,9 @@ def main():
             ev[k][j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    # the widened ops, timed after the step on the same inputs (not part of it)
+    extras = time_extras(L, _lib, torch, stream, Gd, Rd, R, dV, w, N, os_, B, P)
+
     per_kernel = {name: [] for name, _ in kernels}
     step_ms = []
     for k in range(args.steps):
@@ -311,6 +344,7 @@ def main():
         "roofline_tap": roof_tap,
         "traffic_all": traffic or None,
         "counter_calibration_copy_bytes": copy_bytes,
+        "extras": extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
