@@ -167,6 +167,141 @@ def time_extras(L, _lib, torch, stream, Gd, Rd, R, dV, w, N, os_, B, P, reps=5):
     return out
 
 
+# --------------------------------------------------------- oversampling study
+
+def blob_slice_truth(params, R, n_out: int, N: int, cutoff: float):
+    """Analytic central slices of the blob phantom: the continuous Fourier
+    transform of sum a exp(-|x - c|^2 / 2 s^2), box centre at the origin,
+    at the sample points p = R^T (kx, ky, 0) (frequency p / N cycles/voxel):
+    a (2 pi s^2)^(3/2) exp(-2 pi^2 s^2 |p|^2 / N^2) exp(-2 pi i p.(c - N/2) / N).
+    Returns [P, n_out, n_out//2+1] complex128 and the kept mask."""
+    c, sg, a = params
+    c = c - N // 2                                   # (z, y, x) relative to the centre
+    kx = np.arange(n_out // 2 + 1)[None, :].astype(np.float64)
+    iy = np.arange(n_out)[:, None]
+    ky = np.where(iy <= (n_out - 1) // 2, iy, iy - n_out).astype(np.float64)
+    keep = (kx * kx + ky * ky <= cutoff * cutoff) if cutoff >= 0 else np.ones((n_out, n_out // 2 + 1), bool)
+    kxk, kyk = np.broadcast_to(kx, keep.shape)[keep], np.broadcast_to(ky, keep.shape)[keep]
+    out = np.zeros((R.shape[0], n_out, n_out // 2 + 1), np.complex128)
+    for n in range(R.shape[0]):
+        p = kxk[:, None] * R[n, 0][None, :] + kyk[:, None] * R[n, 1][None, :]   # (x, y, z)
+        p2 = np.sum(p * p, axis=1)
+        pc = p[:, 0:1] * c[None, :, 2] + p[:, 1:2] * c[None, :, 1] + p[:, 2:3] * c[None, :, 0]
+        amp = a * (2 * np.pi * sg * sg) ** 1.5
+        val = (amp[None, :] * np.exp(-2 * np.pi ** 2 * sg[None, :] ** 2 * p2[:, None] / N ** 2)
+               * np.exp(-2j * np.pi * pc / N)).sum(axis=1)
+        out[n][keep] = val
+    return out, keep
+
+
+def shell_stats(got, truth, keep, n_out: int, fracs=(0.1, 0.2, 0.3, 0.4, 0.45, 0.5)):
+    """Fourier ring correlation, relative error and amplitude ratio of
+    got vs truth per ring |k| / n_out in (f - 0.05, f]."""
+    kx = np.arange(n_out // 2 + 1)[None, :]
+    iy = np.arange(n_out)[:, None]
+    ky = np.where(iy <= (n_out - 1) // 2, iy, iy - n_out)
+    r = np.sqrt(kx * kx + ky * ky) / n_out
+    res = {}
+    for f in fracs:
+        m = keep & (r > f - 0.05) & (r <= f)
+        g, t = got[:, m], truth[:, m]
+        frc = float(np.real(np.sum(g * np.conj(t))) / np.sqrt(np.sum(np.abs(g) ** 2) * np.sum(np.abs(t) ** 2)))
+        err = float(np.linalg.norm(g - t) / np.linalg.norm(t))
+        ratio = float(np.sum(np.abs(g)) / np.sum(np.abs(t)))
+        res[f"{f:g}"] = {"frc": round(frc, 6), "rel_err": round(err, 6), "amp_ratio": round(ratio, 5)}
+    return res
+
+
+def oversampling_study(args):
+    """Cubic at oversampling 1 against linear at oversampling 2 with the
+    padding and FFT done on the fly, on the c4 phantom: wall time of the
+    forward pipeline (FFT of the real volume + projection) and of the
+    training step (+ adjoint, pose gradients, inverse FFT of the volume
+    gradient), and accuracy of the projections against the analytic slices
+    of the blobs.  One JSON line."""
+    import torch
+
+    from cryo_em_fourier_amd import _lib
+
+    w = synth.WORKLOADS["c4"]
+    rng = synth.rng_for(w.cfg_id, synth.STREAM_VOLUME)
+    params = synth.blob_params(rng, w.N, w.n_blobs)
+    real = synth.blob_volume(synth.rng_for(w.cfg_id, synth.STREAM_VOLUME), w.N, w.n_blobs)
+    R = synth.make_rotations(w)
+    L = _lib.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    realt = torch.from_numpy(real).to(dev)
+    Rd = torch.from_numpy(R).to(dev)
+    P, n_out, Wo = w.P, w.N_out, w.N_out // 2 + 1
+    G = torch.randn((1, P, n_out, Wo), dtype=torch.complex64, device=dev,
+                    generator=torch.Generator(device=dev).manual_seed(4))
+    out = torch.empty((1, P, n_out, Wo), dtype=torch.complex64, device=dev)
+    dR = torch.empty_like(Rd)
+
+    def spectrum(os_):
+        M = w.N * os_
+        x = realt
+        if os_ != 1:
+            big = torch.zeros((M, M, M), dtype=torch.float32, device=dev)
+            off = M // 2 - w.N // 2
+            big[off:off + w.N, off:off + w.N, off:off + w.N] = realt
+            x = big
+        return torch.fft.rfftn(torch.fft.ifftshift(x), dim=(0, 1, 2))[None].contiguous()
+
+    def to_real(dV, os_):
+        M = w.N * os_
+        x = torch.fft.fftshift(torch.fft.irfftn(dV[0], s=(M, M, M), dim=(0, 1, 2)))
+        off = M // 2 - w.N // 2
+        return x[off:off + w.N, off:off + w.N, off:off + w.N]
+
+    def pipeline(interp, os_, backward):
+        V = spectrum(os_)
+        M = V.shape[1]
+        _lib.check(L.tp_project_3d(V.data_ptr(), 1, M, Rd.data_ptr(), 1, P, None, 1, n_out, interp, float(os_),
+                                   w.cutoff, out.data_ptr(), sh), "project")
+        if backward:
+            dV = torch.empty_like(V)
+            _lib.check(L.tp_backproject_3d(G.data_ptr(), 1, P, n_out, Rd.data_ptr(), 1, None, 1, M, interp,
+                                           float(os_), w.cutoff, dV.data_ptr(), sh), "backproject")
+            _lib.check(L.tp_grad_pose(3, V.data_ptr(), 1, M, G.data_ptr(), Rd.data_ptr(), 1, P, None, 1, n_out,
+                                      interp, float(os_), w.cutoff, dR.data_ptr(), None, sh), "grad_pose")
+            to_real(dV, os_)
+
+    def timed(f, reps=5):
+        f()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            f()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
+    cases = {"cubic_os1": (synth.CUBIC, 1), "linear_os2": (synth.LINEAR, 2),
+             "linear_os1": (synth.LINEAR, 1), "cubic_os2": (synth.CUBIC, 2)}
+    Ps = min(args.study_poses, P)
+    truth, keep = blob_slice_truth(params, R[0, :Ps].astype(np.float64), n_out, w.N, w.cutoff)
+    res = {}
+    for name, (interp, os_) in cases.items():
+        t_fwd = timed(lambda: pipeline(interp, os_, False))
+        t_step = timed(lambda: pipeline(interp, os_, True), reps=3)
+        pipeline(interp, os_, False)
+        got = out[0, :Ps].cpu().numpy().astype(np.complex128)
+        res[name] = {"fwd_pipeline_ms": round(t_fwd, 3), "step_pipeline_ms": round(t_step, 3),
+                     "fwd_proj_per_s": round(P / (t_fwd * 1e-3), 1),
+                     "rings": shell_stats(got, truth, keep, n_out)}
+        print(f"# {name}: fwd {t_fwd:.2f} ms, step {t_step:.2f} ms", file=sys.stderr, flush=True)
+    res["speedup_cubic_os1_over_linear_os2"] = {
+        "fwd": round(res["linear_os2"]["fwd_pipeline_ms"] / res["cubic_os1"]["fwd_pipeline_ms"], 3),
+        "step": round(res["linear_os2"]["step_pipeline_ms"] / res["cubic_os1"]["step_pipeline_ms"], 3)}
+    print(json.dumps({"study": "oversampling", "workload": "c4 blob phantom, box 256, 4096 poses, cutoff 128, "
+                      "no shifts; accuracy on the first %d poses against analytic blob slices" % Ps,
+                      "results": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,12 +312,19 @@ def main():
     ap.add_argument("--poses", type=int, default=0, help="override the pose count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-poses-per-worker", type=int, default=10)
+    ap.add_argument("--study", choices=["oversampling"], default=None,
+                    help="run a study instead of the step benchmark")
+    ap.add_argument("--study-poses", type=int, default=64, help="poses scored against the analytic slice")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the projector is single-GPU; sharding is a design note only)", file=sys.stderr)
         sys.exit(2)
+
+    if args.study == "oversampling":
+        oversampling_study(args)
+        return
 
     w = synth.WORKLOADS[args.config]
     if args.poses:

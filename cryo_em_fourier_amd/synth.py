@@ -108,17 +108,24 @@ def _ball_points(rng: np.random.Generator, n: int, dim: int, radius: float) -> n
     return d * r[:, None]
 
 
-def blob_volume(rng: np.random.Generator, N: int, n_blobs: int,
-                sigma=(1.5, 4.0), amp=(0.5, 1.0)) -> np.ndarray:
-    """Sum of isotropic Gaussian blobs on an N^3 grid (z, y, x), centred box.
-
-    Centres are uniform in a ball of radius N/4 about the box centre N//2.
-    Each blob is evaluated on a +-4 sigma window (separable), which is exact
-    to ~3e-4 of its peak and keeps generation cheap at N = 256..512.
-    """
+def blob_params(rng: np.random.Generator, N: int, n_blobs: int, sigma=(1.5, 4.0), amp=(0.5, 1.0)):
+    """Centres (z, y, x voxel coordinates, uniform in a ball of radius N/4
+    about the box centre N//2), widths and amplitudes of the blob phantom."""
     c = _ball_points(rng, n_blobs, 3, N / 4.0) + N // 2
     s = rng.uniform(sigma[0], sigma[1], n_blobs)
     a = rng.uniform(amp[0], amp[1], n_blobs)
+    return c, s, a
+
+
+def blob_volume(rng: np.random.Generator, N: int, n_blobs: int,
+                sigma=(1.5, 4.0), amp=(0.5, 1.0)) -> np.ndarray:
+    """Sum of isotropic Gaussian blobs on an N^3 grid (z, y, x), centred box
+    (parameters from ``blob_params``).
+
+    Each blob is evaluated on a +-4 sigma window (separable), which is exact
+    to ~3e-4 of its peak and keeps generation cheap at N = 256..512.
+    """
+    c, s, a = blob_params(rng, N, n_blobs, sigma, amp)
     vol = np.zeros((N, N, N), np.float64)
     for i in range(n_blobs):
         h = int(math.ceil(4 * s[i]))
