@@ -353,3 +353,111 @@ def symmetrize_x0(V):
                 out[b, iy, 0] = 0.5 * (V[b, iy, 0] + np.conj(V[b, my, 0]))
     return out
 
+
+# ------------------------------------------------------------ 3D -> 3D rotation
+
+def output_grid_3d(n_out: int, cutoff: float):
+    """Signed (kx, ky, kz) of every entry of an [n_out, n_out, n_out//2+1]
+    rfft half-spectrum (z, y, x) and the mask of entries inside the sphere
+    kx^2 + ky^2 + kz^2 <= cutoff^2 (all of them when cutoff < 0)."""
+    iz, iy, ix = np.meshgrid(np.arange(n_out), np.arange(n_out), np.arange(n_out // 2 + 1), indexing="ij")
+    kx = ix.astype(np.int64)
+    ky = signed_freq(iy, n_out).astype(np.int64)
+    kz = signed_freq(iz, n_out).astype(np.int64)
+    if cutoff < 0:
+        keep = np.ones(kx.shape, bool)
+    else:
+        keep = (kx * kx + ky * ky + kz * kz).astype(np.float64) <= float(cutoff) ** 2
+    return kx, ky, kz, keep
+
+
+def _rot_points(kx, ky, kz, Rm, os: float):
+    """p = os * R^T k = os * (kx R[0,:] + ky R[1,:] + kz R[2,:]), (n, 3)."""
+    Rm = np.asarray(Rm, np.float64)
+    p = float(os) * (kx[:, None] * Rm[0][None, :] + ky[:, None] * Rm[1][None, :] + kz[:, None] * Rm[2][None, :])
+    ok = np.all(np.isfinite(p) & (np.abs(p) <= COORD_LIMIT), axis=1)
+    return np.where(ok[:, None], p, 0.0), ok
+
+
+def _phase3(kx, ky, kz, sv, n_out: int):
+    """exp(-2 pi i (kx s_x + ky s_y + kz s_z) / n_out)."""
+    sv = np.asarray(sv, np.float64)
+    return np.exp(-2j * np.pi * (kx * sv[0] + ky * sv[1] + kz * sv[2]) / n_out)
+
+
+def rotate_3d(V, R, s, n_out: int, interp: int, os: float = 1.0, cutoff: float = -1.0):
+    """3D -> 3D rotation [it tech. §2: 3D -> 3D projection for general
+    rotations]: every frequency k of the output half-spectrum samples the
+    reference at p = os R^T k with the central slice's fold and kernels (so
+    its kz = 0 plane is ``project``'s slice), times the phase of a 3-vector
+    shift in output voxels; 0 outside the cutoff sphere.
+
+    V [B, N, N, N//2+1], R [B_rot, P, 3, 3], s [B_shift, P, 3] or None
+    -> [B, P, n_out, n_out, n_out//2+1].
+    """
+    V = np.asarray(V, np.complex128)
+    R = np.asarray(R, np.float64)
+    _, N = _dims(V, R)
+    B, P = V.shape[0], R.shape[1]
+    kx, ky, kz, keep = output_grid_3d(n_out, cutoff)
+    kxk, kyk, kzk = kx[keep], ky[keep], kz[keep]
+    out = np.zeros((B, P, n_out, n_out, n_out // 2 + 1), np.complex128)
+    for b in range(B):
+        Vflat = V[b].reshape(-1)
+        for n in range(P):
+            sv = (0.0, 0.0, 0.0) if s is None else s[_bidx(s.shape[0], b), n]
+            p, ok = _rot_points(kxk, kyk, kzk, R[_bidx(R.shape[0], b), n], os)
+            S, _ = _interpolate(Vflat, N, p, interp, False)
+            out[b, n][keep] = _phase3(kxk, kyk, kzk, sv, n_out) * np.where(ok, S, 0.0)
+    return out
+
+
+def rotate_backproject_3d(G, R, s, N: int, interp: int, os: float = 1.0, cutoff: float = -1.0):
+    """Adjoint of ``rotate_3d`` w.r.t. Re<a, b>: G [B, P, n, n, n//2+1] ->
+    [B, N, N, N//2+1]."""
+    G = np.asarray(G, np.complex128)
+    R = np.asarray(R, np.float64)
+    B, P, n_out = G.shape[0], G.shape[1], G.shape[2]
+    kx, ky, kz, keep = output_grid_3d(n_out, cutoff)
+    kxk, kyk, kzk = kx[keep], ky[keep], kz[keep]
+    A = np.zeros((B, N, N, N // 2 + 1), np.complex128)
+    for b in range(B):
+        Aflat = np.zeros(A[b].size, np.complex128)
+        for n in range(P):
+            sv = (0.0, 0.0, 0.0) if s is None else s[_bidx(s.shape[0], b), n]
+            p, ok = _rot_points(kxk, kyk, kzk, R[_bidx(R.shape[0], b), n], os)
+            c = np.conj(_phase3(kxk, kyk, kzk, sv, n_out)) * G[b, n][keep]
+            _scatter(Aflat, N, p, np.where(ok, c, 0.0), interp)
+        A[b] = Aflat.reshape(A[b].shape)
+    return A
+
+
+def rotate_grad_pose(V, G, R, s, n_out: int, interp: int, os: float = 1.0, cutoff: float = -1.0):
+    """Gradients of L = Re sum conj(G) rotate_3d(V, R, s) w.r.t. R (all
+    three rows: dL/dR_ij = os sum k_i dL/dp_j) and s (3 components)."""
+    V = np.asarray(V, np.complex128)
+    G = np.asarray(G, np.complex128)
+    R = np.asarray(R, np.float64)
+    _, N = _dims(V, R)
+    B, P = V.shape[0], R.shape[1]
+    kx, ky, kz, keep = output_grid_3d(n_out, cutoff)
+    ks = (kx[keep], ky[keep], kz[keep])
+    dR = np.zeros(R.shape, np.float64)
+    Bs = 1 if s is None else s.shape[0]
+    ds = np.zeros((Bs, P, 3), np.float64)
+    for b in range(B):
+        Vflat = V[b].reshape(-1)
+        for n in range(P):
+            br, bs = _bidx(R.shape[0], b), _bidx(Bs, b)
+            sv = (0.0, 0.0, 0.0) if s is None else s[bs, n]
+            p, ok = _rot_points(*ks, R[br, n], os)
+            S, dS = _interpolate(Vflat, N, p, interp, True)
+            S = np.where(ok, S, 0.0)
+            dS = np.where(ok[:, None], dS, 0.0)
+            g = np.conj(G[b, n][keep]) * _phase3(*ks, sv, n_out)
+            dLdp = np.real(g[:, None] * dS)
+            for i in range(3):
+                dR[br, n, i, :] += float(os) * np.sum(ks[i][:, None] * dLdp, axis=0)
+                ds[bs, n, i] += np.sum(np.real(g * (-2j * np.pi * ks[i] / n_out) * S))
+    return dR, ds
+

@@ -44,6 +44,12 @@ MUTATIONS = [
     ("symmetrize without conjugate", "0.5 * (V[b, iz, iy, 0] + np.conj(V[b, mz, my, 0]))",
      "0.5 * (V[b, iz, iy, 0] + V[b, mz, my, 0])"),
     ("symmetrize not halved 2D", "0.5 * (V[b, iy, 0] + np.conj(V[b, my, 0]))", "(V[b, iy, 0] + np.conj(V[b, my, 0]))"),
+    ("rotation uses R, not R^T",
+     "kx[:, None] * Rm[0][None, :] + ky[:, None] * Rm[1][None, :] + kz[:, None] * Rm[2][None, :]",
+     "kx[:, None] * Rm[:, 0][None, :] + ky[:, None] * Rm[:, 1][None, :] + kz[:, None] * Rm[:, 2][None, :]"),
+    ("rotation drops kz", "+ kz[:, None] * Rm[2][None, :])", ")"),
+    ("3D phase drops s_z", "(kx * sv[0] + ky * sv[1] + kz * sv[2]) / n_out", "(kx * sv[0] + ky * sv[1]) / n_out"),
+    ("rotation gradient row 2 dropped", "for i in range(3):\n                dR[br, n, i, :]", "for i in range(2):\n                dR[br, n, i, :]"),
 ]
 
 
@@ -62,6 +68,7 @@ def test_pins_catch_planted_mistake(name, old, new, tmp_path):
     env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run(
         [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-         "tests/test_oracle_kernels.py", "tests/test_oracle_projector.py", "tests/test_oracle_extras.py"],
+         "tests/test_oracle_kernels.py", "tests/test_oracle_projector.py", "tests/test_oracle_extras.py",
+         "tests/test_oracle_rotate.py"],
         cwd=tmp_path, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch: {name}\n{r.stdout[-2000:]}"
