@@ -10,6 +10,7 @@ from .ops import (  # noqa: F401
     backproject_weights_3d,
     project_2d,
     project_3d,
+    rotate_3d,
     tp_backproject_2d,
     tp_backproject_3d,
     tp_backproject_weights_2d,
@@ -17,6 +18,9 @@ from .ops import (  # noqa: F401
     tp_grad_pose,
     tp_project_2d,
     tp_project_3d,
+    tp_rotate_3d,
+    tp_rotate_backproject_3d,
+    tp_rotate_grad_pose,
     tp_symmetrize_x0,
 )
 
@@ -27,6 +31,7 @@ __all__ = [
     "backproject_weights_3d",
     "project_2d",
     "project_3d",
+    "rotate_3d",
     "tp_backproject_2d",
     "tp_backproject_3d",
     "tp_backproject_weights_2d",
@@ -34,5 +39,8 @@ __all__ = [
     "tp_grad_pose",
     "tp_project_2d",
     "tp_project_3d",
+    "tp_rotate_3d",
+    "tp_rotate_backproject_3d",
+    "tp_rotate_grad_pose",
     "tp_symmetrize_x0",
 ]

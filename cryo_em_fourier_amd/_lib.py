@@ -26,6 +26,9 @@ EXPORTS = (
     "tp_backproject_weights_3d",
     "tp_backproject_weights_2d",
     "tp_symmetrize_x0",
+    "tp_rotate_3d",
+    "tp_rotate_backproject_3d",
+    "tp_rotate_grad_pose",
 )
 
 _vp = ctypes.c_void_p
@@ -51,6 +54,14 @@ _SIGS = {
     "tp_backproject_weights_2d": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp], _int),
     # ndim, ref, B, N, stream
     "tp_symmetrize_x0": ([_int, _vp, _i64, _i64, _vp], _int),
+    # vol, B, N, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, out, stream
+    "tp_rotate_3d": ([_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp], _int),
+    # grad_out, B, P, N_out, rot, B_rot, shift, B_shift, N, interp, os, cutoff, vol_out, stream
+    "tp_rotate_backproject_3d": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp],
+                                 _int),
+    # vol, B, N, grad_out, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, grad_rot, grad_shift, stream
+    "tp_rotate_grad_pose": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp,
+                             _vp], _int),
 }
 
 _lib = None

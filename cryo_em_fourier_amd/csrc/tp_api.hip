@@ -130,6 +130,24 @@ tp_status backproject_weights(int ndim, const float* w, int64_t B, int64_t P, in
   return hip_status(tp::launch_backproject_weights(p, interp, s));
 }
 
+// The 3D -> 3D rotation: the reference's checks, then a tiling of the
+// [N_out, N_out, N_out/2+1] output (16 kx columns x 16 (kz, ky) rows).
+tp_status rotate_fill(const Common& c, tp::OpParams& p) {
+  const tp_status st = check_and_fill(c, p);
+  if (st != TP_OK) return st;
+  const uint64_t rows = (uint64_t)c.N_out * (uint64_t)c.N_out;
+  const uint64_t tx = (uint64_t)(p.Wo + tp::kTileX - 1) / tp::kTileX;
+  const uint64_t ty = (rows + tp::kTileY - 1) / tp::kTileY;
+  const uint64_t blocks = (uint64_t)c.B * (uint64_t)c.P * tx * ty;
+  if (blocks > kMaxBlocks || tx * ty > 0x7FFFFFFFull) return TP_EUNSUPPORTED;
+  p.tiles_x = (int)tx;
+  p.tiles_y = (int)ty;
+  p.tiles_per_pose = (int)(tx * ty);
+  p.tile_y = tp::kTileY;
+  p.nblocks = (uint32_t)blocks;
+  return TP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,6 +206,59 @@ tp_status tp_backproject_weights_2d(const float* weights, int64_t B, int64_t P, 
                                     float oversampling, float cutoff, float* wimg_out, void* stream) {
   return backproject_weights(2, weights, B, P, N_out, rot, B_rot, N, interp, oversampling, cutoff, wimg_out,
                              stream);
+}
+
+tp_status tp_rotate_3d(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot, int64_t P,
+                       const float* shift, int64_t B_shift, int64_t N_out, int interp, float oversampling,
+                       float cutoff, tp_c64* out, void* stream) {
+  if (!vol || !out || !aligned8(vol) || !aligned8(out)) return TP_EINVAL;
+  tp::OpParams p;
+  const Common c{B, N, P, N_out, B_rot, B_shift, interp, 3, oversampling, cutoff, rot, shift};
+  const tp_status st = rotate_fill(c, p);
+  if (st != TP_OK) return st;
+  p.ref = reinterpret_cast<const float2*>(vol);
+  p.img_out = reinterpret_cast<float2*>(out);
+  return hip_status(tp::launch_rotate(p, interp, 0, (hipStream_t)stream));
+}
+
+tp_status tp_rotate_backproject_3d(const tp_c64* grad_out, int64_t B, int64_t P, int64_t N_out, const float* rot,
+                                   int64_t B_rot, const float* shift, int64_t B_shift, int64_t N, int interp,
+                                   float oversampling, float cutoff, tp_c64* vol_out, void* stream) {
+  if (!grad_out || !vol_out || !aligned8(grad_out) || !aligned8(vol_out)) return TP_EINVAL;
+  tp::OpParams p;
+  const Common c{B, N, P, N_out, B_rot, B_shift, interp, 3, oversampling, cutoff, rot, shift};
+  const tp_status st = rotate_fill(c, p);
+  if (st != TP_OK) return st;
+  p.img = reinterpret_cast<const float2*>(grad_out);
+  p.ref_out = reinterpret_cast<float2*>(vol_out);
+  const hipStream_t s = (hipStream_t)stream;
+  if (tp::launch_zero(p.ref_out, ref_bytes_total(p), s) != hipSuccess) return TP_EHIP;
+  return hip_status(tp::launch_rotate(p, interp, 1, s));
+}
+
+tp_status tp_rotate_grad_pose(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* grad_out, const float* rot,
+                              int64_t B_rot, int64_t P, const float* shift, int64_t B_shift, int64_t N_out,
+                              int interp, float oversampling, float cutoff, float* grad_rot, float* grad_shift,
+                              void* stream) {
+  if (!vol || !grad_out || !aligned8(vol) || !aligned8(grad_out)) return TP_EINVAL;
+  if ((grad_rot && !aligned4(grad_rot)) || (grad_shift && !aligned4(grad_shift))) return TP_EINVAL;
+  if (grad_shift && B_shift != 1 && B_shift != B) return TP_EINVAL;
+  tp::OpParams p;
+  const Common c{B, N, P, N_out, B_rot, B_shift, interp, 3, oversampling, cutoff, rot, shift};
+  const tp_status st = rotate_fill(c, p);
+  if (st != TP_OK) return st;
+  if (!grad_rot && !grad_shift) return TP_OK;
+  p.ref = reinterpret_cast<const float2*>(vol);
+  p.img = reinterpret_cast<const float2*>(grad_out);
+  p.grad_rot = grad_rot;
+  p.grad_shift = grad_shift;
+  if (!shift) p.B_shift = (int)B_shift;
+  const hipStream_t s = (hipStream_t)stream;
+  if (grad_rot && tp::launch_zero(grad_rot, (size_t)p.B_rot * p.P * 9 * sizeof(float), s) != hipSuccess)
+    return TP_EHIP;
+  if (grad_shift && tp::launch_zero(grad_shift, (size_t)p.B_shift * p.P * 3 * sizeof(float), s) != hipSuccess)
+    return TP_EHIP;
+  return hip_status(tp::launch_rotate(p, interp, 2, s));
 }
 
 tp_status tp_symmetrize_x0(int ndim, tp_c64* ref, int64_t B, int64_t N, void* stream) {

@@ -39,17 +39,6 @@ __device__ __forceinline__ Out locate(const OpParams& p) {
   return o;
 }
 
-__device__ __forceinline__ RefGeom ref_geom(const OpParams& p) {
-  RefGeom g;
-  g.N = p.N;
-  g.xmax = p.N / 2;
-  g.lo = -(p.N / 2);
-  g.hi = (p.N + 1) / 2 - 1;
-  g.row = (uint32_t)(p.N / 2 + 1) * 8u;
-  g.plane = (uint32_t)p.N * g.row;
-  return g;
-}
-
 // p = os * (kx R[0,:] + ky R[1,:]) in fp64; false if a component is not finite
 // or beyond +-2^30 (such samples read 0).
 template <int NDIM>

@@ -1,0 +1,230 @@
+// 3D -> 3D rotation of a reference half-spectrum (subtomogram averaging):
+// forward gather, its adjoint and the pose gradients, for gfx950.
+//
+// Every output frequency k = (kx, ky, kz) of an [N_out, N_out, N_out/2+1]
+// half-spectrum samples the reference at p = os R^T k = os (kx R[0,:] +
+// ky R[1,:] + kz R[2,:]) with the same per-tap Friedel fold and kernels as
+// the central slice (which is the kz = 0 plane of this op), times the shift
+// phase exp(-2 pi i k.s / N_out) of a 3-vector shift, inside the sphere
+// |k| <= cutoff.  One lane per output; a 256-lane workgroup covers 16 kx
+// columns of 16 (kz, ky) rows of one pose.  The adjoint scatters every tap
+// with float atomics (the op serves boxes of tens to a few hundred voxels).
+#include "tp_internal.h"
+#include "tp_stencil.h"
+
+namespace tp {
+
+namespace {
+
+struct ROut {
+  int b, n, kx, ky, kz;
+  size_t idx;   // output element
+  bool in, keep;
+};
+
+__device__ __forceinline__ ROut rlocate(const OpParams& p) {
+  ROut o;
+  const uint32_t g = xcd_remap(blockIdx.x, gridDim.x);
+  const uint32_t tile = g % (uint32_t)p.tiles_per_pose;
+  const uint32_t bn = g / (uint32_t)p.tiles_per_pose;
+  o.n = (int)(bn % (uint32_t)p.P);
+  o.b = (int)(bn / (uint32_t)p.P);
+  o.kx = (int)(tile % (uint32_t)p.tiles_x) * kTileX + (int)threadIdx.x % kTileX;
+  const long long row = (long long)(tile / (uint32_t)p.tiles_x) * kTileY + (int)threadIdx.x / kTileX;
+  const long long rows = (long long)p.No * p.No;
+  o.in = o.kx < p.Wo && row < rows;
+  const int iz = (int)(row / p.No), iy = (int)(row % p.No);
+  o.ky = signed_row(iy, p.No);
+  o.kz = signed_row(iz, p.No);
+  const long long k2 = (long long)o.kx * o.kx + (long long)o.ky * o.ky + (long long)o.kz * o.kz;
+  o.keep = o.in && (p.cut2 < 0 || k2 <= p.cut2);
+  o.idx = (((size_t)o.b * p.P + o.n) * (size_t)rows + (size_t)row) * p.Wo + o.kx;
+  return o;
+}
+
+__device__ __forceinline__ const float* rrow(const OpParams& p, const ROut& o) {
+  return p.rot + ((size_t)(p.B_rot == 1 ? 0 : o.b) * p.P + o.n) * 9;
+}
+
+// p = os R^T k in fp64; false if a component is not finite or beyond 2^30.
+__device__ __forceinline__ bool rsample(const OpParams& p, const ROut& o, double* q) {
+  const float* R = rrow(p, o);
+  const double os = (double)p.os;
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    q[j] = os * ((double)o.kx * (double)R[j] + (double)o.ky * (double)R[3 + j] + (double)o.kz * (double)R[6 + j]);
+    ok = ok && (fabs(q[j]) <= kCoordLimit);
+  }
+  return ok;
+}
+
+// exp(-2 pi i (kx sx + ky sy + kz sz) / N_out), turns reduced in fp64.
+__device__ __forceinline__ float2 rphase(const OpParams& p, const ROut& o) {
+  if (!p.shift) return make_float2(1.f, 0.f);
+  const float* s = p.shift + ((size_t)(p.B_shift == 1 ? 0 : o.b) * p.P + o.n) * 3;
+  double t = ((double)o.kx * s[0] + (double)o.ky * s[1] + (double)o.kz * s[2]) * p.inv_no;
+  t -= rint(t);
+  float sn, cs;
+  sincospif((float)(-2.0 * t), &sn, &cs);
+  return make_float2(cs, sn);
+}
+
+template <int INTERP>
+__global__ __launch_bounds__(kBlock) void k_rotate(OpParams p) {
+  const ROut o = rlocate(p);
+  if (!o.in) return;
+  float2 res = make_float2(0.f, 0.f);
+  double q[3];
+  if (o.keep && rsample(p, o, q)) {
+    const RefGeom g = ref_geom(p);
+    const rsrc_t rs = make_rsrc(p.ref + (size_t)o.b * p.ref_elems, p.ref_bytes);
+    // main stencil around m = |p_x|-side sample, secondary across x = 0
+    const bool c = q[0] < 0.0;
+    double m[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) m[j] = c ? -q[j] : q[j];
+    const float2 mv = gather3<INTERP>(rs, g, m[0], m[1], m[2], c ? 1 : 0);
+    float2 sv = make_float2(0.f, 0.f);
+    if (needs_secondary<INTERP>(m[0], c ? 0 : 1)) sv = gather3<INTERP>(rs, g, -m[0], -m[1], -m[2], c ? 0 : 1);
+    res = c ? make_float2(mv.x + sv.x, sv.y - mv.y) : make_float2(mv.x + sv.x, mv.y - sv.y);
+    res = cmul(rphase(p, o), res);
+  }
+  p.img_out[o.idx] = res;
+}
+
+// Adjoint: c = conj(phase) G spread over the forward's taps; a tap with
+// x < 0 receives conj(w c) at -t; taps outside the stored range drop.
+template <int INTERP>
+__global__ __launch_bounds__(kBlock) void k_rotate_adjoint(OpParams p) {
+  using K = Kern<INTERP>;
+  constexpr int T = K::T;
+  const ROut o = rlocate(p);
+  double q[3];
+  if (!o.keep || !rsample(p, o, q)) return;
+  const float2 c = cmul(conjf2(rphase(p, o)), p.img[o.idx]);
+  if (c.x == 0.f && c.y == 0.f) return;
+  const AxisPos ax = axis_pos(q[0], K::OFF), ay = axis_pos(q[1], K::OFF), az = axis_pos(q[2], K::OFF);
+  float wx[T], wy[T], wz[T];
+  K::w(ax.f, wx);
+  K::w(ay.f, wy);
+  K::w(az.f, wz);
+  const int N = p.N, hx = N / 2, lo = -(N / 2), hi = (N + 1) / 2 - 1, wh = N / 2 + 1;
+  float2* out = p.ref_out + (size_t)o.b * p.ref_elems;
+#pragma unroll
+  for (int dz = 0; dz < T; ++dz)
+#pragma unroll
+    for (int dy = 0; dy < T; ++dy)
+#pragma unroll
+      for (int dx = 0; dx < T; ++dx) {
+        int tx = ax.x0 + dx, ty = ay.x0 + dy, tz = az.x0 + dz;
+        const bool fold = tx < 0;
+        if (fold) {
+          tx = -tx;
+          ty = -ty;
+          tz = -tz;
+        }
+        if (tx > hx || ty < lo || ty > hi || tz < lo || tz > hi) continue;
+        const float w = wx[dx] * wy[dy] * wz[dz];
+        float2* dst = out + ((size_t)(tz < 0 ? tz + N : tz) * N + (ty < 0 ? ty + N : ty)) * wh + tx;
+        unsafeAtomicAdd(&dst->x, w * c.x);
+        unsafeAtomicAdd(&dst->y, fold ? -w * c.y : w * c.y);
+      }
+}
+
+// Pose gradients of L = Re sum conj(G) rotate(V): dL/dR[i][j] =
+// os sum k_i Re(conj(G) phase dS/dp_j) (all three rows), dL/ds_j =
+// sum (2 pi k_j / N_out) Im(conj(G) phase S).
+template <int INTERP>
+__global__ __launch_bounds__(kBlock) void k_rotate_grad(OpParams p) {
+  constexpr int NV = 12;
+  __shared__ double red[kBlock / 64][16];
+  const ROut o = rlocate(p);
+  double acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0;
+  double q[3];
+  const bool active = o.keep && rsample(p, o, q);
+  if (active) {
+    const RefGeom g = ref_geom(p);
+    const rsrc_t rs = make_rsrc(p.ref + (size_t)o.b * p.ref_elems, p.ref_bytes);
+    const bool c = q[0] < 0.0;
+    double m[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) m[j] = c ? -q[j] : q[j];
+    float2 mv[4], sv[4];
+    gather3_grad<INTERP>(rs, g, m[0], m[1], m[2], c ? 1 : 0, mv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sv[j] = make_float2(0.f, 0.f);
+    if (needs_secondary<INTERP>(m[0], c ? 0 : 1)) gather3_grad<INTERP>(rs, g, -m[0], -m[1], -m[2], c ? 0 : 1, sv);
+    // S and dS/dp through m = +-p (as the central-slice gradient kernels)
+    float2 S, dS[3];
+    if (c) {
+      S = make_float2(mv[0].x + sv[0].x, sv[0].y - mv[0].y);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) dS[j] = make_float2(sv[j + 1].x - mv[j + 1].x, sv[j + 1].y + mv[j + 1].y);
+    } else {
+      S = make_float2(mv[0].x + sv[0].x, mv[0].y - sv[0].y);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) dS[j] = make_float2(mv[j + 1].x - sv[j + 1].x, mv[j + 1].y + sv[j + 1].y);
+    }
+    const float2 gph = cmul(conjf2(p.img[o.idx]), rphase(p, o));
+    const double os = (double)p.os;
+    const double k[3] = {(double)o.kx, (double)o.ky, (double)o.kz};
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const double dldp = (double)gph.x * dS[j].x - (double)gph.y * dS[j].y;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) acc[3 * i + j] = os * k[i] * dldp;
+    }
+    const double im_gs = (double)gph.x * S.y + (double)gph.y * S.x;
+    const double two_pi_over_n = 6.283185307179586476925 * p.inv_no;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) acc[9 + i] = two_pi_over_n * k[i] * im_gs;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const double d0 = wave_sum8(acc), d1 = wave_sum8(acc + 8);
+  if ((lane & 7) == 0) {
+    red[wave][lane >> 3] = d0;
+    red[wave][8 + (lane >> 3)] = d1;
+  }
+  __syncthreads();
+  if (threadIdx.x < NV) {
+    const int i = threadIdx.x;
+    double v = 0.0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) v += red[w][i];
+    if (v == 0.0) return;
+    const uint32_t gi = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t bn = gi / (uint32_t)p.tiles_per_pose;
+    const int n = (int)(bn % (uint32_t)p.P), b = (int)(bn / (uint32_t)p.P);
+    if (i < 9) {
+      if (p.grad_rot) {
+        const size_t br = p.B_rot == 1 ? 0 : (size_t)b;
+        unsafeAtomicAdd(p.grad_rot + (br * p.P + n) * 9 + i, (float)v);
+      }
+    } else if (p.grad_shift) {
+      const size_t bs = p.B_shift == 1 ? 0 : (size_t)b;
+      unsafeAtomicAdd(p.grad_shift + (bs * p.P + n) * 3 + (i - 9), (float)v);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rotate(const OpParams& p, int interp, int what, hipStream_t s) {
+  const dim3 grid(p.nblocks), block(kBlock);
+  if (what == 0) {
+    if (interp) hipLaunchKernelGGL((k_rotate<1>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_rotate<0>), grid, block, 0, s, p);
+  } else if (what == 1) {
+    if (interp) hipLaunchKernelGGL((k_rotate_adjoint<1>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_rotate_adjoint<0>), grid, block, 0, s, p);
+  } else {
+    if (interp) hipLaunchKernelGGL((k_rotate_grad<1>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_rotate_grad<0>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tp

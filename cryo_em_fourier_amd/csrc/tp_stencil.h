@@ -5,8 +5,20 @@
 #pragma once
 
 #include "tp_device.h"
+#include "tp_internal.h"
 
 namespace tp {
+
+__device__ __forceinline__ RefGeom ref_geom(const OpParams& p) {
+  RefGeom g;
+  g.N = p.N;
+  g.xmax = p.N / 2;
+  g.lo = -(p.N / 2);
+  g.hi = (p.N + 1) / 2 - 1;
+  g.row = (uint32_t)(p.N / 2 + 1) * 8u;
+  g.plane = (uint32_t)p.N * g.row;
+  return g;
+}
 
 // x axis: weights (zeroed outside [xmin, xmax]) and the byte offset of the
 // first loaded tap, which is moved to x >= 0 by shifting the weights.

@@ -17,6 +17,9 @@ autograd functions wrapping the native ops):
   with the x = 0 plane symmetrised.  Its backward is the forward projection
   (gradient to the projections) and ``tp_grad_pose`` with the reference and
   upstream roles swapped (Re<Y, P^T G> = Re<P Y, G>).
+* ``rotate_3d``: the 3D -> 3D rotation of a half-spectrum (it page tech.
+  section 2: 3D -> 3D for general rotations), with gradients to the
+  reference (its adjoint), the rotations and the 3-vector shifts.
 * ``backproject_weights_3d`` / ``backproject_weights_2d``: the real weight
   volume of a dual-volume reconstruction, with gradients to the weights
   (the real forward projection) and to the rotations (ar page tech. section
@@ -337,4 +340,106 @@ def backproject_weights_2d(weights, rot, N=None, interp="cubic", oversampling=1.
     if N is None:
         N = int(round(weights.shape[2] * float(oversampling)))
     return _BackprojectWeights.apply(weights, rot, 2, N, interp, oversampling, cutoff)
+
+
+# -------------------------------------------------------- 3D -> 3D rotation
+
+def _rot_poses(rot, shift, B, dev):
+    _need(rot, "rot", torch.float32, 4)
+    B_rot, P = rot.shape[0], rot.shape[1]
+    if tuple(rot.shape[2:]) != (3, 3) or B_rot not in (1, B) or rot.device != dev:
+        raise ValueError(f"rot must be [1 or {B}, P, 3, 3] on the reference's device, got {tuple(rot.shape)}")
+    B_shift = 1
+    if shift is not None:
+        _need(shift, "shift", torch.float32, 3)
+        B_shift = shift.shape[0]
+        if tuple(shift.shape[1:]) != (P, 3) or B_shift not in (1, B) or shift.device != dev:
+            raise ValueError(f"shift must be [1 or {B}, {P}, 3], got {tuple(shift.shape)}")
+    return B_rot, P, B_shift
+
+
+def tp_rotate_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """vol [B,N,N,N//2+1] c64, rot [B_rot,P,3,3], shift [B_shift,P,3] or None
+    -> [B,P,n_out,n_out,n_out//2+1] c64."""
+    B, N = _ref_dims(vol, 3, "reference")
+    B_rot, P, B_shift = _rot_poses(rot, shift, B, vol.device)
+    if n_out is None:
+        n_out = int(round(N / float(oversampling)))
+    out = torch.empty((B, P, n_out, n_out, n_out // 2 + 1), dtype=torch.complex64, device=vol.device)
+    st = _lib.lib().tp_rotate_3d(vol.data_ptr(), B, N, rot.data_ptr(), B_rot, P, _ptr(shift), B_shift, n_out,
+                                 _interp(interp), float(oversampling), float(cutoff), out.data_ptr(),
+                                 _stream(vol.device))
+    _lib.check(st, "tp_rotate_3d")
+    return out
+
+
+def tp_rotate_backproject_3d(grad_out, rot, shift=None, N=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """Adjoint of tp_rotate_3d: [B,P,n,n,n//2+1] -> [B,N,N,N//2+1]."""
+    _need(grad_out, "grad_out", torch.complex64, 5)
+    B, P, n_out = grad_out.shape[0], grad_out.shape[1], grad_out.shape[2]
+    if tuple(grad_out.shape[3:]) != (n_out, n_out // 2 + 1):
+        raise ValueError(f"grad_out must be [B, P, n, n, n//2+1], got {tuple(grad_out.shape)}")
+    B_rot, P2, B_shift = _rot_poses(rot, shift, B, grad_out.device)
+    if P2 != P:
+        raise ValueError(f"rot has {P2} poses, grad_out has {P}")
+    if N is None:
+        N = int(round(n_out * float(oversampling)))
+    out = torch.empty((B, N, N, N // 2 + 1), dtype=torch.complex64, device=grad_out.device)
+    st = _lib.lib().tp_rotate_backproject_3d(grad_out.data_ptr(), B, P, n_out, rot.data_ptr(), B_rot, _ptr(shift),
+                                             B_shift, N, _interp(interp), float(oversampling), float(cutoff),
+                                             out.data_ptr(), _stream(grad_out.device))
+    _lib.check(st, "tp_rotate_backproject_3d")
+    return out
+
+
+def tp_rotate_grad_pose(vol, grad_out, rot, shift=None, interp="cubic", oversampling=1.0, cutoff=-1.0,
+                        want_rot=True, want_shift=True, B_shift=None):
+    """Rotation and shift gradients of Re sum conj(grad_out) * rotate_3d(vol, rot, shift):
+    (grad_rot [B_rot,P,3,3] or None, grad_shift [B_shift,P,3] or None)."""
+    B, N = _ref_dims(vol, 3, "reference")
+    B_rot, P, Bs = _rot_poses(rot, shift, B, vol.device)
+    _need(grad_out, "grad_out", torch.complex64, 5)
+    n_out = grad_out.shape[2]
+    if tuple(grad_out.shape) != (B, P, n_out, n_out, n_out // 2 + 1):
+        raise ValueError(f"grad_out must be [{B}, {P}, n, n, n//2+1], got {tuple(grad_out.shape)}")
+    if shift is None:
+        Bs = 1 if B_shift is None else int(B_shift)
+    gr = torch.empty_like(rot) if want_rot else None
+    gs = torch.empty((Bs, P, 3), dtype=torch.float32, device=vol.device) if want_shift else None
+    st = _lib.lib().tp_rotate_grad_pose(vol.data_ptr(), B, N, grad_out.data_ptr(), rot.data_ptr(), B_rot, P,
+                                        _ptr(shift), Bs, n_out, _interp(interp), float(oversampling), float(cutoff),
+                                        _ptr(gr), _ptr(gs), _stream(vol.device))
+    _lib.check(st, "tp_rotate_grad_pose")
+    return gr, gs
+
+
+class _Rotate(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, vol, rot, shift, n_out, interp, oversampling, cutoff):
+        out = tp_rotate_3d(vol, rot, shift, n_out, interp, oversampling, cutoff)
+        ctx.save_for_backward(vol, rot, shift)
+        ctx.cfg = (interp, oversampling, cutoff)
+        return out
+
+    @staticmethod
+    def backward(ctx, g):
+        vol, rot, shift = ctx.saved_tensors
+        interp, oversampling, cutoff = ctx.cfg
+        g = g.contiguous()
+        if g.dtype != torch.complex64:
+            g = g.to(torch.complex64)
+        d_vol = d_rot = d_shift = None
+        if ctx.needs_input_grad[0]:
+            d_vol = tp_rotate_backproject_3d(g, rot, shift, vol.shape[1], interp, oversampling, cutoff)
+        want_rot = ctx.needs_input_grad[1]
+        want_shift = shift is not None and ctx.needs_input_grad[2]
+        if want_rot or want_shift:
+            d_rot, d_shift = tp_rotate_grad_pose(vol, g, rot, shift, interp, oversampling, cutoff,
+                                                 want_rot=want_rot, want_shift=want_shift)
+        return d_vol, d_rot, d_shift, None, None, None, None
+
+
+def rotate_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """Differentiable 3D->3D rotation (gradients to vol, rot and shift)."""
+    return _Rotate.apply(vol, rot, shift, n_out, interp, oversampling, cutoff)
 

@@ -179,6 +179,51 @@ tp_status tp_backproject_weights_2d(const float* weights, int64_t B, int64_t P, 
 tp_status tp_symmetrize_x0(int ndim, tp_c64* ref, int64_t B, int64_t N, void* stream);
 
 /*
+ * 3D -> 3D rotation of a reference half-spectrum (subtomogram averaging; it
+ * page tech. section 2, list of operations: 3D -> 3D for general
+ * rotations).  Every output frequency k = (kx, ky, kz) of an
+ * [N_out, N_out, N_out/2+1] half-spectrum samples the reference at
+ *   p = oversampling * (kx rot[0,:] + ky rot[1,:] + kz rot[2,:])
+ * with the central slice's fold, kernels and out-of-range rules (the kz = 0
+ * plane of the output is tp_project_3d's slice), times
+ * exp(-2 pi i (kx s_x + ky s_y + kz s_z) / N_out), and is 0 outside the
+ * sphere kx^2 + ky^2 + kz^2 <= cutoff^2 (cutoff < 0: none).
+ *   vol    [B, N, N, N/2+1] complex64, input
+ *   rot    [B_rot, P, 3, 3] float32
+ *   shift  [B_shift, P, 3] float32 (s_x, s_y, s_z in output voxels) or NULL
+ *   out    [B, P, N_out, N_out, N_out/2+1] complex64, overwritten
+ * Errors as tp_project_3d (the grid counts 16 x 16 output tiles of the
+ * N_out^2 (kz, ky) rows).
+ */
+tp_status tp_rotate_3d(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot, int64_t P,
+                       const float* shift, int64_t B_shift, int64_t N_out, int interp, float oversampling,
+                       float cutoff, tp_c64* out, void* stream);
+
+/*
+ * Adjoint of tp_rotate_3d for Re sum conj(a) b: every kept output
+ * c = conj(phase) * grad_out is spread with the forward's weights onto its
+ * taps (a folded tap receives conj(w c) at -t), merged with float atomics.
+ *   grad_out [B, P, N_out, N_out, N_out/2+1] complex64, input
+ *   vol_out  [B, N, N, N/2+1] complex64, overwritten
+ */
+tp_status tp_rotate_backproject_3d(const tp_c64* grad_out, int64_t B, int64_t P, int64_t N_out, const float* rot,
+                                   int64_t B_rot, const float* shift, int64_t B_shift, int64_t N, int interp,
+                                   float oversampling, float cutoff, tp_c64* vol_out, void* stream);
+
+/*
+ * Gradients of L = Re sum conj(grad_out) * rotate(vol, rot, shift):
+ *   dL/dR[i][j] = os sum_k k_i Re(conj(G) phase dS/dp_j)  (all three rows)
+ *   dL/ds_j     = sum_k (2 pi k_j / N_out) Im(conj(G) phase S)
+ *   grad_rot [B_rot, P, 3, 3] float32, overwritten, or NULL
+ *   grad_shift [B_shift, P, 3] float32, overwritten, or NULL (with
+ *              shift == NULL the shift is 0 and B_shift rows are kept)
+ */
+tp_status tp_rotate_grad_pose(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* grad_out, const float* rot,
+                              int64_t B_rot, int64_t P, const float* shift, int64_t B_shift, int64_t N_out,
+                              int interp, float oversampling, float cutoff, float* grad_rot, float* grad_shift,
+                              void* stream);
+
+/*
  * Gradients of L = Re sum conj(grad_out) * project(ref, rot, shift) w.r.t.
  * the rotations and the shifts (ndim = 3: tp_project_3d, ndim = 2:
  * tp_project_2d), by the chain rule through the interpolation kernel's

@@ -137,3 +137,20 @@ def test_weights_and_symmetrize_check_arguments():
     assert L.tp_symmetrize_x0(3, FAKE_ODD, 1, 8, None) == EINVAL
     assert L.tp_symmetrize_x0(2, FAKE, 0, 8, None) == EINVAL
     assert L.tp_symmetrize_x0(2, FAKE, 1, 70000, None) == EUNSUP
+
+
+def test_rotate_entry_points_check_arguments():
+    L = _lib.lib()
+    # vol, B, N, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, out, stream
+    assert L.tp_rotate_3d(None, 1, 16, FAKE, 1, 2, None, 1, 16, 1, 1.0, -1.0, FAKE, None) == EINVAL
+    assert L.tp_rotate_3d(FAKE, 1, 16, FAKE, 1, 2, None, 1, 16, 3, 1.0, -1.0, FAKE, None) == EINVAL
+    assert L.tp_rotate_3d(FAKE, 2, 16, FAKE, 3, 2, None, 1, 16, 1, 1.0, -1.0, FAKE, None) == EINVAL
+    assert L.tp_rotate_3d(FAKE, 1, 1024, FAKE, 1, 2, None, 1, 16, 1, 1.0, -1.0, FAKE, None) == EUNSUP
+    assert L.tp_rotate_3d(FAKE, 1, 16, FAKE, 1, 1 << 30, None, 1, 4096, 1, 1.0, -1.0, FAKE, None) == EUNSUP
+    # grad_out, B, P, N_out, rot, B_rot, shift, B_shift, N, interp, os, cutoff, vol_out, stream
+    assert L.tp_rotate_backproject_3d(FAKE, 1, 2, 16, FAKE, 1, None, 1, 16, 1, 0.0, -1.0, FAKE, None) == EINVAL
+    assert L.tp_rotate_backproject_3d(FAKE_ODD, 1, 2, 16, FAKE, 1, None, 1, 16, 1, 1.0, -1.0, FAKE, None) == EINVAL
+    # vol, B, N, grad_out, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, gr, gs, stream
+    assert L.tp_rotate_grad_pose(FAKE, 1, 16, None, FAKE, 1, 2, None, 1, 16, 1, 1.0, -1.0, FAKE, None, None) == EINVAL
+    assert L.tp_rotate_grad_pose(FAKE, 1, 16, FAKE, FAKE, 1, 2, None, 1, 16, 1, 1.0, math.nan, FAKE, None,
+                                 None) == EINVAL

@@ -1,6 +1,7 @@
 """GPU parity of the ops beyond the core path: the dual-volume weight
-backprojection, the x = 0 symmetrisation, and backprojection (plain and
-weights) as differentiable ops, against the fp64 oracle.
+backprojection, the x = 0 symmetrisation, backprojection (plain and
+weights) as differentiable ops, and the 3D -> 3D rotation with its adjoint
+and gradients, against the fp64 oracle.
 
 Sizes span several bricks and, with 300 poses, pose-chunked bricks near the
 origin (merged with float atomics).  Bar: relative L2 <= 1e-5 and max-abs <=
@@ -123,3 +124,85 @@ def test_backproject_weights_autograd_matches_oracle(ndim):
     dR, _ = oracle.grad_pose(Yw.astype(np.complex128), W.astype(np.complex128), R, None, n_out, CUBIC, 1.0, cutoff)
     assert_parity(Wt.grad.cpu().numpy(), d_w, "d weights")
     assert_parity(Rt.grad.cpu().numpy(), dR, "d rot (weights)")
+
+
+# ------------------------------------------------------------ 3D -> 3D rotation
+
+ROT_CASES = {
+    # name: N, n_out, P, B, B_rot, shifted, interp, os, cutoff, pose kind
+    "cubic": (24, 24, 4, 1, 1, True, CUBIC, 1.0, 11.0, "so3"),
+    "linear-odd-nocut": (17, 17, 3, 1, 1, True, LINEAR, 1.0, -1.0, "so3"),
+    "cubic-os2": (32, 16, 3, 1, 1, False, CUBIC, 2.0, 7.0, "so3"),
+    "batch": (16, 18, 2, 2, 2, True, CUBIC, 16 / 18, 8.5, "so3"),
+    "cube": (20, 20, 24, 1, 1, True, CUBIC, 1.0, 9.0, "cube"),
+}
+
+
+@functools.lru_cache(maxsize=None)
+def rot_case(name):
+    import itertools
+
+    N, n_out, P, B, B_rot, shifted, interp, os_, cutoff, kind = ROT_CASES[name]
+    rng = np.random.default_rng(sum(map(ord, name)))
+    V = complex_normal(rng, (B, N, N, N // 2 + 1))
+    if kind == "cube":
+        mats = []
+        for perm in itertools.permutations(range(3)):
+            for signs in itertools.product((1, -1), repeat=3):
+                M = np.zeros((3, 3))
+                for i, j in enumerate(perm):
+                    M[i, j] = signs[i]
+                if np.isclose(np.linalg.det(M), 1.0):
+                    mats.append(M)
+        R = np.stack(mats)[None].astype(np.float32)
+    else:
+        R = np.stack([synth.uniform_rotations(rng, P) for _ in range(B_rot)]).astype(np.float32)
+    s = rng.uniform(-3, 3, (B_rot, P, 3)).astype(np.float32) if shifted else None
+    G = complex_normal(rng, (B, P, n_out, n_out, n_out // 2 + 1))
+    return dict(V=V, R=R, s=s, G=G, N=N, n_out=n_out, interp=interp, os=np.float32(os_), cutoff=np.float32(cutoff))
+
+
+@pytest.mark.parametrize("name", list(ROT_CASES))
+def test_rotate_3d_matches_oracle(name):
+    from cryo_em_fourier_amd import tp_rotate_3d
+
+    c = rot_case(name)
+    log(f"[rotate_3d] {name}")
+    s = None if c["s"] is None else to_dev(c["s"])
+    got = tp_rotate_3d(to_dev(c["V"]), to_dev(c["R"]), s, c["n_out"], c["interp"], float(c["os"]),
+                       float(c["cutoff"])).cpu().numpy()
+    ref = oracle.rotate_3d(c["V"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(got, ref, f"rotate_3d {name}")
+
+
+@pytest.mark.parametrize("name", list(ROT_CASES))
+def test_rotate_backproject_3d_matches_oracle(name):
+    from cryo_em_fourier_amd import tp_rotate_backproject_3d
+
+    c = rot_case(name)
+    log(f"[rotate_backproject_3d] {name}")
+    s = None if c["s"] is None else to_dev(c["s"])
+    got = tp_rotate_backproject_3d(to_dev(c["G"]), to_dev(c["R"]), s, c["N"], c["interp"], float(c["os"]),
+                                   float(c["cutoff"])).cpu().numpy()
+    ref = oracle.rotate_backproject_3d(c["G"], c["R"], c["s"], c["N"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(got, ref, f"rotate_backproject_3d {name}")
+
+
+@pytest.mark.parametrize("name", ["cubic", "linear-odd-nocut", "batch", "cube"])
+def test_rotate_autograd_matches_oracle(name):
+    """L = Re sum conj(G) rotate_3d(V): gradients to V (the adjoint), R and s."""
+    from cryo_em_fourier_amd import rotate_3d
+
+    c = rot_case(name)
+    log(f"[rotate autograd] {name}")
+    Vt = to_dev(c["V"]).requires_grad_(True)
+    Rt = to_dev(c["R"]).requires_grad_(True)
+    st = None if c["s"] is None else to_dev(c["s"]).requires_grad_(True)
+    out = rotate_3d(Vt, Rt, st, c["n_out"], c["interp"], float(c["os"]), float(c["cutoff"]))
+    (to_dev(c["G"]).conj() * out).real.sum().backward()
+    dV = oracle.rotate_backproject_3d(c["G"], c["R"], c["s"], c["N"], c["interp"], c["os"], c["cutoff"])
+    dR, ds = oracle.rotate_grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(Vt.grad.cpu().numpy(), dV, f"rotate dV {name}")
+    assert_parity(Rt.grad.cpu().numpy(), dR, f"rotate dR {name}")
+    if st is not None:
+        assert_parity(st.grad.cpu().numpy(), ds, f"rotate ds {name}")
