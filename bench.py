@@ -153,8 +153,34 @@ def time_extras(L, _lib, torch, stream, Gd, Rd, R, dV, w, N, os_, B, P, reps=5):
     def sym():
         _lib.check(L.tp_symmetrize_x0(3, dV.data_ptr(), B, N, sh), "tp_symmetrize_x0")
 
-    out = {}
-    for name, f in (("backproject_weights", weights), ("symmetrize_x0", sym)):
+    # 3D -> 3D rotation on a subtomogram-sized workload: box 64 blob phantom,
+    # 512 poses, cubic, cutoff 32, shifts U[-3, 3] voxels
+    rng = np.random.default_rng([7, 0])
+    n3, p3 = 64, 512
+    sub = torch.from_numpy(synth.rfft_spectrum(synth.blob_volume(rng, n3, 40), 3)[None]).to(dV.device)
+    r3 = torch.from_numpy(synth.uniform_rotations(rng, p3)[None].astype(np.float32)).to(dV.device)
+    s3 = torch.from_numpy(rng.uniform(-3, 3, (1, p3, 3)).astype(np.float32)).to(dV.device)
+    o3 = torch.empty((1, p3, n3, n3, n3 // 2 + 1), dtype=torch.complex64, device=dV.device)
+    g3 = torch.randn_like(o3)
+    v3 = torch.empty_like(sub)
+    gr3 = torch.empty_like(r3)
+    gs3 = torch.empty_like(s3)
+
+    def rot_fwd():
+        _lib.check(L.tp_rotate_3d(sub.data_ptr(), 1, n3, r3.data_ptr(), 1, p3, s3.data_ptr(), 1, n3, 1, 1.0, 32.0,
+                                  o3.data_ptr(), sh), "tp_rotate_3d")
+
+    def rot_adj():
+        _lib.check(L.tp_rotate_backproject_3d(g3.data_ptr(), 1, p3, n3, r3.data_ptr(), 1, s3.data_ptr(), 1, n3, 1,
+                                              1.0, 32.0, v3.data_ptr(), sh), "tp_rotate_backproject_3d")
+
+    def rot_grad():
+        _lib.check(L.tp_rotate_grad_pose(sub.data_ptr(), 1, n3, g3.data_ptr(), r3.data_ptr(), 1, p3, s3.data_ptr(), 1,
+                                         n3, 1, 1.0, 32.0, gr3.data_ptr(), gs3.data_ptr(), sh), "tp_rotate_grad_pose")
+
+    out = {"rotate_workload": "box 64 blob phantom, 512 poses, cubic, cutoff 32, shifts U[-3,3]"}
+    for name, f in (("backproject_weights", weights), ("symmetrize_x0", sym), ("rotate_3d", rot_fwd),
+                    ("rotate_backproject_3d", rot_adj), ("rotate_grad_pose", rot_grad)):
         f()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         ev[0].record(stream)
@@ -163,7 +189,7 @@ def time_extras(L, _lib, torch, stream, Gd, Rd, R, dV, w, N, os_, B, P, reps=5):
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
         out[name + "_ms"] = round(float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])), 4)
-    del Wd, wV
+    del Wd, wV, o3, g3
     return out
 
 

@@ -43,6 +43,8 @@ constexpr int kPrefetch = 2;        // hits whose G values a thread loads at onc
 // and 29 bits leave another factor 4 of int32 headroom.
 constexpr int kQuantumBits = 29;
 
+constexpr int kSlice = 0, kWeights = 1, kVolume = 2;
+
 template <int NDIM> struct Brick;
 template <> struct Brick<3> { static constexpr int X = 16, Y = 16, Z = 16; };
 template <> struct Brick<2> { static constexpr int X = 64, Y = 64, Z = 1; };
@@ -106,7 +108,7 @@ __device__ __forceinline__ int brick_chunks(const OpParams& p, const BrickParams
   return (int)fmin(fmax(c, 1.0), (double)bp.cmax);
 }
 
-template <int NDIM>
+template <int NDIM, bool VOL>
 __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams& bp) {
   using BR = Brick<NDIM>;
   BrickPos r;
@@ -130,7 +132,8 @@ __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams&
   } else {
     r.z0 = r.z1 = 0;
   }
-  const int nch = brick_chunks<NDIM>(p, bp, r.x0, r.y0, r.z0);
+  // every pose of a volume lattice reaches every brick inside its sphere
+  const int nch = VOL ? bp.cmax : brick_chunks<NDIM>(p, bp, r.x0, r.y0, r.z0);
   r.valid = ch < nch;
   r.chunked = nch > 1;
   r.n0 = (int)((long long)p.P * ch / nch);
@@ -174,6 +177,179 @@ __device__ __forceinline__ void lattice_load(const OpParams& p, size_t img, int 
   }
 }
 
+// ---- volume lattice (the adjoint of the 3D -> 3D rotation) ----
+// Lattice point k = (kx, ky, kz) of the full output volume carries the real
+// output k when kx >= 0 and the mirror of the real output -k when kx <= 0;
+// p = kx u + ky v + kz w with u, v, w = os R[0, :], os R[1, :], os R[2, :].
+
+__device__ __forceinline__ void lattice_parts3(const OpParams& p, int kx, int ky, int kz, bool& real, bool& mirr) {
+  const int rlo = -(p.No / 2), rhi = (p.No - 1) / 2;
+  real = kx >= 0 && kx <= p.No / 2 && ky >= rlo && ky <= rhi && kz >= rlo && kz <= rhi;
+  mirr = kx <= 0 && -kx <= p.No / 2 && -ky >= rlo && -ky <= rhi && -kz >= rlo && -kz <= rhi;
+}
+
+__device__ __forceinline__ size_t out_index3(const OpParams& p, size_t img, int kx, int ky, int kz) {
+  return ((img * p.No + (kz < 0 ? kz + p.No : kz)) * p.No + (ky < 0 ? ky + p.No : ky)) * p.Wo + kx;
+}
+
+// Scan test of a volume lattice: finite rows, and the box within the largest
+// |p| of a kept output (|k| <= cutoff, or the output cube's corner, times
+// the Frobenius norm of os R, which bounds its largest singular value).
+__device__ __forceinline__ bool vol_meets(const OpParams& p, int b, const Box& bx, int n) {
+  const float* R = p.rot + ((size_t)(p.B_rot == 1 ? 0 : b) * p.P + n) * 9;
+  double f2 = 0.0;
+  for (int i = 0; i < 9; ++i) {
+    const double r = (double)p.os * (double)R[i];
+    if (!isfinite(r)) return false;
+    f2 += r * r;
+  }
+  const double h = 0.5 * p.No;
+  const double k2 = p.cut2 >= 0 ? fmin((double)p.cut2, 3.0 * h * h) : 3.0 * h * h;
+  double d2 = 0.0;
+  for (int j = 0; j < 3; ++j) {
+    const double d = bx.lo[j] > 0.0 ? bx.lo[j] : (bx.hi[j] < 0.0 ? -bx.hi[j] : 0.0);
+    d2 += d * d;
+  }
+  return d2 <= k2 * f2 * (1.0 + 1e-9) + 1e-9;
+}
+
+// Pose view of a volume lattice: the box's preimage k = A^-1 p (A = [u v w])
+// bounds the (kx, ky, kz) ranges; a singular A keeps the whole clipped range.
+__device__ __forceinline__ PoseView vol_view(const OpParams& p, int b, const Box& bx, int n) {
+  PoseView pv;
+  const float* R = p.rot + ((size_t)(p.B_rot == 1 ? 0 : b) * p.P + n) * 9;
+  const double os = (double)p.os;
+  for (int j = 0; j < 3; ++j) {
+    pv.u[j] = os * (double)R[j];
+    pv.v[j] = os * (double)R[3 + j];
+    pv.w[j] = os * (double)R[6 + j];
+    pv.iu[j] = pv.u[j] != 0.0 ? 1.0 / pv.u[j] : 0.0;
+  }
+  pv.sx = pv.sy = pv.sz = 0.f;
+  if (p.shift) {
+    const float* s = p.shift + ((size_t)(p.B_shift == 1 ? 0 : b) * p.P + n) * 3;
+    pv.sx = s[0];
+    pv.sy = s[1];
+    pv.sz = s[2];
+  }
+  int lim = p.No / 2;
+  if (p.cut2 >= 0) lim = min(lim, (int)floor(sqrt((double)p.cut2)));
+  pv.kx0 = pv.ky0 = pv.kz0 = -lim;
+  pv.kx1 = pv.ky1 = pv.kz1 = lim;
+  // A[j][i]: component j of the column of k_i
+  const double A[3][3] = {{pv.u[0], pv.v[0], pv.w[0]}, {pv.u[1], pv.v[1], pv.w[1]}, {pv.u[2], pv.v[2], pv.w[2]}};
+  const double det = A[0][0] * (A[1][1] * A[2][2] - A[1][2] * A[2][1]) -
+                     A[0][1] * (A[1][0] * A[2][2] - A[1][2] * A[2][0]) +
+                     A[0][2] * (A[1][0] * A[2][1] - A[1][1] * A[2][0]);
+  pv.dens = 1e30f;
+  if (det != 0.0 && isfinite(det)) {
+    pv.dens = (float)fmax(1.0, 1.0 / fabs(det));
+    double inv[3][3];  // inverse by cofactors
+    inv[0][0] = (A[1][1] * A[2][2] - A[1][2] * A[2][1]) / det;
+    inv[0][1] = (A[0][2] * A[2][1] - A[0][1] * A[2][2]) / det;
+    inv[0][2] = (A[0][1] * A[1][2] - A[0][2] * A[1][1]) / det;
+    inv[1][0] = (A[1][2] * A[2][0] - A[1][0] * A[2][2]) / det;
+    inv[1][1] = (A[0][0] * A[2][2] - A[0][2] * A[2][0]) / det;
+    inv[1][2] = (A[0][2] * A[1][0] - A[0][0] * A[1][2]) / det;
+    inv[2][0] = (A[1][0] * A[2][1] - A[1][1] * A[2][0]) / det;
+    inv[2][1] = (A[0][1] * A[2][0] - A[0][0] * A[2][1]) / det;
+    inv[2][2] = (A[0][0] * A[1][1] - A[0][1] * A[1][0]) / det;
+    int* lo[3] = {&pv.kx0, &pv.ky0, &pv.kz0};
+    int* hi[3] = {&pv.kx1, &pv.ky1, &pv.kz1};
+    for (int i = 0; i < 3; ++i) {
+      double kmin = 0.0, kmax = 0.0;
+      for (int j = 0; j < 3; ++j) {
+        const double a = bx.lo[j] * inv[i][j], c = bx.hi[j] * inv[i][j];
+        kmin += fmin(a, c);
+        kmax += fmax(a, c);
+      }
+      if (fabs(kmin) < 1e9 && fabs(kmax) < 1e9) {
+        *lo[i] = max(*lo[i], (int)floor(kmin) - 1);
+        *hi[i] = min(*hi[i], (int)ceil(kmax) + 1);
+      }
+    }
+  }
+  pv.hit = finite3(pv.u) && finite3(pv.v) && finite3(pv.w) && pv.kx0 <= pv.kx1 && pv.ky0 <= pv.ky1 &&
+           pv.kz0 <= pv.kz1;
+  if (pv.hit)
+    pv.dens = fminf(pv.dens, 0.25f * (float)(pv.kx1 - pv.kx0 + 1) * (float)(pv.ky1 - pv.ky0 + 1) *
+                                 (float)(pv.kz1 - pv.kz0 + 1) + 1.f);
+  return pv;
+}
+
+// Volume hit tags: 10-bit offsets of kz, ky, kx in the pose's box.
+__device__ __forceinline__ uint32_t vhit(int dkz, int dky, int dkx) {
+  return ((uint32_t)dkz << 20) | ((uint32_t)dky << 10) | (uint32_t)dkx;
+}
+
+// List a volume lattice's points in the (widened) box, row by row over
+// (ky, kz); flat indices [h0, h0 + cap) go to s_hits.  Returns the total.
+__device__ __forceinline__ int list_hits_vol(const OpParams& p, const Box& bx, const PoseView& pv, int h0, int cap,
+                                             uint32_t* s_hits, int* s_wcnt) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nky = pv.ky1 - pv.ky0 + 1, nkz = pv.kz1 - pv.kz0 + 1;
+  const int rows_total = pv.hit ? nky * nkz : 0;
+  const int h1 = h0 + cap;
+  int carry = 0;
+  for (int rw = 0; rw < rows_total; rw += kBlock) {
+    const int r = rw + tid;
+    int cr = 0, a = 0, dky = 0, dkz = 0;
+    if (r < rows_total) {
+      dky = r % nky;
+      dkz = r / nky;
+      const int ky = pv.ky0 + dky, kz = pv.kz0 + dkz;
+      double ta = (double)pv.kx0, tb = (double)pv.kx1;
+      bool empty = false;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const double lo = bx.lo[j] - 1e-6, hi = bx.hi[j] + 1e-6;
+        const double c = (double)ky * pv.v[j] + (double)kz * pv.w[j];
+        if (pv.iu[j] == 0.0) {
+          empty = empty || !(c >= lo && c < hi);
+        } else {
+          const double t0 = (lo - c) * pv.iu[j], t1 = (hi - c) * pv.iu[j];
+          ta = fmax(ta, fmin(t0, t1));
+          tb = fmin(tb, fmax(t0, t1));
+        }
+      }
+      if (p.cut2 >= 0) {
+        const long long rem = p.cut2 - (long long)ky * ky - (long long)kz * kz;
+        if (rem < 0) {
+          empty = true;
+        } else {
+          long long m = (long long)sqrt((double)rem);
+          while ((m + 1) * (m + 1) <= rem) ++m;
+          while (m * m > rem) --m;
+          ta = fmax(ta, (double)-m);
+          tb = fmin(tb, (double)m);
+        }
+      }
+      a = (int)ceil(ta);
+      const int b = empty ? a - 1 : (int)floor(tb);
+      cr = max(0, b - a + 1);
+      a -= pv.kx0;
+    }
+    int incl = cr;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_wcnt[wave] = incl;
+    __syncthreads();
+    int off = carry + incl - cr, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) {
+      off += w < wave ? s_wcnt[w] : 0;
+      tot += s_wcnt[w];
+    }
+    for (int j = max(0, h0 - off); j < cr && off + j < h1; ++j) s_hits[off + j - h0] = vhit(dkz, dky, a + j);
+    carry += tot;
+    __syncthreads();
+  }
+  return carry;
+}
+
 // Phase B: sample point and the values spread by a lattice point that hit.
 struct Cand {
   double q[3];
@@ -191,6 +367,24 @@ __device__ __forceinline__ void lattice_values(const OpParams& p, const PoseView
     // conj(phase(k)) G(k), and for the mirror conj(phase(-k)) G(-k) =
     // phase(k) G(-k): one phase per lattice point
     const float2 ph = shift_phase(kx, ky, pv.sx, pv.sy, p.inv_no);
+    cr = cmul(conjf2(ph), gr);
+    cm = cmul(ph, gm);
+  }
+  cd.v0 = cr;
+  cd.v1 = make_float2(cr.x + cm.x, cr.y - cm.y);
+}
+
+__device__ __forceinline__ void lattice_values3(const OpParams& p, const PoseView& pv, int kx, int ky, int kz,
+                                                float2 gr, float2 gm, Cand& cd) {
+#pragma unroll
+  for (int j = 0; j < 3; ++j) cd.q[j] = (double)kx * pv.u[j] + (double)ky * pv.v[j] + (double)kz * pv.w[j];
+  float2 cr = gr, cm = gm;
+  if (p.shift) {
+    double t = ((double)kx * pv.sx + (double)ky * pv.sy + (double)kz * pv.sz) * p.inv_no;
+    t -= rint(t);
+    float sn, cs;
+    sincospif((float)(-2.0 * t), &sn, &cs);
+    const float2 ph = make_float2(cs, sn);
     cr = cmul(conjf2(ph), gr);
     cm = cmul(ph, gm);
   }
@@ -254,9 +448,15 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
   }
 }
 
-template <int NDIM, int INTERP, bool WEIGHTS>
+// MODE: kSlice (the projector's adjoint), kWeights (real weight volume),
+// kVolume (the adjoint of the 3D -> 3D rotation: volume lattices, one pose
+// per group).
+template <int NDIM, int INTERP, int MODE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_adjoint_bricks(OpParams p,
                                                                                            BrickParams bp) {
+  constexpr bool WEIGHTS = MODE == kWeights;
+  constexpr bool VOL = MODE == kVolume;
+  constexpr int GMAX = VOL ? 1 : kGroupMax;
   using BR = Brick<NDIM>;
   __shared__ unsigned long long acc[kVox];
   __shared__ uint32_t s_hits[kHitCap];
@@ -265,7 +465,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   __shared__ int s_wcnt[kBlock / 64];
   __shared__ float s_red[kBlock / 64];
 
-  const BrickPos br = decode<NDIM>(p, bp);
+  const BrickPos br = decode<NDIM, VOL>(p, bp);
   if (!br.valid) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -279,14 +479,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 
   const Box bx = reach_box<NDIM, INTERP>(br);
   for (int w0 = br.n0; w0 < br.n1; w0 += kBlock) {
-    // the poses whose plane can reach this brick, in order
-    const int total = scan_poses<NDIM>(p, br.b, bx, w0, br.n1, s_poses, s_wcnt);
+    // the poses whose plane (volume) can reach this brick, in order
+    const int total = VOL ? scan_poses_if([&](int n) { return vol_meets(p, br.b, bx, n); }, w0, br.n1, s_poses,
+                                          s_wcnt)
+                          : scan_poses<NDIM>(p, br.b, bx, w0, br.n1, s_poses, s_wcnt);
 
-    // groups of up to kGroupMax poses; a group whose lattice points overflow
-    // the hit list is spread in slices of kHitCap
-    for (int g0 = 0; g0 < total; g0 += kGroupMax) {
-      const int cnt = min(kGroupMax, total - g0);
-      if (tid < cnt) s_view[tid] = pose_view<NDIM>(p, br.b, bx, s_poses[g0 + tid], false);
+    // groups of up to GMAX poses; a group whose lattice points overflow the
+    // hit list is spread in slices of kHitCap
+    for (int g0 = 0; g0 < total; g0 += GMAX) {
+      const int cnt = min(GMAX, total - g0);
+      if (tid < cnt)
+        s_view[tid] = VOL ? vol_view(p, br.b, bx, s_poses[g0 + tid]) : pose_view<NDIM>(p, br.b, bx, s_poses[g0 + tid], false);
       __syncthreads();
       float dens_sum = 0.f;
       for (int g = 0; g < cnt; ++g)
@@ -295,7 +498,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       for (int h0 = 0, hits_total = 1; h0 < hits_total; h0 += kHitCap) {
         // phase A: list the lattice points that can reach the brick (this
         // slice keeps the flat indices [h0, h0 + kHitCap))
-        hits_total = list_hits<NDIM, kGroupMax>(p, bx, s_view, cnt, h0, kHitCap, s_hits, s_wcnt);
+        hits_total = VOL ? list_hits_vol(p, bx, s_view[0], h0, kHitCap, s_hits, s_wcnt)
+                         : list_hits<NDIM, kGroupMax>(p, bx, s_view, cnt, h0, kHitCap, s_hits, s_wcnt);
         const int nh = max(0, min(hits_total, h0 + kHitCap) - h0);
 
         // phase B: spread the hits.  The fixed-point quantum assumes the
@@ -323,9 +527,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
               gr[k] = gm[k] = make_float2(0.f, 0.f);
               if (i < nh) {
                 const uint32_t h = s_hits[i];
-                const PoseView& pv = s_view[hit_pose(h)];
-                lattice_load<WEIGHTS>(p, (size_t)br.b * p.P + s_poses[g0 + hit_pose(h)], hit_kx(h, pv), hit_ky(h, pv), gr[k],
-                             gm[k]);
+                if (VOL) {
+                  const PoseView& pv = s_view[0];
+                  const int kx = pv.kx0 + (int)(h & 0x3FFu), ky = pv.ky0 + (int)((h >> 10) & 0x3FFu),
+                            kz = pv.kz0 + (int)(h >> 20);
+                  const size_t img = (size_t)br.b * p.P + s_poses[g0];
+                  bool real, mirr;
+                  lattice_parts3(p, kx, ky, kz, real, mirr);
+                  gr[k] = real ? p.img[out_index3(p, img, kx, ky, kz)] : make_float2(0.f, 0.f);
+                  gm[k] = mirr ? p.img[out_index3(p, img, -kx, -ky, -kz)] : make_float2(0.f, 0.f);
+                } else {
+                  const PoseView& pv = s_view[hit_pose(h)];
+                  lattice_load<WEIGHTS>(p, (size_t)br.b * p.P + s_poses[g0 + hit_pose(h)], hit_kx(h, pv),
+                                        hit_ky(h, pv), gr[k], gm[k]);
+                }
               }
             }
 #pragma unroll
@@ -337,9 +552,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
               const int i = i0 + tid + k * kBlock;
               if (i >= nh) continue;
               const uint32_t h = s_hits[i];
-              const PoseView& pv = s_view[hit_pose(h)];
               Cand cd;
-              lattice_values<NDIM>(p, pv, hit_kx(h, pv), hit_ky(h, pv), gr[k], gm[k], cd);
+              if (VOL) {
+                const PoseView& pv = s_view[0];
+                lattice_values3(p, pv, pv.kx0 + (int)(h & 0x3FFu), pv.ky0 + (int)((h >> 10) & 0x3FFu),
+                                pv.kz0 + (int)(h >> 20), gr[k], gm[k], cd);
+              } else {
+                const PoseView& pv = s_view[hit_pose(h)];
+                lattice_values<NDIM>(p, pv, hit_kx(h, pv), hit_ky(h, pv), gr[k], gm[k], cd);
+              }
               if (in_box<NDIM>(bx, cd.q)) spread<NDIM, INTERP>(br, cd, inv_q, acc);
             }
           }
@@ -415,14 +636,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 }  // namespace
 
 template <int NDIM>
-static BrickParams brick_params(const OpParams& p) {
+static BrickParams brick_params(const OpParams& p, bool vol = false) {
   using BR = Brick<NDIM>;
   BrickParams bp{};
   bp.nb[0] = (p.N / 2 + 1 + BR::X - 1) / BR::X;
   bp.nb[1] = (p.N + BR::Y - 1) / BR::Y;
   bp.nb[2] = NDIM == 3 ? (p.N + BR::Z - 1) / BR::Z : 1;
   bp.nbricks = bp.nb[0] * bp.nb[1] * bp.nb[2];
-  bp.pmax = 256;
+  // a volume lattice sends every pose to every brick: small chunks
+  bp.pmax = vol ? 16 : 256;
   const int c = (p.P + bp.pmax - 1) / bp.pmax;
   bp.cmax = c < 1 ? 1 : (c > 64 ? 64 : c);
   return bp;
@@ -437,11 +659,11 @@ hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s) {
   const BrickParams bp = p.ndim == 3 ? brick_params<3>(p) : brick_params<2>(p);
   const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kBlock);
   if (p.ndim == 3) {
-    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, false>), grid, block, 0, s, p, bp);
-    else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, false>), grid, block, 0, s, p, bp);
+    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, kSlice>), grid, block, 0, s, p, bp);
+    else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, kSlice>), grid, block, 0, s, p, bp);
   } else {
-    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<2, 1, false>), grid, block, 0, s, p, bp);
-    else hipLaunchKernelGGL((k_adjoint_bricks<2, 0, false>), grid, block, 0, s, p, bp);
+    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<2, 1, kSlice>), grid, block, 0, s, p, bp);
+    else hipLaunchKernelGGL((k_adjoint_bricks<2, 0, kSlice>), grid, block, 0, s, p, bp);
   }
   return hipGetLastError();
 }
@@ -450,12 +672,25 @@ hipError_t launch_backproject_weights(const OpParams& p, int interp, hipStream_t
   const BrickParams bp = p.ndim == 3 ? brick_params<3>(p) : brick_params<2>(p);
   const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kBlock);
   if (p.ndim == 3) {
-    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, true>), grid, block, 0, s, p, bp);
-    else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, true>), grid, block, 0, s, p, bp);
+    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, kWeights>), grid, block, 0, s, p, bp);
+    else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, kWeights>), grid, block, 0, s, p, bp);
   } else {
-    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<2, 1, true>), grid, block, 0, s, p, bp);
-    else hipLaunchKernelGGL((k_adjoint_bricks<2, 0, true>), grid, block, 0, s, p, bp);
+    if (interp) hipLaunchKernelGGL((k_adjoint_bricks<2, 1, kWeights>), grid, block, 0, s, p, bp);
+    else hipLaunchKernelGGL((k_adjoint_bricks<2, 0, kWeights>), grid, block, 0, s, p, bp);
   }
+  return hipGetLastError();
+}
+
+uint64_t rotate_adjoint_blocks(const OpParams& p) {
+  const BrickParams bp = brick_params<3>(p, true);
+  return (uint64_t)p.B * (uint64_t)bp.nbricks * (uint64_t)bp.cmax;
+}
+
+hipError_t launch_rotate_adjoint(const OpParams& p, int interp, hipStream_t s) {
+  const BrickParams bp = brick_params<3>(p, true);
+  const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kBlock);
+  if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, kVolume>), grid, block, 0, s, p, bp);
+  else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, kVolume>), grid, block, 0, s, p, bp);
   return hipGetLastError();
 }
 

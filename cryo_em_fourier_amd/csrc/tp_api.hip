@@ -229,11 +229,13 @@ tp_status tp_rotate_backproject_3d(const tp_c64* grad_out, int64_t B, int64_t P,
   const Common c{B, N, P, N_out, B_rot, B_shift, interp, 3, oversampling, cutoff, rot, shift};
   const tp_status st = rotate_fill(c, p);
   if (st != TP_OK) return st;
+  if (N_out > tp::kMaxRotateAdjointOut || B > 65535 || tp::rotate_adjoint_blocks(p) > kMaxBlocks)
+    return TP_EUNSUPPORTED;
   p.img = reinterpret_cast<const float2*>(grad_out);
   p.ref_out = reinterpret_cast<float2*>(vol_out);
   const hipStream_t s = (hipStream_t)stream;
   if (tp::launch_zero(p.ref_out, ref_bytes_total(p), s) != hipSuccess) return TP_EHIP;
-  return hip_status(tp::launch_rotate(p, interp, 1, s));
+  return hip_status(tp::launch_rotate_adjoint(p, interp, s));
 }
 
 tp_status tp_rotate_grad_pose(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* grad_out, const float* rot,

@@ -20,11 +20,13 @@ struct Box {
 
 // Everything about one pose that the brick loop needs (uniform values).
 struct PoseView {
-  double u[3], v[3];      // p = kx u + ky v
+  double u[3], v[3];      // p = kx u + ky v (+ kz w for a volume lattice)
   double iu[3];           // 1 / u (0 where u = 0)
-  float sx, sy;
-  float dens;             // max(1, 1 / |u x v|): lattice points per unit area bound
+  double w[3];            // volume lattice only
+  float sx, sy, sz;
+  float dens;             // max(1, 1 / |u x v|) (volume: 1 / |det|): lattice points per unit area (volume)
   int kx0, kx1, ky0, ky1; // candidate rectangle, clipped to the output range
+  int kz0, kz1;           // volume lattice only
   int hit;
 };
 
@@ -206,15 +208,14 @@ __device__ __forceinline__ int hit_pose(uint32_t h) { return (int)(h >> 28); }
 __device__ __forceinline__ int hit_kx(uint32_t h, const PoseView& pv) { return pv.kx0 + (int)(h & 0x3FFFu); }
 __device__ __forceinline__ int hit_ky(uint32_t h, const PoseView& pv) { return pv.ky0 + (int)((h >> 14) & 0x3FFFu); }
 
-// Workgroup scan of poses [w0, min(w0 + kBlock, n1)): the poses whose plane
-// meets the box, in order, into s_poses; returns their count.  Every thread
-// of the (kBlock-thread) workgroup calls it.
-template <int NDIM>
-__device__ __forceinline__ int scan_poses(const OpParams& p, int b, const Box& bx, int w0, int n1, int* s_poses,
-                                          int* s_wcnt) {
+// Workgroup scan of poses [w0, min(w0 + kBlock, n1)): the poses n with
+// meets(n), in order, into s_poses; returns their count.  Every thread of
+// the (kBlock-thread) workgroup calls it.
+template <typename Meets>
+__device__ __forceinline__ int scan_poses_if(Meets meets, int w0, int n1, int* s_poses, int* s_wcnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = w0 + tid;
-  const bool hit = n < n1 && plane_meets<NDIM>(p, b, bx, n);
+  const bool hit = n < n1 && meets(n);
   const unsigned long long m = __ballot(hit);
   __syncthreads();
   if (lane == 0) s_wcnt[wave] = __popcll(m);
@@ -228,6 +229,13 @@ __device__ __forceinline__ int scan_poses(const OpParams& p, int b, const Box& b
   if (hit) s_poses[off + __popcll(m & ((1ull << lane) - 1ull))] = n;
   __syncthreads();
   return total;
+}
+
+// The poses whose plane meets the box.
+template <int NDIM>
+__device__ __forceinline__ int scan_poses(const OpParams& p, int b, const Box& bx, int w0, int n1, int* s_poses,
+                                          int* s_wcnt) {
+  return scan_poses_if([&](int n) { return plane_meets<NDIM>(p, b, bx, n); }, w0, n1, s_poses, s_wcnt);
 }
 
 // List the lattice points of the poses s_view[0, cnt) (cnt <= MAXG) whose

@@ -47,8 +47,12 @@ hipError_t launch_project(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_backproject_weights(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_symmetrize_x0(float2* ref, int ndim, int B, int N, hipStream_t s);
-// 3D -> 3D rotation (tp_rotate.hip): what = 0 forward, 1 adjoint, 2 pose gradients
+// 3D -> 3D rotation (tp_rotate.hip): what = 0 forward, 2 pose gradients;
+// its adjoint is the brick adjoint over volume lattices (tp_adjoint.hip)
 hipError_t launch_rotate(const OpParams& p, int interp, int what, hipStream_t s);
+hipError_t launch_rotate_adjoint(const OpParams& p, int interp, hipStream_t s);
+uint64_t rotate_adjoint_blocks(const OpParams& p);
+constexpr int64_t kMaxRotateAdjointOut = 1023;  // 10-bit lattice offsets
 hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
 uint64_t adjoint_blocks(const OpParams& p);

@@ -7,8 +7,8 @@
 // the central slice (which is the kz = 0 plane of this op), times the shift
 // phase exp(-2 pi i k.s / N_out) of a 3-vector shift, inside the sphere
 // |k| <= cutoff.  One lane per output; a 256-lane workgroup covers 16 kx
-// columns of 16 (kz, ky) rows of one pose.  The adjoint scatters every tap
-// with float atomics (the op serves boxes of tens to a few hundred voxels).
+// columns of 16 (kz, ky) rows of one pose.  The adjoint is the brick adjoint
+// of tp_adjoint.hip run over volume lattices.
 #include "tp_internal.h"
 #include "tp_stencil.h"
 
@@ -91,45 +91,6 @@ __global__ __launch_bounds__(kBlock) void k_rotate(OpParams p) {
     res = cmul(rphase(p, o), res);
   }
   p.img_out[o.idx] = res;
-}
-
-// Adjoint: c = conj(phase) G spread over the forward's taps; a tap with
-// x < 0 receives conj(w c) at -t; taps outside the stored range drop.
-template <int INTERP>
-__global__ __launch_bounds__(kBlock) void k_rotate_adjoint(OpParams p) {
-  using K = Kern<INTERP>;
-  constexpr int T = K::T;
-  const ROut o = rlocate(p);
-  double q[3];
-  if (!o.keep || !rsample(p, o, q)) return;
-  const float2 c = cmul(conjf2(rphase(p, o)), p.img[o.idx]);
-  if (c.x == 0.f && c.y == 0.f) return;
-  const AxisPos ax = axis_pos(q[0], K::OFF), ay = axis_pos(q[1], K::OFF), az = axis_pos(q[2], K::OFF);
-  float wx[T], wy[T], wz[T];
-  K::w(ax.f, wx);
-  K::w(ay.f, wy);
-  K::w(az.f, wz);
-  const int N = p.N, hx = N / 2, lo = -(N / 2), hi = (N + 1) / 2 - 1, wh = N / 2 + 1;
-  float2* out = p.ref_out + (size_t)o.b * p.ref_elems;
-#pragma unroll
-  for (int dz = 0; dz < T; ++dz)
-#pragma unroll
-    for (int dy = 0; dy < T; ++dy)
-#pragma unroll
-      for (int dx = 0; dx < T; ++dx) {
-        int tx = ax.x0 + dx, ty = ay.x0 + dy, tz = az.x0 + dz;
-        const bool fold = tx < 0;
-        if (fold) {
-          tx = -tx;
-          ty = -ty;
-          tz = -tz;
-        }
-        if (tx > hx || ty < lo || ty > hi || tz < lo || tz > hi) continue;
-        const float w = wx[dx] * wy[dy] * wz[dz];
-        float2* dst = out + ((size_t)(tz < 0 ? tz + N : tz) * N + (ty < 0 ? ty + N : ty)) * wh + tx;
-        unsafeAtomicAdd(&dst->x, w * c.x);
-        unsafeAtomicAdd(&dst->y, fold ? -w * c.y : w * c.y);
-      }
 }
 
 // Pose gradients of L = Re sum conj(G) rotate(V): dL/dR[i][j] =
@@ -217,9 +178,6 @@ hipError_t launch_rotate(const OpParams& p, int interp, int what, hipStream_t s)
   if (what == 0) {
     if (interp) hipLaunchKernelGGL((k_rotate<1>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((k_rotate<0>), grid, block, 0, s, p);
-  } else if (what == 1) {
-    if (interp) hipLaunchKernelGGL((k_rotate_adjoint<1>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_rotate_adjoint<0>), grid, block, 0, s, p);
   } else {
     if (interp) hipLaunchKernelGGL((k_rotate_grad<1>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((k_rotate_grad<0>), grid, block, 0, s, p);

@@ -202,9 +202,11 @@ tp_status tp_rotate_3d(const tp_c64* vol, int64_t B, int64_t N, const float* rot
 /*
  * Adjoint of tp_rotate_3d for Re sum conj(a) b: every kept output
  * c = conj(phase) * grad_out is spread with the forward's weights onto its
- * taps (a folded tap receives conj(w c) at -t), merged with float atomics.
+ * taps (a folded tap receives conj(w c) at -t), accumulated per brick of the
+ * reference like tp_backproject_3d.
  *   grad_out [B, P, N_out, N_out, N_out/2+1] complex64, input
  *   vol_out  [B, N, N, N/2+1] complex64, overwritten
+ * Errors as tp_backproject_3d, with N_out limited to 1023.
  */
 tp_status tp_rotate_backproject_3d(const tp_c64* grad_out, int64_t B, int64_t P, int64_t N_out, const float* rot,
                                    int64_t B_rot, const float* shift, int64_t B_shift, int64_t N, int interp,

@@ -150,6 +150,8 @@ def test_rotate_entry_points_check_arguments():
     # grad_out, B, P, N_out, rot, B_rot, shift, B_shift, N, interp, os, cutoff, vol_out, stream
     assert L.tp_rotate_backproject_3d(FAKE, 1, 2, 16, FAKE, 1, None, 1, 16, 1, 0.0, -1.0, FAKE, None) == EINVAL
     assert L.tp_rotate_backproject_3d(FAKE_ODD, 1, 2, 16, FAKE, 1, None, 1, 16, 1, 1.0, -1.0, FAKE, None) == EINVAL
+    # 10-bit lattice offsets in the adjoint's hit lists
+    assert L.tp_rotate_backproject_3d(FAKE, 1, 2, 1024, FAKE, 1, None, 1, 16, 1, 1.0, -1.0, FAKE, None) == EUNSUP
     # vol, B, N, grad_out, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, gr, gs, stream
     assert L.tp_rotate_grad_pose(FAKE, 1, 16, None, FAKE, 1, 2, None, 1, 16, 1, 1.0, -1.0, FAKE, None, None) == EINVAL
     assert L.tp_rotate_grad_pose(FAKE, 1, 16, FAKE, FAKE, 1, 2, None, 1, 16, 1, 1.0, math.nan, FAKE, None,

@@ -135,6 +135,7 @@ ROT_CASES = {
     "cubic-os2": (32, 16, 3, 1, 1, False, CUBIC, 2.0, 7.0, "so3"),
     "batch": (16, 18, 2, 2, 2, True, CUBIC, 16 / 18, 8.5, "so3"),
     "cube": (20, 20, 24, 1, 1, True, CUBIC, 1.0, 9.0, "cube"),
+    "chunked-os1.5": (48, 32, 40, 1, 1, True, CUBIC, 1.5, 15.0, "so3"),
 }
 
 
