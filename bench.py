@@ -1,9 +1,13 @@
 """Throughput of the Fourier-slice projector's hot path on one MI355X.
 
-One step = the whole path on one batch: forward projection (tp_project_3d),
-then the backward of a loss on its output: the adjoint for the reference
-gradient (tp_backproject_3d) and the rotation + shift gradients
-(tp_grad_pose).  Default workload (``c4``): a 256^3 blob phantom (rfft
+One step = the whole path on one batch: forward projection, then the
+backward of a loss on its output: the adjoint for the reference gradient
+(tp_backproject_3d) and the rotation + shift gradients.  By default the
+forward saves each output's Jacobian with respect to its sample point
+(tp_project_3d_jac) and the pose gradients stream it (tp_grad_pose_jac);
+``--pose-grads recompute`` times tp_project_3d + tp_grad_pose instead, which
+gathers from the reference a second time.  The other path's forward and
+gradient times ride along in ``extras``.  Default workload (``c4``): a 256^3 blob phantom (rfft
 half-spectrum 256x256x129 complex64), 4096 uniform SO(3) poses, shifts
 U[-10,10] px, Catmull-Rom cubic, oversampling 1, cutoff 128.
 
@@ -181,16 +185,22 @@ def time_extras(L, _lib, torch, stream, Gd, Rd, R, dV, w, N, os_, B, P, reps=5):
     out = {"rotate_workload": "box 64 blob phantom, 512 poses, cubic, cutoff 32, shifts U[-3,3]"}
     for name, f in (("backproject_weights", weights), ("symmetrize_x0", sym), ("rotate_3d", rot_fwd),
                     ("rotate_backproject_3d", rot_adj), ("rotate_grad_pose", rot_grad)):
-        f()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        ev[0].record(stream)
-        for i in range(reps):
-            f()
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        out[name + "_ms"] = round(float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])), 4)
+        out[name + "_ms"] = time_launches(torch, stream, f, reps)
     del Wd, wV, o3, g3
     return out
+
+
+def time_launches(torch, stream, f, reps=5):
+    """Mean per-launch time (ms) of f over reps launches after one warmup,
+    HIP events on the launch stream."""
+    f()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        f()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return round(float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])), 4)
 
 
 # --------------------------------------------------------- oversampling study
@@ -336,6 +346,8 @@ def main():
     ap.add_argument("--config", default="c4", choices=["c3", "c4", "c5"])
     ap.add_argument("--oversampling", type=int, default=1, choices=[1, 2])
     ap.add_argument("--poses", type=int, default=0, help="override the pose count")
+    ap.add_argument("--pose-grads", choices=["jacobian", "recompute"], default="jacobian",
+                    help="pose gradients from the forward's saved Jacobian, or by a second gather pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-poses-per-worker", type=int, default=10)
     ap.add_argument("--study", choices=["oversampling"], default=None,
@@ -384,6 +396,7 @@ def main():
     Gd = torch.from_numpy(G).to(dev)
     del G
     out = torch.empty((w.B, w.P, w.N_out, Wo), dtype=torch.complex64, device=dev)
+    jac = torch.empty((w.B, w.P, 3, w.N_out, Wo), dtype=torch.complex64, device=dev)
     dV = torch.empty_like(Vd)
     dR = torch.empty_like(Rd)
     ds = torch.empty_like(sd)
@@ -396,6 +409,11 @@ def main():
                                    s.shape[0], w.N_out, w.interp, os_, w.cutoff, out.data_ptr(), sh),
                    "tp_project_3d")
 
+    def fwd_jac():
+        _lib.check(L.tp_project_3d_jac(Vd.data_ptr(), B, N, Rd.data_ptr(), R.shape[0], P, sd.data_ptr(),
+                                       s.shape[0], w.N_out, w.interp, os_, w.cutoff, out.data_ptr(), jac.data_ptr(),
+                                       sh), "tp_project_3d_jac")
+
     def adj():
         _lib.check(L.tp_backproject_3d(Gd.data_ptr(), B, P, w.N_out, Rd.data_ptr(), R.shape[0],
                                        sd.data_ptr(), s.shape[0], N, w.interp, os_, w.cutoff,
@@ -406,7 +424,17 @@ def main():
                                   sd.data_ptr(), s.shape[0], w.N_out, w.interp, os_, w.cutoff,
                                   dR.data_ptr(), ds.data_ptr(), sh), "tp_grad_pose")
 
-    kernels = [("project", fwd), ("backproject", adj), ("grad_pose", grad)]
+    def grad_jac():
+        _lib.check(L.tp_grad_pose_jac(Gd.data_ptr(), out.data_ptr(), jac.data_ptr(), B, P, w.N_out, R.shape[0],
+                                      s.shape[0], os_, w.cutoff, dR.data_ptr(), ds.data_ptr(), sh),
+                   "tp_grad_pose_jac")
+
+    if args.pose_grads == "jacobian":
+        kernels = [("project_jac", fwd_jac), ("backproject", adj), ("grad_pose_jac", grad_jac)]
+        other = [("project", fwd), ("grad_pose", grad)]
+    else:
+        kernels = [("project", fwd), ("backproject", adj), ("grad_pose", grad)]
+        other = [("project_jac", fwd_jac), ("grad_pose_jac", grad_jac)]
 
     # calibration for HBM byte counters: one plain streaming copy (y = x * 1)
     # of known size, outside the timed region.  A counter run of this same
@@ -434,6 +462,8 @@ def main():
     wall = time.perf_counter() - t_start
     # the widened ops, timed after the step on the same inputs (not part of it)
     extras = time_extras(L, _lib, torch, stream, Gd, Rd, R, dV, w, N, os_, B, P)
+    for name, f in other:  # the other pose-gradient path, same inputs
+        extras[name + "_ms"] = time_launches(torch, stream, f)
 
     per_kernel = {name: [] for name, _ in kernels}
     step_ms = []
@@ -445,7 +475,8 @@ def main():
     med = {n: float(np.median(v)) for n, v in per_kernel.items()}
     ms_step = float(np.mean(step_ms))
     fwd_bwd_rate = B * P / (ms_step * 1e-3)
-    fwd_rate = B * P / (avg["project"] * 1e-3)
+    fwd_ms = avg["project"] if "project" in avg else extras["project_ms"]
+    fwd_rate = B * P / (fwd_ms * 1e-3)  # the plain forward (no Jacobian saved)
 
     # algorithmic traffic / work per launch
     n_c = in_cutoff_count(w.N_out, w.cutoff)
@@ -454,13 +485,16 @@ def main():
     ref_bytes = V.nbytes
     img_bytes = B * P * w.N_out * Wo * 8
     pose_bytes = R.nbytes + s.nbytes
+    grad_bytes = dR.numel() * 4 + ds.numel() * 4
     hbm = {  # compulsory HBM bytes per launch
         "project": ref_bytes + img_bytes + pose_bytes,
+        "project_jac": ref_bytes + 4 * img_bytes + pose_bytes,   # out + 3 Jacobian planes
         "backproject": units * 8 + 2 * ref_bytes + pose_bytes,
-        "grad_pose": ref_bytes + units * 8 + pose_bytes + dR.numel() * 4 + ds.numel() * 4,
+        "grad_pose": ref_bytes + units * 8 + pose_bytes + grad_bytes,
+        "grad_pose_jac": units * 40 + grad_bytes,                # G, out and jac inside the cutoff
     }
-    tap_bytes = {"project": units * taps * 8, "backproject": units * taps * 8,
-                 "grad_pose": units * taps * 8}
+    tap_bytes = {"project": units * taps * 8, "project_jac": units * taps * 8, "backproject": units * taps * 8,
+                 "grad_pose": units * taps * 8, "grad_pose_jac": 0}
     dom = max(avg, key=avg.get)
     achieved = hbm[dom] / (avg[dom] * 1e-3) / 1e9
     wl_key = f"{w.name}_os{args.oversampling}" + (f"_p{P}" if args.poses else "")
@@ -481,7 +515,7 @@ def main():
     tap_roof = {
         k: {"achieved": round(tap_bytes[k] / (avg[k] * 1e-3) / 1e9, 1),
             "frac": round(tap_bytes[k] / (avg[k] * 1e-3) / 1e9 / L2_PEAK_GBS, 4)}
-        for k in avg
+        for k in avg if tap_bytes[k]
     }
     roof_tap = {"bound": "l2", "peak": L2_PEAK_GBS, "unit": "GB/s",
                 "tap_bytes_per_launch": tap_bytes[dom], "kernels": tap_roof}
@@ -501,6 +535,7 @@ def main():
         "config": {
             "workload": f"{w.name}: 3D->2D forward+backward, box {w.N}, {P} poses, cubic, "
                         f"oversampling {args.oversampling}, cutoff {w.cutoff:g}, shifts U[-{w.shift_max:g},{w.shift_max:g}]",
+            "pose_grads": args.pose_grads,
             "box": w.N, "spectrum_box": N, "poses": P, "batch": B, "interp": "cubic" if w.interp else "linear",
             "oversampling": args.oversampling, "cutoff": w.cutoff, "in_cutoff_outputs_per_pose": n_c,
         },

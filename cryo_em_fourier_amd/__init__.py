@@ -16,8 +16,10 @@ from .ops import (  # noqa: F401
     tp_backproject_weights_2d,
     tp_backproject_weights_3d,
     tp_grad_pose,
+    tp_grad_pose_jac,
     tp_project_2d,
     tp_project_3d,
+    tp_project_3d_jac,
     tp_rotate_3d,
     tp_rotate_backproject_3d,
     tp_rotate_grad_pose,
@@ -37,8 +39,10 @@ __all__ = [
     "tp_backproject_weights_2d",
     "tp_backproject_weights_3d",
     "tp_grad_pose",
+    "tp_grad_pose_jac",
     "tp_project_2d",
     "tp_project_3d",
+    "tp_project_3d_jac",
     "tp_rotate_3d",
     "tp_rotate_backproject_3d",
     "tp_rotate_grad_pose",

@@ -29,6 +29,8 @@ EXPORTS = (
     "tp_rotate_3d",
     "tp_rotate_backproject_3d",
     "tp_rotate_grad_pose",
+    "tp_project_3d_jac",
+    "tp_grad_pose_jac",
 )
 
 _vp = ctypes.c_void_p
@@ -62,6 +64,11 @@ _SIGS = {
     # vol, B, N, grad_out, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, grad_rot, grad_shift, stream
     "tp_rotate_grad_pose": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp,
                              _vp], _int),
+    # vol, B, N, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, out, jac, stream
+    "tp_project_3d_jac": ([_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp, _vp],
+                          _int),
+    # grad_out, proj, jac, B, P, N_out, B_rot, B_shift, os, cutoff, grad_rot, grad_shift, stream
+    "tp_grad_pose_jac": ([_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp], _int),
 }
 
 _lib = None

@@ -18,6 +18,9 @@ struct OpParams {
   float* grad_shift;      // [B_shift, P, 2] or nullptr
   const float* wimg;      // real weights [B, P, No, No/2+1] (weight backprojection)
   float* wref_out;        // real weight volume, the reference's shape
+  const float2* proj;     // saved forward output (pose gradients from a Jacobian)
+  const float2* jac;      // saved Jacobian [B, P, 3, No, Wo]
+  float2* jac_out;        // Jacobian output of the saving forward
   int B, P, N, No, Wo, B_rot, B_shift, ndim;
   float os;
   long long cut2;         // keep kx^2+ky^2 <= cut2; -1: keep everything
@@ -54,6 +57,10 @@ hipError_t launch_rotate_adjoint(const OpParams& p, int interp, hipStream_t s);
 uint64_t rotate_adjoint_blocks(const OpParams& p);
 constexpr int64_t kMaxRotateAdjointOut = 1023;  // 10-bit lattice offsets
 hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s);
+// 3D forward that saves the Jacobian of each output w.r.t. its sample point,
+// and the pose gradients from it (one workgroup per (batch, pose))
+hipError_t launch_project_jac(const OpParams& p, int interp, hipStream_t s);
+hipError_t launch_grad_jac(const OpParams& p, hipStream_t s);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
 uint64_t adjoint_blocks(const OpParams& p);
 

@@ -231,17 +231,17 @@ __global__ __launch_bounds__(kBlock) void k_project3p(OpParams p) {
   p.img_out[img_index(p, o)] = res;
 }
 
+// S and dS/dp at an output's sample point from the value and derivative
+// gathers, summed over the lane pair (both lanes hold the totals; zero where
+// the output is not active).
 template <int INTERP>
-__global__ __launch_bounds__(kBlock) void k_grad3p(OpParams p) {
-  constexpr int NV = 8;  // dR rows 0 and 1, then ds_x, ds_y
-  __shared__ double red[kBlock / 64][NV];
-  const Out o = locate<true>(p);
-  const int h = threadIdx.x & 1;
-  double q[3] = {0.0, 0.0, 0.0};
-  const bool active = o.keep && sample_point<3>(p, o, q);
-  const bool c = active && q[0] < 0.0;
-  float2 S = make_float2(0.f, 0.f), dS[3] = {S, S, S};
+__device__ __forceinline__ void pair_grad_values(const OpParams& p, const Out& o, int h, bool active,
+                                                 const double* q, float2& S, float2* dS) {
+  S = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) dS[j] = S;
   if (active) {
+    const bool c = q[0] < 0.0;
     const RefGeom g = ref_geom(p);
     const rsrc_t rs = make_rsrc(p.ref + (size_t)o.b * p.ref_elems, p.ref_bytes);
     double m[3], mneg[3];
@@ -267,9 +267,21 @@ __global__ __launch_bounds__(kBlock) void k_grad3p(OpParams p) {
       for (int j = 0; j < 3; ++j) dS[j] = make_float2(mv[j + 1].x - sv[j + 1].x, mv[j + 1].y + sv[j + 1].y);
     }
   }
-  S = pair_sum(S);
+  S = pair_sum(S);  // both lanes of a pair share `active`
 #pragma unroll
   for (int j = 0; j < 3; ++j) dS[j] = pair_sum(dS[j]);
+}
+
+template <int INTERP>
+__global__ __launch_bounds__(kBlock) void k_grad3p(OpParams p) {
+  constexpr int NV = 8;  // dR rows 0 and 1, then ds_x, ds_y
+  __shared__ double red[kBlock / 64][NV];
+  const Out o = locate<true>(p);
+  const int h = threadIdx.x & 1;
+  double q[3] = {0.0, 0.0, 0.0};
+  const bool active = o.keep && sample_point<3>(p, o, q);
+  float2 S, dS[3];
+  pair_grad_values<INTERP>(p, o, h, active, q, S, dS);
   double acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.0;
@@ -314,6 +326,100 @@ __global__ __launch_bounds__(kBlock) void k_grad3p(OpParams p) {
     } else if (p.grad_shift) {
       const size_t bs = p.B_shift == 1 ? 0 : (size_t)o.b;
       unsafeAtomicAdd(p.grad_shift + (bs * p.P + o.n) * 2 + (i - 6), (float)v);
+    }
+  }
+}
+
+// Forward that also saves the Jacobian of every output with respect to its
+// sample point, jac_j = phase * dS/dp_j, so that the pose gradients need no
+// second pass over the reference (k_grad_jac).  The gathers are
+// k_grad3p's; lane 0 of a pair writes the output and jac_x, lane 1 jac_y and
+// jac_z ([B, P, 3, No, Wo], one plane per component).
+template <int INTERP>
+__global__ __launch_bounds__(kBlock) void k_project3p_jac(OpParams p) {
+  const Out o = locate<true>(p);
+  const int h = threadIdx.x & 1;
+  double q[3] = {0.0, 0.0, 0.0};
+  const bool active = o.keep && sample_point<3>(p, o, q);
+  float2 S, dS[3];
+  pair_grad_values<INTERP>(p, o, h, active, q, S, dS);
+  if (!o.in) return;
+  if (active && p.shift) {
+    const float2 s = pose_shift(p, o);
+    const float2 ph = shift_phase(o.kx, o.ky, s.x, s.y, p.inv_no);
+    S = cmul(ph, S);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dS[j] = cmul(ph, dS[j]);
+  }
+  const size_t plane = (size_t)p.No * p.Wo;
+  const size_t pose = (size_t)o.b * p.P + o.n;
+  const size_t e = (size_t)o.iy * p.Wo + o.kx;
+  float2* jac = p.jac_out + pose * 3 * plane + e;
+  if (h == 0) {
+    p.img_out[pose * plane + e] = S;
+    jac[0] = dS[0];
+  } else {
+    jac[plane] = dS[1];
+    jac[2 * plane] = dS[2];
+  }
+}
+
+// Pose gradients from a saved Jacobian and projection:
+//   dL/dR[i][j] = os sum_k k_i Re(conj(G) jac_j),
+//   dL/ds_j     = (2 pi / No) sum_k k_j Im(conj(G) proj),
+// the sums of k_grad3p.  One workgroup per (batch, pose) streams the pose's
+// outputs inside the cutoff (coalesced), sums in fp64 and adds its eight
+// totals to the zeroed gradients.
+__global__ __launch_bounds__(kBlock) void k_grad_jac(OpParams p) {
+  constexpr int NV = 8;
+  __shared__ double red[kBlock / 64][NV];
+  const uint32_t bn = blockIdx.x;
+  const int n = (int)(bn % (uint32_t)p.P), b = (int)(bn / (uint32_t)p.P);
+  const uint32_t plane = (uint32_t)p.No * (uint32_t)p.Wo;
+  const float2* G = p.img + (size_t)bn * plane;
+  const float2* Y = p.proj + (size_t)bn * plane;
+  const float2* J = p.jac + (size_t)bn * 3 * plane;
+  double acc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = 0.0;
+#pragma unroll 2
+  for (uint32_t e = threadIdx.x; e < plane; e += kBlock) {
+    const int iy = (int)(e / (uint32_t)p.Wo), kx = (int)(e - (uint32_t)iy * (uint32_t)p.Wo);
+    const int ky = signed_row(iy, p.No);
+    if (p.cut2 >= 0 && (long long)kx * kx + (long long)ky * ky > p.cut2) continue;
+    const float2 g = G[e], y = Y[e], j0 = J[e], j1 = J[e + plane], j2 = J[e + 2 * plane];
+    const double a0 = (double)g.x * j0.x + (double)g.y * j0.y;
+    const double a1 = (double)g.x * j1.x + (double)g.y * j1.y;
+    const double a2 = (double)g.x * j2.x + (double)g.y * j2.y;
+    const double im = (double)g.x * y.y - (double)g.y * y.x;
+    const double dx = (double)kx, dy = (double)ky;
+    acc[0] = fma(dx, a0, acc[0]);
+    acc[1] = fma(dx, a1, acc[1]);
+    acc[2] = fma(dx, a2, acc[2]);
+    acc[3] = fma(dy, a0, acc[3]);
+    acc[4] = fma(dy, a1, acc[4]);
+    acc[5] = fma(dy, a2, acc[5]);
+    acc[6] = fma(dx, im, acc[6]);
+    acc[7] = fma(dy, im, acc[7]);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const double d = wave_sum8(acc);
+  if ((lane & 7) == 0) red[wave][lane >> 3] = d;
+  __syncthreads();
+  if (threadIdx.x < NV) {
+    const int i = threadIdx.x;
+    double v = 0.0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) v += red[w][i];
+    if (v == 0.0) return;
+    if (i < 6) {
+      if (p.grad_rot) {
+        const size_t br = p.B_rot == 1 ? 0 : (size_t)b;
+        unsafeAtomicAdd(p.grad_rot + ((br * p.P + n) * 3 + i / 3) * 3 + i % 3, (float)((double)p.os * v));
+      }
+    } else if (p.grad_shift) {
+      const size_t bs = p.B_shift == 1 ? 0 : (size_t)b;
+      unsafeAtomicAdd(p.grad_shift + (bs * p.P + n) * 2 + (i - 6), (float)(6.283185307179586476925 * p.inv_no * v));
     }
   }
 }
@@ -383,6 +489,18 @@ hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s) {
     if (interp) hipLaunchKernelGGL((k_grad_pose<2, 1>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((k_grad_pose<2, 0>), grid, block, 0, s, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_project_jac(const OpParams& p, int interp, hipStream_t s) {
+  const dim3 grid(p.nblocks), block(kBlock);
+  if (interp) hipLaunchKernelGGL((k_project3p_jac<1>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((k_project3p_jac<0>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_jac(const OpParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_grad_jac, dim3((unsigned)((size_t)p.B * p.P)), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 

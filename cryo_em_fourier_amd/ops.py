@@ -11,7 +11,12 @@ autograd functions wrapping the native ops):
 
 * ``project_3d`` / ``project_2d``: the backward calls the adjoint for the
   reference gradient and ``tp_grad_pose`` for the rotation and shift
-  gradients, each only when needed.
+  gradients, each only when needed.  When the 3D op needs pose gradients
+  its forward runs ``tp_project_3d_jac``, which also saves each output's
+  Jacobian with respect to its sample point (3 complex values per output),
+  and the backward takes them from ``tp_grad_pose_jac`` in one streaming
+  pass instead of a second pass of gathers (``save_jacobian=False`` keeps
+  the recomputing path and its smaller memory).
 * ``backproject_3d`` / ``backproject_2d``: backprojection as an op of its
   own (2D -> 3D; it page tech. section 2, list of operations), optionally
   with the x = 0 plane symmetrised.  Its backward is the forward projection
@@ -174,17 +179,67 @@ def tp_grad_pose(ref, grad_out, rot, shift=None, interp="cubic", oversampling=1.
     return gr, gs
 
 
+def tp_project_3d_jac(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """tp_project_3d that also returns the Jacobian of each output w.r.t. its
+    sample point: (out [B,P,n,n//2+1], jac [B,P,3,n,n//2+1]) c64."""
+    B, N = _ref_dims(vol, 3, "reference")
+    B_rot, P, B_shift = _pose_dims(rot, shift, 3, B, vol.device)
+    if n_out is None:
+        n_out = int(round(N / float(oversampling)))
+    out = torch.empty((B, P, n_out, n_out // 2 + 1), dtype=torch.complex64, device=vol.device)
+    jac = torch.empty((B, P, 3, n_out, n_out // 2 + 1), dtype=torch.complex64, device=vol.device)
+    st = _lib.lib().tp_project_3d_jac(vol.data_ptr(), B, N, rot.data_ptr(), B_rot, P, _ptr(shift), B_shift,
+                                      n_out, _interp(interp), float(oversampling), float(cutoff), out.data_ptr(),
+                                      jac.data_ptr(), _stream(vol.device))
+    _lib.check(st, "tp_project_3d_jac")
+    return out, jac
+
+
+def tp_grad_pose_jac(grad_out, proj, jac, B_rot=1, B_shift=1, oversampling=1.0, cutoff=-1.0,
+                     want_rot=True, want_shift=True):
+    """Pose gradients from tp_project_3d_jac's (proj, jac):
+    (grad_rot [B_rot,P,3,3] or None, grad_shift [B_shift,P,2] or None)."""
+    _need(grad_out, "grad_out", torch.complex64, 4)
+    _need(proj, "proj", torch.complex64, 4)
+    _need(jac, "jac", torch.complex64, 5)
+    B, P, n_out = proj.shape[0], proj.shape[1], proj.shape[2]
+    if tuple(proj.shape) != (B, P, n_out, n_out // 2 + 1) or grad_out.shape != proj.shape:
+        raise ValueError(f"grad_out and proj must be [B, P, n, n//2+1], got {tuple(grad_out.shape)}, "
+                         f"{tuple(proj.shape)}")
+    if tuple(jac.shape) != (B, P, 3, n_out, n_out // 2 + 1):
+        raise ValueError(f"jac must be [{B}, {P}, 3, {n_out}, {n_out // 2 + 1}], got {tuple(jac.shape)}")
+    if grad_out.device != proj.device or jac.device != proj.device:
+        raise ValueError("grad_out, proj and jac must be on one device")
+    gr = torch.empty((B_rot, P, 3, 3), dtype=torch.float32, device=proj.device) if want_rot else None
+    gs = torch.empty((B_shift, P, 2), dtype=torch.float32, device=proj.device) if want_shift else None
+    st = _lib.lib().tp_grad_pose_jac(grad_out.data_ptr(), proj.data_ptr(), jac.data_ptr(), B, P, n_out,
+                                     int(B_rot), int(B_shift), float(oversampling), float(cutoff), _ptr(gr),
+                                     _ptr(gs), _stream(proj.device))
+    _lib.check(st, "tp_grad_pose_jac")
+    return gr, gs
+
+
 class _Project(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, ref, rot, shift, ndim, n_out, interp, oversampling, cutoff):
-        out = _project(ndim, ref, rot, shift, n_out, interp, oversampling, cutoff)
-        ctx.save_for_backward(ref, rot, shift)
+    def forward(ctx, ref, rot, shift, ndim, n_out, interp, oversampling, cutoff, save_jacobian):
+        pose_grads = ctx.needs_input_grad[1] or (shift is not None and ctx.needs_input_grad[2])
+        jac = None
+        if ndim == 3 and save_jacobian and pose_grads:
+            out, jac = tp_project_3d_jac(ref, rot, shift, n_out, interp, oversampling, cutoff)
+            ctx.save_for_backward(ref, rot, shift, out, jac)
+        else:
+            out = _project(ndim, ref, rot, shift, n_out, interp, oversampling, cutoff)
+            ctx.save_for_backward(ref, rot, shift)
+        ctx.has_jac = jac is not None
         ctx.cfg = (ndim, interp, oversampling, cutoff)
         return out
 
     @staticmethod
     def backward(ctx, g):
-        ref, rot, shift = ctx.saved_tensors
+        if ctx.has_jac:
+            ref, rot, shift, out, jac = ctx.saved_tensors
+        else:
+            ref, rot, shift = ctx.saved_tensors
         ndim, interp, oversampling, cutoff = ctx.cfg
         g = g.contiguous()
         if g.dtype != torch.complex64:
@@ -194,20 +249,28 @@ class _Project(torch.autograd.Function):
             d_ref = _backproject(ndim, g, rot, shift, ref.shape[1], interp, oversampling, cutoff)
         want_rot = ctx.needs_input_grad[1]
         want_shift = shift is not None and ctx.needs_input_grad[2]
-        if want_rot or want_shift:
+        if (want_rot or want_shift) and ctx.has_jac:
+            B_shift = shift.shape[0] if shift is not None else 1
+            d_rot, d_shift = tp_grad_pose_jac(g, out, jac, rot.shape[0], B_shift, oversampling, cutoff,
+                                              want_rot=want_rot, want_shift=want_shift)
+        elif want_rot or want_shift:
             d_rot, d_shift = tp_grad_pose(ref, g, rot, shift, interp, oversampling, cutoff,
                                           want_rot=want_rot, want_shift=want_shift)
-        return d_ref, d_rot, d_shift, None, None, None, None, None
+        return d_ref, d_rot, d_shift, None, None, None, None, None, None
 
 
-def project_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
-    """Differentiable 3D->2D projection (gradients to vol, rot and shift)."""
-    return _Project.apply(vol, rot, shift, 3, n_out, interp, oversampling, cutoff)
+def project_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0,
+               save_jacobian=True):
+    """Differentiable 3D->2D projection (gradients to vol, rot and shift).
+
+    With pose gradients needed and save_jacobian, the forward keeps 24 bytes
+    per output for a backward without a second gather pass."""
+    return _Project.apply(vol, rot, shift, 3, n_out, interp, oversampling, cutoff, save_jacobian)
 
 
 def project_2d(img, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
     """Differentiable 2D->2D projection (gradients to img, rot and shift)."""
-    return _Project.apply(img, rot, shift, 2, n_out, interp, oversampling, cutoff)
+    return _Project.apply(img, rot, shift, 2, n_out, interp, oversampling, cutoff, False)
 
 
 # --------------------------------------------------- weights and x = 0 plane

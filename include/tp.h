@@ -247,6 +247,47 @@ tp_status tp_grad_pose(int ndim, const tp_c64* ref, int64_t B, int64_t N,
                        int64_t N_out, int interp, float oversampling, float cutoff,
                        float* grad_rot, float* grad_shift, void* stream);
 
+/*
+ * Forward 3D -> 2D that also saves what the pose gradients need, so that
+ * they take one streaming pass instead of a second pass of gathers over the
+ * reference (the analytic gradients of the ar page tech. section 2, by the
+ * same chain rule as tp_grad_pose):
+ *   out  [B, P, N_out, N_out/2+1] complex64, overwritten: the values of
+ *        tp_project_3d for the same arguments (same arithmetic up to the
+ *        order of float additions)
+ *   jac  [B, P, 3, N_out, N_out/2+1] complex64, overwritten: for each
+ *        output, phase * dS/dp_j (j = x, y, z), the derivative of the output
+ *        with respect to its sample point p in reference index units; 0
+ *        outside the cutoff and where the output reads 0
+ * Other arguments and errors as tp_project_3d.
+ */
+tp_status tp_project_3d_jac(const tp_c64* vol, int64_t B, int64_t N,
+                            const float* rot, int64_t B_rot, int64_t P,
+                            const float* shift, int64_t B_shift,
+                            int64_t N_out, int interp, float oversampling, float cutoff,
+                            tp_c64* out, tp_c64* jac, void* stream);
+
+/*
+ * Pose gradients of L = Re sum conj(grad_out) * project_3d(...) from the
+ * saved out and jac of tp_project_3d_jac (same B, P, N_out, oversampling and
+ * cutoff; B_rot and B_shift as that call's):
+ *   dL/dR[i][j] = os * sum_k k_i Re(conj(G) jac_j)       (i = 0: kx, 1: ky)
+ *   dL/ds_j     = (2 pi / N_out) sum_k k_j Im(conj(G) out)
+ * the values of tp_grad_pose (ndim = 3) for that call, without reading the
+ * reference.  Only outputs inside the cutoff are read.
+ *   grad_out   [B, P, N_out, N_out/2+1] complex64, input
+ *   proj, jac  the outputs of tp_project_3d_jac, input
+ *   grad_rot   [B_rot, P, 3, 3] float32, overwritten (last row 0), or NULL
+ *   grad_shift [B_shift, P, 2] float32, overwritten, or NULL
+ * Errors: TP_EINVAL for null or misaligned buffers, sizes <= 0, B_rot or
+ * B_shift not in {1, B}, a bad oversampling or a NaN cutoff;
+ * TP_EUNSUPPORTED for N_out above 65535 or B * P above 2^31 - 1.
+ */
+tp_status tp_grad_pose_jac(const tp_c64* grad_out, const tp_c64* proj, const tp_c64* jac,
+                           int64_t B, int64_t P, int64_t N_out, int64_t B_rot, int64_t B_shift,
+                           float oversampling, float cutoff,
+                           float* grad_rot, float* grad_shift, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -156,3 +156,25 @@ def test_rotate_entry_points_check_arguments():
     assert L.tp_rotate_grad_pose(FAKE, 1, 16, None, FAKE, 1, 2, None, 1, 16, 1, 1.0, -1.0, FAKE, None, None) == EINVAL
     assert L.tp_rotate_grad_pose(FAKE, 1, 16, FAKE, FAKE, 1, 2, None, 1, 16, 1, 1.0, math.nan, FAKE, None,
                                  None) == EINVAL
+
+
+def test_jacobian_entry_points_check_arguments():
+    L = _lib.lib()
+    # vol, B, N, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, out, jac, stream
+    assert L.tp_project_3d_jac(FAKE, 1, 32, FAKE, 1, 4, None, 1, 32, 1, 1.0, -1.0, FAKE, None, None) == EINVAL
+    assert L.tp_project_3d_jac(FAKE, 1, 32, FAKE, 1, 4, None, 1, 32, 1, 1.0, -1.0, FAKE, FAKE_ODD, None) == EINVAL
+    assert L.tp_project_3d_jac(FAKE, 1, 32, FAKE, 1, 4, None, 1, 32, 2, 1.0, -1.0, FAKE, FAKE, None) == EINVAL
+    assert L.tp_project_3d_jac(FAKE, 1, 70000, FAKE, 1, 4, None, 1, 32, 1, 1.0, -1.0, FAKE, FAKE, None) == EUNSUP
+    # grad_out, proj, jac, B, P, N_out, B_rot, B_shift, os, cutoff, grad_rot, grad_shift, stream
+    assert L.tp_grad_pose_jac(FAKE, None, FAKE, 1, 4, 32, 1, 1, 1.0, -1.0, FAKE, None, None) == EINVAL
+    assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE_ODD, 1, 4, 32, 1, 1, 1.0, -1.0, FAKE, None, None) == EINVAL
+    assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 0, 4, 32, 1, 1, 1.0, -1.0, FAKE, None, None) == EINVAL
+    assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 2, 4, 32, 3, 1, 1.0, -1.0, FAKE, None, None) == EINVAL
+    assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 2, 4, 32, 1, 3, 1.0, -1.0, None, FAKE, None) == EINVAL
+    assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 1, 4, 32, 1, 1, 0.0, -1.0, FAKE, None, None) == EINVAL
+    assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 1, 4, 32, 1, 1, 1.0, math.nan, FAKE, None, None) == EINVAL
+    assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 1, 4, 32, 1, 1, 1.0, -1.0, FAKE + 2, None, None) == EINVAL
+    assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 1, 4, 70000, 1, 1, 1.0, -1.0, FAKE, None, None) == EUNSUP
+    assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 1 << 20, 1 << 12, 32, 1, 1, 1.0, -1.0, FAKE, None, None) == EUNSUP
+    # nothing requested: a no-op that touches no pointer
+    assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 1, 4, 32, 1, 1, 1.0, -1.0, None, None, None) == _lib.TP_OK

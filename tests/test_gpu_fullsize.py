@@ -107,6 +107,34 @@ def test_fullsize_grad_pose_sampled_poses(key):
 
 
 @pytest.mark.parametrize("key", KEYS)
+def test_fullsize_grad_pose_jac_sampled_poses(key):
+    """The Jacobian-saving forward over all poses, then the pose gradients
+    from it with the sparse upstream gradient."""
+    import torch
+
+    from cryo_em_fourier_amd import tp_grad_pose_jac, tp_project_3d_jac
+
+    c = workload(key)
+    w = c["w"]
+    log(f"[fullsize grad_pose_jac] {key}: {w.P} poses, upstream nonzero on {c['idx'].tolist()}")
+    out, jac = tp_project_3d_jac(to_dev(c["V"]), to_dev(c["R"]), to_dev(c["s"]), w.N_out, w.interp, c["os"],
+                                 w.cutoff)
+    gr, gs = tp_grad_pose_jac(_sparse_upstream(c), out, jac, c["R"].shape[0], c["s"].shape[0], c["os"], w.cutoff)
+    got = out[:, c["idx"]].cpu().numpy()
+    del out, jac
+    torch.cuda.empty_cache()
+    ref = oracle.project(c["V"], c["R"][:, c["idx"]], c["s"][:, c["idx"]], w.N_out, w.interp, c["os"], w.cutoff)
+    assert_parity(got, ref, f"forward (jac) {key}")
+    gr, gs = gr.cpu().numpy(), gs.cpu().numpy()
+    dR, ds = oracle.grad_pose(c["V"], c["G_sub"], c["R"][:, c["idx"]], c["s"][:, c["idx"]], w.N_out, w.interp,
+                              c["os"], w.cutoff)
+    assert_parity(gr[:, c["idx"]], dR, f"grad_rot (jac) {key}")
+    assert_parity(gs[:, c["idx"]], ds, f"grad_shift (jac) {key}")
+    rest = np.setdiff1d(np.arange(w.P), c["idx"])
+    assert not gr[:, rest].any() and not gs[:, rest].any(), "poses with zero upstream must get zero gradients"
+
+
+@pytest.mark.parametrize("key", KEYS)
 def test_fullsize_adjoint_identity_dense(key):
     import torch
 

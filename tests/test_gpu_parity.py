@@ -130,6 +130,30 @@ def test_grad_pose_3d_matches_oracle(name):
     assert_parity(gs.cpu().numpy(), ds, f"grad_shift {name}")
 
 
+@pytest.mark.parametrize("name", CASES3)
+def test_project_3d_jac_and_grad_pose_jac_match_oracle(name):
+    """The Jacobian-saving forward gives the forward's values, and the pose
+    gradients taken from its Jacobian give the oracle's gradients."""
+    from cryo_em_fourier_amd import tp_grad_pose_jac, tp_project_3d_jac
+
+    c = case3d(name)
+    log(f"[project_3d_jac + grad_pose_jac] {name}")
+    V, R, s, G = _dev(c)
+    out, jac = tp_project_3d_jac(V, R, s, c["n_out"], c["interp"], float(c["os"]), float(c["cutoff"]))
+    ref = oracle.project(c["V"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(out.cpu().numpy(), ref, f"project_3d_jac {name}")
+    B_shift = 1 if c["s"] is None else c["s"].shape[0]
+    gr, gs = tp_grad_pose_jac(G, out, jac, c["R"].shape[0], B_shift, float(c["os"]), float(c["cutoff"]))
+    dR, ds = oracle.grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
+    gr, gs = gr.cpu().numpy(), gs.cpu().numpy()
+    if name == "adv-linear":
+        keep = [0, 1, 4, 5, 6]  # one-sided derivatives at kinks, as in the gradient test above
+        gr, dR, gs, ds = gr[:, keep], dR[:, keep], gs[:, keep], ds[:, keep]
+    assert_parity(gr, dR, f"grad_rot (jac) {name}")
+    assert_parity(gs, ds, f"grad_shift (jac) {name}")
+    assert not gr[:, :, 2].any(), "the last row of dL/dR is 0"
+
+
 # ------------------------------------------------------------------- 2D
 
 @functools.lru_cache(maxsize=None)
@@ -239,7 +263,8 @@ def test_adjoint_identity_on_gpu(ndim):
     assert abs(lhs - rhs) <= 1e-6 * scale
 
 
-def test_autograd_matches_direct_calls():
+@pytest.mark.parametrize("save_jacobian", [True, False])
+def test_autograd_matches_direct_calls(save_jacobian):
     import torch
 
     from cryo_em_fourier_amd import project_3d, tp_backproject_3d, tp_grad_pose
@@ -247,7 +272,8 @@ def test_autograd_matches_direct_calls():
     c = case3d("batch")
     V, R, s, G = _dev(c)
     Vg, Rg, sg = V.clone().requires_grad_(), R.clone().requires_grad_(), s.clone().requires_grad_()
-    out = project_3d(Vg, Rg, sg, c["n_out"], c["interp"], float(c["os"]), float(c["cutoff"]))
+    out = project_3d(Vg, Rg, sg, c["n_out"], c["interp"], float(c["os"]), float(c["cutoff"]),
+                     save_jacobian=save_jacobian)
     loss = torch.sum((torch.conj(G) * out).real)
     loss.backward()
     dV = tp_backproject_3d(G, R, s, c["N"], c["interp"], float(c["os"]), float(c["cutoff"]))
