@@ -13,7 +13,9 @@
 // the plane lattice points whose stencil can touch the brick and adds their
 // tap contributions to the brick in LDS.  LDS float atomics are slow on this
 // part, integer ones are not: contributions are accumulated as int32 fixed
-// point (exact, order independent), with a power-of-two quantum chosen per
+// point (exact, order independent; a (re, im) pair packed in one 64-bit
+// word, or one int32 for the real weight volume), with a power-of-two
+// quantum chosen per
 // group of poses from a bound on |G| that is checked against the values read
 // (a group that exceeds it is redone), so the sums cannot overflow; each
 // group is flushed into fp32 registers.  Bricks are split over pose chunks in
@@ -31,7 +33,8 @@ namespace {
 constexpr int kVox = 4096;          // voxels per brick
 constexpr int kPerThread = kVox / kBlock;
 constexpr int kGroupMax = 16;       // poses per fixed-point group
-constexpr int kHitCap = 4096;       // lattice points per group (LDS hit list)
+constexpr int kHitCap = 2560;       // lattice points per group slice (LDS hit list; sized so 3
+                                    // workgroups fit a CU's LDS beside the accumulator)
 constexpr int kPrefetch = 2;        // hits whose G values a thread loads at once
 // Fixed point: per group, |sum| < 2^kQuantumBits q at every voxel, with
 // q = 2^e / 2^kQuantumBits >= 8 sum_poses(dens) max|G| / 2^kQuantumBits.
@@ -49,24 +52,25 @@ template <int NDIM> struct Brick;
 template <> struct Brick<3> { static constexpr int X = 16, Y = 16, Z = 16; };
 template <> struct Brick<2> { static constexpr int X = 64, Y = 64, Z = 1; };
 
-// LDS slot of brick-local voxel (x, y, z).  Entries are 8 bytes, so only the
-// low 4 bits of the slot pick the bank pair; XOR-ing x with a hash of (y, z)
-// spreads the taps of a wave over the bank pairs.
+// LDS accumulator of a brick: W slots (packed (re, im) pairs, or int32 real
+// parts for the weight volume) holding the brick's (y, z) rows of X voxels
+// at a stride of S = X + kGuard slots, starting kGuard slots in, so the
+// kGuard slots before each row are shared guard slots: a tap up to kGuard
+// voxels beyond the brick in x, on either side, lands in them and they are
+// never read.  A tap's slot is then its row's base plus a compile-time
+// offset, and no x test is needed.  Bank pairs are slot mod 16: the odd row
+// stride and a z-plane stride of 5 mod 16 (padded) keep taps that differ in
+// y or z only off each other's banks.
+constexpr int kGuard = 3;  // the cubic stencil reaches 3 voxels past its first tap
 template <int NDIM>
-__device__ __forceinline__ int row_hash(int y, int z) {
-  return NDIM == 3 ? ((y + 3 * z) & 15) : ((y * 5) & 63);
-}
+struct AccLayout {
+  static constexpr int S = Brick<NDIM>::X + kGuard;
+  static constexpr int PZ = NDIM == 3 ? Brick<NDIM>::Y * S + ((5 - Brick<NDIM>::Y * S % 16) + 16) % 16 : 0;
+  static constexpr int W = (NDIM == 3 ? Brick<NDIM>::Z * PZ : Brick<NDIM>::Y * S) + kGuard;
+};
 template <int NDIM>
-__device__ __forceinline__ int slot_of(int x, int y, int z) {
-  using BR = Brick<NDIM>;
-  return ((z * BR::Y + y) * BR::X) | (x ^ row_hash<NDIM>(y, z));
-}
-
-// float -> int32, rounding to nearest (ties up): one VALU instruction.
-__device__ __forceinline__ int cvt_rpi(float x) {
-  int r;
-  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
-  return r;
+__device__ __forceinline__ int acc_word(int x, int y, int z) {
+  return kGuard + z * AccLayout<NDIM>::PZ + y * AccLayout<NDIM>::S + x;
 }
 
 // (re, im) int32 pair as one int64, re * 2^32 + im: sums of such values
@@ -78,6 +82,13 @@ __device__ __forceinline__ unsigned long long pack_pair(int re, int im) {
 __device__ __forceinline__ void unpack_pair(unsigned long long v, int& re, int& im) {
   im = (int)(unsigned)(v & 0xFFFFFFFFull);
   re = (int)(long long)((long long)v >> 32) + (im < 0 ? 1 : 0);
+}
+
+// float -> int32, rounding to nearest (ties up): one VALU instruction.
+__device__ __forceinline__ int cvt_rpi(float x) {
+  int r;
+  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
 }
 
 struct BrickPos {
@@ -392,13 +403,27 @@ __device__ __forceinline__ void lattice_values3(const OpParams& p, const PoseVie
   cd.v1 = make_float2(cr.x + cm.x, cr.y - cm.y);
 }
 
+// Hit of thread tid within a block of kBlock consecutive hits: waves 0 and 1
+// take alternate hits of the first half, waves 2 and 3 of the second.
+// Consecutive hits are neighbouring lattice points whose sample points can
+// share a voxel, and lanes adding to one LDS address in the same instruction
+// serialise; two lattice steps apart (two voxels at oversampling 1) they
+// cannot.  Measured against strides 1, 4 and 8, which were slower.
+__device__ __forceinline__ int hit_slot(int tid) { return (tid & 63) * 2 + ((tid >> 6) & 1) + (tid >> 7) * 64 * 2; }
+
 // Spread one lattice point over its taps inside the brick (int32 fixed point).
-template <int NDIM, int INTERP>
-__device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float inv_q,
-                                       unsigned long long* acc) {
+// The point lies in the brick's reach box, so its first x tap is at most
+// kGuard voxels before the brick and its last at most kGuard after it: taps
+// outside the brick in x fall into guard words.  Rows outside in y or z are
+// skipped.  REAL: int32 real parts only (the weight volume), else packed
+// pairs.
+template <int NDIM, int INTERP, bool REAL>
+__device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float inv_q, unsigned long long* acc) {
   using BR = Brick<NDIM>;
+  using L = AccLayout<NDIM>;
   using K = Kern<INTERP>;
   constexpr int T = K::T;
+  static_assert(T - 1 <= kGuard, "guard words must cover the stencil");
   const AxisPos ax = axis_pos(cd.q[0], K::OFF), ay = axis_pos(cd.q[1], K::OFF);
   float wx[T], wy[T], wz[T];
   K::w(ax.f, wx);
@@ -412,20 +437,15 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
 #pragma unroll
     for (int d = 0; d < T; ++d) wz[d] = d == 0 ? 1.f : 0.f;
   }
-  // x weights folded with the per-x value (x = 0 takes the real part only);
-  // taps outside the brick get weight 0 and a clamped slot
+  // x weights folded with the per-x value (x = 0 takes the real part only)
   float are[T], aim[T];
-  int xl[T];
 #pragma unroll
   for (int d = 0; d < T; ++d) {
-    const int tx = ax.x0 + d;
-    const float2 v = tx >= 1 ? cd.v1 : cd.v0;
-    const bool inx = tx >= br.x0 && tx <= br.x1;
-    are[d] = inx ? wx[d] * v.x * inv_q : 0.f;
-    aim[d] = inx ? wx[d] * v.y * inv_q : 0.f;
-    xl[d] = (inx ? tx - br.x0 : 0) * (int)sizeof(unsigned long long);  // byte offset in the row
+    const float2 v = ax.x0 + d >= 1 ? cd.v1 : cd.v0;
+    are[d] = wx[d] * v.x * inv_q;
+    aim[d] = wx[d] * v.y * inv_q;
   }
-  char* accb = reinterpret_cast<char*>(acc);
+  const int x0w = acc_word<NDIM>(ax.x0 - br.x0, 0, 0);
 #pragma unroll
   for (int dz = 0; dz < (NDIM == 3 ? T : 1); ++dz) {
     const int tz = z0 + dz;
@@ -435,14 +455,11 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
       const int ty = ay.x0 + dy;
       if (ty < br.y0 || ty > br.y1) continue;
       const float wyz = wy[dy] * wz[dz];
-      const int yl = ty - br.y0, zl = NDIM == 3 ? tz - br.z0 : 0;
-      // slot_of() in bytes: the shift distributes over | and ^
-      constexpr int E = (int)sizeof(unsigned long long);
-      const int row = (zl * BR::Y + yl) * BR::X * E, h = row_hash<NDIM>(yl, zl) * E;
+      const int w = x0w + (NDIM == 3 ? tz - br.z0 : 0) * L::PZ + (ty - br.y0) * L::S;
 #pragma unroll
       for (int dx = 0; dx < T; ++dx) {
-        const int ir = cvt_rpi(are[dx] * wyz), ii = cvt_rpi(aim[dx] * wyz);
-        atomicAdd(reinterpret_cast<unsigned long long*>(accb + (row | (xl[dx] ^ h))), pack_pair(ir, ii));
+        if (REAL) atomicAdd(reinterpret_cast<int*>(acc) + w + dx, cvt_rpi(are[dx] * wyz));
+        else atomicAdd(acc + w + dx, pack_pair(cvt_rpi(are[dx] * wyz), cvt_rpi(aim[dx] * wyz)));
       }
     }
   }
@@ -458,7 +475,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   constexpr bool VOL = MODE == kVolume;
   constexpr int GMAX = VOL ? 1 : kGroupMax;
   using BR = Brick<NDIM>;
-  __shared__ unsigned long long acc[kVox];
+  using AL = AccLayout<NDIM>;
+  __shared__ unsigned long long acc[AL::W];
+  int* acc_r = reinterpret_cast<int*>(acc);  // the weight volume's int32 slots
   __shared__ uint32_t s_hits[kHitCap];
   __shared__ int s_poses[kBlock];
   __shared__ PoseView s_view[kGroupMax];
@@ -472,10 +491,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   float m_prev = 0.f;  // max |G| of the previous group (0: none yet)
   float fre[kPerThread], fim[kPerThread];
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    fre[i] = fim[i] = 0.f;
-    acc[tid + i * kBlock] = 0ull;
-  }
+  for (int i = 0; i < kPerThread; ++i) fre[i] = fim[i] = 0.f;
+  for (int i = tid; i < AL::W; i += kBlock) acc[i] = 0ull;
+  __syncthreads();
 
   const Box bx = reach_box<NDIM, INTERP>(br);
   for (int w0 = br.n0; w0 < br.n1; w0 += kBlock) {
@@ -523,7 +541,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             float2 gr[kPrefetch], gm[kPrefetch];
 #pragma unroll
             for (int k = 0; k < kPrefetch; ++k) {
-              const int i = i0 + tid + k * kBlock;
+              const int i = i0 + hit_slot(tid) + k * kBlock;
               gr[k] = gm[k] = make_float2(0.f, 0.f);
               if (i < nh) {
                 const uint32_t h = s_hits[i];
@@ -549,7 +567,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             if (measure_only) continue;
 #pragma unroll
             for (int k = 0; k < kPrefetch; ++k) {
-              const int i = i0 + tid + k * kBlock;
+              const int i = i0 + hit_slot(tid) + k * kBlock;
               if (i >= nh) continue;
               const uint32_t h = s_hits[i];
               Cand cd;
@@ -561,7 +579,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
                 const PoseView& pv = s_view[hit_pose(h)];
                 lattice_values<NDIM>(p, pv, hit_kx(h, pv), hit_ky(h, pv), gr[k], gm[k], cd);
               }
-              if (in_box<NDIM>(bx, cd.q)) spread<NDIM, INTERP>(br, cd, inv_q, acc);
+              if (in_box<NDIM>(bx, cd.q)) spread<NDIM, INTERP, WEIGHTS>(br, cd, inv_q, acc);
             }
           }
 #pragma unroll
@@ -578,19 +596,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
             for (int i = 0; i < kPerThread; ++i) {
               const int v = tid + i * kBlock;
-              const int sl = slot_of<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
-              int ir, ii;
-              unpack_pair(acc[sl], ir, ii);
-              fre[i] = fmaf((float)ir, q, fre[i]);
-              fim[i] = fmaf((float)ii, q, fim[i]);
-              acc[sl] = 0ull;
+              const int sl = acc_word<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
+              if (WEIGHTS) {
+                fre[i] = fmaf((float)acc_r[sl], q, fre[i]);
+                acc_r[sl] = 0;
+              } else {
+                int ir, ii;
+                unpack_pair(acc[sl], ir, ii);
+                fre[i] = fmaf((float)ir, q, fre[i]);
+                fim[i] = fmaf((float)ii, q, fim[i]);
+                acc[sl] = 0ull;
+              }
             }
             m_prev = gmax;
             break;
           }
           if (!measure_only) {
 #pragma unroll
-            for (int i = 0; i < kPerThread; ++i) acc[tid + i * kBlock] = 0ull;
+            for (int i = 0; i < kPerThread; ++i) {
+              const int v = tid + i * kBlock;
+              const int sl = acc_word<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
+              if (WEIGHTS) acc_r[sl] = 0;
+              else acc[sl] = 0ull;
+            }
             __syncthreads();
           }
           m_assume = gmax;

@@ -335,8 +335,10 @@ __global__ __launch_bounds__(kBlock) void k_grad3p(OpParams p) {
 // second pass over the reference (k_grad_jac).  The gathers are
 // k_grad3p's; lane 0 of a pair writes the output and jac_x, lane 1 jac_y and
 // jac_z ([B, P, 3, No, Wo], one plane per component).
+// (4 waves per SIMD: capping registers at 128 measured faster than the 148
+// the compiler picks on its own)
 template <int INTERP>
-__global__ __launch_bounds__(kBlock) void k_project3p_jac(OpParams p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_project3p_jac(OpParams p) {
   const Out o = locate<true>(p);
   const int h = threadIdx.x & 1;
   double q[3] = {0.0, 0.0, 0.0};
