@@ -135,6 +135,8 @@ def cpu_baseline(V, R, s, w: synth.Workload, N: int, os_: float, poses_per_worke
         "kind": "oracle",
         "sample": f"{n} of {w.P} poses (seeded), {workers} single-threaded workers, fork pool",
         "fwd_proj_per_s": n / (fwd / workers) if fwd > 0 else None,
+        # one core: poses per second of a single-threaded worker's own time
+        "value_1core": n / (fwd + bwd) if fwd + bwd > 0 else None,
         "wall_s": wall,
     }
 
