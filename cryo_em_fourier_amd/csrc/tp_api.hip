@@ -131,19 +131,20 @@ tp_status backproject_weights(int ndim, const float* w, int64_t B, int64_t P, in
 }
 
 // The 3D -> 3D rotation: the reference's checks, then a tiling of the
-// [N_out, N_out, N_out/2+1] output (16 kx columns x 16 (kz, ky) rows).
+// [N_out, N_out, N_out/2+1] output (16 kx columns x 8 (kz, ky) rows, two
+// lanes per output).
 tp_status rotate_fill(const Common& c, tp::OpParams& p) {
   const tp_status st = check_and_fill(c, p);
   if (st != TP_OK) return st;
   const uint64_t rows = (uint64_t)c.N_out * (uint64_t)c.N_out;
   const uint64_t tx = (uint64_t)(p.Wo + tp::kTileX - 1) / tp::kTileX;
-  const uint64_t ty = (rows + tp::kTileY - 1) / tp::kTileY;
+  const uint64_t ty = (rows + tp::kTileYPairs - 1) / tp::kTileYPairs;
   const uint64_t blocks = (uint64_t)c.B * (uint64_t)c.P * tx * ty;
   if (blocks > kMaxBlocks || tx * ty > 0x7FFFFFFFull) return TP_EUNSUPPORTED;
   p.tiles_x = (int)tx;
   p.tiles_y = (int)ty;
   p.tiles_per_pose = (int)(tx * ty);
-  p.tile_y = tp::kTileY;
+  p.tile_y = tp::kTileYPairs;
   p.nblocks = (uint32_t)blocks;
   return TP_OK;
 }

@@ -122,10 +122,15 @@ struct RefGeom {
   uint32_t plane;   // bytes per z-plane: N * row (3D)
 };
 
+// Byte offset of index t along an axis of byte stride `stride` (kBig outside
+// the stored range).  A 24-bit multiply (full rate) is exact here: the index
+// is below 2^16, and an entry of at most 2^31 bytes keeps the row and plane
+// strides below 2^24 (a plane exceeds 2^24 bytes only for N >= 128 with
+// N * plane > 2^31) and every offset below 2^31.
 __device__ __forceinline__ uint32_t axis_off(int t, const RefGeom& g, uint32_t stride) {
   const bool ok = t >= g.lo && t <= g.hi;
   const int w = t < 0 ? t + g.N : t;
-  return ok ? (uint32_t)w * stride : kBig;
+  return ok ? __umul24((uint32_t)w, stride) : kBig;
 }
 
 // exp(-2 pi i (kx sx + ky sy) / n_out); turns reduced in fp64 so that large

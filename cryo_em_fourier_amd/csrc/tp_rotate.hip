@@ -6,9 +6,10 @@
 // ky R[1,:] + kz R[2,:]) with the same per-tap Friedel fold and kernels as
 // the central slice (which is the kz = 0 plane of this op), times the shift
 // phase exp(-2 pi i k.s / N_out) of a 3-vector shift, inside the sphere
-// |k| <= cutoff.  One lane per output; a 256-lane workgroup covers 16 kx
-// columns of 16 (kz, ky) rows of one pose.  The adjoint is the brick adjoint
-// of tp_adjoint.hip run over volume lattices.
+// |k| <= cutoff.  Two lanes per output, each gathering half of every x-row
+// (as the central-slice kernels); a 256-lane workgroup covers 16 kx columns
+// of 8 (kz, ky) rows of one pose.  The adjoint is the brick adjoint of
+// tp_adjoint.hip run over volume lattices.
 #include "tp_internal.h"
 #include "tp_stencil.h"
 
@@ -29,8 +30,9 @@ __device__ __forceinline__ ROut rlocate(const OpParams& p) {
   const uint32_t bn = g / (uint32_t)p.tiles_per_pose;
   o.n = (int)(bn % (uint32_t)p.P);
   o.b = (int)(bn / (uint32_t)p.P);
-  o.kx = (int)(tile % (uint32_t)p.tiles_x) * kTileX + (int)threadIdx.x % kTileX;
-  const long long row = (long long)(tile / (uint32_t)p.tiles_x) * kTileY + (int)threadIdx.x / kTileX;
+  const int oi = (int)(threadIdx.x >> 1);  // lane pair
+  o.kx = (int)(tile % (uint32_t)p.tiles_x) * kTileX + oi % kTileX;
+  const long long row = (long long)(tile / (uint32_t)p.tiles_x) * kTileYPairs + oi / kTileX;
   const long long rows = (long long)p.No * p.No;
   o.in = o.kx < p.Wo && row < rows;
   const int iz = (int)(row / p.No), iy = (int)(row % p.No);
@@ -73,10 +75,11 @@ __device__ __forceinline__ float2 rphase(const OpParams& p, const ROut& o) {
 template <int INTERP>
 __global__ __launch_bounds__(kBlock) void k_rotate(OpParams p) {
   const ROut o = rlocate(p);
-  if (!o.in) return;
+  const int h = threadIdx.x & 1;
   float2 res = make_float2(0.f, 0.f);
-  double q[3];
-  if (o.keep && rsample(p, o, q)) {
+  double q[3] = {0.0, 0.0, 0.0};
+  const bool active = o.keep && rsample(p, o, q);
+  if (active) {
     const RefGeom g = ref_geom(p);
     const rsrc_t rs = make_rsrc(p.ref + (size_t)o.b * p.ref_elems, p.ref_bytes);
     // main stencil around m = |p_x|-side sample, secondary across x = 0
@@ -84,12 +87,14 @@ __global__ __launch_bounds__(kBlock) void k_rotate(OpParams p) {
     double m[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) m[j] = c ? -q[j] : q[j];
-    const float2 mv = gather3<INTERP>(rs, g, m[0], m[1], m[2], c ? 1 : 0);
+    const float2 mv = gather3_half<INTERP>(rs, g, m[0], m[1], m[2], c ? 1 : 0, h);
     float2 sv = make_float2(0.f, 0.f);
-    if (needs_secondary<INTERP>(m[0], c ? 0 : 1)) sv = gather3<INTERP>(rs, g, -m[0], -m[1], -m[2], c ? 0 : 1);
+    if (needs_secondary<INTERP>(m[0], c ? 0 : 1)) sv = gather3_half<INTERP>(rs, g, -m[0], -m[1], -m[2], c ? 0 : 1, h);
     res = c ? make_float2(mv.x + sv.x, sv.y - mv.y) : make_float2(mv.x + sv.x, mv.y - sv.y);
-    res = cmul(rphase(p, o), res);
   }
+  res = pair_sum(res);  // both lanes of a pair share `active`
+  if (!o.in || h) return;
+  if (active) res = cmul(rphase(p, o), res);
   p.img_out[o.idx] = res;
 }
 
@@ -101,11 +106,13 @@ __global__ __launch_bounds__(kBlock) void k_rotate_grad(OpParams p) {
   constexpr int NV = 12;
   __shared__ double red[kBlock / 64][16];
   const ROut o = rlocate(p);
+  const int h = threadIdx.x & 1;
   double acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0;
-  double q[3];
+  double q[3] = {0.0, 0.0, 0.0};
   const bool active = o.keep && rsample(p, o, q);
+  float2 S = make_float2(0.f, 0.f), dS[3] = {S, S, S};
   if (active) {
     const RefGeom g = ref_geom(p);
     const rsrc_t rs = make_rsrc(p.ref + (size_t)o.b * p.ref_elems, p.ref_bytes);
@@ -114,12 +121,11 @@ __global__ __launch_bounds__(kBlock) void k_rotate_grad(OpParams p) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) m[j] = c ? -q[j] : q[j];
     float2 mv[4], sv[4];
-    gather3_grad<INTERP>(rs, g, m[0], m[1], m[2], c ? 1 : 0, mv);
+    gather3_grad_half<INTERP>(rs, g, m[0], m[1], m[2], c ? 1 : 0, h, mv);
 #pragma unroll
     for (int j = 0; j < 4; ++j) sv[j] = make_float2(0.f, 0.f);
-    if (needs_secondary<INTERP>(m[0], c ? 0 : 1)) gather3_grad<INTERP>(rs, g, -m[0], -m[1], -m[2], c ? 0 : 1, sv);
+    if (needs_secondary<INTERP>(m[0], c ? 0 : 1)) gather3_grad_half<INTERP>(rs, g, -m[0], -m[1], -m[2], c ? 0 : 1, h, sv);
     // S and dS/dp through m = +-p (as the central-slice gradient kernels)
-    float2 S, dS[3];
     if (c) {
       S = make_float2(mv[0].x + sv[0].x, sv[0].y - mv[0].y);
 #pragma unroll
@@ -129,6 +135,11 @@ __global__ __launch_bounds__(kBlock) void k_rotate_grad(OpParams p) {
 #pragma unroll
       for (int j = 0; j < 3; ++j) dS[j] = make_float2(mv[j + 1].x - sv[j + 1].x, mv[j + 1].y + sv[j + 1].y);
     }
+  }
+  S = pair_sum(S);  // both lanes of a pair share `active`
+#pragma unroll
+  for (int j = 0; j < 3; ++j) dS[j] = pair_sum(dS[j]);
+  if (active && h == 0) {
     const float2 gph = cmul(conjf2(p.img[o.idx]), rphase(p, o));
     const double os = (double)p.os;
     const double k[3] = {(double)o.kx, (double)o.ky, (double)o.kz};

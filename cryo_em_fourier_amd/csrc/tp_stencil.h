@@ -224,9 +224,13 @@ __device__ __forceinline__ float2 gather3_half(rsrc_t rs, const RefGeom& g, doub
   const uint32_t xo = setup_x<INTERP, false>(g, qx, xmin, wx, nullptr) + 8u * H * h;
   setup_yz<INTERP, false>(g, qy, g.row, wy, nullptr, yb);
   setup_yz<INTERP, false>(g, qz, g.plane, wz, nullptr, zb);
-  float wh[H];
+  // the lane's x weights folded into the y weights: two multiply-adds per
+  // component and row
+  float cy[T][H];
 #pragma unroll
-  for (int d = 0; d < H; ++d) wh[d] = h ? wx[H + d] : wx[d];
+  for (int dy = 0; dy < T; ++dy)
+#pragma unroll
+    for (int d = 0; d < H; ++d) cy[dy][d] = wy[dy] * (h ? wx[H + d] : wx[d]);
 #pragma unroll
   for (int d = 0; d < T; ++d) yb[d] = yb[d] == kBig ? kBig : yb[d] + xo;
   float2 acc = make_float2(0.f, 0.f);
@@ -236,18 +240,17 @@ __device__ __forceinline__ float2 gather3_half(rsrc_t rs, const RefGeom& g, doub
 #pragma unroll
     for (int dy = 0; dy < T; ++dy) {
       const uint32_t ro = zb[dz] + yb[dy];
-      float2 r;
       if (H == 2) {
         const float4 v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)ro, 0, 0));
-        r.x = fmaf(wh[0], v.x, wh[H - 1] * v.z);
-        r.y = fmaf(wh[0], v.y, wh[H - 1] * v.w);
+        pl.x = fmaf(cy[dy][0], v.x, pl.x);
+        pl.y = fmaf(cy[dy][0], v.y, pl.y);
+        pl.x = fmaf(cy[dy][H - 1], v.z, pl.x);
+        pl.y = fmaf(cy[dy][H - 1], v.w, pl.y);
       } else {
         const float2 v = load_c64(rs, ro);
-        r.x = wh[0] * v.x;
-        r.y = wh[0] * v.y;
+        pl.x = fmaf(cy[dy][0], v.x, pl.x);
+        pl.y = fmaf(cy[dy][0], v.y, pl.y);
       }
-      pl.x = fmaf(wy[dy], r.x, pl.x);
-      pl.y = fmaf(wy[dy], r.y, pl.y);
     }
     acc.x = fmaf(wz[dz], pl.x, acc.x);
     acc.y = fmaf(wz[dz], pl.y, acc.y);
