@@ -31,9 +31,10 @@ namespace tp {
 namespace {
 
 constexpr int kVox = 4096;          // voxels per brick
-constexpr int kPerThread = kVox / kBlock;
+constexpr int kAdjBlock = 512;      // threads per brick workgroup (8 waves)
+constexpr int kPerThread = kVox / kAdjBlock;
 constexpr int kGroupMax = 16;       // poses per fixed-point group
-constexpr int kHitCap = 2560;       // lattice points per group slice (LDS hit list; sized so 3
+constexpr int kHitCap = 8192;       // lattice points per group slice (LDS hit list; sized so 2
                                     // workgroups fit a CU's LDS beside the accumulator)
 constexpr int kPrefetch = 2;        // hits whose G values a thread loads at once
 // Fixed point: per group, |sum| < 2^kQuantumBits q at every voxel, with
@@ -302,7 +303,7 @@ __device__ __forceinline__ int list_hits_vol(const OpParams& p, const Box& bx, c
   const int rows_total = pv.hit ? nky * nkz : 0;
   const int h1 = h0 + cap;
   int carry = 0;
-  for (int rw = 0; rw < rows_total; rw += kBlock) {
+  for (int rw = 0; rw < rows_total; rw += kAdjBlock) {
     const int r = rw + tid;
     int cr = 0, a = 0, dky = 0, dkz = 0;
     if (r < rows_total) {
@@ -350,7 +351,7 @@ __device__ __forceinline__ int list_hits_vol(const OpParams& p, const Box& bx, c
     __syncthreads();
     int off = carry + incl - cr, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) {
+    for (int w = 0; w < kAdjBlock / 64; ++w) {
       off += w < wave ? s_wcnt[w] : 0;
       tot += s_wcnt[w];
     }
@@ -403,8 +404,8 @@ __device__ __forceinline__ void lattice_values3(const OpParams& p, const PoseVie
   cd.v1 = make_float2(cr.x + cm.x, cr.y - cm.y);
 }
 
-// Hit of thread tid within a block of kBlock consecutive hits: waves 0 and 1
-// take alternate hits of the first half, waves 2 and 3 of the second.
+// Hit of thread tid within a block of kAdjBlock consecutive hits: each pair
+// of waves takes alternate hits of its own 128.
 // Consecutive hits are neighbouring lattice points whose sample points can
 // share a voxel, and lanes adding to one LDS address in the same instruction
 // serialise; two lattice steps apart (two voxels at oversampling 1) they
@@ -469,7 +470,7 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
 // kVolume (the adjoint of the 3D -> 3D rotation: volume lattices, one pose
 // per group).
 template <int NDIM, int INTERP, int MODE>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_adjoint_bricks(OpParams p,
+__global__ __launch_bounds__(kAdjBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_adjoint_bricks(OpParams p,
                                                                                            BrickParams bp) {
   constexpr bool WEIGHTS = MODE == kWeights;
   constexpr bool VOL = MODE == kVolume;
@@ -479,10 +480,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   __shared__ unsigned long long acc[AL::W];
   int* acc_r = reinterpret_cast<int*>(acc);  // the weight volume's int32 slots
   __shared__ uint32_t s_hits[kHitCap];
-  __shared__ int s_poses[kBlock];
+  __shared__ int s_poses[kAdjBlock];
   __shared__ PoseView s_view[kGroupMax];
-  __shared__ int s_wcnt[kBlock / 64];
-  __shared__ float s_red[kBlock / 64];
+  __shared__ int s_wcnt[kAdjBlock / 64];
+  __shared__ float s_red[kAdjBlock / 64];
 
   const BrickPos br = decode<NDIM, VOL>(p, bp);
   if (!br.valid) return;
@@ -492,15 +493,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   float fre[kPerThread], fim[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) fre[i] = fim[i] = 0.f;
-  for (int i = tid; i < AL::W; i += kBlock) acc[i] = 0ull;
+  for (int i = tid; i < AL::W; i += kAdjBlock) acc[i] = 0ull;
   __syncthreads();
 
   const Box bx = reach_box<NDIM, INTERP>(br);
-  for (int w0 = br.n0; w0 < br.n1; w0 += kBlock) {
+  for (int w0 = br.n0; w0 < br.n1; w0 += kAdjBlock) {
     // the poses whose plane (volume) can reach this brick, in order
-    const int total = VOL ? scan_poses_if([&](int n) { return vol_meets(p, br.b, bx, n); }, w0, br.n1, s_poses,
-                                          s_wcnt)
-                          : scan_poses<NDIM>(p, br.b, bx, w0, br.n1, s_poses, s_wcnt);
+    const int total = VOL ? scan_poses_if<kAdjBlock>([&](int n) { return vol_meets(p, br.b, bx, n); }, w0, br.n1,
+                                                     s_poses, s_wcnt)
+                          : scan_poses<NDIM, kAdjBlock>(p, br.b, bx, w0, br.n1, s_poses, s_wcnt);
 
     // groups of up to GMAX poses; a group whose lattice points overflow the
     // hit list is spread in slices of kHitCap
@@ -517,7 +518,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         // phase A: list the lattice points that can reach the brick (this
         // slice keeps the flat indices [h0, h0 + kHitCap))
         hits_total = VOL ? list_hits_vol(p, bx, s_view[0], h0, kHitCap, s_hits, s_wcnt)
-                         : list_hits<NDIM, kGroupMax>(p, bx, s_view, cnt, h0, kHitCap, s_hits, s_wcnt);
+                         : list_hits<NDIM, kGroupMax, kAdjBlock>(p, bx, s_view, cnt, h0, kHitCap, s_hits, s_wcnt);
         const int nh = max(0, min(hits_total, h0 + kHitCap) - h0);
 
         // phase B: spread the hits.  The fixed-point quantum assumes the
@@ -537,11 +538,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             q = ldexpf(1.f, e - kQuantumBits);
           }
           float amax = 0.f;
-          for (int i0 = 0; i0 < nh; i0 += kPrefetch * kBlock) {
+          for (int i0 = 0; i0 < nh; i0 += kPrefetch * kAdjBlock) {
             float2 gr[kPrefetch], gm[kPrefetch];
 #pragma unroll
             for (int k = 0; k < kPrefetch; ++k) {
-              const int i = i0 + hit_slot(tid) + k * kBlock;
+              const int i = i0 + hit_slot(tid) + k * kAdjBlock;
               gr[k] = gm[k] = make_float2(0.f, 0.f);
               if (i < nh) {
                 const uint32_t h = s_hits[i];
@@ -567,7 +568,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             if (measure_only) continue;
 #pragma unroll
             for (int k = 0; k < kPrefetch; ++k) {
-              const int i = i0 + hit_slot(tid) + k * kBlock;
+              const int i = i0 + hit_slot(tid) + k * kAdjBlock;
               if (i >= nh) continue;
               const uint32_t h = s_hits[i];
               Cand cd;
@@ -589,13 +590,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           __syncthreads();
           float gmax = s_red[0];
 #pragma unroll
-          for (int w = 1; w < kBlock / 64; ++w) gmax = fmaxf(gmax, s_red[w]);
+          for (int w = 1; w < kAdjBlock / 64; ++w) gmax = fmaxf(gmax, s_red[w]);
           if (!(gmax > 0.f)) break;  // an all-zero slice adds nothing
           if (!measure_only && gmax <= m_assume) {
             // flush the slice into fp32 registers
 #pragma unroll
             for (int i = 0; i < kPerThread; ++i) {
-              const int v = tid + i * kBlock;
+              const int v = tid + i * kAdjBlock;
               const int sl = acc_word<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
               if (WEIGHTS) {
                 fre[i] = fmaf((float)acc_r[sl], q, fre[i]);
@@ -614,7 +615,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           if (!measure_only) {
 #pragma unroll
             for (int i = 0; i < kPerThread; ++i) {
-              const int v = tid + i * kBlock;
+              const int v = tid + i * kAdjBlock;
               const int sl = acc_word<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
               if (WEIGHTS) acc_r[sl] = 0;
               else acc[sl] = 0ull;
@@ -635,7 +636,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const int wh = p.N / 2 + 1;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const int v = tid + i * kBlock;
+    const int v = tid + i * kAdjBlock;
     const int x = br.x0 + v % BR::X;
     const int y = br.y0 + (v / BR::X) % BR::Y;
     const int z = br.z0 + v / (BR::X * BR::Y);
@@ -685,7 +686,7 @@ uint64_t adjoint_blocks(const OpParams& p) {
 
 hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s) {
   const BrickParams bp = p.ndim == 3 ? brick_params<3>(p) : brick_params<2>(p);
-  const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kBlock);
+  const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kAdjBlock);
   if (p.ndim == 3) {
     if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, kSlice>), grid, block, 0, s, p, bp);
     else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, kSlice>), grid, block, 0, s, p, bp);
@@ -698,7 +699,7 @@ hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s) {
 
 hipError_t launch_backproject_weights(const OpParams& p, int interp, hipStream_t s) {
   const BrickParams bp = p.ndim == 3 ? brick_params<3>(p) : brick_params<2>(p);
-  const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kBlock);
+  const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kAdjBlock);
   if (p.ndim == 3) {
     if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, kWeights>), grid, block, 0, s, p, bp);
     else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, kWeights>), grid, block, 0, s, p, bp);
@@ -716,7 +717,7 @@ uint64_t rotate_adjoint_blocks(const OpParams& p) {
 
 hipError_t launch_rotate_adjoint(const OpParams& p, int interp, hipStream_t s) {
   const BrickParams bp = brick_params<3>(p, true);
-  const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kBlock);
+  const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(kAdjBlock);
   if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, kVolume>), grid, block, 0, s, p, bp);
   else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, kVolume>), grid, block, 0, s, p, bp);
   return hipGetLastError();

@@ -208,10 +208,10 @@ __device__ __forceinline__ int hit_pose(uint32_t h) { return (int)(h >> 28); }
 __device__ __forceinline__ int hit_kx(uint32_t h, const PoseView& pv) { return pv.kx0 + (int)(h & 0x3FFFu); }
 __device__ __forceinline__ int hit_ky(uint32_t h, const PoseView& pv) { return pv.ky0 + (int)((h >> 14) & 0x3FFFu); }
 
-// Workgroup scan of poses [w0, min(w0 + kBlock, n1)): the poses n with
+// Workgroup scan of poses [w0, min(w0 + BS, n1)): the poses n with
 // meets(n), in order, into s_poses; returns their count.  Every thread of
-// the (kBlock-thread) workgroup calls it.
-template <typename Meets>
+// the (BS-thread) workgroup calls it.
+template <int BS = kBlock, typename Meets>
 __device__ __forceinline__ int scan_poses_if(Meets meets, int w0, int n1, int* s_poses, int* s_wcnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = w0 + tid;
@@ -222,7 +222,7 @@ __device__ __forceinline__ int scan_poses_if(Meets meets, int w0, int n1, int* s
   __syncthreads();
   int off = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < kBlock / 64; ++w) {
+  for (int w = 0; w < BS / 64; ++w) {
     off += w < wave ? s_wcnt[w] : 0;
     total += s_wcnt[w];
   }
@@ -232,10 +232,10 @@ __device__ __forceinline__ int scan_poses_if(Meets meets, int w0, int n1, int* s
 }
 
 // The poses whose plane meets the box.
-template <int NDIM>
+template <int NDIM, int BS = kBlock>
 __device__ __forceinline__ int scan_poses(const OpParams& p, int b, const Box& bx, int w0, int n1, int* s_poses,
                                           int* s_wcnt) {
-  return scan_poses_if([&](int n) { return plane_meets<NDIM>(p, b, bx, n); }, w0, n1, s_poses, s_wcnt);
+  return scan_poses_if<BS>([&](int n) { return plane_meets<NDIM>(p, b, bx, n); }, w0, n1, s_poses, s_wcnt);
 }
 
 // List the lattice points of the poses s_view[0, cnt) (cnt <= MAXG) whose
@@ -243,7 +243,7 @@ __device__ __forceinline__ int scan_poses(const OpParams& p, int b, const Box& b
 // over the rows of pose 0, then pose 1, ...; entries with flat index in
 // [h0, h0 + cap) go to s_hits[flat - h0].  Returns the total count (the same
 // for every h0).  Every thread of the workgroup calls it.
-template <int NDIM, int MAXG>
+template <int NDIM, int MAXG, int BS = kBlock>
 __device__ __forceinline__ int list_hits(const OpParams& p, const Box& bx, const PoseView* s_view, int cnt,
                                          int h0, int cap, uint32_t* s_hits, int* s_wcnt) {
   static_assert(MAXG <= kHitPoses, "pose slot does not fit the hit tag");
@@ -259,7 +259,7 @@ __device__ __forceinline__ int list_hits(const OpParams& p, const Box& bx, const
   }
   const int h1 = h0 + cap;
   int carry = 0;
-  for (int rw = 0; rw < rows_total; rw += kBlock) {
+  for (int rw = 0; rw < rows_total; rw += BS) {
     const int r = rw + tid;
     int g = 0, rb = 0, cr = 0, a = 0;
 #pragma unroll
@@ -287,7 +287,7 @@ __device__ __forceinline__ int list_hits(const OpParams& p, const Box& bx, const
     __syncthreads();
     int off = carry + incl - cr, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) {
+    for (int w = 0; w < BS / 64; ++w) {
       off += w < wave ? s_wcnt[w] : 0;
       tot += s_wcnt[w];
     }
