@@ -324,18 +324,7 @@ __device__ __forceinline__ int list_hits_vol(const OpParams& p, const Box& bx, c
           tb = fmin(tb, fmax(t0, t1));
         }
       }
-      if (p.cut2 >= 0) {
-        const long long rem = p.cut2 - (long long)ky * ky - (long long)kz * kz;
-        if (rem < 0) {
-          empty = true;
-        } else {
-          long long m = (long long)sqrt((double)rem);
-          while ((m + 1) * (m + 1) <= rem) ++m;
-          while (m * m > rem) --m;
-          ta = fmax(ta, (double)-m);
-          tb = fmin(tb, (double)m);
-        }
-      }
+      if (p.cut2 >= 0) clip_kx_to_disk(p.cut2 - (long long)ky * ky - (long long)kz * kz, ta, tb, empty);
       a = (int)ceil(ta);
       const int b = empty ? a - 1 : (int)floor(tb);
       cr = max(0, b - a + 1);

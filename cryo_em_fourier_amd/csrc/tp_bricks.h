@@ -74,11 +74,12 @@ __device__ __forceinline__ PoseView pose_view(const OpParams& p, int b, const Bo
   pv.hit = 1;
   pv.dens = 1e30f;
   if (D > 0.0 && isfinite(D)) {
-    pv.dens = (float)fmax(1.0, 1.0 / sqrt(D));
+    const double iD = 1.0 / D;  // one division; the rectangle below has a margin of 1
+    pv.dens = (float)fmax(1.0, sqrt(iD));
     double ud[3], vd[3];  // dual basis: kx = p . ud, ky = p . vd for points on the plane
     for (int j = 0; j < 3; ++j) {
-      ud[j] = (vv * pv.u[j] - uv * pv.v[j]) / D;
-      vd[j] = (uu * pv.v[j] - uv * pv.u[j]) / D;
+      ud[j] = (vv * pv.u[j] - uv * pv.v[j]) * iD;
+      vd[j] = (uu * pv.v[j] - uv * pv.u[j]) * iD;
     }
     // the plane through the origin with normal u x v must cross the box
     double nrm[3] = {pv.u[1] * pv.v[2] - pv.u[2] * pv.v[1], pv.u[2] * pv.v[0] - pv.u[0] * pv.v[2],
@@ -156,6 +157,24 @@ __device__ __forceinline__ bool in_box(const Box& bx, const double* q) {
   return in;
 }
 
+// Clip [ta, tb] to |kx| <= floor(sqrt(rem)), rem = cut2 - (the other
+// squared frequencies); empty when rem < 0.  Remainders of 2^30 or more clip
+// nothing (|kx| <= 2^15).  Below that the fp32 root is within 0.01 of the
+// true one, so one integer correction each way gives the floor (squares stay
+// below 2^32).
+__device__ __forceinline__ void clip_kx_to_disk(long long rem, double& ta, double& tb, bool& empty) {
+  if (rem < 0) {
+    empty = true;
+  } else if (rem < (1ll << 30)) {
+    const uint32_t r = (uint32_t)rem;
+    uint32_t m = (uint32_t)sqrtf((float)r);
+    if ((m + 1u) * (m + 1u) <= r) ++m;
+    if (m * m > r) --m;
+    ta = fmax(ta, -(double)m);
+    tb = fmin(tb, (double)m);
+  }
+}
+
 // The kx range [a, b] of row ky whose sample points fall in the box widened
 // by 1e-6 (the margin covers the rounding of this fp64 arithmetic; callers
 // decide membership exactly from the sample point itself), clipped to the
@@ -177,18 +196,7 @@ __device__ __forceinline__ void row_range(const OpParams& p, const PoseView& pv,
       tb = fmin(tb, fmax(t0, t1));
     }
   }
-  if (p.cut2 >= 0) {
-    const long long rem = p.cut2 - (long long)ky * ky;
-    if (rem < 0) {
-      empty = true;
-    } else {
-      long long m = (long long)sqrt((double)rem);
-      while ((m + 1) * (m + 1) <= rem) ++m;
-      while (m * m > rem) --m;
-      ta = fmax(ta, (double)-m);
-      tb = fmin(tb, (double)m);
-    }
-  }
+  if (p.cut2 >= 0) clip_kx_to_disk(p.cut2 - (long long)ky * ky, ta, tb, empty);
   a = (int)ceil(ta);
   b = empty ? a - 1 : (int)floor(tb);
 }
