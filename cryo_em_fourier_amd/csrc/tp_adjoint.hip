@@ -15,10 +15,9 @@
 // part, integer ones are not: contributions are accumulated as int32 fixed
 // point (exact, order independent; a (re, im) pair packed in one 64-bit
 // word, or one int32 for the real weight volume), with a power-of-two
-// quantum chosen per
-// group of poses from a bound on |G| that is checked against the values read
-// (a group that exceeds it is redone), so the sums cannot overflow; each
-// group is flushed into fp32 registers.  Bricks are split over pose chunks in
+// quantum chosen per group of poses from a bound on |G| that is checked
+// against the values read (a group that exceeds it is redone), so the sums
+// cannot overflow; each group is flushed into fp32 registers.  Bricks are split over pose chunks in
 // proportion to the poses expected to cross them (near the origin: all of
 // them); chunks of one brick merge with coalesced float atomics, unsplit
 // bricks are written with plain stores.

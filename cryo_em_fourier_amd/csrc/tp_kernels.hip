@@ -1,12 +1,15 @@
 // Projector kernels for gfx950: forward gather and pose gradients (the
-// adjoint lives in tp_adjoint.hip); 2D and 3D references; linear and
-// Catmull-Rom interpolation.
+// adjoint lives in tp_adjoint.hip, the brick gradient gather in
+// tp_gather.hip); 2D and 3D references; linear and Catmull-Rom
+// interpolation; the forward that saves each output's Jacobian and the pose
+// gradients taken from it.
 //
-// One thread per output frequency.  A 256-thread workgroup covers a 16x16
-// tile (kx, ky-row) of one projection; the grid enumerates (batch, pose, tile)
-// pose-major and is remapped so each XCD walks contiguous tiles of the same
-// pose.  The rotation and shift of a pose are wave-uniform (kernel-argument
-// derived addresses -> scalar loads).
+// 2D: one thread per output frequency, a 256-thread workgroup covers a 16x16
+// tile (kx, ky-row) of one projection.  3D: two lanes per output, each
+// gathering half of every x-row, so a workgroup covers 16x8 outputs.  The
+// grid enumerates (batch, pose, tile) pose-major and is remapped so each XCD
+// walks contiguous tiles of the same pose.  The rotation and shift of a pose
+// are wave-uniform (kernel-argument derived addresses -> scalar loads).
 #include "tp_internal.h"
 #include "tp_stencil.h"
 
