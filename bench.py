@@ -44,15 +44,20 @@ L2_PEAK_GBS = 8 * 16 * 128 * 2.4
 
 
 def kernel_source_digest() -> str:
-    """sha256 over the HIP sources: counter data is valid only for these."""
+    """sha256 over the HIP sources with comments and blank lines removed:
+    counter data is valid only for this code (a comment edit keeps it)."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "cryo_em_fourier_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+                text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+            lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+            code = "\n".join(ln for ln in lines if ln.strip())
+            h.update(f.encode() + b"\0" + code.encode())
     return h.hexdigest()
 
 
