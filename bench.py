@@ -110,6 +110,142 @@ def _oracle_worker(idx):
     return len(idx), t1 - t0, t2 - t1
 
 
+def _oracle_worker_2d(idx):
+    import oracle
+
+    c = _CPU
+    V, R, s, G = c["V"][idx], c["R"][idx], c["s"][idx], c["G"][idx]
+    t0 = time.perf_counter()
+    oracle.project(V, R, s, c["n_out"], c["interp"], c["os"], c["cutoff"])
+    t1 = time.perf_counter()
+    oracle.backproject(G, R, s, c["N"], c["interp"], c["os"], c["cutoff"])
+    oracle.grad_pose(V, G, R, s, c["n_out"], c["interp"], c["os"], c["cutoff"])
+    t2 = time.perf_counter()
+    return len(idx), t1 - t0, t2 - t1
+
+
+def cpu_baseline_2d(V, R, s, G, w: synth.Workload, images_per_worker: int):
+    """The oracle's 2D path on a seeded sample of images, in forked workers."""
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    workers = max(1, min(16, ncpu))
+    rng = np.random.default_rng(12345)
+    n_img = min(w.B, max(images_per_worker, 1) * 32)  # all 256 images at the default: a few seconds
+    sample = np.sort(rng.choice(w.B, size=n_img, replace=False))
+    _CPU.update(V=V[sample], R=R[sample], s=s[sample], G=G[sample], n_out=w.N_out, N=w.N,
+                interp=w.interp, os=1.0, cutoff=w.cutoff)
+    chunks = [list(range(i, n_img, workers)) for i in range(workers)]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        res = pool.map(_oracle_worker_2d, [c for c in chunks if c])
+    wall = time.perf_counter() - t0
+    n = sum(r[0] for r in res)
+    fwd = sum(r[1] for r in res)
+    bwd = sum(r[2] for r in res)
+    return {
+        "value": n / wall,
+        "unit": "images/s fwd+bwd",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{n} of {w.B} images (seeded), {workers} single-threaded workers, fork pool",
+        "value_1core": n / (fwd + bwd) if fwd + bwd > 0 else None,
+        "wall_s": wall,
+    }
+
+
+def bench_2d(args, w: synth.Workload):
+    """The 2D -> 2D path on the c2 workload (one in-plane pose per image):
+    tp_project_2d + tp_backproject_2d + tp_grad_pose(ndim = 2) per step."""
+    V = synth.make_reference(w)
+    R = synth.make_rotations(w)
+    s = synth.make_shifts(w)
+    G = synth.make_upstream(w)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_2d(V, R, s, G, w, args.cpu_poses_per_worker)
+
+    import torch
+
+    from cryo_em_fourier_amd import _lib
+
+    L = _lib.lib()
+    dev = torch.device("cuda:0")
+    Wo = w.N_out // 2 + 1
+    Vd, Rd, sd, Gd = (torch.from_numpy(x).to(dev) for x in (V, R, s, G))
+    out = torch.empty((w.B, w.P, w.N_out, Wo), dtype=torch.complex64, device=dev)
+    dV = torch.empty_like(Vd)
+    dR = torch.empty_like(Rd)
+    ds = torch.empty_like(sd)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    B, P, N = w.B, w.P, w.N
+
+    def fwd():
+        _lib.check(L.tp_project_2d(Vd.data_ptr(), B, N, Rd.data_ptr(), R.shape[0], P, sd.data_ptr(), s.shape[0],
+                                   w.N_out, w.interp, 1.0, w.cutoff, out.data_ptr(), sh), "tp_project_2d")
+
+    def adj():
+        _lib.check(L.tp_backproject_2d(Gd.data_ptr(), B, P, w.N_out, Rd.data_ptr(), R.shape[0], sd.data_ptr(),
+                                       s.shape[0], N, w.interp, 1.0, w.cutoff, dV.data_ptr(), sh),
+                   "tp_backproject_2d")
+
+    def grad():
+        _lib.check(L.tp_grad_pose(2, Vd.data_ptr(), B, N, Gd.data_ptr(), Rd.data_ptr(), R.shape[0], P,
+                                  sd.data_ptr(), s.shape[0], w.N_out, w.interp, 1.0, w.cutoff, dR.data_ptr(),
+                                  ds.data_ptr(), sh), "tp_grad_pose")
+
+    kernels = [("project_2d", fwd), ("backproject_2d", adj), ("grad_pose_2d", grad)]
+    for _ in range(args.warmup):
+        for _, f in kernels:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        for j, (_, f) in enumerate(kernels):
+            f()
+            ev[k][j + 1].record(stream)
+    torch.cuda.synchronize()
+    per = {n: [ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(args.steps)] for j, (n, _) in enumerate(kernels)}
+    avg = {n: float(np.mean(v)) for n, v in per.items()}
+    ms_step = float(np.mean([ev[k][0].elapsed_time(ev[k][-1]) for k in range(args.steps)]))
+    n_c = in_cutoff_count(w.N_out, w.cutoff)
+    units = B * P * n_c
+    taps = 16 if w.interp == synth.CUBIC else 4
+    img_bytes = B * P * w.N_out * Wo * 8
+    hbm = {"project_2d": V.nbytes + img_bytes + R.nbytes + s.nbytes,
+           "backproject_2d": units * 8 + 2 * V.nbytes + R.nbytes + s.nbytes,
+           "grad_pose_2d": V.nbytes + units * 8 + R.nbytes + s.nbytes}
+    dom = max(avg, key=avg.get)
+    achieved = hbm[dom] / (avg[dom] * 1e-3) / 1e9
+    res = {
+        "metric": "images/sec fwd+bwd, 2D 128^2 cubic (2D -> 2D path)",
+        "value": round(B * P / (ms_step * 1e-3), 1),
+        "unit": "images/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"c2: 2D->2D forward+backward, {B} images {w.N}^2, one in-plane pose each, cubic, "
+                               f"cutoff {w.cutoff:g}, shifts U[-{w.shift_max:g},{w.shift_max:g}]",
+                   "images": B, "box": w.N, "in_cutoff_outputs_per_image": n_c},
+        "kernel_ms_mean": {k: round(v, 4) for k, v in avg.items()},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": hbm[dom]},
+        "roofline_tap": {"bound": "l2", "peak": L2_PEAK_GBS, "unit": "GB/s",
+                         "kernels": {k: {"achieved": round(units * taps * 8 / (avg[k] * 1e-3) / 1e9, 1)} for k in avg}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline(V, R, s, w: synth.Workload, N: int, os_: float, poses_per_worker: int):
     """Time the oracle on a bounded pose sample with a fork pool (no GPU yet)."""
     try:
@@ -350,7 +486,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c4", choices=["c3", "c4", "c5"])
+    ap.add_argument("--config", default="c4", choices=["c2", "c3", "c4", "c5"],
+                    help="c2 runs the 2D -> 2D path (images/s); the others the 3D -> 2D path")
     ap.add_argument("--oversampling", type=int, default=1, choices=[1, 2])
     ap.add_argument("--poses", type=int, default=0, help="override the pose count")
     ap.add_argument("--pose-grads", choices=["jacobian", "recompute"], default="jacobian",
@@ -372,6 +509,9 @@ def main():
         return
 
     w = synth.WORKLOADS[args.config]
+    if w.ndim == 2:
+        bench_2d(args, w)
+        return
     if args.poses:
         w = synth.Workload(**{**w.__dict__, "P": args.poses})
     os_ = float(args.oversampling)
