@@ -310,6 +310,45 @@ def test_empty_cutoff_and_edge_sizes():
     assert np.all(gr.cpu().numpy() == 0) and np.all(gs.cpu().numpy() == 0)
 
 
+def test_jacobian_path_edge_cases():
+    """The saved-Jacobian pair at cutoff 0 (DC only: zero pose gradients),
+    N_out = 1, no shift with a pose broadcast over the batch, and one
+    gradient requested at a time."""
+    from cryo_em_fourier_amd import tp_grad_pose_jac, tp_project_3d_jac
+
+    c = case3d("odd-nocut")
+    V, R, s, G = _dev(c)
+    log("[jacobian edge] cutoff 0")
+    out, jac = tp_project_3d_jac(V, R, s, c["n_out"], c["interp"], 1.0, 0.0)
+    assert_parity(out.cpu().numpy(), oracle.project(c["V"], c["R"], c["s"], c["n_out"], c["interp"], 1.0, 0.0),
+                  "jac forward cutoff 0")
+    gr, gs = tp_grad_pose_jac(G, out, jac, 1, 1, 1.0, 0.0)
+    assert not gr.cpu().numpy().any() and not gs.cpu().numpy().any()
+    log("[jacobian edge] N_out 1")
+    out1, jac1 = tp_project_3d_jac(V, R, s, 1, c["interp"], 1.0, -1.0)
+    assert_parity(out1.cpu().numpy(), oracle.project(c["V"], c["R"], c["s"], 1, c["interp"], 1.0, -1.0),
+                  "jac forward N_out 1")
+    G1 = to_dev(c["G"][:, :, :1, :1].copy())
+    gr, gs = tp_grad_pose_jac(G1, out1, jac1, 1, 1, 1.0, -1.0)
+    dR, ds = oracle.grad_pose(c["V"], c["G"][:, :, :1, :1], c["R"], c["s"], 1, c["interp"], 1.0, -1.0)
+    # the DC output has k = 0: every pose gradient is 0
+    assert not gr.cpu().numpy().any() and not np.asarray(dR).any()
+    log("[jacobian edge] batch 2, broadcast pose, no shift, one gradient at a time")
+    b = case3d("batch-bcast")
+    Vb, Rb, _, Gb = _dev(b)
+    outb, jacb = tp_project_3d_jac(Vb, Rb, None, b["n_out"], b["interp"], float(b["os"]), float(b["cutoff"]))
+    dR, ds = oracle.grad_pose(b["V"], b["G"], b["R"], None, b["n_out"], b["interp"], b["os"], b["cutoff"])
+    gr, none_s = tp_grad_pose_jac(Gb, outb, jacb, 1, 1, float(b["os"]), float(b["cutoff"]), want_shift=False)
+    assert none_s is None
+    assert_parity(gr.cpu().numpy(), dR, "jac grad_rot broadcast")
+    none_r, gs = tp_grad_pose_jac(Gb, outb, jacb, 1, b["V"].shape[0], float(b["os"]), float(b["cutoff"]),
+                                  want_rot=False)
+    assert none_r is None
+    dR2, ds2 = oracle.grad_pose(b["V"], b["G"], b["R"], np.zeros((b["V"].shape[0], b["R"].shape[1], 2), np.float32),
+                                b["n_out"], b["interp"], b["os"], b["cutoff"])
+    assert_parity(gs.cpu().numpy(), ds2, "jac grad_shift per batch entry")
+
+
 def test_nonfinite_rotation_reads_zero():
     from cryo_em_fourier_amd import tp_project_3d
 
