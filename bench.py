@@ -417,6 +417,7 @@ def oversampling_study(args):
     G = torch.randn((1, P, n_out, Wo), dtype=torch.complex64, device=dev,
                     generator=torch.Generator(device=dev).manual_seed(4))
     out = torch.empty((1, P, n_out, Wo), dtype=torch.complex64, device=dev)
+    jac = torch.empty((1, P, 3, n_out, Wo), dtype=torch.complex64, device=dev)
     dR = torch.empty_like(Rd)
 
     def spectrum(os_):
@@ -436,17 +437,22 @@ def oversampling_study(args):
         return x[off:off + w.N, off:off + w.N, off:off + w.N]
 
     def pipeline(interp, os_, backward):
+        # forward only: tp_project_3d; training step: the bench step's calls
+        # (Jacobian-saving forward, adjoint, pose gradients from the Jacobian)
         V = spectrum(os_)
         M = V.shape[1]
-        _lib.check(L.tp_project_3d(V.data_ptr(), 1, M, Rd.data_ptr(), 1, P, None, 1, n_out, interp, float(os_),
-                                   w.cutoff, out.data_ptr(), sh), "project")
-        if backward:
-            dV = torch.empty_like(V)
-            _lib.check(L.tp_backproject_3d(G.data_ptr(), 1, P, n_out, Rd.data_ptr(), 1, None, 1, M, interp,
-                                           float(os_), w.cutoff, dV.data_ptr(), sh), "backproject")
-            _lib.check(L.tp_grad_pose(3, V.data_ptr(), 1, M, G.data_ptr(), Rd.data_ptr(), 1, P, None, 1, n_out,
-                                      interp, float(os_), w.cutoff, dR.data_ptr(), None, sh), "grad_pose")
-            to_real(dV, os_)
+        if not backward:
+            _lib.check(L.tp_project_3d(V.data_ptr(), 1, M, Rd.data_ptr(), 1, P, None, 1, n_out, interp,
+                                       float(os_), w.cutoff, out.data_ptr(), sh), "project")
+            return
+        _lib.check(L.tp_project_3d_jac(V.data_ptr(), 1, M, Rd.data_ptr(), 1, P, None, 1, n_out, interp, float(os_),
+                                       w.cutoff, out.data_ptr(), jac.data_ptr(), sh), "project_jac")
+        dV = torch.empty_like(V)
+        _lib.check(L.tp_backproject_3d(G.data_ptr(), 1, P, n_out, Rd.data_ptr(), 1, None, 1, M, interp,
+                                       float(os_), w.cutoff, dV.data_ptr(), sh), "backproject")
+        _lib.check(L.tp_grad_pose_jac(G.data_ptr(), out.data_ptr(), jac.data_ptr(), 1, P, n_out, 1, 1, float(os_),
+                                      w.cutoff, dR.data_ptr(), None, sh), "grad_pose_jac")
+        to_real(dV, os_)
 
     def timed(f, reps=5):
         f()
