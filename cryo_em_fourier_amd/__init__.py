@@ -21,8 +21,10 @@ from .ops import (  # noqa: F401
     tp_project_3d,
     tp_project_3d_jac,
     tp_rotate_3d,
+    tp_rotate_3d_jac,
     tp_rotate_backproject_3d,
     tp_rotate_grad_pose,
+    tp_rotate_grad_pose_jac,
     tp_symmetrize_x0,
 )
 
@@ -44,7 +46,9 @@ __all__ = [
     "tp_project_3d",
     "tp_project_3d_jac",
     "tp_rotate_3d",
+    "tp_rotate_3d_jac",
     "tp_rotate_backproject_3d",
     "tp_rotate_grad_pose",
+    "tp_rotate_grad_pose_jac",
     "tp_symmetrize_x0",
 ]

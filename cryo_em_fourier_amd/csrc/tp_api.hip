@@ -358,4 +358,59 @@ tp_status tp_grad_pose_jac(const tp_c64* grad_out, const tp_c64* proj, const tp_
   return hip_status(tp::launch_grad_jac(p, s));
 }
 
+tp_status tp_rotate_3d_jac(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot, int64_t P,
+                           const float* shift, int64_t B_shift, int64_t N_out, int interp, float oversampling,
+                           float cutoff, tp_c64* out, tp_c64* jac, void* stream) {
+  if (!vol || !out || !jac || !aligned8(vol) || !aligned8(out) || !aligned8(jac)) return TP_EINVAL;
+  tp::OpParams p;
+  const Common c{B, N, P, N_out, B_rot, B_shift, interp, 3, oversampling, cutoff, rot, shift};
+  const tp_status st = rotate_fill(c, p);
+  if (st != TP_OK) return st;
+  if (N_out > tp::kMaxRotateAdjointOut) return TP_EUNSUPPORTED;
+  p.ref = reinterpret_cast<const float2*>(vol);
+  p.img_out = reinterpret_cast<float2*>(out);
+  p.jac_out = reinterpret_cast<float2*>(jac);
+  return hip_status(tp::launch_rotate_jac(p, interp, (hipStream_t)stream));
+}
+
+tp_status tp_rotate_grad_pose_jac(const tp_c64* grad_out, const tp_c64* out, const tp_c64* jac, int64_t B,
+                                  int64_t P, int64_t N_out, int64_t B_rot, int64_t B_shift, float oversampling,
+                                  float cutoff, float* grad_rot, float* grad_shift, void* stream) {
+  if (!grad_out || !out || !jac || !aligned8(grad_out) || !aligned8(out) || !aligned8(jac)) return TP_EINVAL;
+  if ((grad_rot && !aligned4(grad_rot)) || (grad_shift && !aligned4(grad_shift))) return TP_EINVAL;
+  if (B <= 0 || P <= 0 || N_out <= 0) return TP_EINVAL;
+  if (B_rot != 1 && B_rot != B) return TP_EINVAL;
+  if (grad_shift && B_shift != 1 && B_shift != B) return TP_EINVAL;
+  if (!std::isfinite(oversampling) || !(oversampling > 0.f) || std::isnan(cutoff)) return TP_EINVAL;
+  if (N_out > tp::kMaxRotateAdjointOut || (uint64_t)B * (uint64_t)P > kMaxBlocks) return TP_EUNSUPPORTED;
+  if (!grad_rot && !grad_shift) return TP_OK;
+  tp::OpParams p{};
+  p.B = (int)B;
+  p.P = (int)P;
+  p.No = (int)N_out;
+  p.Wo = (int)(N_out / 2 + 1);
+  p.B_rot = (int)B_rot;
+  p.B_shift = grad_shift ? (int)B_shift : 1;
+  p.ndim = 3;
+  p.os = oversampling;
+  if (cutoff < 0.f) {
+    p.cut2 = -1;
+  } else {
+    const double c2 = (double)cutoff * (double)cutoff;
+    p.cut2 = c2 > 9.0e18 ? (long long)9.0e18 : (long long)std::floor(c2);
+  }
+  p.inv_no = 1.0 / (double)N_out;
+  p.img = reinterpret_cast<const float2*>(grad_out);
+  p.proj = reinterpret_cast<const float2*>(out);
+  p.jac = reinterpret_cast<const float2*>(jac);
+  p.grad_rot = grad_rot;
+  p.grad_shift = grad_shift;
+  const hipStream_t s = (hipStream_t)stream;
+  if (grad_rot && tp::launch_zero(grad_rot, (size_t)p.B_rot * p.P * 9 * sizeof(float), s) != hipSuccess)
+    return TP_EHIP;
+  if (grad_shift && tp::launch_zero(grad_shift, (size_t)p.B_shift * p.P * 3 * sizeof(float), s) != hipSuccess)
+    return TP_EHIP;
+  return hip_status(tp::launch_rotate_grad_jac(p, s));
+}
+
 }  // extern "C"

@@ -54,6 +54,9 @@ hipError_t launch_symmetrize_x0(float2* ref, int ndim, int B, int N, hipStream_t
 // its adjoint is the brick adjoint over volume lattices (tp_adjoint.hip)
 hipError_t launch_rotate(const OpParams& p, int interp, int what, hipStream_t s);
 hipError_t launch_rotate_adjoint(const OpParams& p, int interp, hipStream_t s);
+// the rotation that saves its Jacobian, and the pose gradients from it
+hipError_t launch_rotate_jac(const OpParams& p, int interp, hipStream_t s);
+hipError_t launch_rotate_grad_jac(const OpParams& p, hipStream_t s);
 uint64_t rotate_adjoint_blocks(const OpParams& p);
 constexpr int64_t kMaxRotateAdjointOut = 1023;  // 10-bit lattice offsets
 hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s);

@@ -24,7 +24,8 @@ autograd functions wrapping the native ops):
   upstream roles swapped (Re<Y, P^T G> = Re<P Y, G>).
 * ``rotate_3d``: the 3D -> 3D rotation of a half-spectrum (it page tech.
   section 2: 3D -> 3D for general rotations), with gradients to the
-  reference (its adjoint), the rotations and the 3-vector shifts.
+  reference (its adjoint), the rotations and the 3-vector shifts (from a
+  Jacobian saved by the forward, as ``project_3d``).
 * ``backproject_weights_3d`` / ``backproject_weights_2d``: the real weight
   volume of a dual-volume reconstruction, with gradients to the weights
   (the real forward projection) and to the rotations (ar page tech. section
@@ -476,17 +477,67 @@ def tp_rotate_grad_pose(vol, grad_out, rot, shift=None, interp="cubic", oversamp
     return gr, gs
 
 
+def tp_rotate_3d_jac(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
+    """tp_rotate_3d that also returns the Jacobian of each output w.r.t. its
+    sample point: (out [B,P,n,n,n//2+1], jac [B,P,3,n,n,n//2+1]) c64."""
+    B, N = _ref_dims(vol, 3, "reference")
+    B_rot, P, B_shift = _rot_poses(rot, shift, B, vol.device)
+    if n_out is None:
+        n_out = int(round(N / float(oversampling)))
+    out = torch.empty((B, P, n_out, n_out, n_out // 2 + 1), dtype=torch.complex64, device=vol.device)
+    jac = torch.empty((B, P, 3, n_out, n_out, n_out // 2 + 1), dtype=torch.complex64, device=vol.device)
+    st = _lib.lib().tp_rotate_3d_jac(vol.data_ptr(), B, N, rot.data_ptr(), B_rot, P, _ptr(shift), B_shift, n_out,
+                                     _interp(interp), float(oversampling), float(cutoff), out.data_ptr(),
+                                     jac.data_ptr(), _stream(vol.device))
+    _lib.check(st, "tp_rotate_3d_jac")
+    return out, jac
+
+
+def tp_rotate_grad_pose_jac(grad_out, out, jac, B_rot=1, B_shift=1, oversampling=1.0, cutoff=-1.0,
+                            want_rot=True, want_shift=True):
+    """Pose gradients from tp_rotate_3d_jac's (out, jac):
+    (grad_rot [B_rot,P,3,3] or None, grad_shift [B_shift,P,3] or None)."""
+    _need(grad_out, "grad_out", torch.complex64, 5)
+    _need(out, "out", torch.complex64, 5)
+    _need(jac, "jac", torch.complex64, 6)
+    B, P, n_out = out.shape[0], out.shape[1], out.shape[2]
+    if tuple(out.shape) != (B, P, n_out, n_out, n_out // 2 + 1) or grad_out.shape != out.shape:
+        raise ValueError(f"grad_out and out must be [B, P, n, n, n//2+1], got {tuple(grad_out.shape)}, "
+                         f"{tuple(out.shape)}")
+    if tuple(jac.shape) != (B, P, 3) + tuple(out.shape[2:]):
+        raise ValueError(f"jac must be [{B}, {P}, 3, {n_out}, {n_out}, {n_out // 2 + 1}], got {tuple(jac.shape)}")
+    if grad_out.device != out.device or jac.device != out.device:
+        raise ValueError("grad_out, out and jac must be on one device")
+    gr = torch.empty((B_rot, P, 3, 3), dtype=torch.float32, device=out.device) if want_rot else None
+    gs = torch.empty((B_shift, P, 3), dtype=torch.float32, device=out.device) if want_shift else None
+    st = _lib.lib().tp_rotate_grad_pose_jac(grad_out.data_ptr(), out.data_ptr(), jac.data_ptr(), B, P, n_out,
+                                            int(B_rot), int(B_shift), float(oversampling), float(cutoff), _ptr(gr),
+                                            _ptr(gs), _stream(out.device))
+    _lib.check(st, "tp_rotate_grad_pose_jac")
+    return gr, gs
+
+
 class _Rotate(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, vol, rot, shift, n_out, interp, oversampling, cutoff):
-        out = tp_rotate_3d(vol, rot, shift, n_out, interp, oversampling, cutoff)
-        ctx.save_for_backward(vol, rot, shift)
+    def forward(ctx, vol, rot, shift, n_out, interp, oversampling, cutoff, save_jacobian):
+        pose_grads = ctx.needs_input_grad[1] or (shift is not None and ctx.needs_input_grad[2])
+        jac = None
+        if save_jacobian and pose_grads:
+            out, jac = tp_rotate_3d_jac(vol, rot, shift, n_out, interp, oversampling, cutoff)
+            ctx.save_for_backward(vol, rot, shift, out, jac)
+        else:
+            out = tp_rotate_3d(vol, rot, shift, n_out, interp, oversampling, cutoff)
+            ctx.save_for_backward(vol, rot, shift)
+        ctx.has_jac = jac is not None
         ctx.cfg = (interp, oversampling, cutoff)
         return out
 
     @staticmethod
     def backward(ctx, g):
-        vol, rot, shift = ctx.saved_tensors
+        if ctx.has_jac:
+            vol, rot, shift, out, jac = ctx.saved_tensors
+        else:
+            vol, rot, shift = ctx.saved_tensors
         interp, oversampling, cutoff = ctx.cfg
         g = g.contiguous()
         if g.dtype != torch.complex64:
@@ -496,13 +547,23 @@ class _Rotate(torch.autograd.Function):
             d_vol = tp_rotate_backproject_3d(g, rot, shift, vol.shape[1], interp, oversampling, cutoff)
         want_rot = ctx.needs_input_grad[1]
         want_shift = shift is not None and ctx.needs_input_grad[2]
-        if want_rot or want_shift:
+        if (want_rot or want_shift) and ctx.has_jac:
+            B_shift = shift.shape[0] if shift is not None else 1
+            d_rot, d_shift = tp_rotate_grad_pose_jac(g, out, jac, rot.shape[0], B_shift, oversampling, cutoff,
+                                                     want_rot=want_rot, want_shift=want_shift)
+        elif want_rot or want_shift:
             d_rot, d_shift = tp_rotate_grad_pose(vol, g, rot, shift, interp, oversampling, cutoff,
                                                  want_rot=want_rot, want_shift=want_shift)
-        return d_vol, d_rot, d_shift, None, None, None, None
+        return d_vol, d_rot, d_shift, None, None, None, None, None
 
 
-def rotate_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
-    """Differentiable 3D->3D rotation (gradients to vol, rot and shift)."""
-    return _Rotate.apply(vol, rot, shift, n_out, interp, oversampling, cutoff)
+def rotate_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0, save_jacobian=True):
+    """Differentiable 3D->3D rotation (gradients to vol, rot and shift).
 
+    With pose gradients needed and save_jacobian (output boxes up to 1023),
+    the forward keeps 24 bytes per output for a backward without a second
+    gather pass."""
+    if n_out is None:
+        n_out = int(round(vol.shape[1] / float(oversampling)))
+    save_jacobian = save_jacobian and n_out <= 1023
+    return _Rotate.apply(vol, rot, shift, n_out, interp, oversampling, cutoff, save_jacobian)

@@ -288,6 +288,38 @@ tp_status tp_grad_pose_jac(const tp_c64* grad_out, const tp_c64* proj, const tp_
                            float oversampling, float cutoff,
                            float* grad_rot, float* grad_shift, void* stream);
 
+/*
+ * 3D -> 3D rotation that also saves, for its pose gradients, the Jacobian of
+ * every output with respect to its sample point (the rotation's counterpart
+ * of tp_project_3d_jac; same chain rule as tp_rotate_grad_pose):
+ *   out  [B, P, N_out, N_out, N_out/2+1] complex64, overwritten: the values
+ *        of tp_rotate_3d for the same arguments
+ *   jac  [B, P, 3, N_out, N_out, N_out/2+1] complex64, overwritten:
+ *        phase * dS/dp_j (j = x, y, z) per output; 0 outside the sphere and
+ *        where the output reads 0
+ * Other arguments and errors as tp_rotate_3d; N_out above 1023 is
+ * TP_EUNSUPPORTED.
+ */
+tp_status tp_rotate_3d_jac(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot, int64_t P,
+                           const float* shift, int64_t B_shift, int64_t N_out, int interp, float oversampling,
+                           float cutoff, tp_c64* out, tp_c64* jac, void* stream);
+
+/*
+ * Pose gradients of L = Re sum conj(grad_out) * rotate_3d(...) from the
+ * saved out and jac of tp_rotate_3d_jac (same B, P, N_out, oversampling and
+ * cutoff; B_rot and B_shift as that call's):
+ *   dL/dR[i][j] = os * sum_k k_i Re(conj(G) jac_j)     (i, j = x, y, z)
+ *   dL/ds_j     = (2 pi / N_out) sum_k k_j Im(conj(G) out)
+ * the values of tp_rotate_grad_pose for that call, without reading the
+ * reference.  Only outputs inside the sphere are read.
+ *   grad_rot   [B_rot, P, 3, 3] float32, overwritten, or NULL
+ *   grad_shift [B_shift, P, 3] float32, overwritten, or NULL
+ * Errors as tp_grad_pose_jac; N_out above 1023 is TP_EUNSUPPORTED.
+ */
+tp_status tp_rotate_grad_pose_jac(const tp_c64* grad_out, const tp_c64* out, const tp_c64* jac, int64_t B,
+                                  int64_t P, int64_t N_out, int64_t B_rot, int64_t B_shift, float oversampling,
+                                  float cutoff, float* grad_rot, float* grad_shift, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

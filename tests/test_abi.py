@@ -178,3 +178,18 @@ def test_jacobian_entry_points_check_arguments():
     assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 1 << 20, 1 << 12, 32, 1, 1, 1.0, -1.0, FAKE, None, None) == EUNSUP
     # nothing requested: a no-op that touches no pointer
     assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 1, 4, 32, 1, 1, 1.0, -1.0, None, None, None) == _lib.TP_OK
+
+
+def test_rotation_jacobian_entry_points_check_arguments():
+    L = _lib.lib()
+    # vol, B, N, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, out, jac, stream
+    assert L.tp_rotate_3d_jac(FAKE, 1, 16, FAKE, 1, 2, None, 1, 16, 1, 1.0, -1.0, FAKE, None, None) == EINVAL
+    assert L.tp_rotate_3d_jac(FAKE, 1, 16, FAKE, 1, 2, None, 1, 16, 1, 1.0, -1.0, FAKE, FAKE_ODD, None) == EINVAL
+    assert L.tp_rotate_3d_jac(FAKE, 2, 16, FAKE, 3, 2, None, 1, 16, 1, 1.0, -1.0, FAKE, FAKE, None) == EINVAL
+    assert L.tp_rotate_3d_jac(FAKE, 1, 16, FAKE, 1, 2, None, 1, 1024, 1, 1.0, -1.0, FAKE, FAKE, None) == EUNSUP
+    # grad_out, out, jac, B, P, N_out, B_rot, B_shift, os, cutoff, grad_rot, grad_shift, stream
+    assert L.tp_rotate_grad_pose_jac(None, FAKE, FAKE, 1, 2, 16, 1, 1, 1.0, -1.0, FAKE, None, None) == EINVAL
+    assert L.tp_rotate_grad_pose_jac(FAKE, FAKE, FAKE, 2, 2, 16, 3, 1, 1.0, -1.0, FAKE, None, None) == EINVAL
+    assert L.tp_rotate_grad_pose_jac(FAKE, FAKE, FAKE, 1, 2, 16, 1, 1, -1.0, -1.0, FAKE, None, None) == EINVAL
+    assert L.tp_rotate_grad_pose_jac(FAKE, FAKE, FAKE, 1, 2, 1024, 1, 1, 1.0, -1.0, FAKE, None, None) == EUNSUP
+    assert L.tp_rotate_grad_pose_jac(FAKE, FAKE, FAKE, 1, 2, 16, 1, 1, 1.0, -1.0, None, None, None) == _lib.TP_OK

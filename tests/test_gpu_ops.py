@@ -189,17 +189,40 @@ def test_rotate_backproject_3d_matches_oracle(name):
     assert_parity(got, ref, f"rotate_backproject_3d {name}")
 
 
+@pytest.mark.parametrize("name", list(ROT_CASES))
+def test_rotate_jac_and_grad_pose_jac_match_oracle(name):
+    """The Jacobian-saving rotation gives the rotation's values, and the pose
+    gradients taken from its Jacobian give the oracle's."""
+    from cryo_em_fourier_amd import tp_rotate_3d_jac, tp_rotate_grad_pose_jac
+
+    c = rot_case(name)
+    log(f"[rotate_3d_jac + rotate_grad_pose_jac] {name}")
+    s = None if c["s"] is None else to_dev(c["s"])
+    out, jac = tp_rotate_3d_jac(to_dev(c["V"]), to_dev(c["R"]), s, c["n_out"], c["interp"], float(c["os"]),
+                                float(c["cutoff"]))
+    ref = oracle.rotate_3d(c["V"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(out.cpu().numpy(), ref, f"rotate_3d_jac {name}")
+    B_shift = 1 if c["s"] is None else c["s"].shape[0]
+    gr, gs = tp_rotate_grad_pose_jac(to_dev(c["G"]), out, jac, c["R"].shape[0], B_shift, float(c["os"]),
+                                     float(c["cutoff"]))
+    dR, ds = oracle.rotate_grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(gr.cpu().numpy(), dR, f"rotate grad_rot (jac) {name}")
+    assert_parity(gs.cpu().numpy(), ds, f"rotate grad_shift (jac) {name}")
+
+
+@pytest.mark.parametrize("save_jacobian", [True, False])
 @pytest.mark.parametrize("name", ["cubic", "linear-odd-nocut", "batch", "cube"])
-def test_rotate_autograd_matches_oracle(name):
+def test_rotate_autograd_matches_oracle(name, save_jacobian):
     """L = Re sum conj(G) rotate_3d(V): gradients to V (the adjoint), R and s."""
     from cryo_em_fourier_amd import rotate_3d
 
     c = rot_case(name)
-    log(f"[rotate autograd] {name}")
+    log(f"[rotate autograd] {name} save_jacobian={save_jacobian}")
     Vt = to_dev(c["V"]).requires_grad_(True)
     Rt = to_dev(c["R"]).requires_grad_(True)
     st = None if c["s"] is None else to_dev(c["s"]).requires_grad_(True)
-    out = rotate_3d(Vt, Rt, st, c["n_out"], c["interp"], float(c["os"]), float(c["cutoff"]))
+    out = rotate_3d(Vt, Rt, st, c["n_out"], c["interp"], float(c["os"]), float(c["cutoff"]),
+                    save_jacobian=save_jacobian)
     (to_dev(c["G"]).conj() * out).real.sum().backward()
     dV = oracle.rotate_backproject_3d(c["G"], c["R"], c["s"], c["N"], c["interp"], c["os"], c["cutoff"])
     dR, ds = oracle.rotate_grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
