@@ -42,8 +42,9 @@ tp_status check_and_fill(const Common& c, tp::OpParams& p) {
   const uint64_t elems = (c.ndim == 3 ? (uint64_t)c.N * (uint64_t)c.N : (uint64_t)c.N) * wh;
   if (elems * 8ull > kMaxRefBytes) return TP_EUNSUPPORTED;
   const int64_t wo = c.N_out / 2 + 1;
+  const int64_t tile_x = c.ndim == 3 ? tp::kTileXPairs : tp::kTileX;
   const int64_t tile_y = c.ndim == 3 ? tp::kTileYPairs : tp::kTileY;
-  const int64_t tx = (wo + tp::kTileX - 1) / tp::kTileX;
+  const int64_t tx = (wo + tile_x - 1) / tile_x;
   const int64_t ty = (c.N_out + tile_y - 1) / tile_y;
   const uint64_t blocks = (uint64_t)c.B * (uint64_t)c.P * (uint64_t)(tx * ty);
   if (blocks > kMaxBlocks) return TP_EUNSUPPORTED;
@@ -131,13 +132,13 @@ tp_status backproject_weights(int ndim, const float* w, int64_t B, int64_t P, in
 }
 
 // The 3D -> 3D rotation: the reference's checks, then a tiling of the
-// [N_out, N_out, N_out/2+1] output (16 kx columns x 8 (kz, ky) rows, two
+// [N_out, N_out, N_out/2+1] output (8 kx columns x 16 (kz, ky) rows, two
 // lanes per output).
 tp_status rotate_fill(const Common& c, tp::OpParams& p) {
   const tp_status st = check_and_fill(c, p);
   if (st != TP_OK) return st;
   const uint64_t rows = (uint64_t)c.N_out * (uint64_t)c.N_out;
-  const uint64_t tx = (uint64_t)(p.Wo + tp::kTileX - 1) / tp::kTileX;
+  const uint64_t tx = (uint64_t)(p.Wo + tp::kTileXPairs - 1) / tp::kTileXPairs;
   const uint64_t ty = (rows + tp::kTileYPairs - 1) / tp::kTileYPairs;
   const uint64_t blocks = (uint64_t)c.B * (uint64_t)c.P * tx * ty;
   if (blocks > kMaxBlocks || tx * ty > 0x7FFFFFFFull) return TP_EUNSUPPORTED;

@@ -40,11 +40,14 @@ struct BrickParams {
   int pmax;           // target poses per chunk
 };
 
-// Output tile of one workgroup: TX kx-columns x TY ky-rows (one lane per
-// output), or TX x kTileYPairs with two lanes per output (3D kernels).
+// Output tile of one workgroup: kTileX kx-columns x kTileY ky-rows with one
+// lane per output (2D kernels), or kTileXPairs x kTileYPairs with two lanes
+// per output (3D kernels: a wave covers 8 kx x 4 rows, whose sample points
+// share more cache lines than a 16 x 2 strip; measured 5 % faster).
 constexpr int kTileX = 16;
 constexpr int kTileY = 16;
-constexpr int kTileYPairs = 8;
+constexpr int kTileXPairs = 8;
+constexpr int kTileYPairs = 16;
 
 hipError_t launch_project(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s);

@@ -6,7 +6,8 @@
 //
 // 2D: one thread per output frequency, a 256-thread workgroup covers a 16x16
 // tile (kx, ky-row) of one projection.  3D: two lanes per output, each
-// gathering half of every x-row, so a workgroup covers 16x8 outputs.  The
+// gathering half of every x-row, so a workgroup covers 8x16 outputs (a wave
+// 8x4).  The
 // grid enumerates (batch, pose, tile) pose-major and is remapped so each XCD
 // walks contiguous tiles of the same pose.  The rotation and shift of a pose
 // are wave-uniform (kernel-argument derived addresses -> scalar loads).
@@ -33,8 +34,9 @@ __device__ __forceinline__ Out locate(const OpParams& p) {
   o.n = (int)(bn % (uint32_t)p.P);
   o.b = (int)(bn / (uint32_t)p.P);
   const int oi = PAIRS ? (int)(threadIdx.x >> 1) : (int)threadIdx.x;
-  o.kx = (int)(tile % (uint32_t)p.tiles_x) * kTileX + oi % kTileX;
-  o.iy = (int)(tile / (uint32_t)p.tiles_x) * p.tile_y + oi / kTileX;
+  constexpr int TX = PAIRS ? kTileXPairs : kTileX;
+  o.kx = (int)(tile % (uint32_t)p.tiles_x) * TX + oi % TX;
+  o.iy = (int)(tile / (uint32_t)p.tiles_x) * p.tile_y + oi / TX;
   o.in = o.kx < p.Wo && o.iy < p.No;
   o.ky = signed_row(o.iy, p.No);
   const long long k2 = (long long)o.kx * o.kx + (long long)o.ky * o.ky;

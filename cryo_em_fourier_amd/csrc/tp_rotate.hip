@@ -7,8 +7,8 @@
 // the central slice (which is the kz = 0 plane of this op), times the shift
 // phase exp(-2 pi i k.s / N_out) of a 3-vector shift, inside the sphere
 // |k| <= cutoff.  Two lanes per output, each gathering half of every x-row
-// (as the central-slice kernels); a 256-lane workgroup covers 16 kx columns
-// of 8 (kz, ky) rows of one pose.  The adjoint is the brick adjoint of
+// (as the central-slice kernels); a 256-lane workgroup covers 8 kx columns
+// of 16 (kz, ky) rows of one pose.  The adjoint is the brick adjoint of
 // tp_adjoint.hip run over volume lattices.
 #include "tp_internal.h"
 #include "tp_stencil.h"
@@ -31,8 +31,8 @@ __device__ __forceinline__ ROut rlocate(const OpParams& p) {
   o.n = (int)(bn % (uint32_t)p.P);
   o.b = (int)(bn / (uint32_t)p.P);
   const int oi = (int)(threadIdx.x >> 1);  // lane pair
-  o.kx = (int)(tile % (uint32_t)p.tiles_x) * kTileX + oi % kTileX;
-  const long long row = (long long)(tile / (uint32_t)p.tiles_x) * kTileYPairs + oi / kTileX;
+  o.kx = (int)(tile % (uint32_t)p.tiles_x) * kTileXPairs + oi % kTileXPairs;
+  const long long row = (long long)(tile / (uint32_t)p.tiles_x) * kTileYPairs + oi / kTileXPairs;
   const long long rows = (long long)p.No * p.No;
   o.in = o.kx < p.Wo && row < rows;
   const int iz = (int)(row / p.No), iy = (int)(row % p.No);

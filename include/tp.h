@@ -192,7 +192,7 @@ tp_status tp_symmetrize_x0(int ndim, tp_c64* ref, int64_t B, int64_t N, void* st
  *   rot    [B_rot, P, 3, 3] float32
  *   shift  [B_shift, P, 3] float32 (s_x, s_y, s_z in output voxels) or NULL
  *   out    [B, P, N_out, N_out, N_out/2+1] complex64, overwritten
- * Errors as tp_project_3d (the grid counts 16 x 8 output tiles of the
+ * Errors as tp_project_3d (the grid counts 8 x 16 output tiles of the
  * N_out^2 (kz, ky) rows).
  */
 tp_status tp_rotate_3d(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot, int64_t P,
