@@ -2,12 +2,12 @@
 
 One step = the whole path on one batch: forward projection, then the
 backward of a loss on its output: the adjoint for the reference gradient
-(tp_backproject_3d) and the rotation + shift gradients.  By default the
-forward saves each output's Jacobian with respect to its sample point
-(tp_project_3d_jac) and the pose gradients stream it (tp_grad_pose_jac);
-``--pose-grads recompute`` times tp_project_3d + tp_grad_pose instead, which
-gathers from the reference a second time.  The other path's forward and
-gradient times ride along in ``extras``.  Default workload (``c4``): a 256^3 blob phantom (rfft
+and the rotation + shift gradients.  By default the forward saves each
+output's Jacobian with respect to its sample point (tp_project_3d_jac) and
+one launch (tp_backward_3d_jac) runs the adjoint and streams the Jacobian
+for the pose gradients; ``--pose-grads recompute`` times tp_project_3d +
+tp_backproject_3d + tp_grad_pose instead, which gathers from the reference a
+second time.  The other kernels' times ride along in ``extras``.  Default workload (``c4``): a 256^3 blob phantom (rfft
 half-spectrum 256x256x129 complex64), 4096 uniform SO(3) poses, shifts
 U[-10,10] px, Catmull-Rom cubic, oversampling 1, cutoff 128.
 
@@ -448,7 +448,8 @@ def oversampling_study(args):
 
     def pipeline(interp, os_, backward):
         # forward only: tp_project_3d; training step: the bench step's calls
-        # (Jacobian-saving forward, adjoint, pose gradients from the Jacobian)
+        # (Jacobian-saving forward, then the adjoint and the pose gradients
+        # from the Jacobian in one launch)
         V = spectrum(os_)
         M = V.shape[1]
         if not backward:
@@ -458,10 +459,9 @@ def oversampling_study(args):
         _lib.check(L.tp_project_3d_jac(V.data_ptr(), 1, M, Rd.data_ptr(), 1, P, None, 1, n_out, interp, float(os_),
                                        w.cutoff, out.data_ptr(), jac.data_ptr(), sh), "project_jac")
         dV = torch.empty_like(V)
-        _lib.check(L.tp_backproject_3d(G.data_ptr(), 1, P, n_out, Rd.data_ptr(), 1, None, 1, M, interp,
-                                       float(os_), w.cutoff, dV.data_ptr(), sh), "backproject")
-        _lib.check(L.tp_grad_pose_jac(G.data_ptr(), out.data_ptr(), jac.data_ptr(), 1, P, n_out, 1, 1, float(os_),
-                                      w.cutoff, dR.data_ptr(), None, sh), "grad_pose_jac")
+        _lib.check(L.tp_backward_3d_jac(G.data_ptr(), out.data_ptr(), jac.data_ptr(), 1, P, n_out, Rd.data_ptr(), 1,
+                                        None, 1, M, interp, float(os_), w.cutoff, dV.data_ptr(), dR.data_ptr(), None,
+                                        sh), "backward_jac")
         to_real(dV, os_)
 
     def timed(f, reps=5):
@@ -592,12 +592,17 @@ def main():
                                       s.shape[0], os_, w.cutoff, dR.data_ptr(), ds.data_ptr(), sh),
                    "tp_grad_pose_jac")
 
+    def bwd_jac():
+        _lib.check(L.tp_backward_3d_jac(Gd.data_ptr(), out.data_ptr(), jac.data_ptr(), B, P, w.N_out, Rd.data_ptr(),
+                                        R.shape[0], sd.data_ptr(), s.shape[0], N, w.interp, os_, w.cutoff,
+                                        dV.data_ptr(), dR.data_ptr(), ds.data_ptr(), sh), "tp_backward_3d_jac")
+
     if args.pose_grads == "jacobian":
-        kernels = [("project_jac", fwd_jac), ("backproject", adj), ("grad_pose_jac", grad_jac)]
-        other = [("project", fwd), ("grad_pose", grad)]
+        kernels = [("project_jac", fwd_jac), ("backward_jac", bwd_jac)]
+        other = [("project", fwd), ("backproject", adj), ("grad_pose_jac", grad_jac), ("grad_pose", grad)]
     else:
         kernels = [("project", fwd), ("backproject", adj), ("grad_pose", grad)]
-        other = [("project_jac", fwd_jac), ("grad_pose_jac", grad_jac)]
+        other = [("project_jac", fwd_jac), ("backward_jac", bwd_jac), ("grad_pose_jac", grad_jac)]
 
     # calibration for HBM byte counters: one plain streaming copy (y = x * 1)
     # of known size, outside the timed region.  A counter run of this same
@@ -655,9 +660,11 @@ def main():
         "backproject": units * 8 + 2 * ref_bytes + pose_bytes,
         "grad_pose": ref_bytes + units * 8 + pose_bytes + grad_bytes,
         "grad_pose_jac": units * 40 + grad_bytes,                # G, out and jac inside the cutoff
+        # both: G, out and jac inside the cutoff, the volume (fill + write)
+        "backward_jac": units * 40 + 2 * ref_bytes + pose_bytes + grad_bytes,
     }
     tap_bytes = {"project": units * taps * 8, "project_jac": units * taps * 8, "backproject": units * taps * 8,
-                 "grad_pose": units * taps * 8, "grad_pose_jac": 0}
+                 "grad_pose": units * taps * 8, "grad_pose_jac": 0, "backward_jac": units * taps * 8}
     dom = max(avg, key=avg.get)
     achieved = hbm[dom] / (avg[dom] * 1e-3) / 1e9
     wl_key = f"{w.name}_os{args.oversampling}" + (f"_p{P}" if args.poses else "")

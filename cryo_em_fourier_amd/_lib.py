@@ -31,6 +31,7 @@ EXPORTS = (
     "tp_rotate_grad_pose",
     "tp_project_3d_jac",
     "tp_grad_pose_jac",
+    "tp_backward_3d_jac",
     "tp_rotate_3d_jac",
     "tp_rotate_grad_pose_jac",
 )
@@ -71,6 +72,10 @@ _SIGS = {
                           _int),
     # grad_out, proj, jac, B, P, N_out, B_rot, B_shift, os, cutoff, grad_rot, grad_shift, stream
     "tp_grad_pose_jac": ([_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp], _int),
+    # grad_out, proj, jac, B, P, N_out, rot, B_rot, shift, B_shift, N, interp, os, cutoff, vol_out,
+    # grad_rot, grad_shift, stream
+    "tp_backward_3d_jac": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp,
+                            _vp, _vp, _vp], _int),
     # as tp_project_3d_jac / tp_grad_pose_jac, for the 3D -> 3D rotation
     "tp_rotate_3d_jac": ([_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp, _vp],
                          _int),

@@ -22,6 +22,7 @@
 // them); chunks of one brick merge with coalesced float atomics, unsplit
 // bricks are written with plain stores.
 #include "tp_bricks.h"
+#include "tp_gradjac.h"
 #include "tp_internal.h"
 #include "tp_stencil.h"
 
@@ -54,7 +55,9 @@ constexpr int kPrefetch = 2;        // hits whose G values a thread loads at onc
 // and 29 bits leave another factor 4 of int32 headroom.
 constexpr int kQuantumBits = 29;
 
-constexpr int kSlice = 0, kWeights = 1, kVolume = 2;
+// kSliceGrad: kSlice followed by B * P workgroups (1D grid) that each reduce
+// one pose's gradients from a saved Jacobian (the fused backward)
+constexpr int kSlice = 0, kWeights = 1, kVolume = 2, kSliceGrad = 3;
 
 template <int NDIM> struct Brick;
 template <> struct Brick<3> { static constexpr int X = 16, Y = 16, Z = 16; };
@@ -128,14 +131,13 @@ __device__ __forceinline__ int brick_chunks(const OpParams& p, const BrickParams
 }
 
 template <int NDIM, bool VOL>
-__device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams& bp) {
+__device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams& bp, uint32_t lin) {
   using BR = Brick<NDIM>;
   BrickPos r;
   // plain round-robin over the XCDs: consecutive bricks (and the mostly empty
   // high chunk slots) spread evenly; bricks share little data across XCDs.
   // High chunk slots go first: only the busiest bricks near the origin have
   // them, so the long workgroups start early and the short ones fill the end.
-  const uint32_t lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const int brick = (int)(lin % (uint32_t)bp.nbricks);
   const int ch = bp.cmax - 1 - (int)((lin / (uint32_t)bp.nbricks) % (uint32_t)bp.cmax);
   r.b = (int)(lin / ((uint32_t)bp.nbricks * (uint32_t)bp.cmax));
@@ -153,7 +155,7 @@ __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams&
   }
   // every pose of a volume lattice reaches every brick inside its sphere
   const int nch = VOL ? bp.cmax : brick_chunks<NDIM>(p, bp, r.x0, r.y0, r.z0);
-  r.valid = ch < nch;
+  r.valid = ch < nch && r.b < p.B;
   r.chunked = nch > 1;
   r.n0 = (int)((long long)p.P * ch / nch);
   r.n1 = (int)((long long)p.P * (ch + 1) / nch);
@@ -465,7 +467,7 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
 
 // MODE: kSlice (the projector's adjoint), kWeights (real weight volume),
 // kVolume (the adjoint of the 3D -> 3D rotation: volume lattices, one pose
-// per group).
+// per group), kSliceGrad (kSlice and the pose gradients from a Jacobian).
 template <int NDIM, int INTERP, int MODE, int BS>
 __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>::WAVES_PER_EU))) void k_adjoint_bricks(OpParams p,
                                                                                            BrickParams bp) {
@@ -484,7 +486,18 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>
   __shared__ int s_wcnt[BS / 64];
   __shared__ float s_red[BS / 64];
 
-  const BrickPos br = decode<NDIM, VOL>(p, bp);
+  const uint32_t lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  if constexpr (MODE == kSliceGrad) {
+    // fused backward: the workgroups after the bricks stream one pose's
+    // gradient reduction each (HBM-bound), filling the CUs that the
+    // LDS-bound bricks leave idle at the end of the launch
+    const uint32_t adj = (uint32_t)bp.nbricks * (uint32_t)bp.cmax * (uint32_t)p.B;
+    if (lin >= adj) {
+      grad_jac_pose<BS>(p, lin - adj, reinterpret_cast<double(*)[8]>(acc));
+      return;
+    }
+  }
+  const BrickPos br = decode<NDIM, VOL>(p, bp, lin);
   if (!br.valid) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -690,12 +703,13 @@ static bool wide_adjoint(const OpParams& p) { return p.os <= 1.25f; }
 
 template <int MODE, int BS>
 static void launch_modes(const OpParams& p, const BrickParams& bp, int ndim, int interp, hipStream_t s) {
-  const dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(BS);
+  dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(BS);
+  if (MODE == kSliceGrad) grid = dim3((unsigned)((uint64_t)bp.nbricks * bp.cmax * p.B + (uint64_t)p.B * p.P));
   if (ndim == 3) {
     if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, MODE, BS>), grid, block, 0, s, p, bp);
     else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, MODE, BS>), grid, block, 0, s, p, bp);
   } else {
-    if constexpr (MODE != kVolume) {  // volume lattices are 3D only
+    if constexpr (MODE == kSlice || MODE == kWeights) {  // volume lattices and the fused backward are 3D only
       if (interp) hipLaunchKernelGGL((k_adjoint_bricks<2, 1, MODE, BS>), grid, block, 0, s, p, bp);
       else hipLaunchKernelGGL((k_adjoint_bricks<2, 0, MODE, BS>), grid, block, 0, s, p, bp);
     }
@@ -712,6 +726,18 @@ static hipError_t launch_adjoint(const OpParams& p, const BrickParams& bp, int n
 hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s) {
   const BrickParams bp = p.ndim == 3 ? brick_params<3>(p) : brick_params<2>(p);
   return launch_adjoint<kSlice>(p, bp, p.ndim, interp, s);
+}
+
+// The adjoint and the pose gradients from a saved Jacobian in one launch:
+// measured at c4, 6.2 ms against 6.7 ms for the two launches (the gradient
+// workgroups fill the adjoint's tail).  Spreading them among the bricks
+// instead was slower (7.2 to 8.8 ms): they take the LDS-bound bricks' slots.
+hipError_t launch_backward_jac(const OpParams& p, int interp, hipStream_t s) {
+  return launch_adjoint<kSliceGrad>(p, brick_params<3>(p), 3, interp, s);
+}
+
+uint64_t backward_jac_blocks(const OpParams& p) {
+  return adjoint_blocks(p) + (uint64_t)p.B * (uint64_t)p.P;
 }
 
 hipError_t launch_backproject_weights(const OpParams& p, int interp, hipStream_t s) {

@@ -67,6 +67,9 @@ hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s);
 // and the pose gradients from it (one workgroup per (batch, pose))
 hipError_t launch_project_jac(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_grad_jac(const OpParams& p, hipStream_t s);
+// the adjoint with the pose gradients from a saved Jacobian in the same launch
+hipError_t launch_backward_jac(const OpParams& p, int interp, hipStream_t s);
+uint64_t backward_jac_blocks(const OpParams& p);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
 uint64_t adjoint_blocks(const OpParams& p);
 

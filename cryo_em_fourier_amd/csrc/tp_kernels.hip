@@ -11,6 +11,7 @@
 // grid enumerates (batch, pose, tile) pose-major and is remapped so each XCD
 // walks contiguous tiles of the same pose.  The rotation and shift of a pose
 // are wave-uniform (kernel-argument derived addresses -> scalar loads).
+#include "tp_gradjac.h"
 #include "tp_internal.h"
 #include "tp_stencil.h"
 
@@ -350,85 +351,28 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   const bool active = o.keep && sample_point<3>(p, o, q);
   float2 S, dS[3];
   pair_grad_values<INTERP>(p, o, h, active, q, S, dS);
-  if (!o.in) return;
+  // lane 0 of a pair stores the output and jac_x, lane 1 jac_y and jac_z
+  float2 a = h ? dS[1] : S, c = h ? dS[2] : dS[0];
   if (active && p.shift) {
     const float2 s = pose_shift(p, o);
     const float2 ph = shift_phase(o.kx, o.ky, s.x, s.y, p.inv_no);
-    S = cmul(ph, S);
-#pragma unroll
-    for (int j = 0; j < 3; ++j) dS[j] = cmul(ph, dS[j]);
+    a = cmul(ph, a);
+    c = cmul(ph, c);
   }
+  if (!o.in) return;
   const size_t plane = (size_t)p.No * p.Wo;
   const size_t pose = (size_t)o.b * p.P + o.n;
   const size_t e = (size_t)o.iy * p.Wo + o.kx;
   float2* jac = p.jac_out + pose * 3 * plane + e;
-  if (h == 0) {
-    p.img_out[pose * plane + e] = S;
-    jac[0] = dS[0];
-  } else {
-    jac[plane] = dS[1];
-    jac[2 * plane] = dS[2];
-  }
+  *(h ? jac + plane : p.img_out + pose * plane + e) = a;
+  *(h ? jac + 2 * plane : jac) = c;
 }
 
-// Pose gradients from a saved Jacobian and projection:
-//   dL/dR[i][j] = os sum_k k_i Re(conj(G) jac_j),
-//   dL/ds_j     = (2 pi / No) sum_k k_j Im(conj(G) proj),
-// the sums of k_grad3p.  One workgroup per (batch, pose) streams the pose's
-// outputs inside the cutoff (coalesced), sums in fp64 and adds its eight
-// totals to the zeroed gradients.
+// Pose gradients from a saved Jacobian and projection: one workgroup per
+// (batch, pose) streams the pose's outputs inside the cutoff (coalesced).
 __global__ __launch_bounds__(kBlock) void k_grad_jac(OpParams p) {
-  constexpr int NV = 8;
-  __shared__ double red[kBlock / 64][NV];
-  const uint32_t bn = blockIdx.x;
-  const int n = (int)(bn % (uint32_t)p.P), b = (int)(bn / (uint32_t)p.P);
-  const uint32_t plane = (uint32_t)p.No * (uint32_t)p.Wo;
-  const float2* G = p.img + (size_t)bn * plane;
-  const float2* Y = p.proj + (size_t)bn * plane;
-  const float2* J = p.jac + (size_t)bn * 3 * plane;
-  double acc[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) acc[i] = 0.0;
-#pragma unroll 2
-  for (uint32_t e = threadIdx.x; e < plane; e += kBlock) {
-    const int iy = (int)(e / (uint32_t)p.Wo), kx = (int)(e - (uint32_t)iy * (uint32_t)p.Wo);
-    const int ky = signed_row(iy, p.No);
-    if (p.cut2 >= 0 && (long long)kx * kx + (long long)ky * ky > p.cut2) continue;
-    const float2 g = G[e], y = Y[e], j0 = J[e], j1 = J[e + plane], j2 = J[e + 2 * plane];
-    const double a0 = (double)g.x * j0.x + (double)g.y * j0.y;
-    const double a1 = (double)g.x * j1.x + (double)g.y * j1.y;
-    const double a2 = (double)g.x * j2.x + (double)g.y * j2.y;
-    const double im = (double)g.x * y.y - (double)g.y * y.x;
-    const double dx = (double)kx, dy = (double)ky;
-    acc[0] = fma(dx, a0, acc[0]);
-    acc[1] = fma(dx, a1, acc[1]);
-    acc[2] = fma(dx, a2, acc[2]);
-    acc[3] = fma(dy, a0, acc[3]);
-    acc[4] = fma(dy, a1, acc[4]);
-    acc[5] = fma(dy, a2, acc[5]);
-    acc[6] = fma(dx, im, acc[6]);
-    acc[7] = fma(dy, im, acc[7]);
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const double d = wave_sum8(acc);
-  if ((lane & 7) == 0) red[wave][lane >> 3] = d;
-  __syncthreads();
-  if (threadIdx.x < NV) {
-    const int i = threadIdx.x;
-    double v = 0.0;
-#pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) v += red[w][i];
-    if (v == 0.0) return;
-    if (i < 6) {
-      if (p.grad_rot) {
-        const size_t br = p.B_rot == 1 ? 0 : (size_t)b;
-        unsafeAtomicAdd(p.grad_rot + ((br * p.P + n) * 3 + i / 3) * 3 + i % 3, (float)((double)p.os * v));
-      }
-    } else if (p.grad_shift) {
-      const size_t bs = p.B_shift == 1 ? 0 : (size_t)b;
-      unsafeAtomicAdd(p.grad_shift + (bs * p.P + n) * 2 + (i - 6), (float)(6.283185307179586476925 * p.inv_no * v));
-    }
-  }
+  __shared__ double red[kBlock / 64][8];
+  grad_jac_pose<kBlock>(p, blockIdx.x, red);
 }
 
 // Hermitian symmetry of the x = 0 plane: V(0, y, z) <- (V(0, y, z) +

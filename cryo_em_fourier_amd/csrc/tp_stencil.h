@@ -318,10 +318,13 @@ __device__ __forceinline__ void gather3_grad_half(rsrc_t rs, const RefGeom& g, d
   out[3] = sz;
 }
 
-// Sum of a value over the two lanes of a pair.
-__device__ __forceinline__ float2 pair_sum(float2 v) {
-  return make_float2(v.x + __shfl_xor(v.x, 1, 64), v.y + __shfl_xor(v.y, 1, 64));
+// Sum of a value over the two lanes of a pair: a DPP quad permutation (lanes
+// 1, 0, 3, 2) feeds the add, with no LDS round trip.  Every lane of the wave
+// must be active.
+__device__ __forceinline__ float pair_sum1(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
+__device__ __forceinline__ float2 pair_sum(float2 v) { return make_float2(pair_sum1(v.x), pair_sum1(v.y)); }
 
 // Does the secondary sum at -m (x-taps >= xmin2) have a tap of nonzero
 // weight?  For the cubic kernel a tap of zero weight still has a nonzero

@@ -289,6 +289,26 @@ tp_status tp_grad_pose_jac(const tp_c64* grad_out, const tp_c64* proj, const tp_
                            float* grad_rot, float* grad_shift, void* stream);
 
 /*
+ * The backward of tp_project_3d_jac in one launch: the adjoint of
+ * tp_backproject_3d and the pose gradients of tp_grad_pose_jac, whose
+ * streaming reduction runs on workgroups placed after the adjoint's bricks,
+ * so that they fill the CUs the bricks leave idle at the end.  The adjoint
+ * is the exact adjoint of the forward (ko page tech. section 2), the
+ * gradients the analytic ones of the ar page tech. section 2.
+ *   grad_out   [B, P, N_out, N_out/2+1] complex64, input
+ *   proj, jac  the outputs of tp_project_3d_jac for the same arguments, input
+ *   vol_out    [B, N, N, N/2+1] complex64, overwritten: tp_backproject_3d's
+ *   grad_rot   [B_rot, P, 3, 3] float32, overwritten (last row 0), or NULL
+ *   grad_shift [B_shift, P, 2] float32, overwritten, or NULL
+ * Other arguments and errors as tp_backproject_3d and tp_grad_pose_jac.
+ */
+tp_status tp_backward_3d_jac(const tp_c64* grad_out, const tp_c64* proj, const tp_c64* jac,
+                             int64_t B, int64_t P, int64_t N_out,
+                             const float* rot, int64_t B_rot, const float* shift, int64_t B_shift,
+                             int64_t N, int interp, float oversampling, float cutoff,
+                             tp_c64* vol_out, float* grad_rot, float* grad_shift, void* stream);
+
+/*
  * 3D -> 3D rotation that also saves, for its pose gradients, the Jacobian of
  * every output with respect to its sample point (the rotation's counterpart
  * of tp_project_3d_jac; same chain rule as tp_rotate_grad_pose):

@@ -180,6 +180,33 @@ def test_jacobian_entry_points_check_arguments():
     assert L.tp_grad_pose_jac(FAKE, FAKE, FAKE, 1, 4, 32, 1, 1, 1.0, -1.0, None, None, None) == _lib.TP_OK
 
 
+def test_fused_backward_checks_arguments():
+    L = _lib.lib()
+    f = L.tp_backward_3d_jac
+    # grad_out, proj, jac, B, P, N_out, rot, B_rot, shift, B_shift, N, interp, os, cutoff, vol_out,
+    # grad_rot, grad_shift, stream
+    ok = [FAKE, FAKE, FAKE, 1, 4, 32, FAKE, 1, None, 1, 32, 1, 1.0, -1.0, FAKE, FAKE, None, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a2=None) == EINVAL                 # no jac
+    assert call(a14=None) == EINVAL                # no volume
+    assert call(a1=FAKE_ODD) == EINVAL             # misaligned proj
+    assert call(a15=FAKE + 2) == EINVAL            # misaligned grad_rot
+    assert call(a3=0) == EINVAL                    # B = 0
+    assert call(a7=3) == EINVAL                    # B_rot not in {1, B}
+    assert call(a16=FAKE, a9=3) == EINVAL          # B_shift not in {1, B} with grad_shift
+    assert call(a11=2) == EINVAL                   # interpolation
+    assert call(a12=0.0) == EINVAL                 # oversampling
+    assert call(a13=math.nan) == EINVAL            # cutoff
+    assert call(a5=(1 << 14)) == EUNSUP            # lattice offsets are 14-bit
+    assert call(a10=70000) == EUNSUP               # box
+
+
 def test_rotation_jacobian_entry_points_check_arguments():
     L = _lib.lib()
     # vol, B, N, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, out, jac, stream

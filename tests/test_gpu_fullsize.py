@@ -109,29 +109,36 @@ def test_fullsize_grad_pose_sampled_poses(key):
 @pytest.mark.parametrize("key", KEYS)
 def test_fullsize_grad_pose_jac_sampled_poses(key):
     """The Jacobian-saving forward over all poses, then the pose gradients
-    from it with the sparse upstream gradient."""
+    from it with the sparse upstream gradient, alone and in the fused backward
+    (the benchmark's step) with the adjoint."""
     import torch
 
-    from cryo_em_fourier_amd import tp_grad_pose_jac, tp_project_3d_jac
+    from cryo_em_fourier_amd import tp_backward_3d_jac, tp_grad_pose_jac, tp_project_3d_jac
 
     c = workload(key)
     w = c["w"]
-    log(f"[fullsize grad_pose_jac] {key}: {w.P} poses, upstream nonzero on {c['idx'].tolist()}")
-    out, jac = tp_project_3d_jac(to_dev(c["V"]), to_dev(c["R"]), to_dev(c["s"]), w.N_out, w.interp, c["os"],
-                                 w.cutoff)
-    gr, gs = tp_grad_pose_jac(_sparse_upstream(c), out, jac, c["R"].shape[0], c["s"].shape[0], c["os"], w.cutoff)
+    log(f"[fullsize grad_pose_jac + backward_3d_jac] {key}: {w.P} poses, upstream nonzero on {c['idx'].tolist()}")
+    R, s = to_dev(c["R"]), to_dev(c["s"])
+    out, jac = tp_project_3d_jac(to_dev(c["V"]), R, s, w.N_out, w.interp, c["os"], w.cutoff)
+    G = _sparse_upstream(c)
+    gr, gs = tp_grad_pose_jac(G, out, jac, c["R"].shape[0], c["s"].shape[0], c["os"], w.cutoff)
+    vol_f, gr_f, gs_f = tp_backward_3d_jac(G, out, jac, R, s, c["N"], w.interp, c["os"], w.cutoff)
     got = out[:, c["idx"]].cpu().numpy()
-    del out, jac
+    del out, jac, G
     torch.cuda.empty_cache()
     ref = oracle.project(c["V"], c["R"][:, c["idx"]], c["s"][:, c["idx"]], w.N_out, w.interp, c["os"], w.cutoff)
     assert_parity(got, ref, f"forward (jac) {key}")
-    gr, gs = gr.cpu().numpy(), gs.cpu().numpy()
     dR, ds = oracle.grad_pose(c["V"], c["G_sub"], c["R"][:, c["idx"]], c["s"][:, c["idx"]], w.N_out, w.interp,
                               c["os"], w.cutoff)
-    assert_parity(gr[:, c["idx"]], dR, f"grad_rot (jac) {key}")
-    assert_parity(gs[:, c["idx"]], ds, f"grad_shift (jac) {key}")
     rest = np.setdiff1d(np.arange(w.P), c["idx"])
-    assert not gr[:, rest].any() and not gs[:, rest].any(), "poses with zero upstream must get zero gradients"
+    for tag, a, b in (("jac", gr, gs), ("fused", gr_f, gs_f)):
+        a, b = a.cpu().numpy(), b.cpu().numpy()
+        assert_parity(a[:, c["idx"]], dR, f"grad_rot ({tag}) {key}")
+        assert_parity(b[:, c["idx"]], ds, f"grad_shift ({tag}) {key}")
+        assert not a[:, rest].any() and not b[:, rest].any(), "poses with zero upstream must get zero gradients"
+    ref = oracle.backproject(c["G_sub"], c["R"][:, c["idx"]], c["s"][:, c["idx"]], c["N"], w.interp, c["os"],
+                             w.cutoff)
+    assert_parity(vol_f.cpu().numpy(), ref, f"adjoint (fused) {key}")
 
 
 @pytest.mark.parametrize("key", KEYS)

@@ -154,6 +154,28 @@ def test_project_3d_jac_and_grad_pose_jac_match_oracle(name):
     assert not gr[:, :, 2].any(), "the last row of dL/dR is 0"
 
 
+@pytest.mark.parametrize("name", CASES3)
+def test_backward_3d_jac_matches_oracle(name):
+    """The fused backward gives the oracle's adjoint and pose gradients (the
+    values of tp_backproject_3d and tp_grad_pose_jac)."""
+    from cryo_em_fourier_amd import tp_backward_3d_jac, tp_project_3d_jac
+
+    c = case3d(name)
+    log(f"[backward_3d_jac] {name}")
+    V, R, s, G = _dev(c)
+    out, jac = tp_project_3d_jac(V, R, s, c["n_out"], c["interp"], float(c["os"]), float(c["cutoff"]))
+    d_vol, gr, gs = tp_backward_3d_jac(G, out, jac, R, s, c["N"], c["interp"], float(c["os"]), float(c["cutoff"]))
+    ref = oracle.backproject(c["G"], c["R"], c["s"], c["N"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(d_vol.cpu().numpy(), ref, f"backward_3d_jac volume {name}")
+    dR, ds = oracle.grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
+    gr, gs = gr.cpu().numpy(), gs.cpu().numpy()
+    if name == "adv-linear":
+        keep = [0, 1, 4, 5, 6]  # one-sided derivatives at kinks, as in the gradient test above
+        gr, dR, gs, ds = gr[:, keep], dR[:, keep], gs[:, keep], ds[:, keep]
+    assert_parity(gr, dR, f"grad_rot (backward_3d_jac) {name}")
+    assert_parity(gs, ds, f"grad_shift (backward_3d_jac) {name}")
+
+
 # ------------------------------------------------------------------- 2D
 
 @functools.lru_cache(maxsize=None)
@@ -347,6 +369,45 @@ def test_jacobian_path_edge_cases():
     dR2, ds2 = oracle.grad_pose(b["V"], b["G"], b["R"], np.zeros((b["V"].shape[0], b["R"].shape[1], 2), np.float32),
                                 b["n_out"], b["interp"], b["os"], b["cutoff"])
     assert_parity(gs.cpu().numpy(), ds2, "jac grad_shift per batch entry")
+
+
+def test_fused_backward_edge_cases():
+    """tp_backward_3d_jac at cutoff 0, N_out = 1, a pose broadcast over the
+    batch without a shift (grad_shift per batch entry), one gradient at a
+    time, and none (the plain adjoint)."""
+    from cryo_em_fourier_amd import tp_backward_3d_jac, tp_project_3d_jac
+
+    c = case3d("odd-nocut")
+    V, R, s, G = _dev(c)
+    for n_out, cut in ((c["n_out"], 0.0), (1, -1.0)):
+        log(f"[fused edge] N_out {n_out} cutoff {cut}")
+        out, jac = tp_project_3d_jac(V, R, s, n_out, c["interp"], 1.0, cut)
+        Gc = to_dev(c["G"][:, :, :n_out, :n_out // 2 + 1].copy())
+        vol, gr, gs = tp_backward_3d_jac(Gc, out, jac, R, s, c["N"], c["interp"], 1.0, cut)
+        ref = oracle.backproject(c["G"][:, :, :n_out, :n_out // 2 + 1], c["R"], c["s"], c["N"], c["interp"], 1.0, cut)
+        assert_parity(vol.cpu().numpy(), ref, f"fused volume N_out {n_out} cutoff {cut}")
+        # only the DC output is kept: k = 0 gives zero pose gradients
+        assert not gr.cpu().numpy().any() and not gs.cpu().numpy().any()
+    log("[fused edge] batch 2, broadcast pose, no shift, one gradient at a time, none")
+    b = case3d("batch-bcast")
+    Vb, Rb, _, Gb = _dev(b)
+    args = (b["N"], b["interp"], float(b["os"]), float(b["cutoff"]))
+    outb, jacb = tp_project_3d_jac(Vb, Rb, None, b["n_out"], b["interp"], float(b["os"]), float(b["cutoff"]))
+    ref = oracle.backproject(b["G"], b["R"], None, *args)
+    dR, _ = oracle.grad_pose(b["V"], b["G"], b["R"], None, b["n_out"], b["interp"], b["os"], b["cutoff"])
+    nb = b["V"].shape[0]
+    _, ds = oracle.grad_pose(b["V"], b["G"], b["R"], np.zeros((nb, b["R"].shape[1], 2), np.float32), b["n_out"],
+                             b["interp"], b["os"], b["cutoff"])
+    vol, gr, none_s = tp_backward_3d_jac(Gb, outb, jacb, Rb, None, *args, want_shift=False)
+    assert none_s is None
+    assert_parity(vol.cpu().numpy(), ref, "fused volume broadcast")
+    assert_parity(gr.cpu().numpy(), dR, "fused grad_rot broadcast")
+    vol, none_r, gs = tp_backward_3d_jac(Gb, outb, jacb, Rb, None, *args, want_rot=False, B_shift=nb)
+    assert none_r is None
+    assert_parity(gs.cpu().numpy(), ds, "fused grad_shift per batch entry")
+    vol, none_r, none_s = tp_backward_3d_jac(Gb, outb, jacb, Rb, None, *args, want_rot=False, want_shift=False)
+    assert none_r is None and none_s is None
+    assert_parity(vol.cpu().numpy(), ref, "fused volume without gradients")
 
 
 def test_nonfinite_rotation_reads_zero():
