@@ -334,10 +334,16 @@ def time_extras(L, _lib, torch, stream, Gd, Rd, R, dV, w, N, os_, B, P, reps=5):
         _lib.check(L.tp_rotate_grad_pose_jac(g3.data_ptr(), o3.data_ptr(), j3.data_ptr(), 1, p3, n3, 1, 1, 1.0, 32.0,
                                              gr3.data_ptr(), gs3.data_ptr(), sh), "tp_rotate_grad_pose_jac")
 
+    def rot_bwd_jac():
+        _lib.check(L.tp_rotate_backward_3d_jac(g3.data_ptr(), o3.data_ptr(), j3.data_ptr(), 1, p3, n3, r3.data_ptr(),
+                                               1, s3.data_ptr(), 1, n3, 1, 1.0, 32.0, v3.data_ptr(), gr3.data_ptr(),
+                                               gs3.data_ptr(), sh), "tp_rotate_backward_3d_jac")
+
     out = {"rotate_workload": "box 64 blob phantom, 512 poses, cubic, cutoff 32, shifts U[-3,3]"}
     for name, f in (("backproject_weights", weights), ("symmetrize_x0", sym), ("rotate_3d", rot_fwd),
                     ("rotate_backproject_3d", rot_adj), ("rotate_grad_pose", rot_grad),
-                    ("rotate_3d_jac", rot_fwd_jac), ("rotate_grad_pose_jac", rot_grad_jac)):
+                    ("rotate_3d_jac", rot_fwd_jac), ("rotate_grad_pose_jac", rot_grad_jac),
+                    ("rotate_backward_3d_jac", rot_bwd_jac)):
         out[name + "_ms"] = time_launches(torch, stream, f, reps)
     del Wd, wV, o3, g3, j3
     return out

@@ -34,6 +34,7 @@ EXPORTS = (
     "tp_backward_3d_jac",
     "tp_rotate_3d_jac",
     "tp_rotate_grad_pose_jac",
+    "tp_rotate_backward_3d_jac",
 )
 
 _vp = ctypes.c_void_p
@@ -80,6 +81,9 @@ _SIGS = {
     "tp_rotate_3d_jac": ([_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp, _vp],
                          _int),
     "tp_rotate_grad_pose_jac": ([_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp], _int),
+    # as tp_backward_3d_jac, for the 3D -> 3D rotation
+    "tp_rotate_backward_3d_jac": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _int, _f32, _f32,
+                                   _vp, _vp, _vp, _vp], _int),
 }
 
 _lib = None

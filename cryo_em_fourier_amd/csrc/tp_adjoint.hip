@@ -55,9 +55,10 @@ constexpr int kPrefetch = 2;        // hits whose G values a thread loads at onc
 // and 29 bits leave another factor 4 of int32 headroom.
 constexpr int kQuantumBits = 29;
 
-// kSliceGrad: kSlice followed by B * P workgroups (1D grid) that each reduce
-// one pose's gradients from a saved Jacobian (the fused backward)
-constexpr int kSlice = 0, kWeights = 1, kVolume = 2, kSliceGrad = 3;
+// kSliceGrad / kVolumeGrad: kSlice / kVolume followed by B * P workgroups
+// (1D grid) that each reduce one pose's gradients from a saved Jacobian (the
+// fused backwards of the projection and of the rotation)
+constexpr int kSlice = 0, kWeights = 1, kVolume = 2, kSliceGrad = 3, kVolumeGrad = 4;
 
 template <int NDIM> struct Brick;
 template <> struct Brick<3> { static constexpr int X = 16, Y = 16, Z = 16; };
@@ -467,12 +468,13 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
 
 // MODE: kSlice (the projector's adjoint), kWeights (real weight volume),
 // kVolume (the adjoint of the 3D -> 3D rotation: volume lattices, one pose
-// per group), kSliceGrad (kSlice and the pose gradients from a Jacobian).
+// per group), kSliceGrad / kVolumeGrad (kSlice / kVolume and the pose
+// gradients from a Jacobian).
 template <int NDIM, int INTERP, int MODE, int BS>
 __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>::WAVES_PER_EU))) void k_adjoint_bricks(OpParams p,
                                                                                            BrickParams bp) {
   constexpr bool WEIGHTS = MODE == kWeights;
-  constexpr bool VOL = MODE == kVolume;
+  constexpr bool VOL = MODE == kVolume || MODE == kVolumeGrad;
   constexpr int GMAX = VOL ? 1 : kGroupMax;
   using BR = Brick<NDIM>;
   using AL = AccLayout<NDIM>;
@@ -487,13 +489,14 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>
   __shared__ float s_red[BS / 64];
 
   const uint32_t lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  if constexpr (MODE == kSliceGrad) {
+  if constexpr (MODE == kSliceGrad || MODE == kVolumeGrad) {
     // fused backward: the workgroups after the bricks stream one pose's
     // gradient reduction each (HBM-bound), filling the CUs that the
     // LDS-bound bricks leave idle at the end of the launch
     const uint32_t adj = (uint32_t)bp.nbricks * (uint32_t)bp.cmax * (uint32_t)p.B;
     if (lin >= adj) {
-      grad_jac_pose<BS>(p, lin - adj, reinterpret_cast<double(*)[8]>(acc));
+      if constexpr (MODE == kSliceGrad) grad_jac_pose<BS>(p, lin - adj, reinterpret_cast<double(*)[8]>(acc));
+      else grad_jac_vol<BS>(p, lin - adj, reinterpret_cast<double(*)[16]>(acc));
       return;
     }
   }
@@ -704,7 +707,7 @@ static bool wide_adjoint(const OpParams& p) { return p.os <= 1.25f; }
 template <int MODE, int BS>
 static void launch_modes(const OpParams& p, const BrickParams& bp, int ndim, int interp, hipStream_t s) {
   dim3 grid((unsigned)bp.nbricks, (unsigned)bp.cmax, (unsigned)p.B), block(BS);
-  if (MODE == kSliceGrad) grid = dim3((unsigned)((uint64_t)bp.nbricks * bp.cmax * p.B + (uint64_t)p.B * p.P));
+  if (MODE == kSliceGrad || MODE == kVolumeGrad) grid = dim3((unsigned)((uint64_t)bp.nbricks * bp.cmax * p.B + (uint64_t)p.B * p.P));
   if (ndim == 3) {
     if (interp) hipLaunchKernelGGL((k_adjoint_bricks<3, 1, MODE, BS>), grid, block, 0, s, p, bp);
     else hipLaunchKernelGGL((k_adjoint_bricks<3, 0, MODE, BS>), grid, block, 0, s, p, bp);
@@ -748,6 +751,16 @@ hipError_t launch_backproject_weights(const OpParams& p, int interp, hipStream_t
 uint64_t rotate_adjoint_blocks(const OpParams& p) {
   const BrickParams bp = brick_params<3>(p, true);
   return (uint64_t)p.B * (uint64_t)bp.nbricks * (uint64_t)bp.cmax;
+}
+
+// the rotation's adjoint and its pose gradients from a saved Jacobian in one
+// launch (as launch_backward_jac)
+hipError_t launch_rotate_backward_jac(const OpParams& p, int interp, hipStream_t s) {
+  return launch_adjoint<kVolumeGrad>(p, brick_params<3>(p, true), 3, interp, s);
+}
+
+uint64_t rotate_backward_jac_blocks(const OpParams& p) {
+  return rotate_adjoint_blocks(p) + (uint64_t)p.B * (uint64_t)p.P;
 }
 
 hipError_t launch_rotate_adjoint(const OpParams& p, int interp, hipStream_t s) {

@@ -390,6 +390,38 @@ tp_status tp_backward_3d_jac(const tp_c64* grad_out, const tp_c64* proj, const t
   return hip_status(tp::launch_backward_jac(p, interp, s));
 }
 
+tp_status tp_rotate_backward_3d_jac(const tp_c64* grad_out, const tp_c64* out, const tp_c64* jac, int64_t B,
+                                   int64_t P, int64_t N_out, const float* rot, int64_t B_rot, const float* shift,
+                                   int64_t B_shift, int64_t N, int interp, float oversampling, float cutoff,
+                                   tp_c64* vol_out, float* grad_rot, float* grad_shift, void* stream) {
+  if (!grad_out || !out || !jac || !vol_out) return TP_EINVAL;
+  if (!aligned8(grad_out) || !aligned8(out) || !aligned8(jac) || !aligned8(vol_out)) return TP_EINVAL;
+  if ((grad_rot && !aligned4(grad_rot)) || (grad_shift && !aligned4(grad_shift))) return TP_EINVAL;
+  if (grad_shift && B_shift != 1 && B_shift != B) return TP_EINVAL;
+  tp::OpParams p;
+  const Common c{B, N, P, N_out, B_rot, B_shift, interp, 3, oversampling, cutoff, rot, shift};
+  const tp_status st = rotate_fill(c, p);
+  if (st != TP_OK) return st;
+  if (N_out > tp::kMaxRotateAdjointOut || B > 65535 || tp::rotate_backward_jac_blocks(p) > kMaxBlocks)
+    return TP_EUNSUPPORTED;
+  p.img = reinterpret_cast<const float2*>(grad_out);
+  p.ref_out = reinterpret_cast<float2*>(vol_out);
+  p.proj = reinterpret_cast<const float2*>(out);
+  p.jac = reinterpret_cast<const float2*>(jac);
+  p.grad_rot = grad_rot;
+  p.grad_shift = grad_shift;
+  // with no shift tensor the shift is 0, but grad_shift keeps its B_shift rows
+  if (!shift && grad_shift) p.B_shift = (int)B_shift;
+  const hipStream_t s = (hipStream_t)stream;
+  if (tp::launch_zero(p.ref_out, ref_bytes_total(p), s) != hipSuccess) return TP_EHIP;
+  if (!grad_rot && !grad_shift) return hip_status(tp::launch_rotate_adjoint(p, interp, s));
+  if (grad_rot && tp::launch_zero(grad_rot, (size_t)p.B_rot * p.P * 9 * sizeof(float), s) != hipSuccess)
+    return TP_EHIP;
+  if (grad_shift && tp::launch_zero(grad_shift, (size_t)p.B_shift * p.P * 3 * sizeof(float), s) != hipSuccess)
+    return TP_EHIP;
+  return hip_status(tp::launch_rotate_backward_jac(p, interp, s));
+}
+
 tp_status tp_rotate_3d_jac(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot, int64_t P,
                            const float* shift, int64_t B_shift, int64_t N_out, int interp, float oversampling,
                            float cutoff, tp_c64* out, tp_c64* jac, void* stream) {

@@ -61,6 +61,9 @@ hipError_t launch_rotate_adjoint(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_rotate_jac(const OpParams& p, int interp, hipStream_t s);
 hipError_t launch_rotate_grad_jac(const OpParams& p, hipStream_t s);
 uint64_t rotate_adjoint_blocks(const OpParams& p);
+// the rotation's adjoint and its pose gradients from a saved Jacobian in one launch
+hipError_t launch_rotate_backward_jac(const OpParams& p, int interp, hipStream_t s);
+uint64_t rotate_backward_jac_blocks(const OpParams& p);
 constexpr int64_t kMaxRotateAdjointOut = 1023;  // 10-bit lattice offsets
 hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s);
 // 3D forward that saves the Jacobian of each output w.r.t. its sample point,

@@ -10,6 +10,7 @@
 // (as the central-slice kernels); a 256-lane workgroup covers 8 kx columns
 // of 16 (kz, ky) rows of one pose.  The adjoint is the brick adjoint of
 // tp_adjoint.hip run over volume lattices.
+#include "tp_gradjac.h"
 #include "tp_internal.h"
 #include "tp_stencil.h"
 
@@ -208,84 +209,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   float2 S, dS[3];
   rpair_grad_values<INTERP>(p, o, h, active, q, S, dS);
   if (!o.in) return;
-  if (active) {
+  // lane 0 of a pair stores the output and jac_x, lane 1 jac_y and jac_z
+  float2 a = h ? dS[1] : S, c = h ? dS[2] : dS[0];
+  if (active && p.shift) {
     const float2 ph = rphase(p, o);
-    S = cmul(ph, S);
-#pragma unroll
-    for (int j = 0; j < 3; ++j) dS[j] = cmul(ph, dS[j]);
+    a = cmul(ph, a);
+    c = cmul(ph, c);
   }
   const size_t vol = (size_t)p.No * p.No * p.Wo;
   const size_t pose = (size_t)o.b * p.P + o.n;
   float2* jac = p.jac_out + pose * 3 * vol + (o.idx - pose * vol);
-  if (h == 0) {
-    p.img_out[o.idx] = S;
-    jac[0] = dS[0];
-  } else {
-    jac[vol] = dS[1];
-    jac[2 * vol] = dS[2];
-  }
+  *(h ? jac + vol : p.img_out + o.idx) = a;
+  *(h ? jac + 2 * vol : jac) = c;
 }
 
-// Pose gradients from a saved Jacobian and rotation output:
-//   dL/dR[i][j] = os sum_k k_i Re(conj(G) jac_j),
-//   dL/ds_j     = (2 pi / No) sum_k k_j Im(conj(G) out),
-// the sums of k_rotate_grad.  One workgroup per (batch, pose) streams the
-// pose's outputs inside the sphere, sums in fp64 and adds its twelve totals
-// to the zeroed gradients.
+// Pose gradients from a saved Jacobian and rotation output: one workgroup
+// per (batch, pose) streams the pose's outputs inside the sphere.
 __global__ __launch_bounds__(kBlock) void k_rotate_grad_jac(OpParams p) {
-  constexpr int NV = 12;
   __shared__ double red[kBlock / 64][16];
-  const uint32_t bn = blockIdx.x;
-  const int n = (int)(bn % (uint32_t)p.P), b = (int)(bn / (uint32_t)p.P);
-  const uint32_t vol = (uint32_t)p.No * (uint32_t)p.No * (uint32_t)p.Wo;
-  const float2* G = p.img + (size_t)bn * vol;
-  const float2* Y = p.proj + (size_t)bn * vol;
-  const float2* J = p.jac + (size_t)bn * 3 * vol;
-  double acc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0;
-  for (uint32_t e = threadIdx.x; e < vol; e += kBlock) {
-    const uint32_t row = e / (uint32_t)p.Wo;
-    const int kx = (int)(e - row * (uint32_t)p.Wo);
-    const int ky = signed_row((int)(row % (uint32_t)p.No), p.No);
-    const int kz = signed_row((int)(row / (uint32_t)p.No), p.No);
-    if (p.cut2 >= 0 && (long long)kx * kx + (long long)ky * ky + (long long)kz * kz > p.cut2) continue;
-    const float2 g = G[e], y = Y[e], j0 = J[e], j1 = J[e + vol], j2 = J[e + 2 * vol];
-    const double a[3] = {(double)g.x * j0.x + (double)g.y * j0.y, (double)g.x * j1.x + (double)g.y * j1.y,
-                         (double)g.x * j2.x + (double)g.y * j2.y};
-    const double im = (double)g.x * y.y - (double)g.y * y.x;
-    const double k[3] = {(double)kx, (double)ky, (double)kz};
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-#pragma unroll
-      for (int j = 0; j < 3; ++j) acc[3 * i + j] = fma(k[i], a[j], acc[3 * i + j]);
-      acc[9 + i] = fma(k[i], im, acc[9 + i]);
-    }
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const double d0 = wave_sum8(acc), d1 = wave_sum8(acc + 8);
-  if ((lane & 7) == 0) {
-    red[wave][lane >> 3] = d0;
-    red[wave][8 + (lane >> 3)] = d1;
-  }
-  __syncthreads();
-  if (threadIdx.x < NV) {
-    const int i = threadIdx.x;
-    double v = 0.0;
-#pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) v += red[w][i];
-    if (v == 0.0) return;
-    if (i < 9) {
-      if (p.grad_rot) {
-        const size_t br = p.B_rot == 1 ? 0 : (size_t)b;
-        unsafeAtomicAdd(p.grad_rot + (br * p.P + n) * 9 + i, (float)((double)p.os * v));
-      }
-    } else if (p.grad_shift) {
-      const size_t bs = p.B_shift == 1 ? 0 : (size_t)b;
-      unsafeAtomicAdd(p.grad_shift + (bs * p.P + n) * 3 + (i - 9),
-                      (float)(6.283185307179586476925 * p.inv_no * v));
-    }
-  }
+  grad_jac_vol<kBlock>(p, blockIdx.x, red);
 }
 
 }  // namespace

@@ -557,6 +557,41 @@ def tp_rotate_grad_pose_jac(grad_out, out, jac, B_rot=1, B_shift=1, oversampling
     return gr, gs
 
 
+def tp_rotate_backward_3d_jac(grad_out, out, jac, rot, shift=None, N=None, interp="cubic", oversampling=1.0,
+                              cutoff=-1.0, want_rot=True, want_shift=True, B_shift=None):
+    """The backward of tp_rotate_3d_jac in one launch: (d_vol [B,N,N,N//2+1],
+    grad_rot [B_rot,P,3,3] or None, grad_shift [B_shift,P,3] or None), the
+    values of tp_rotate_backproject_3d and tp_rotate_grad_pose_jac."""
+    _need(grad_out, "grad_out", torch.complex64, 5)
+    _need(out, "out", torch.complex64, 5)
+    _need(jac, "jac", torch.complex64, 6)
+    B, P, n_out = out.shape[0], out.shape[1], out.shape[2]
+    if tuple(out.shape) != (B, P, n_out, n_out, n_out // 2 + 1) or grad_out.shape != out.shape:
+        raise ValueError(f"grad_out and out must be [B, P, n, n, n//2+1], got {tuple(grad_out.shape)}, "
+                         f"{tuple(out.shape)}")
+    if tuple(jac.shape) != (B, P, 3) + tuple(out.shape[2:]):
+        raise ValueError(f"jac must be [{B}, {P}, 3, {n_out}, {n_out}, {n_out // 2 + 1}], got {tuple(jac.shape)}")
+    if grad_out.device != out.device or jac.device != out.device:
+        raise ValueError("grad_out, out and jac must be on one device")
+    B_rot, P2, Bs = _rot_poses(rot, shift, B, out.device)
+    if P2 != P:
+        raise ValueError(f"rot has {P2} poses, out has {P}")
+    if shift is None:
+        Bs = 1 if B_shift is None else int(B_shift)
+    if N is None:
+        N = int(round(n_out * float(oversampling)))
+    dev = out.device
+    vol = torch.empty((B, N, N, N // 2 + 1), dtype=torch.complex64, device=dev)
+    gr = torch.empty((B_rot, P, 3, 3), dtype=torch.float32, device=dev) if want_rot else None
+    gs = torch.empty((Bs, P, 3), dtype=torch.float32, device=dev) if want_shift else None
+    st = _lib.lib().tp_rotate_backward_3d_jac(grad_out.data_ptr(), out.data_ptr(), jac.data_ptr(), B, P, n_out,
+                                              rot.data_ptr(), B_rot, _ptr(shift), Bs, int(N), _interp(interp),
+                                              float(oversampling), float(cutoff), vol.data_ptr(), _ptr(gr),
+                                              _ptr(gs), _stream(dev))
+    _lib.check(st, "tp_rotate_backward_3d_jac")
+    return vol, gr, gs
+
+
 class _Rotate(torch.autograd.Function):
     @staticmethod
     def forward(ctx, vol, rot, shift, n_out, interp, oversampling, cutoff, save_jacobian):
@@ -583,10 +618,15 @@ class _Rotate(torch.autograd.Function):
         if g.dtype != torch.complex64:
             g = g.to(torch.complex64)
         d_vol = d_rot = d_shift = None
-        if ctx.needs_input_grad[0]:
-            d_vol = tp_rotate_backproject_3d(g, rot, shift, vol.shape[1], interp, oversampling, cutoff)
         want_rot = ctx.needs_input_grad[1]
         want_shift = shift is not None and ctx.needs_input_grad[2]
+        if ctx.needs_input_grad[0] and (want_rot or want_shift) and ctx.has_jac:
+            # both gradients from one launch
+            d_vol, d_rot, d_shift = tp_rotate_backward_3d_jac(g, out, jac, rot, shift, vol.shape[1], interp,
+                                                              oversampling, cutoff, want_rot, want_shift)
+            return d_vol, d_rot, d_shift, None, None, None, None, None
+        if ctx.needs_input_grad[0]:
+            d_vol = tp_rotate_backproject_3d(g, rot, shift, vol.shape[1], interp, oversampling, cutoff)
         if (want_rot or want_shift) and ctx.has_jac:
             B_shift = shift.shape[0] if shift is not None else 1
             d_rot, d_shift = tp_rotate_grad_pose_jac(g, out, jac, rot.shape[0], B_shift, oversampling, cutoff,

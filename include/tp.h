@@ -340,6 +340,25 @@ tp_status tp_rotate_grad_pose_jac(const tp_c64* grad_out, const tp_c64* out, con
                                   int64_t P, int64_t N_out, int64_t B_rot, int64_t B_shift, float oversampling,
                                   float cutoff, float* grad_rot, float* grad_shift, void* stream);
 
+/*
+ * The backward of tp_rotate_3d_jac in one launch (the rotation's counterpart
+ * of tp_backward_3d_jac): the adjoint of tp_rotate_backproject_3d and the
+ * pose gradients of tp_rotate_grad_pose_jac, whose streaming reduction runs
+ * on workgroups after the adjoint's bricks.
+ *   grad_out   [B, P, N_out, N_out, N_out/2+1] complex64, input
+ *   out, jac   the outputs of tp_rotate_3d_jac for the same arguments, input
+ *   vol_out    [B, N, N, N/2+1] complex64, overwritten
+ *   grad_rot   [B_rot, P, 3, 3] float32, overwritten, or NULL
+ *   grad_shift [B_shift, P, 3] float32, overwritten, or NULL
+ * Other arguments and errors as tp_rotate_backproject_3d and
+ * tp_rotate_grad_pose_jac.
+ */
+tp_status tp_rotate_backward_3d_jac(const tp_c64* grad_out, const tp_c64* out, const tp_c64* jac,
+                                    int64_t B, int64_t P, int64_t N_out,
+                                    const float* rot, int64_t B_rot, const float* shift, int64_t B_shift,
+                                    int64_t N, int interp, float oversampling, float cutoff,
+                                    tp_c64* vol_out, float* grad_rot, float* grad_shift, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -207,6 +207,30 @@ def test_fused_backward_checks_arguments():
     assert call(a10=70000) == EUNSUP               # box
 
 
+def test_rotation_fused_backward_checks_arguments():
+    L = _lib.lib()
+    f = L.tp_rotate_backward_3d_jac
+    # grad_out, out, jac, B, P, N_out, rot, B_rot, shift, B_shift, N, interp, os, cutoff, vol_out,
+    # grad_rot, grad_shift, stream
+    ok = [FAKE, FAKE, FAKE, 1, 2, 16, FAKE, 1, None, 1, 16, 1, 1.0, -1.0, FAKE, FAKE, None, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a0=None) == EINVAL                 # no upstream gradient
+    assert call(a14=None) == EINVAL                # no volume
+    assert call(a2=FAKE_ODD) == EINVAL             # misaligned jac
+    assert call(a16=FAKE + 2) == EINVAL            # misaligned grad_shift
+    assert call(a7=3, a3=2) == EINVAL              # B_rot not in {1, B}
+    assert call(a16=FAKE, a9=3) == EINVAL          # B_shift not in {1, B} with grad_shift
+    assert call(a12=-1.0) == EINVAL                # oversampling
+    assert call(a13=math.nan) == EINVAL            # cutoff
+    assert call(a5=1024) == EUNSUP                 # 10-bit lattice offsets
+
+
 def test_rotation_jacobian_entry_points_check_arguments():
     L = _lib.lib()
     # vol, B, N, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, out, jac, stream

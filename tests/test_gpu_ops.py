@@ -210,6 +210,31 @@ def test_rotate_jac_and_grad_pose_jac_match_oracle(name):
     assert_parity(gs.cpu().numpy(), ds, f"rotate grad_shift (jac) {name}")
 
 
+@pytest.mark.parametrize("name", list(ROT_CASES))
+def test_rotate_backward_3d_jac_matches_oracle(name):
+    """The rotation's fused backward gives the oracle's adjoint and pose
+    gradients (the values of tp_rotate_backproject_3d and
+    tp_rotate_grad_pose_jac); with no gradient requested, the adjoint alone."""
+    from cryo_em_fourier_amd import tp_rotate_3d_jac, tp_rotate_backward_3d_jac
+
+    c = rot_case(name)
+    log(f"[rotate_backward_3d_jac] {name}")
+    R = to_dev(c["R"])
+    s = None if c["s"] is None else to_dev(c["s"])
+    args = (c["N"], c["interp"], float(c["os"]), float(c["cutoff"]))
+    out, jac = tp_rotate_3d_jac(to_dev(c["V"]), R, s, c["n_out"], c["interp"], float(c["os"]), float(c["cutoff"]))
+    G = to_dev(c["G"])
+    vol, gr, gs = tp_rotate_backward_3d_jac(G, out, jac, R, s, *args)
+    dV = oracle.rotate_backproject_3d(c["G"], c["R"], c["s"], *args)
+    dR, ds = oracle.rotate_grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(vol.cpu().numpy(), dV, f"rotate fused volume {name}")
+    assert_parity(gr.cpu().numpy(), dR, f"rotate fused grad_rot {name}")
+    assert_parity(gs.cpu().numpy(), ds, f"rotate fused grad_shift {name}")
+    vol, none_r, none_s = tp_rotate_backward_3d_jac(G, out, jac, R, s, *args, want_rot=False, want_shift=False)
+    assert none_r is None and none_s is None
+    assert_parity(vol.cpu().numpy(), dV, f"rotate fused volume without gradients {name}")
+
+
 @pytest.mark.parametrize("save_jacobian", [True, False])
 @pytest.mark.parametrize("name", ["cubic", "linear-odd-nocut", "batch", "cube"])
 def test_rotate_autograd_matches_oracle(name, save_jacobian):
