@@ -21,6 +21,11 @@
 // proportion to the poses expected to cross them (near the origin: all of
 // them); chunks of one brick merge with coalesced float atomics, unsplit
 // bricks are written with plain stores.
+//
+// The same kernel runs the weight volume (real weights, int32 slots), the
+// adjoint of the 3D -> 3D rotation (volume lattices), and the fused
+// backwards: the adjoint followed, in the same launch, by workgroups that
+// stream the pose gradients from a saved Jacobian (tp_gradjac.h).
 #include "tp_bricks.h"
 #include "tp_gradjac.h"
 #include "tp_internal.h"
