@@ -44,15 +44,16 @@ L2_PEAK_GBS = 8 * 16 * 128 * 2.4
 
 
 def kernel_source_digest() -> str:
-    """sha256 over the HIP sources with comments and blank lines removed:
-    counter data is valid only for this code (a comment edit keeps it)."""
+    """sha256 over the projector's HIP sources (not the peak probes) with
+    comments and blank lines removed: counter data is valid only for this
+    code (a comment edit keeps it)."""
     import hashlib
     import re
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "cryo_em_fourier_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
+        if f.endswith((".hip", ".h")) and f != "peaks.hip":
             with open(os.path.join(csrc, f), encoding="utf-8") as fh:
                 text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
             lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
@@ -346,6 +347,74 @@ def time_extras(L, _lib, torch, stream, Gd, Rd, R, dV, w, N, os_, B, P, reps=5):
                     ("rotate_backward_3d_jac", rot_bwd_jac)):
         out[name + "_ms"] = time_launches(torch, stream, f, reps)
     del Wd, wV, o3, g3, j3
+    return out
+
+
+def measure_peaks(torch, dev, stream, reps=5):
+    """Sustained peaks of this GPU from the probes of libtp_peaks.so (built
+    beside libtp.so): read GB/s from HBM (4 GiB buffer, beyond the Infinity
+    Cache), from the Infinity Cache (128 MiB, beyond L2) and from L2 (each
+    XCD re-reading its own 2 MiB), fp32 FMA TFLOP/s without packed math, and
+    LDS 64-bit atomic lane operations per second.  Best of `reps` launches
+    after one warmup, HIP events on the launch stream."""
+    import ctypes
+
+    from cryo_em_fourier_amd import build as _build
+
+    if not os.path.exists(_build.PEAKS_LIB):
+        raise RuntimeError(f"{_build.PEAKS_LIB} is missing: run python -m cryo_em_fourier_amd.build")
+    Lp = ctypes.CDLL(_build.PEAKS_LIB)
+    vp, u64, i64, ci = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int
+    Lp.tpk_read.argtypes = [vp, u64, i64, u64, ci, ci, vp, vp]
+    Lp.tpk_fma.argtypes = [i64, ci, vp, vp]
+    Lp.tpk_lds_add.argtypes = [i64, ci, vp, vp]
+    for f in (Lp.tpk_read, Lp.tpk_fma, Lp.tpk_lds_add, Lp.tpk_threads_per_block):
+        f.restype = ci
+    sh = stream.cuda_stream
+    threads = Lp.tpk_threads_per_block()
+    blocks = 256 * 8  # 8 workgroups per CU
+    sink = torch.zeros(4096, dtype=torch.int64, device=dev)
+
+    def best_ms(f):
+        f()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for k in range(reps):
+            f()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        return min(ev[k].elapsed_time(ev[k + 1]) for k in range(reps))
+
+    def check(st, name):
+        if st != 0:
+            raise RuntimeError(f"{name} failed ({st})")
+
+    # the best of a few buffer sizes and workgroup counts per level: the
+    # probes are sensitive to their shape, so the L2 figure is a measured
+    # lower bound of what 16-byte coalesced loads can pull from L2
+    out = {}
+    for name, sizes, passes_per_mib, regions in (("hbm_read_GBs", (4 << 30,), 0, 1),
+                                                 ("mall_read_GBs", (64 << 20, 128 << 20), 1024, 1),
+                                                 ("l2_read_GBs", (8 * (2 << 20), 8 * (3 << 20)), 1024, 8)):
+        best = 0.0
+        for nbytes in sizes:
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            n16 = nbytes // 16
+            passes = max(1, passes_per_mib * (1 << 20) // nbytes)
+            rot = (n16 // regions) * 5 // 11 + 1
+            for nb in (1024, 2048, 4096):
+                ms = best_ms(lambda: check(Lp.tpk_read(buf.data_ptr(), n16, passes, rot, regions, nb,
+                                                       sink.data_ptr(), sh), "tpk_read"))
+                best = max(best, nbytes * passes / (ms * 1e-3) / 1e9)
+            del buf
+        out[name] = round(best, 1)
+    iters = 20000
+    ms = best_ms(lambda: check(Lp.tpk_fma(iters, blocks, sink.data_ptr(), sh), "tpk_fma"))
+    out["fp32_fma_TFLOPs"] = round(16.0 * iters * blocks * threads / (ms * 1e-3) / 1e12, 2)
+    iters = 5000
+    ms = best_ms(lambda: check(Lp.tpk_lds_add(iters, blocks, sink.data_ptr(), sh), "tpk_lds_add"))
+    out["lds_add64_Glanes_per_s"] = round(8.0 * iters * blocks * threads / (ms * 1e-3) / 1e9, 1)
+    torch.cuda.synchronize()
     return out
 
 
@@ -695,6 +764,29 @@ def main():
     }
     roof_tap = {"bound": "l2", "peak": L2_PEAK_GBS, "unit": "GB/s",
                 "tap_bytes_per_launch": tap_bytes[dom], "kernels": tap_roof}
+    # the same fractions against this GPU's measured peaks (probes run after
+    # the timed steps); the adjoint's LDS adds against the measured LDS rate
+    peaks = measure_peaks(torch, dev, stream)
+    frac_measured = {}
+    for k in avg:
+        f = {"hbm_compulsory": round(hbm[k] / (avg[k] * 1e-3) / 1e9 / peaks["hbm_read_GBs"], 4)}
+        if tap_bytes[k]:
+            f["l2_tap"] = round(tap_bytes[k] / (avg[k] * 1e-3) / 1e9 / peaks["l2_read_GBs"], 4)
+        if k in ("backproject", "backward_jac"):
+            f["lds_tap_adds"] = round(units * taps / (avg[k] * 1e-3) / 1e9 / peaks["lds_add64_Glanes_per_s"], 4)
+        frac_measured[k] = f
+    peaks["fractions"] = frac_measured
+    # the tap-gather roofline of the whole step at the measured L2 peak, with
+    # the scope table's accounting: B_tap = 8 B x taps x in-cutoff outputs
+    # per call; a forward touches B_tap, a forward + backward 3 B_tap (a
+    # gather for the pose gradients and a scatter for the volume)
+    b_tap = units * taps * 8
+    roof_fwd = B * P / (b_tap / (peaks["l2_read_GBs"] * 1e9))
+    peaks["l2_tap_roofline"] = {
+        "fwd_proj_per_s": round(roof_fwd, 1), "fwd_frac": round(fwd_rate / roof_fwd, 4),
+        "fwd_bwd_proj_per_s": round(roof_fwd / 3, 1), "fwd_bwd_frac": round(fwd_bwd_rate / (roof_fwd / 3), 4),
+        "b_tap_per_call": b_tap,
+    }
     res = {
         "metric": METRIC,
         "value": round(fwd_bwd_rate, 1),
@@ -721,6 +813,7 @@ def main():
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "roofline_tap": roof_tap,
+        "peaks_measured": peaks,
         "traffic_all": traffic or None,
         "counter_calibration_copy_bytes": copy_bytes,
         "extras": extras,

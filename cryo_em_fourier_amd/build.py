@@ -1,4 +1,6 @@
-"""Build the projector's HIP library in-tree: cryo_em_fourier_amd/libtp.so.
+"""Build the projector's HIP library in-tree: cryo_em_fourier_amd/libtp.so,
+and the peak probes that bench.py measures roofline denominators with:
+cryo_em_fourier_amd/libtp_peaks.so (not part of the projector's path).
 
     python -m cryo_em_fourier_amd.build
 
@@ -16,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtp.so")
 SOURCES = ["tp_api.hip", "tp_kernels.hip", "tp_adjoint.hip", "tp_gather.hip", "tp_rotate.hip"]
+PEAKS_LIB = os.path.join(HERE, "libtp_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = os.environ.get("TP_OFFLOAD_ARCH", "gfx950")
 
 
@@ -40,9 +44,9 @@ def flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _compile(sources: list[str], out: str, verbose: bool) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc(), *flags(), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -50,8 +54,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"hipcc failed ({r.returncode})")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile both libraries; returns the projector library's path."""
+    _compile(PEAKS_SOURCES, PEAKS_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

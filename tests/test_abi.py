@@ -244,3 +244,28 @@ def test_rotation_jacobian_entry_points_check_arguments():
     assert L.tp_rotate_grad_pose_jac(FAKE, FAKE, FAKE, 1, 2, 16, 1, 1, -1.0, -1.0, FAKE, None, None) == EINVAL
     assert L.tp_rotate_grad_pose_jac(FAKE, FAKE, FAKE, 1, 2, 1024, 1, 1, 1.0, -1.0, FAKE, None, None) == EUNSUP
     assert L.tp_rotate_grad_pose_jac(FAKE, FAKE, FAKE, 1, 2, 16, 1, 1, 1.0, -1.0, None, None, None) == _lib.TP_OK
+
+
+def test_peak_probe_library_loads_and_checks_arguments():
+    """The roofline probes (libtp_peaks.so) export what include/tp_peaks.h
+    declares and reject invalid arguments before launching anything."""
+    from cryo_em_fourier_amd import build as _build
+
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tp_peaks.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(tpk_[a-z0-9_]+)\s*\(", src)))
+    assert names == ["tpk_fma", "tpk_lds_add", "tpk_read", "tpk_threads_per_block"]
+    L = ctypes.CDLL(_build.PEAKS_LIB)
+    for n in names:
+        assert hasattr(L, n), n
+    vp, u64, i64, ci = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int
+    L.tpk_read.argtypes = [vp, u64, i64, u64, ci, ci, vp, vp]
+    L.tpk_fma.argtypes = [i64, ci, vp, vp]
+    L.tpk_lds_add.argtypes = [i64, ci, vp, vp]
+    assert L.tpk_threads_per_block() == 256
+    assert L.tpk_read(None, 1024, 1, 0, 1, 8, FAKE, None) == -1        # no buffer
+    assert L.tpk_read(FAKE + 8, 1024, 1, 0, 1, 8, FAKE, None) == -1    # misaligned
+    assert L.tpk_read(FAKE, 1024, 1, 0, 3, 9, FAKE, None) == -1        # regions not 1 or 8
+    assert L.tpk_read(FAKE, 1020, 1, 0, 8, 8, FAKE, None) == -1        # n16 not a multiple of regions
+    assert L.tpk_read(FAKE, 1024, 0, 0, 1, 8, FAKE, None) == -1        # no pass
+    assert L.tpk_fma(0, 8, FAKE, None) == -1
+    assert L.tpk_lds_add(10, 0, FAKE, None) == -1
