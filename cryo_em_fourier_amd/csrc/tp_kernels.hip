@@ -70,17 +70,19 @@ __device__ __forceinline__ size_t img_index(const OpParams& p, const Out& o) {
   return ((size_t)((size_t)o.b * p.P + o.n) * p.No + o.iy) * p.Wo + o.kx;
 }
 
+// The one-lane-per-output kernels below run the 2D path only (the 3D
+// forwards and gradients use lane pairs).
 template <int NDIM, int INTERP>
 __device__ __forceinline__ float2 gather(rsrc_t rs, const RefGeom& g, const double* q, int xmin) {
-  if constexpr (NDIM == 3) return gather3<INTERP>(rs, g, q[0], q[1], q[2], xmin);
-  else return gather2<INTERP>(rs, g, q[0], q[1], xmin);
+  static_assert(NDIM == 2, "3D gathers use the lane-pair kernels");
+  return gather2<INTERP>(rs, g, q[0], q[1], xmin);
 }
 
 template <int NDIM, int INTERP>
 __device__ __forceinline__ void gather_grad(rsrc_t rs, const RefGeom& g, const double* q, int xmin,
                                             float2* out) {
-  if constexpr (NDIM == 3) gather3_grad<INTERP>(rs, g, q[0], q[1], q[2], xmin, out);
-  else gather2_grad<INTERP>(rs, g, q[0], q[1], xmin, out);
+  static_assert(NDIM == 2, "3D gathers use the lane-pair kernels");
+  gather2_grad<INTERP>(rs, g, q[0], q[1], xmin, out);
 }
 
 // ------------------------------------------------------------------ forward
@@ -405,18 +407,6 @@ __global__ __launch_bounds__(kBlock) void k_zero(uint32_t* ptr, size_t words) {
 }
 
 }  // namespace
-
-#define TP_DISPATCH(KERNEL, p, interp, s)                                                  \
-  do {                                                                                     \
-    const dim3 grid((p).nblocks), block(kBlock);                                           \
-    if ((p).ndim == 3) {                                                                   \
-      if (interp) hipLaunchKernelGGL((KERNEL<3, 1>), grid, block, 0, s, p);                 \
-      else hipLaunchKernelGGL((KERNEL<3, 0>), grid, block, 0, s, p);                        \
-    } else {                                                                               \
-      if (interp) hipLaunchKernelGGL((KERNEL<2, 1>), grid, block, 0, s, p);                 \
-      else hipLaunchKernelGGL((KERNEL<2, 0>), grid, block, 0, s, p);                        \
-    }                                                                                      \
-  } while (0)
 
 hipError_t launch_project(const OpParams& p, int interp, hipStream_t s) {
   const dim3 grid(p.nblocks), block(kBlock);

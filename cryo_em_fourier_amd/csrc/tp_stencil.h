@@ -66,41 +66,8 @@ __device__ __forceinline__ void setup_yz(const RefGeom& g, double q, uint32_t st
 
 // ---------------------------------------------------------------- gather
 
-// Sum over taps with x >= xmin of w * V[t] at q (3D).
-template <int INTERP>
-__device__ __forceinline__ float2 gather3(rsrc_t rs, const RefGeom& g, double qx, double qy,
-                                          double qz, int xmin) {
-  constexpr int T = Kern<INTERP>::T;
-  float wx[T], wy[T], wz[T];
-  uint32_t yb[T], zb[T];
-  const uint32_t xo = setup_x<INTERP, false>(g, qx, xmin, wx, nullptr);
-  setup_yz<INTERP, false>(g, qy, g.row, wy, nullptr, yb);
-  setup_yz<INTERP, false>(g, qz, g.plane, wz, nullptr, zb);
-#pragma unroll
-  for (int d = 0; d < T; ++d) yb[d] = yb[d] == kBig ? kBig : yb[d] + xo;
-  float2 acc = make_float2(0.f, 0.f);
-#pragma unroll
-  for (int dz = 0; dz < T; ++dz) {
-    float2 pl = make_float2(0.f, 0.f);
-#pragma unroll
-    for (int dy = 0; dy < T; ++dy) {
-      const uint32_t ro = zb[dz] + yb[dy];
-      float2 r = make_float2(0.f, 0.f);
-#pragma unroll
-      for (int dx = 0; dx < T; ++dx) {
-        const float2 v = load_c64(rs, ro + 8u * dx);
-        r.x = fmaf(wx[dx], v.x, r.x);
-        r.y = fmaf(wx[dx], v.y, r.y);
-      }
-      pl.x = fmaf(wy[dy], r.x, pl.x);
-      pl.y = fmaf(wy[dy], r.y, pl.y);
-    }
-    acc.x = fmaf(wz[dz], pl.x, acc.x);
-    acc.y = fmaf(wz[dz], pl.y, acc.y);
-  }
-  return acc;
-}
-
+// Sum over taps with x >= xmin of w * V[t] at q (2D; the 3D forwards use
+// the lane-pair form below).
 template <int INTERP>
 __device__ __forceinline__ float2 gather2(rsrc_t rs, const RefGeom& g, double qx, double qy,
                                           int xmin) {
@@ -126,56 +93,8 @@ __device__ __forceinline__ float2 gather2(rsrc_t rs, const RefGeom& g, double qx
   return acc;
 }
 
-// Value and gradient w.r.t. the sample point: out[0] = S, out[1 + j] = dS/dq_j.
-template <int INTERP>
-__device__ __forceinline__ void gather3_grad(rsrc_t rs, const RefGeom& g, double qx, double qy,
-                                             double qz, int xmin, float2* out) {
-  constexpr int T = Kern<INTERP>::T;
-  float wx[T], wy[T], wz[T], dwx[T], dwy[T], dwz[T];
-  uint32_t yb[T], zb[T];
-  const uint32_t xo = setup_x<INTERP, true>(g, qx, xmin, wx, dwx);
-  setup_yz<INTERP, true>(g, qy, g.row, wy, dwy, yb);
-  setup_yz<INTERP, true>(g, qz, g.plane, wz, dwz, zb);
-#pragma unroll
-  for (int d = 0; d < T; ++d) yb[d] = yb[d] == kBig ? kBig : yb[d] + xo;
-  float2 s = make_float2(0.f, 0.f), sx = s, sy = s, sz = s;
-#pragma unroll
-  for (int dz = 0; dz < T; ++dz) {
-    float2 p0 = make_float2(0.f, 0.f), px = p0, py = p0;  // plane sums: w, dx-w, dy-w
-#pragma unroll
-    for (int dy = 0; dy < T; ++dy) {
-      const uint32_t ro = zb[dz] + yb[dy];
-      float2 r = make_float2(0.f, 0.f), rd = r;
-#pragma unroll
-      for (int dx = 0; dx < T; ++dx) {
-        const float2 v = load_c64(rs, ro + 8u * dx);
-        r.x = fmaf(wx[dx], v.x, r.x);
-        r.y = fmaf(wx[dx], v.y, r.y);
-        rd.x = fmaf(dwx[dx], v.x, rd.x);
-        rd.y = fmaf(dwx[dx], v.y, rd.y);
-      }
-      p0.x = fmaf(wy[dy], r.x, p0.x);
-      p0.y = fmaf(wy[dy], r.y, p0.y);
-      px.x = fmaf(wy[dy], rd.x, px.x);
-      px.y = fmaf(wy[dy], rd.y, px.y);
-      py.x = fmaf(dwy[dy], r.x, py.x);
-      py.y = fmaf(dwy[dy], r.y, py.y);
-    }
-    s.x = fmaf(wz[dz], p0.x, s.x);
-    s.y = fmaf(wz[dz], p0.y, s.y);
-    sx.x = fmaf(wz[dz], px.x, sx.x);
-    sx.y = fmaf(wz[dz], px.y, sx.y);
-    sy.x = fmaf(wz[dz], py.x, sy.x);
-    sy.y = fmaf(wz[dz], py.y, sy.y);
-    sz.x = fmaf(dwz[dz], p0.x, sz.x);
-    sz.y = fmaf(dwz[dz], p0.y, sz.y);
-  }
-  out[0] = s;
-  out[1] = sx;
-  out[2] = sy;
-  out[3] = sz;
-}
-
+// Value and gradient w.r.t. the sample point (2D): out[0] = S, out[1 + j] =
+// dS/dq_j.
 template <int INTERP>
 __device__ __forceinline__ void gather2_grad(rsrc_t rs, const RefGeom& g, double qx, double qy,
                                              int xmin, float2* out) {
