@@ -50,6 +50,8 @@ def case3d(name):
         "adv-cubic":     (32, 32, 1, 8, 1, 1, CUBIC, 1.0, -1.0, "real", "adv"),
         "adv-linear":    (32, 32, 1, 8, 1, 0, LINEAR, 1.0, -1.0, "cplx", "adv"),
         "ragged":        (40, 37, 1, 4, 1, 1, CUBIC, 40 / 37, 18.0, "cplx", "so3"),
+        "mixed-rot":     (24, 24, 2, 4, 2, 1, CUBIC, 1.0, 11.0, "cplx", "so3"),
+        "mixed-shift":   (22, 20, 2, 3, 1, 2, LINEAR, 1.1, 9.0, "cplx", "so3"),
     }[name]
     N, n_out, B, P, B_rot, B_shift, interp, os_, cutoff, vk, pk = spec
     if vk == "c1":
@@ -73,7 +75,7 @@ def case3d(name):
 
 
 CASES3 = ["c1", "c1-cubic", "odd-nocut", "os2", "os1.5-linear", "batch", "batch-bcast",
-          "adv-cubic", "adv-linear", "ragged"]
+          "adv-cubic", "adv-linear", "ragged", "mixed-rot", "mixed-shift"]
 
 
 def _dev(c):
