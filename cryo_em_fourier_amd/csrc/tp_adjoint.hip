@@ -685,7 +685,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>
 }  // namespace
 
 template <int NDIM>
-static BrickParams brick_params(const OpParams& p, bool vol = false) {
+static BrickParams brick_params(const OpParams& p, bool vol = false, int pmax = 256) {
   using BR = Brick<NDIM>;
   BrickParams bp{};
   bp.nb[0] = (p.N / 2 + 1 + BR::X - 1) / BR::X;
@@ -693,7 +693,7 @@ static BrickParams brick_params(const OpParams& p, bool vol = false) {
   bp.nb[2] = NDIM == 3 ? (p.N + BR::Z - 1) / BR::Z : 1;
   bp.nbricks = bp.nb[0] * bp.nb[1] * bp.nb[2];
   // a volume lattice sends every pose to every brick: small chunks
-  bp.pmax = vol ? 16 : 256;
+  bp.pmax = vol ? 16 : pmax;
   const int c = (p.P + bp.pmax - 1) / bp.pmax;
   bp.cmax = c < 1 ? 1 : (c > 64 ? 64 : c);
   return bp;
@@ -741,7 +741,13 @@ hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s) {
 // workgroups fill the adjoint's tail).  Spreading them among the bricks
 // instead was slower (7.2 to 8.8 ms): they take the LDS-bound bricks' slots.
 hipError_t launch_backward_jac(const OpParams& p, int interp, hipStream_t s) {
-  return launch_adjoint<kSliceGrad>(p, brick_params<3>(p), 3, interp, s);
+  // with many bricks (boxes from 256), larger pose chunks than the plain
+  // adjoint's: fewer, longer brick workgroups, whose uneven end the gradient
+  // workgroups fill (c4: 6.01 ms with 512 poses per chunk, 6.10 with 256,
+  // 6.2 with 768; c5 16.35 against 16.66; a box of 128 has 320 bricks and
+  // needs the smaller chunks to fill the GPU: 1.23 against 0.80 ms)
+  const BrickParams bp = brick_params<3>(p);
+  return launch_adjoint<kSliceGrad>(p, bp.nbricks >= 2048 ? brick_params<3>(p, false, 512) : bp, 3, interp, s);
 }
 
 uint64_t backward_jac_blocks(const OpParams& p) {
