@@ -738,7 +738,7 @@ hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s) {
 }
 
 // The adjoint and the pose gradients from a saved Jacobian in one launch:
-// measured at c4, 6.2 ms against 6.7 ms for the two launches (the gradient
+// measured at c4, 6.0 ms against 6.65 ms for the two launches (the gradient
 // workgroups fill the adjoint's tail).  Spreading them among the bricks
 // instead was slower (7.2 to 8.8 ms): they take the LDS-bound bricks' slots.
 hipError_t launch_backward_jac(const OpParams& p, int interp, hipStream_t s) {
