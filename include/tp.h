@@ -299,8 +299,10 @@ tp_status tp_grad_pose_jac(const tp_c64* grad_out, const tp_c64* proj, const tp_
  *   proj, jac  the outputs of tp_project_3d_jac for the same arguments, input
  *   vol_out    [B, N, N, N/2+1] complex64, overwritten: tp_backproject_3d's
  *   grad_rot   [B_rot, P, 3, 3] float32, overwritten (last row 0), or NULL
- *   grad_shift [B_shift, P, 2] float32, overwritten, or NULL
- * Other arguments and errors as tp_backproject_3d and tp_grad_pose_jac.
+ *   grad_shift [B_shift, P, 2] float32, overwritten, or NULL (with shift ==
+ *              NULL the shift is 0 and grad_shift still has B_shift rows)
+ * With both gradients NULL this is tp_backproject_3d.  Other arguments and
+ * errors as tp_backproject_3d and tp_grad_pose_jac.
  */
 tp_status tp_backward_3d_jac(const tp_c64* grad_out, const tp_c64* proj, const tp_c64* jac,
                              int64_t B, int64_t P, int64_t N_out,
@@ -349,8 +351,10 @@ tp_status tp_rotate_grad_pose_jac(const tp_c64* grad_out, const tp_c64* out, con
  *   out, jac   the outputs of tp_rotate_3d_jac for the same arguments, input
  *   vol_out    [B, N, N, N/2+1] complex64, overwritten
  *   grad_rot   [B_rot, P, 3, 3] float32, overwritten, or NULL
- *   grad_shift [B_shift, P, 3] float32, overwritten, or NULL
- * Other arguments and errors as tp_rotate_backproject_3d and
+ *   grad_shift [B_shift, P, 3] float32, overwritten, or NULL (with shift ==
+ *              NULL the shift is 0 and grad_shift still has B_shift rows)
+ * With both gradients NULL this is tp_rotate_backproject_3d.  Other
+ * arguments and errors as tp_rotate_backproject_3d and
  * tp_rotate_grad_pose_jac.
  */
 tp_status tp_rotate_backward_3d_jac(const tp_c64* grad_out, const tp_c64* out, const tp_c64* jac,
