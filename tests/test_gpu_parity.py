@@ -413,15 +413,35 @@ def test_fused_backward_edge_cases():
 
 
 def test_nonfinite_rotation_reads_zero():
-    from cryo_em_fourier_amd import tp_project_3d
+    """Poses whose sample points are beyond 2^30 or not finite read 0 and add
+    nothing: forward, adjoint and pose gradients of every path, fused
+    included, against the oracle (whose gradients for them are 0)."""
+    from cryo_em_fourier_amd import (tp_backproject_3d, tp_backward_3d_jac, tp_grad_pose, tp_grad_pose_jac,
+                                     tp_project_3d, tp_project_3d_jac)
 
     c = case3d("odd-nocut")
     R = np.stack([np.eye(3) * 1e12, np.full((3, 3), np.nan), np.eye(3)]).astype(np.float32)[None]
-    V = to_dev(c["V"])
-    out = tp_project_3d(V, to_dev(R), None, 12, CUBIC, 1.0, -1.0).cpu().numpy()
+    V, Rd = to_dev(c["V"]), to_dev(R)
+    out = tp_project_3d(V, Rd, None, 12, CUBIC, 1.0, -1.0).cpu().numpy()
     ref = oracle.project(c["V"], R, None, 12, CUBIC, 1.0, -1.0)
     assert np.all(np.isfinite(out))
     assert_parity(out, ref, "non-finite rotations")
+    G = complex_normal(np.random.default_rng(5), (1, 3, 12, 7))
+    Gd = to_dev(G)
+    A = oracle.backproject(G, R, None, c["N"], CUBIC, 1.0, -1.0)
+    dR, _ = oracle.grad_pose(c["V"], G, R, None, 12, CUBIC, 1.0, -1.0)
+    assert_parity(tp_backproject_3d(Gd, Rd, None, c["N"], CUBIC, 1.0, -1.0).cpu().numpy(), A, "adjoint, non-finite")
+    gr, _ = tp_grad_pose(V, Gd, Rd, None, CUBIC, 1.0, -1.0)
+    assert_parity(gr.cpu().numpy(), dR, "grad_rot, non-finite")
+    out_j, jac = tp_project_3d_jac(V, Rd, None, 12, CUBIC, 1.0, -1.0)
+    assert np.all(np.isfinite(jac.cpu().numpy()))
+    assert_parity(out_j.cpu().numpy(), ref, "jac forward, non-finite")
+    gr, _ = tp_grad_pose_jac(Gd, out_j, jac, 1, 1, 1.0, -1.0)
+    assert_parity(gr.cpu().numpy(), dR, "grad_rot (jac), non-finite")
+    vol, gr, gs = tp_backward_3d_jac(Gd, out_j, jac, Rd, None, c["N"], CUBIC, 1.0, -1.0)
+    assert_parity(vol.cpu().numpy(), A, "fused volume, non-finite")
+    assert_parity(gr.cpu().numpy(), dR, "fused grad_rot, non-finite")
+    assert not gr.cpu().numpy()[0, :2].any() and np.all(np.isfinite(gs.cpu().numpy()))
 
 
 @pytest.mark.parametrize("N", [8, 9, 16])
