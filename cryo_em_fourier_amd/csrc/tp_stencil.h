@@ -52,16 +52,39 @@ __device__ __forceinline__ uint32_t setup_x(const RefGeom& g, double q, int xmin
   return (uint32_t)start * 8u;
 }
 
-// y or z axis: weights and byte offsets (kBig for taps outside the stored range).
+// y or z axis: weights and byte offsets (kBig for taps outside the stored
+// range); returns the first tap's coordinate.
 template <int INTERP, bool GRAD>
-__device__ __forceinline__ void setup_yz(const RefGeom& g, double q, uint32_t stride, float* w,
-                                         float* dw, uint32_t* off) {
+__device__ __forceinline__ int setup_yz(const RefGeom& g, double q, uint32_t stride, float* w,
+                                        float* dw, uint32_t* off) {
   using K = Kern<INTERP>;
   const AxisPos a = axis_pos(q, K::OFF);
   K::w(a.f, w);
   if (GRAD) K::dw(a.f, dw);
 #pragma unroll
   for (int d = 0; d < K::T; ++d) off[d] = axis_off(a.x0 + d, g, stride);
+  return a.x0;
+}
+
+// Reorder the T taps of an axis (consecutive coordinates from `first`) so
+// that entry t holds the tap whose coordinate is congruent to t modulo T.
+// When every lane of a wave walks its rows in this order, the lanes of
+// neighbouring outputs, whose stencils overlap, load the same row of the
+// reference in the same instruction: one load touches fewer distinct cache
+// sectors, and the L1's sector rate is what bounds the 3D gathers.  The sum
+// over the taps is the same up to rounding order.
+template <int T, typename V>
+__device__ __forceinline__ void by_residue(V* a, int first) {
+  const int s = (-first) & (T - 1);  // entry t <- a[(t + s) mod T]
+#pragma unroll
+  for (int b = 1; b < T; b <<= 1) {
+    const bool on = (s & b) != 0;
+    V r[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) r[t] = a[(t + b) & (T - 1)];
+#pragma unroll
+    for (int t = 0; t < T; ++t) a[t] = on ? r[t] : a[t];
+  }
 }
 
 // ---------------------------------------------------------------- gather
@@ -141,8 +164,12 @@ __device__ __forceinline__ float2 gather3_half(rsrc_t rs, const RefGeom& g, doub
   float wx[T], wy[T], wz[T];
   uint32_t yb[T], zb[T];
   const uint32_t xo = setup_x<INTERP, false>(g, qx, xmin, wx, nullptr) + 8u * H * h;
-  setup_yz<INTERP, false>(g, qy, g.row, wy, nullptr, yb);
-  setup_yz<INTERP, false>(g, qz, g.plane, wz, nullptr, zb);
+  const int y0 = setup_yz<INTERP, false>(g, qy, g.row, wy, nullptr, yb);
+  const int z0 = setup_yz<INTERP, false>(g, qz, g.plane, wz, nullptr, zb);
+  by_residue<T>(wy, y0);
+  by_residue<T>(yb, y0);
+  by_residue<T>(wz, z0);
+  by_residue<T>(zb, z0);
   // the lane's x weights folded into the y weights: two multiply-adds per
   // component and row
   float cy[T][H];
@@ -184,8 +211,14 @@ __device__ __forceinline__ void gather3_grad_half(rsrc_t rs, const RefGeom& g, d
   float wx[T], wy[T], wz[T], dwx[T], dwy[T], dwz[T];
   uint32_t yb[T], zb[T];
   const uint32_t xo = setup_x<INTERP, true>(g, qx, xmin, wx, dwx) + 8u * H * h;
-  setup_yz<INTERP, true>(g, qy, g.row, wy, dwy, yb);
-  setup_yz<INTERP, true>(g, qz, g.plane, wz, dwz, zb);
+  const int y0 = setup_yz<INTERP, true>(g, qy, g.row, wy, dwy, yb);
+  const int z0 = setup_yz<INTERP, true>(g, qz, g.plane, wz, dwz, zb);
+  by_residue<T>(wy, y0);
+  by_residue<T>(dwy, y0);
+  by_residue<T>(yb, y0);
+  by_residue<T>(wz, z0);
+  by_residue<T>(dwz, z0);
+  by_residue<T>(zb, z0);
   float wh[H], dh[H];
 #pragma unroll
   for (int d = 0; d < H; ++d) {
