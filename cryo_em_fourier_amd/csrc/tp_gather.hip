@@ -15,8 +15,8 @@
 // Gathering from LDS avoids the vector L1's per-cache-line cost of scattered
 // 64-tap stencils, but pays for the tile loads and the enumeration per (pose,
 // brick).  It wins where many poses cross a brick and the lattice is dense
-// (measured: box 256 and 320 cubic at oversampling 1; the per-output kernel
-// wins at oversampling 2 and at box 128), and the host picks it only there.
+// (measured: box 320 cubic at oversampling 1; the per-output kernel wins at
+// box 256 and 128 and at oversampling 2), and the host picks it only there.
 #include "tp_bricks.h"
 #include "tp_internal.h"
 
@@ -436,7 +436,7 @@ hipError_t launch_grad(const OpParams& p, hipStream_t s) {
 }  // namespace
 
 bool use_grad_bricks(const OpParams& p, int interp) {
-  if (!(p.ndim == 3 && p.os <= 1.25f && p.N >= 192 && p.P >= 256)) return false;
+  if (!(p.ndim == 3 && p.os <= 1.25f && p.N >= 288 && p.P >= 256)) return false;
   if (p.No > kMaxBrickOut || p.B > 65535) return false;
   const BrickParams bp = interp ? gather_params<1>(p) : gather_params<0>(p);
   return (uint64_t)p.B * (uint64_t)bp.nbricks * (uint64_t)bp.cmax <= 0x7FFFFFFFull;

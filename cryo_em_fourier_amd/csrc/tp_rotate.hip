@@ -139,8 +139,10 @@ __device__ __forceinline__ void rpair_grad_values(const OpParams& p, const ROut&
 // Pose gradients of L = Re sum conj(G) rotate(V): dL/dR[i][j] =
 // os sum k_i Re(conj(G) phase dS/dp_j) (all three rows), dL/ds_j =
 // sum (2 pi k_j / N_out) Im(conj(G) phase S).
+// (4 waves per SIMD: measured 7 % faster at box 64 than the 161 registers
+// the compiler picks on its own)
 template <int INTERP>
-__global__ __launch_bounds__(kBlock) void k_rotate_grad(OpParams p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_rotate_grad(OpParams p) {
   constexpr int NV = 12;
   __shared__ double red[kBlock / 64][16];
   const ROut o = rlocate(p);

@@ -262,7 +262,7 @@ def test_largest_adjoint_output_box():
 
 @pytest.mark.parametrize("interp,os_,batch", [(1, 1.0, 1), (0, 1.0, 1), (1, 1.2, 2), (0, 1.25, 1)])
 def test_grad_bricks_against_oracle(interp, os_, batch):
-    """Box >= 192, >= 256 poses, oversampling <= 1.25: the sizes where the
+    """Box >= 288, >= 256 poses, oversampling <= 1.25: the sizes where the
     gradients run as the LDS brick gather.  Every pose is processed; the
     upstream gradient is nonzero on a sample that includes on-grid and
     x = 0-plane poses (linear kinks at integer coordinates: both sides take the
@@ -272,7 +272,7 @@ def test_grad_bricks_against_oracle(interp, os_, batch):
     from cryo_em_fourier_amd import tp_grad_pose
     from test_gpu_parity import adversarial_rotations
 
-    N, P = 200, 260
+    N, P = 288, 260
     n_out = int(round(N / os_))
     rng = np.random.default_rng(200 + interp + 10 * batch)
     V = np.stack([synth.rfft_spectrum(synth.blob_volume(rng, int(N / os_) if os_ != 1.0 else N, 60), 3,
