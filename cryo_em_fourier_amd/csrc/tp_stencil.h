@@ -156,6 +156,35 @@ __device__ __forceinline__ void gather2_grad(rsrc_t rs, const RefGeom& g, double
 // Two lanes share one output: lane half h reads x-taps [h*T/2, (h+1)*T/2) of
 // every row with one load, so a load instruction covers the whole row of 32
 // outputs in adjacent lanes (one cache line each) instead of half-rows of 64.
+// In the value gather the y and z axis setups are split over the pair: the
+// even lane sets up y, the odd lane z, and every lane then reads y from the
+// even lane of its pair and z from the odd one (DPP quad permutes 0,0,2,2 and
+// 1,1,3,3).  Both lanes of a pair take the same branches, so the lanes read
+// are always active.  (The gradient gathers keep a full setup per lane: with
+// the derivative weights the exchange spills at 128 registers.)
+
+__device__ __forceinline__ int from_even_lane(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xA0, 0xF, 0xF, false); }
+__device__ __forceinline__ int from_odd_lane(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xF5, 0xF, 0xF, false); }
+
+// The pair's y and z weights and row offsets (in residue order, see
+// by_residue): each lane sets up one axis.
+template <int INTERP>
+__device__ __forceinline__ void setup_yz_pair(const RefGeom& g, double qy, double qz, int h, float* wy,
+                                              uint32_t* yb, float* wz, uint32_t* zb) {
+  constexpr int T = Kern<INTERP>::T;
+  float w[T];
+  uint32_t off[T];
+  const int first = setup_yz<INTERP, false>(g, h ? qz : qy, h ? g.plane : g.row, w, nullptr, off);
+  by_residue<T>(w, first);
+  by_residue<T>(off, first);
+#pragma unroll
+  for (int d = 0; d < T; ++d) {
+    wy[d] = __int_as_float(from_even_lane(__float_as_int(w[d])));
+    wz[d] = __int_as_float(from_odd_lane(__float_as_int(w[d])));
+    yb[d] = (uint32_t)from_even_lane((int)off[d]);
+    zb[d] = (uint32_t)from_odd_lane((int)off[d]);
+  }
+}
 
 template <int INTERP>
 __device__ __forceinline__ float2 gather3_half(rsrc_t rs, const RefGeom& g, double qx, double qy,
@@ -164,12 +193,7 @@ __device__ __forceinline__ float2 gather3_half(rsrc_t rs, const RefGeom& g, doub
   float wx[T], wy[T], wz[T];
   uint32_t yb[T], zb[T];
   const uint32_t xo = setup_x<INTERP, false>(g, qx, xmin, wx, nullptr) + 8u * H * h;
-  const int y0 = setup_yz<INTERP, false>(g, qy, g.row, wy, nullptr, yb);
-  const int z0 = setup_yz<INTERP, false>(g, qz, g.plane, wz, nullptr, zb);
-  by_residue<T>(wy, y0);
-  by_residue<T>(yb, y0);
-  by_residue<T>(wz, z0);
-  by_residue<T>(zb, z0);
+  setup_yz_pair<INTERP>(g, qy, qz, h, wy, yb, wz, zb);
   // the lane's x weights folded into the y weights: two multiply-adds per
   // component and row
   float cy[T][H];
