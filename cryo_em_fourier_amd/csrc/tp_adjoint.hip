@@ -43,10 +43,17 @@ constexpr int kGroupMax = 16;       // poses per fixed-point group
 // sparse ones (oversampling above 1.25), whose bricks hold few hits.  The hit
 // lists are sized so that the workgroups fit a CU's LDS beside the
 // accumulator.
-template <int BS>
+// EXCLZ (3D, 512 threads): z ownership is exclusive.  A lattice point is
+// spread by the brick that holds its first z tap only, and the taps past the
+// brick's last plane go to kGuard guard planes that are added to the next
+// brick's first planes in global memory.  A stencil then crosses brick faces
+// in x and y only, so each brick spreads about 16 % fewer lattice points.
+template <int NDIM, int BS>
 struct AdjShape {
-  static constexpr int HIT_CAP = BS == 512 ? 8192 : 2560;  // lattice points per group slice
-  static constexpr int PER_THREAD = kVox / BS;             // brick voxels per thread
+  static constexpr bool EXCLZ = NDIM == 3 && BS == 512;
+  static constexpr int HIT_CAP = BS == 512 ? (EXCLZ ? 7168 : 8192) : 2560;  // lattice points per group slice
+  static constexpr int NVOX = kVox + (EXCLZ ? 3 * 256 : 0);  // brick voxels, guard planes included
+  static constexpr int PER_THREAD = (NVOX + BS - 1) / BS;     // brick voxels per thread
   static constexpr int WAVES_PER_EU = BS == 512 ? 4 : 3;
 };
 constexpr int kPrefetch = 2;        // hits whose G values a thread loads at once
@@ -79,11 +86,12 @@ template <> struct Brick<2> { static constexpr int X = 64, Y = 64, Z = 1; };
 // stride and a z-plane stride of 5 mod 16 (padded) keep taps that differ in
 // y or z only off each other's banks.
 constexpr int kGuard = 3;  // the cubic stencil reaches 3 voxels past its first tap
-template <int NDIM>
+// ZG guard planes follow the brick's last plane (exclusive z ownership).
+template <int NDIM, int ZG = 0>
 struct AccLayout {
   static constexpr int S = Brick<NDIM>::X + kGuard;
   static constexpr int PZ = NDIM == 3 ? Brick<NDIM>::Y * S + ((5 - Brick<NDIM>::Y * S % 16) + 16) % 16 : 0;
-  static constexpr int W = (NDIM == 3 ? Brick<NDIM>::Z * PZ : Brick<NDIM>::Y * S) + kGuard;
+  static constexpr int W = (NDIM == 3 ? (Brick<NDIM>::Z + ZG) * PZ : Brick<NDIM>::Y * S) + kGuard;
 };
 template <int NDIM>
 __device__ __forceinline__ int acc_word(int x, int y, int z) {
@@ -112,6 +120,9 @@ struct BrickPos {
   int b;            // batch entry
   int x0, y0, z0;   // first voxel (x from 0, y and z signed)
   int x1, y1, z1;   // last voxel (inclusive, clipped to the stored range)
+  int zlim;         // last z plane that taps are spread to (z1, or with
+                    // exclusive z ownership its guard planes in range)
+  bool zbottom;     // the lowest brick of the stored z range
   int n0, n1;       // pose range of this workgroup
   bool chunked;     // merged with atomics
   bool valid;
@@ -159,6 +170,8 @@ __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams&
   } else {
     r.z0 = r.z1 = 0;
   }
+  r.zlim = r.z1;
+  r.zbottom = r.z0 == (NDIM == 3 ? lo : 0);
   // every pose of a volume lattice reaches every brick inside its sphere
   const int nch = VOL ? bp.cmax : brick_chunks<NDIM>(p, bp, r.x0, r.y0, r.z0);
   r.valid = ch < nch && r.b < p.B;
@@ -170,11 +183,15 @@ __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams&
 
 // Sample points whose stencil can reach the brick lie in the brick widened
 // by the stencil reach: [x0 - r, x1 + r) per axis (r = 2 cubic, 1 linear);
-// any point outside has all its taps outside the brick.
-template <int NDIM, int INTERP>
+// any point outside has all its taps outside the brick.  With exclusive z
+// ownership the brick takes in z only the points whose first tap lies in
+// [z0, z1], q_z in [z0 - OFF, z1 + r), except the lowest brick, which also
+// takes those whose first tap lies below the stored range.
+template <int NDIM, int INTERP, bool EXCLZ = false>
 __device__ __forceinline__ Box reach_box(const BrickPos& br) {
   constexpr double reach = INTERP ? 2.0 : 1.0;
   Box bx = {{br.x0 - reach, br.y0 - reach, br.z0 - reach}, {br.x1 + reach, br.y1 + reach, br.z1 + reach}};
+  if (EXCLZ && !br.zbottom) bx.lo[2] = (double)(br.z0 - Kern<INTERP>::OFF);
   if (NDIM == 2) bx.lo[2] = bx.hi[2] = 0.0;
   return bx;
 }
@@ -455,7 +472,7 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
 #pragma unroll
   for (int dz = 0; dz < (NDIM == 3 ? T : 1); ++dz) {
     const int tz = z0 + dz;
-    if (NDIM == 3 && (tz < br.z0 || tz > br.z1)) continue;
+    if (NDIM == 3 && (tz < br.z0 || tz > br.zlim)) continue;
 #pragma unroll
     for (int dy = 0; dy < T; ++dy) {
       const int ty = ay.x0 + dy;
@@ -476,17 +493,20 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
 // per group), kSliceGrad / kVolumeGrad (kSlice / kVolume and the pose
 // gradients from a Jacobian).
 template <int NDIM, int INTERP, int MODE, int BS>
-__global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>::WAVES_PER_EU))) void k_adjoint_bricks(OpParams p,
+__global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDIM, BS>::WAVES_PER_EU))) void k_adjoint_bricks(OpParams p,
                                                                                            BrickParams bp) {
   constexpr bool WEIGHTS = MODE == kWeights;
   constexpr bool VOL = MODE == kVolume || MODE == kVolumeGrad;
   constexpr int GMAX = VOL ? 1 : kGroupMax;
   using BR = Brick<NDIM>;
-  using AL = AccLayout<NDIM>;
+  using SH = AdjShape<NDIM, BS>;
+  constexpr bool EXCLZ = SH::EXCLZ;
+  using AL = AccLayout<NDIM, EXCLZ ? kGuard : 0>;
   __shared__ unsigned long long acc[AL::W];
   int* acc_r = reinterpret_cast<int*>(acc);  // the weight volume's int32 slots
-  constexpr int kHitCap = AdjShape<BS>::HIT_CAP;
-  constexpr int kPerThread = AdjShape<BS>::PER_THREAD;
+  constexpr int kHitCap = SH::HIT_CAP;
+  constexpr int kPerThread = SH::PER_THREAD;
+  constexpr int kNVox = SH::NVOX;
   __shared__ uint32_t s_hits[kHitCap];
   __shared__ int s_poses[BS];
   __shared__ PoseView s_view[kGroupMax];
@@ -505,8 +525,9 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>
       return;
     }
   }
-  const BrickPos br = decode<NDIM, VOL>(p, bp, lin);
+  BrickPos br = decode<NDIM, VOL>(p, bp, lin);
   if (!br.valid) return;
+  if (EXCLZ) br.zlim = min(br.z0 + BR::Z + kGuard - 1, (p.N + 1) / 2 - 1);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float m_prev = 0.f;  // max |G| of the previous group (0: none yet)
@@ -516,7 +537,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>
   for (int i = tid; i < AL::W; i += BS) acc[i] = 0ull;
   __syncthreads();
 
-  const Box bx = reach_box<NDIM, INTERP>(br);
+  const Box bx = reach_box<NDIM, INTERP, EXCLZ>(br);
   for (int w0 = br.n0; w0 < br.n1; w0 += BS) {
     // the poses whose plane (volume) can reach this brick, in order
     const int total = VOL ? scan_poses_if<BS>([&](int n) { return vol_meets(p, br.b, bx, n); }, w0, br.n1, s_poses,
@@ -617,6 +638,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>
 #pragma unroll
             for (int i = 0; i < kPerThread; ++i) {
               const int v = tid + i * BS;
+              if (v >= kNVox) continue;
               const int sl = acc_word<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
               if (WEIGHTS) {
                 fre[i] = fmaf((float)acc_r[sl], q, fre[i]);
@@ -636,6 +658,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>
 #pragma unroll
             for (int i = 0; i < kPerThread; ++i) {
               const int v = tid + i * BS;
+              if (v >= kNVox) continue;
               const int sl = acc_word<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
               if (WEIGHTS) acc_r[sl] = 0;
               else acc[sl] = 0ull;
@@ -651,21 +674,26 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>
   }
 
   // write the brick: plain stores, or float atomics for pose-chunked bricks
+  // and, with exclusive z ownership, for the guard planes and the first
+  // kGuard planes (which the brick below adds its guard planes to)
   float2* out = p.ref_out + (size_t)br.b * p.ref_elems;
   float* wout = p.wref_out + (size_t)br.b * p.ref_elems;
   const int wh = p.N / 2 + 1;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int v = tid + i * BS;
+    if (v >= kNVox) continue;
+    const int zr = v / (BR::X * BR::Y);
     const int x = br.x0 + v % BR::X;
     const int y = br.y0 + (v / BR::X) % BR::Y;
-    const int z = br.z0 + v / (BR::X * BR::Y);
-    if (x > br.x1 || y > br.y1 || (NDIM == 3 && z > br.z1)) continue;
+    const int z = br.z0 + zr;
+    if (x > br.x1 || y > br.y1 || (NDIM == 3 && z > br.zlim)) continue;
+    const bool merge = br.chunked || (EXCLZ && (zr >= BR::Z || (zr < kGuard && !br.zbottom)));
     const size_t row = NDIM == 3 ? (size_t)(z < 0 ? z + p.N : z) * p.N + (y < 0 ? y + p.N : y)
                                  : (size_t)(y < 0 ? y + p.N : y);
     if (WEIGHTS) {
       float* wdst = wout + row * wh + x;
-      if (br.chunked) {
+      if (merge) {
         if (fre[i] != 0.f) unsafeAtomicAdd(wdst, fre[i]);
       } else {
         *wdst = fre[i];
@@ -673,7 +701,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<BS>
       continue;
     }
     float2* dst = out + row * wh + x;
-    if (br.chunked) {
+    if (merge) {
       if (fre[i] != 0.f) unsafeAtomicAdd(&dst->x, fre[i]);
       if (fim[i] != 0.f) unsafeAtomicAdd(&dst->y, fim[i]);
     } else {
