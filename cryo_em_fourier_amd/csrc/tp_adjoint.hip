@@ -51,8 +51,8 @@ constexpr int kGroupMax = 16;       // poses per fixed-point group
 template <int NDIM, int BS>
 struct AdjShape {
   static constexpr bool EXCLZ = NDIM == 3 && BS == 512;
-  static constexpr int HIT_CAP = BS == 512 ? (EXCLZ ? 7168 : 8192) : 2560;  // lattice points per group slice
-  static constexpr int NVOX = kVox + (EXCLZ ? 3 * 256 : 0);  // brick voxels, guard planes included
+  static constexpr int HIT_CAP = BS == 512 ? (EXCLZ ? 5120 : 8192) : 2560;  // lattice points per group slice
+  static constexpr int NVOX = EXCLZ ? 16 * 19 * 19 : kVox;  // brick voxels, guard rows and planes included
   static constexpr int PER_THREAD = (NVOX + BS - 1) / BS;     // brick voxels per thread
   static constexpr int WAVES_PER_EU = BS == 512 ? 4 : 3;
 };
@@ -86,16 +86,18 @@ template <> struct Brick<2> { static constexpr int X = 64, Y = 64, Z = 1; };
 // stride and a z-plane stride of 5 mod 16 (padded) keep taps that differ in
 // y or z only off each other's banks.
 constexpr int kGuard = 3;  // the cubic stencil reaches 3 voxels past its first tap
-// ZG guard planes follow the brick's last plane (exclusive z ownership).
-template <int NDIM, int ZG = 0>
+// G guard rows and planes follow the brick's last row and plane (exclusive
+// y and z ownership).
+template <int NDIM, int G = 0>
 struct AccLayout {
   static constexpr int S = Brick<NDIM>::X + kGuard;
-  static constexpr int PZ = NDIM == 3 ? Brick<NDIM>::Y * S + ((5 - Brick<NDIM>::Y * S % 16) + 16) % 16 : 0;
-  static constexpr int W = (NDIM == 3 ? (Brick<NDIM>::Z + ZG) * PZ : Brick<NDIM>::Y * S) + kGuard;
+  static constexpr int ROWS = Brick<NDIM>::Y + G;
+  static constexpr int PZ = NDIM == 3 ? ROWS * S + ((5 - ROWS * S % 16) + 16) % 16 : 0;
+  static constexpr int W = (NDIM == 3 ? (Brick<NDIM>::Z + G) * PZ : Brick<NDIM>::Y * S) + kGuard;
 };
-template <int NDIM>
+template <int NDIM, int G = 0>
 __device__ __forceinline__ int acc_word(int x, int y, int z) {
-  return kGuard + z * AccLayout<NDIM>::PZ + y * AccLayout<NDIM>::S + x;
+  return kGuard + z * AccLayout<NDIM, G>::PZ + y * AccLayout<NDIM, G>::S + x;
 }
 
 // (re, im) int32 pair as one int64, re * 2^32 + im: sums of such values
@@ -120,9 +122,9 @@ struct BrickPos {
   int b;            // batch entry
   int x0, y0, z0;   // first voxel (x from 0, y and z signed)
   int x1, y1, z1;   // last voxel (inclusive, clipped to the stored range)
-  int zlim;         // last z plane that taps are spread to (z1, or with
-                    // exclusive z ownership its guard planes in range)
-  bool zbottom;     // the lowest brick of the stored z range
+  int ylim, zlim;   // last y row and z plane that taps are spread to (y1
+                    // and z1, or with exclusive ownership the guards in range)
+  bool ybottom, zbottom;  // the lowest brick of the stored y / z range
   int n0, n1;       // pose range of this workgroup
   bool chunked;     // merged with atomics
   bool valid;
@@ -170,7 +172,9 @@ __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams&
   } else {
     r.z0 = r.z1 = 0;
   }
+  r.ylim = r.y1;
   r.zlim = r.z1;
+  r.ybottom = r.y0 == lo;
   r.zbottom = r.z0 == (NDIM == 3 ? lo : 0);
   // every pose of a volume lattice reaches every brick inside its sphere
   const int nch = VOL ? bp.cmax : brick_chunks<NDIM>(p, bp, r.x0, r.y0, r.z0);
@@ -192,6 +196,7 @@ __device__ __forceinline__ Box reach_box(const BrickPos& br) {
   constexpr double reach = INTERP ? 2.0 : 1.0;
   Box bx = {{br.x0 - reach, br.y0 - reach, br.z0 - reach}, {br.x1 + reach, br.y1 + reach, br.z1 + reach}};
   if (EXCLZ && !br.zbottom) bx.lo[2] = (double)(br.z0 - Kern<INTERP>::OFF);
+  if (EXCLZ && !br.ybottom) bx.lo[1] = (double)(br.y0 - Kern<INTERP>::OFF);
   if (NDIM == 2) bx.lo[2] = bx.hi[2] = 0.0;
   return bx;
 }
@@ -440,10 +445,10 @@ __device__ __forceinline__ int hit_slot(int tid) { return (tid & 63) * 2 + ((tid
 // outside the brick in x fall into guard words.  Rows outside in y or z are
 // skipped.  REAL: int32 real parts only (the weight volume), else packed
 // pairs.
-template <int NDIM, int INTERP, bool REAL>
+template <int NDIM, int INTERP, bool REAL, int G = 0>
 __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float inv_q, unsigned long long* acc) {
   using BR = Brick<NDIM>;
-  using L = AccLayout<NDIM>;
+  using L = AccLayout<NDIM, G>;
   using K = Kern<INTERP>;
   constexpr int T = K::T;
   static_assert(T - 1 <= kGuard, "guard words must cover the stencil");
@@ -468,7 +473,7 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
     are[d] = wx[d] * v.x * inv_q;
     aim[d] = wx[d] * v.y * inv_q;
   }
-  const int x0w = acc_word<NDIM>(ax.x0 - br.x0, 0, 0);
+  const int x0w = acc_word<NDIM, G>(ax.x0 - br.x0, 0, 0);
 #pragma unroll
   for (int dz = 0; dz < (NDIM == 3 ? T : 1); ++dz) {
     const int tz = z0 + dz;
@@ -476,7 +481,7 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
 #pragma unroll
     for (int dy = 0; dy < T; ++dy) {
       const int ty = ay.x0 + dy;
-      if (ty < br.y0 || ty > br.y1) continue;
+      if (ty < br.y0 || ty > br.ylim) continue;
       const float wyz = wy[dy] * wz[dz];
       const int w = x0w + (NDIM == 3 ? tz - br.z0 : 0) * L::PZ + (ty - br.y0) * L::S;
 #pragma unroll
@@ -507,6 +512,8 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   constexpr int kHitCap = SH::HIT_CAP;
   constexpr int kPerThread = SH::PER_THREAD;
   constexpr int kNVox = SH::NVOX;
+  constexpr int G = EXCLZ ? kGuard : 0;
+  constexpr int YR = BR::Y + G;  // y rows of the accumulator
   __shared__ uint32_t s_hits[kHitCap];
   __shared__ int s_poses[BS];
   __shared__ PoseView s_view[kGroupMax];
@@ -527,7 +534,10 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   }
   BrickPos br = decode<NDIM, VOL>(p, bp, lin);
   if (!br.valid) return;
-  if (EXCLZ) br.zlim = min(br.z0 + BR::Z + kGuard - 1, (p.N + 1) / 2 - 1);
+  if (EXCLZ) {
+    br.ylim = min(br.y0 + BR::Y + kGuard - 1, (p.N + 1) / 2 - 1);
+    br.zlim = min(br.z0 + BR::Z + kGuard - 1, (p.N + 1) / 2 - 1);
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float m_prev = 0.f;  // max |G| of the previous group (0: none yet)
@@ -621,7 +631,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
                 const PoseView& pv = s_view[hit_pose(h)];
                 lattice_values<NDIM>(p, pv, hit_kx(h, pv), hit_ky(h, pv), gr[k], gm[k], cd);
               }
-              if (in_box<NDIM>(bx, cd.q)) spread<NDIM, INTERP, WEIGHTS>(br, cd, inv_q, acc);
+              if (in_box<NDIM>(bx, cd.q)) spread<NDIM, INTERP, WEIGHTS, G>(br, cd, inv_q, acc);
             }
           }
 #pragma unroll
@@ -639,7 +649,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
             for (int i = 0; i < kPerThread; ++i) {
               const int v = tid + i * BS;
               if (v >= kNVox) continue;
-              const int sl = acc_word<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
+              const int sl = acc_word<NDIM, G>(v % BR::X, (v / BR::X) % YR, v / (BR::X * YR));
               if (WEIGHTS) {
                 fre[i] = fmaf((float)acc_r[sl], q, fre[i]);
                 acc_r[sl] = 0;
@@ -659,7 +669,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
             for (int i = 0; i < kPerThread; ++i) {
               const int v = tid + i * BS;
               if (v >= kNVox) continue;
-              const int sl = acc_word<NDIM>(v % BR::X, (v / BR::X) % BR::Y, v / (BR::X * BR::Y));
+              const int sl = acc_word<NDIM, G>(v % BR::X, (v / BR::X) % YR, v / (BR::X * YR));
               if (WEIGHTS) acc_r[sl] = 0;
               else acc[sl] = 0ull;
             }
@@ -683,12 +693,13 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   for (int i = 0; i < kPerThread; ++i) {
     const int v = tid + i * BS;
     if (v >= kNVox) continue;
-    const int zr = v / (BR::X * BR::Y);
+    const int yr = (v / BR::X) % YR, zr = v / (BR::X * YR);
     const int x = br.x0 + v % BR::X;
-    const int y = br.y0 + (v / BR::X) % BR::Y;
+    const int y = br.y0 + yr;
     const int z = br.z0 + zr;
-    if (x > br.x1 || y > br.y1 || (NDIM == 3 && z > br.zlim)) continue;
-    const bool merge = br.chunked || (EXCLZ && (zr >= BR::Z || (zr < kGuard && !br.zbottom)));
+    if (x > br.x1 || y > br.ylim || (NDIM == 3 && z > br.zlim)) continue;
+    const bool merge = br.chunked || (EXCLZ && (yr >= BR::Y || zr >= BR::Z || (yr < kGuard && !br.ybottom) ||
+                                                (zr < kGuard && !br.zbottom)));
     const size_t row = NDIM == 3 ? (size_t)(z < 0 ? z + p.N : z) * p.N + (y < 0 ? y + p.N : y)
                                  : (size_t)(y < 0 ? y + p.N : y);
     if (WEIGHTS) {
