@@ -52,7 +52,7 @@ template <int NDIM, int BS>
 struct AdjShape {
   static constexpr bool EXCLZ = NDIM == 3 && BS == 512;
   static constexpr int HIT_CAP = BS == 512 ? (EXCLZ ? 5120 : 8192) : 2560;  // lattice points per group slice
-  static constexpr int NVOX = EXCLZ ? 16 * 19 * 19 : kVox;  // brick voxels, guard rows and planes included
+  static constexpr int NVOX = EXCLZ ? 19 * 19 * 19 : kVox;  // brick voxels, guard columns, rows and planes included
   static constexpr int PER_THREAD = (NVOX + BS - 1) / BS;     // brick voxels per thread
   static constexpr int WAVES_PER_EU = BS == 512 ? 4 : 3;
 };
@@ -122,9 +122,10 @@ struct BrickPos {
   int b;            // batch entry
   int x0, y0, z0;   // first voxel (x from 0, y and z signed)
   int x1, y1, z1;   // last voxel (inclusive, clipped to the stored range)
-  int ylim, zlim;   // last y row and z plane that taps are spread to (y1
-                    // and z1, or with exclusive ownership the guards in range)
-  bool ybottom, zbottom;  // the lowest brick of the stored y / z range
+  int xlim, ylim, zlim;  // last x column, y row and z plane that taps are
+                         // spread to (x1, y1 and z1, or with exclusive
+                         // ownership the guards in range)
+  bool xbottom, ybottom, zbottom;  // the lowest brick of the stored x / y / z range
   int n0, n1;       // pose range of this workgroup
   bool chunked;     // merged with atomics
   bool valid;
@@ -172,8 +173,10 @@ __device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams&
   } else {
     r.z0 = r.z1 = 0;
   }
+  r.xlim = r.x1;
   r.ylim = r.y1;
   r.zlim = r.z1;
+  r.xbottom = r.x0 == 0;
   r.ybottom = r.y0 == lo;
   r.zbottom = r.z0 == (NDIM == 3 ? lo : 0);
   // every pose of a volume lattice reaches every brick inside its sphere
@@ -197,6 +200,7 @@ __device__ __forceinline__ Box reach_box(const BrickPos& br) {
   Box bx = {{br.x0 - reach, br.y0 - reach, br.z0 - reach}, {br.x1 + reach, br.y1 + reach, br.z1 + reach}};
   if (EXCLZ && !br.zbottom) bx.lo[2] = (double)(br.z0 - Kern<INTERP>::OFF);
   if (EXCLZ && !br.ybottom) bx.lo[1] = (double)(br.y0 - Kern<INTERP>::OFF);
+  if (EXCLZ && !br.xbottom) bx.lo[0] = (double)(br.x0 - Kern<INTERP>::OFF);
   if (NDIM == 2) bx.lo[2] = bx.hi[2] = 0.0;
   return bx;
 }
@@ -472,6 +476,9 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
     const float2 v = ax.x0 + d >= 1 ? cd.v1 : cd.v0;
     are[d] = wx[d] * v.x * inv_q;
     aim[d] = wx[d] * v.y * inv_q;
+    // with guard columns read back, a tap before x = 0 (whose slot is the
+    // previous row's guard column) must add nothing
+    if (G > 0 && ax.x0 + d < 0) are[d] = aim[d] = 0.f;
   }
   const int x0w = acc_word<NDIM, G>(ax.x0 - br.x0, 0, 0);
 #pragma unroll
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   constexpr int kPerThread = SH::PER_THREAD;
   constexpr int kNVox = SH::NVOX;
   constexpr int G = EXCLZ ? kGuard : 0;
-  constexpr int YR = BR::Y + G;  // y rows of the accumulator
+  constexpr int XR = BR::X + G, YR = BR::Y + G;  // x columns and y rows of the accumulator
   __shared__ uint32_t s_hits[kHitCap];
   __shared__ int s_poses[BS];
   __shared__ PoseView s_view[kGroupMax];
@@ -535,6 +542,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   BrickPos br = decode<NDIM, VOL>(p, bp, lin);
   if (!br.valid) return;
   if (EXCLZ) {
+    br.xlim = min(br.x0 + BR::X + kGuard - 1, p.N / 2);
     br.ylim = min(br.y0 + BR::Y + kGuard - 1, (p.N + 1) / 2 - 1);
     br.zlim = min(br.z0 + BR::Z + kGuard - 1, (p.N + 1) / 2 - 1);
   }
@@ -649,7 +657,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
             for (int i = 0; i < kPerThread; ++i) {
               const int v = tid + i * BS;
               if (v >= kNVox) continue;
-              const int sl = acc_word<NDIM, G>(v % BR::X, (v / BR::X) % YR, v / (BR::X * YR));
+              const int sl = acc_word<NDIM, G>(v % XR, (v / XR) % YR, v / (XR * YR));
               if (WEIGHTS) {
                 fre[i] = fmaf((float)acc_r[sl], q, fre[i]);
                 acc_r[sl] = 0;
@@ -669,7 +677,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
             for (int i = 0; i < kPerThread; ++i) {
               const int v = tid + i * BS;
               if (v >= kNVox) continue;
-              const int sl = acc_word<NDIM, G>(v % BR::X, (v / BR::X) % YR, v / (BR::X * YR));
+              const int sl = acc_word<NDIM, G>(v % XR, (v / XR) % YR, v / (XR * YR));
               if (WEIGHTS) acc_r[sl] = 0;
               else acc[sl] = 0ull;
             }
@@ -693,12 +701,13 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   for (int i = 0; i < kPerThread; ++i) {
     const int v = tid + i * BS;
     if (v >= kNVox) continue;
-    const int yr = (v / BR::X) % YR, zr = v / (BR::X * YR);
-    const int x = br.x0 + v % BR::X;
+    const int xr = v % XR, yr = (v / XR) % YR, zr = v / (XR * YR);
+    const int x = br.x0 + xr;
     const int y = br.y0 + yr;
     const int z = br.z0 + zr;
-    if (x > br.x1 || y > br.ylim || (NDIM == 3 && z > br.zlim)) continue;
-    const bool merge = br.chunked || (EXCLZ && (yr >= BR::Y || zr >= BR::Z || (yr < kGuard && !br.ybottom) ||
+    if (x > br.xlim || y > br.ylim || (NDIM == 3 && z > br.zlim)) continue;
+    const bool merge = br.chunked || (EXCLZ && (xr >= BR::X || yr >= BR::Y || zr >= BR::Z ||
+                                                (xr < kGuard && !br.xbottom) || (yr < kGuard && !br.ybottom) ||
                                                 (zr < kGuard && !br.zbottom)));
     const size_t row = NDIM == 3 ? (size_t)(z < 0 ? z + p.N : z) * p.N + (y < 0 ? y + p.N : y)
                                  : (size_t)(y < 0 ? y + p.N : y);
