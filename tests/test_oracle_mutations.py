@@ -35,7 +35,10 @@ MUTATIONS = [
      "c = np.conj(_phase(kxk, kyk, sv, n_out)) * G[b, n][keep]",
      "c = _phase(kxk, kyk, sv, n_out) * G[b, n][keep]"),
     ("folded index sign", "idx = idx * N + np.mod(tt[..., j], N)", "idx = idx * N + np.mod(-tt[..., j], N)"),
-    ("cutoff exclusive", "<= float(cutoff) ** 2", "< float(cutoff) ** 2"),
+    ("2D cutoff exclusive", "keep = (kx * kx + ky * ky).astype(np.float64) <= float(cutoff) ** 2",
+     "keep = (kx * kx + ky * ky).astype(np.float64) < float(cutoff) ** 2"),
+    ("3D cutoff exclusive", "keep = (kx * kx + ky * ky + kz * kz).astype(np.float64) <= float(cutoff) ** 2",
+     "keep = (kx * kx + ky * ky + kz * kz).astype(np.float64) < float(cutoff) ** 2"),
     ("weights without interpolation weight", "np.add.at(Aflat, idx[valid], (w * c)[valid])",
      "np.add.at(Aflat, idx[valid], c[valid])"),
     ("weights stencil from round", "            base = np.floor(p).astype(np.int64)\n            for d",

@@ -139,3 +139,52 @@ def test_rotate_gradients_match_finite_differences():
             sm[0, n, j] -= h
             fd = (loss(R, sp) - loss(R, sm)) / (2 * h)
             assert abs(fd - ds[0, n, j]) <= 1e-5 * max(1.0, abs(fd)), (n, j, fd, ds[0, n, j])
+
+# Lattice points on the sphere of radius 5 (Pythagorean triples and the axes),
+# written out by hand: the cutoff keeps |k| <= c, boundary included.
+ON_SPHERE_5 = [(5, 0, 0), (0, 5, 0), (0, 0, 5), (0, -5, 0), (0, 0, -5), (3, 4, 0), (4, 3, 0), (4, 0, 3),
+               (3, 0, 4), (0, 3, 4), (0, 4, 3), (3, -4, 0), (4, 0, -3), (0, -3, 4), (0, 4, -3), (0, -4, -3)]
+JUST_OUTSIDE_5 = [(5, 1, 0), (1, 0, 5), (4, 3, 1), (0, 5, 1), (3, 4, 1), (1, 5, 0)]
+
+
+def test_sphere_cutoff_keeps_its_boundary():
+    """At the identity pose the output is the reference inside the sphere:
+    points with |k| = 5 exactly keep their value at cutoff 5, points with
+    |k|^2 = 26 are zero."""
+    rng = np.random.default_rng(21)
+    N = 12
+    V = rng.standard_normal((1, N, N, N // 2 + 1)) + 1j * rng.standard_normal((1, N, N, N // 2 + 1))
+    out = oracle.rotate_3d(V, np.eye(3)[None, None], None, N, CUBIC, 1.0, 5.0)[0, 0]
+    for kx, ky, kz in ON_SPHERE_5:
+        assert out[kz % N, ky % N, kx] == pytest.approx(V[0, kz % N, ky % N, kx], abs=1e-12), (kx, ky, kz)
+    for kx, ky, kz in JUST_OUTSIDE_5:
+        assert out[kz % N, ky % N, kx] == 0, (kx, ky, kz)
+    # and the count of kept entries is the number of lattice points in the
+    # ball of radius 5 with kx >= 0 (brute force over the box)
+    kept = sum(1 for kx in range(0, 6) for ky in range(-5, 6) for kz in range(-5, 6)
+               if kx * kx + ky * ky + kz * kz <= 25)
+    assert int(np.count_nonzero(out)) == kept
+
+
+def test_sphere_cutoff_zero_keeps_only_dc():
+    rng = np.random.default_rng(22)
+    N = 8
+    V = rng.standard_normal((1, N, N, N // 2 + 1)) + 1j * rng.standard_normal((1, N, N, N // 2 + 1))
+    out = oracle.rotate_3d(V, np.eye(3)[None, None], None, N, LINEAR, 1.0, 0.0)[0, 0]
+    assert out[0, 0, 0] == pytest.approx(V[0, 0, 0, 0], abs=1e-12)
+    out[0, 0, 0] = 0
+    assert not out.any()
+
+
+@pytest.mark.parametrize("interp", [LINEAR, CUBIC])
+def test_kz0_plane_is_the_slice_at_an_integer_cutoff(interp):
+    """Cutoff 5 puts (3, 4), (4, 3), (5, 0) and (0, 5) on the circle: the
+    sphere's kz = 0 plane and the slice's disk must keep the same entries."""
+    rng = np.random.default_rng(23)
+    N = 12
+    V = rng.standard_normal((1, N, N, N // 2 + 1)) + 1j * rng.standard_normal((1, N, N, N // 2 + 1))
+    R = np.stack([np.linalg.qr(rng.standard_normal((3, 3)))[0] for _ in range(2)])[None]
+    vol = oracle.rotate_3d(V, R, None, N, interp, 1.0, 5.0)
+    sl = oracle.project(V, R, None, N, interp, 1.0, 5.0)
+    np.testing.assert_allclose(vol[:, :, 0], sl, atol=1e-12)
+    assert np.all(sl[0, :, 4, 3] != 0) and np.all(sl[0, :, 3, 4] != 0)
