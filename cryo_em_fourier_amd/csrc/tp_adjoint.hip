@@ -500,6 +500,39 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
   }
 }
 
+// Mark the accumulator slots (set them to 1) that a lattice point's taps
+// reach inside the brick, where its spread values are not finite: the x = 0
+// taps when v0 is not, the x >= 1 taps when v1 is not (the same taps and row
+// tests as spread(), whatever their weight: the product of a weight of 0 and a
+// non-finite value is not finite either).
+template <int NDIM, int INTERP, bool REAL, int G = 0>
+__device__ __forceinline__ void mark_taps(const BrickPos& br, const double* q, bool bad0, bool bad1,
+                                          unsigned long long* acc) {
+  using L = AccLayout<NDIM, G>;
+  using K = Kern<INTERP>;
+  constexpr int T = K::T;
+  const AxisPos ax = axis_pos(q[0], K::OFF), ay = axis_pos(q[1], K::OFF);
+  const int z0 = NDIM == 3 ? axis_pos(q[2], K::OFF).x0 : 0;
+  const int x0w = acc_word<NDIM, G>(ax.x0 - br.x0, 0, 0);
+  for (int dz = 0; dz < (NDIM == 3 ? T : 1); ++dz) {
+    const int tz = z0 + dz;
+    if (NDIM == 3 && (tz < br.z0 || tz > br.zlim)) continue;
+    for (int dy = 0; dy < T; ++dy) {
+      const int ty = ay.x0 + dy;
+      if (ty < br.y0 || ty > br.ylim) continue;
+      const int w = x0w + (NDIM == 3 ? tz - br.z0 : 0) * L::PZ + (ty - br.y0) * L::S;
+      for (int dx = 0; dx < T; ++dx) {
+        const int tx = ax.x0 + dx;
+        if (tx < 0 || !(tx == 0 ? bad0 : bad1)) continue;
+        if (REAL) reinterpret_cast<int*>(acc)[w + dx] = 1;
+        else acc[w + dx] = 1ull;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ bool finite2(float2 v) { return isfinite(v.x) && isfinite(v.y); }
+
 // MODE: kSlice (the projector's adjoint), kWeights (real weight volume),
 // kVolume (the adjoint of the 3D -> 3D rotation: volume lattices, one pose
 // per group), kSliceGrad / kVolumeGrad (kSlice / kVolume and the pose
@@ -526,6 +559,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   __shared__ PoseView s_view[kGroupMax];
   __shared__ int s_wcnt[BS / 64];
   __shared__ float s_red[BS / 64];
+  __shared__ int s_bad[BS / 64];
 
   const uint32_t lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   if constexpr (MODE == kSliceGrad || MODE == kVolumeGrad) {
@@ -556,138 +590,193 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   __syncthreads();
 
   const Box bx = reach_box<NDIM, INTERP, EXCLZ>(br);
-  for (int w0 = br.n0; w0 < br.n1; w0 += BS) {
-    // the poses whose plane (volume) can reach this brick, in order
-    const int total = VOL ? scan_poses_if<BS>([&](int n) { return vol_meets(p, br.b, bx, n); }, w0, br.n1, s_poses,
-                                              s_wcnt)
-                          : scan_poses<NDIM, BS>(p, br.b, bx, w0, br.n1, s_poses, s_wcnt);
+  int g0 = 0;  // first pose of the current group in s_poses
 
-    // groups of up to GMAX poses; a group whose lattice points overflow the
-    // hit list is spread in slices of kHitCap
-    for (int g0 = 0; g0 < total; g0 += GMAX) {
-      const int cnt = min(GMAX, total - g0);
-      if (tid < cnt)
-        s_view[tid] = VOL ? vol_view(p, br.b, bx, s_poses[g0 + tid]) : pose_view<NDIM>(p, br.b, bx, s_poses[g0 + tid], false);
+  // G entries of hit h of the current group
+  auto load_hit = [&](uint32_t h, float2& gr, float2& gm) {
+    if (VOL) {
+      const PoseView& pv = s_view[0];
+      const int kx = pv.kx0 + (int)(h & 0x3FFu), ky = pv.ky0 + (int)((h >> 10) & 0x3FFu), kz = pv.kz0 + (int)(h >> 20);
+      const size_t img = (size_t)br.b * p.P + s_poses[g0];
+      bool real, mirr;
+      lattice_parts3(p, kx, ky, kz, real, mirr);
+      gr = real ? p.img[out_index3(p, img, kx, ky, kz)] : make_float2(0.f, 0.f);
+      gm = mirr ? p.img[out_index3(p, img, -kx, -ky, -kz)] : make_float2(0.f, 0.f);
+    } else {
+      const PoseView& pv = s_view[hit_pose(h)];
+      lattice_load<WEIGHTS>(p, (size_t)br.b * p.P + s_poses[g0 + hit_pose(h)], hit_kx(h, pv), hit_ky(h, pv), gr, gm);
+    }
+  };
+
+  // Every slice of lattice points that can reach the brick: pose windows of
+  // the chunk, groups of up to GMAX poses, and slices of kHitCap hits when a
+  // group overflows the hit list.  on_slice(nh, dens_sum) runs with the
+  // slice's hits in s_hits[0, nh); a barrier follows it.
+  auto traverse = [&](auto&& on_slice) {
+    for (int w0 = br.n0; w0 < br.n1; w0 += BS) {
+      // the poses whose plane (volume) can reach this brick, in order
+      const int total = VOL ? scan_poses_if<BS>([&](int n) { return vol_meets(p, br.b, bx, n); }, w0, br.n1,
+                                                s_poses, s_wcnt)
+                            : scan_poses<NDIM, BS>(p, br.b, bx, w0, br.n1, s_poses, s_wcnt);
+      for (g0 = 0; g0 < total; g0 += GMAX) {
+        const int cnt = min(GMAX, total - g0);
+        if (tid < cnt)
+          s_view[tid] = VOL ? vol_view(p, br.b, bx, s_poses[g0 + tid])
+                            : pose_view<NDIM>(p, br.b, bx, s_poses[g0 + tid], false);
+        __syncthreads();
+        float dens_sum = 0.f;
+        for (int g = 0; g < cnt; ++g)
+          if (s_view[g].hit) dens_sum += s_view[g].dens;
+        for (int h0 = 0, hits_total = 1; h0 < hits_total; h0 += kHitCap) {
+          // phase A: list the lattice points that can reach the brick (this
+          // slice keeps the flat indices [h0, h0 + kHitCap))
+          hits_total = VOL ? list_hits_vol<BS>(p, bx, s_view[0], h0, kHitCap, s_hits, s_wcnt)
+                           : list_hits<NDIM, kGroupMax, BS>(p, bx, s_view, cnt, h0, kHitCap, s_hits, s_wcnt);
+          on_slice(max(0, min(hits_total, h0 + kHitCap) - h0), dens_sum);
+          __syncthreads();
+        }
+      }
+    }
+  };
+
+  bool brick_bad = false;  // some slice read a non-finite value (uniform)
+  traverse([&](int nh, float dens_sum) {
+    // phase B: spread the hits.  The fixed-point quantum assumes the
+    // group's max |G| is at most twice the previous group's; the values
+    // actually read are checked, and a group that exceeds its assumption
+    // is cleared and redone with the measured bound (the first group of a
+    // workgroup only measures).  See the bound at kQuantumBits.  Values
+    // that are not finite are left out of the sums and of the bound.
+    bool measure_only = m_prev <= 0.f;
+    float m_assume = 2.f * m_prev, q = 0.f;
+    while (nh > 0) {
+      float inv_q = 0.f;
+      if (!measure_only) {
+        int e;
+        frexpf(fminf(8.f * dens_sum * m_assume, 3e38f), &e);
+        e = max(e, -90);  // |G| below ~1e-27 gets a coarser quantum than needed
+        inv_q = ldexpf(1.f, kQuantumBits - e);
+        q = ldexpf(1.f, e - kQuantumBits);
+      }
+      float amax = 0.f;
+      bool bad = false;
+      for (int i0 = 0; i0 < nh; i0 += kPrefetch * BS) {
+        float2 gr[kPrefetch], gm[kPrefetch];
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) {
+          const int i = i0 + hit_slot(tid) + k * BS;
+          gr[k] = gm[k] = make_float2(0.f, 0.f);
+          if (i < nh) load_hit(s_hits[i], gr[k], gm[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) {
+          if (!finite2(gr[k])) { gr[k] = make_float2(0.f, 0.f); bad = true; }
+          if (!finite2(gm[k])) { gm[k] = make_float2(0.f, 0.f); bad = true; }
+          amax = fmaxf(amax, fmaxf(fabsf(gr[k].x) + fabsf(gr[k].y), fabsf(gm[k].x) + fabsf(gm[k].y)));
+        }
+        if (measure_only) continue;
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) {
+          const int i = i0 + hit_slot(tid) + k * BS;
+          if (i >= nh) continue;
+          const uint32_t h = s_hits[i];
+          Cand cd;
+          if (VOL) {
+            const PoseView& pv = s_view[0];
+            lattice_values3(p, pv, pv.kx0 + (int)(h & 0x3FFu), pv.ky0 + (int)((h >> 10) & 0x3FFu),
+                            pv.kz0 + (int)(h >> 20), gr[k], gm[k], cd);
+          } else {
+            const PoseView& pv = s_view[hit_pose(h)];
+            lattice_values<NDIM>(p, pv, hit_kx(h, pv), hit_ky(h, pv), gr[k], gm[k], cd);
+          }
+          if (in_box<NDIM>(bx, cd.q)) spread<NDIM, INTERP, WEIGHTS, G>(br, cd, inv_q, acc);
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      const bool wbad = __ballot(bad) != 0ull;
       __syncthreads();
-      float dens_sum = 0.f;
-      for (int g = 0; g < cnt; ++g)
-        if (s_view[g].hit) dens_sum += s_view[g].dens;
-
-      for (int h0 = 0, hits_total = 1; h0 < hits_total; h0 += kHitCap) {
-        // phase A: list the lattice points that can reach the brick (this
-        // slice keeps the flat indices [h0, h0 + kHitCap))
-        hits_total = VOL ? list_hits_vol<BS>(p, bx, s_view[0], h0, kHitCap, s_hits, s_wcnt)
-                         : list_hits<NDIM, kGroupMax, BS>(p, bx, s_view, cnt, h0, kHitCap, s_hits, s_wcnt);
-        const int nh = max(0, min(hits_total, h0 + kHitCap) - h0);
-
-        // phase B: spread the hits.  The fixed-point quantum assumes the
-        // group's max |G| is at most twice the previous group's; the values
-        // actually read are checked, and a group that exceeds its assumption
-        // is cleared and redone with the measured bound (the first group of a
-        // workgroup only measures).  See the bound at kQuantumBits.
-        bool measure_only = m_prev <= 0.f;
-        float m_assume = 2.f * m_prev, q = 0.f;
-        while (nh > 0) {
-          float inv_q = 0.f;
-          if (!measure_only) {
-            int e;
-            frexpf(fminf(8.f * dens_sum * m_assume, 3e38f), &e);
-            e = max(e, -90);  // |G| below ~1e-27 gets a coarser quantum than needed
-            inv_q = ldexpf(1.f, kQuantumBits - e);
-            q = ldexpf(1.f, e - kQuantumBits);
+      if (lane == 0) {
+        s_red[wave] = amax;
+        s_bad[wave] = wbad;
+      }
+      __syncthreads();
+      float gmax = s_red[0];
+#pragma unroll
+      for (int w = 1; w < BS / 64; ++w) {
+        gmax = fmaxf(gmax, s_red[w]);
+        brick_bad = brick_bad || s_bad[w] != 0;
+      }
+      brick_bad = brick_bad || s_bad[0] != 0;
+      if (!(gmax > 0.f)) break;  // an all-zero slice adds nothing
+      if (!measure_only && gmax <= m_assume) {
+        // flush the slice into fp32 registers
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+          const int v = tid + i * BS;
+          if (v >= kNVox) continue;
+          const int sl = acc_word<NDIM, G>(v % XR, (v / XR) % YR, v / (XR * YR));
+          if (WEIGHTS) {
+            fre[i] = fmaf((float)acc_r[sl], q, fre[i]);
+            acc_r[sl] = 0;
+          } else {
+            int ir, ii;
+            unpack_pair(acc[sl], ir, ii);
+            fre[i] = fmaf((float)ir, q, fre[i]);
+            fim[i] = fmaf((float)ii, q, fim[i]);
+            acc[sl] = 0ull;
           }
-          float amax = 0.f;
-          for (int i0 = 0; i0 < nh; i0 += kPrefetch * BS) {
-            float2 gr[kPrefetch], gm[kPrefetch];
+        }
+        m_prev = gmax;
+        break;
+      }
+      if (!measure_only) {
 #pragma unroll
-            for (int k = 0; k < kPrefetch; ++k) {
-              const int i = i0 + hit_slot(tid) + k * BS;
-              gr[k] = gm[k] = make_float2(0.f, 0.f);
-              if (i < nh) {
-                const uint32_t h = s_hits[i];
-                if (VOL) {
-                  const PoseView& pv = s_view[0];
-                  const int kx = pv.kx0 + (int)(h & 0x3FFu), ky = pv.ky0 + (int)((h >> 10) & 0x3FFu),
-                            kz = pv.kz0 + (int)(h >> 20);
-                  const size_t img = (size_t)br.b * p.P + s_poses[g0];
-                  bool real, mirr;
-                  lattice_parts3(p, kx, ky, kz, real, mirr);
-                  gr[k] = real ? p.img[out_index3(p, img, kx, ky, kz)] : make_float2(0.f, 0.f);
-                  gm[k] = mirr ? p.img[out_index3(p, img, -kx, -ky, -kz)] : make_float2(0.f, 0.f);
-                } else {
-                  const PoseView& pv = s_view[hit_pose(h)];
-                  lattice_load<WEIGHTS>(p, (size_t)br.b * p.P + s_poses[g0 + hit_pose(h)], hit_kx(h, pv),
-                                        hit_ky(h, pv), gr[k], gm[k]);
-                }
-              }
-            }
-#pragma unroll
-            for (int k = 0; k < kPrefetch; ++k)
-              amax = fmaxf(amax, fmaxf(fabsf(gr[k].x) + fabsf(gr[k].y), fabsf(gm[k].x) + fabsf(gm[k].y)));
-            if (measure_only) continue;
-#pragma unroll
-            for (int k = 0; k < kPrefetch; ++k) {
-              const int i = i0 + hit_slot(tid) + k * BS;
-              if (i >= nh) continue;
-              const uint32_t h = s_hits[i];
-              Cand cd;
-              if (VOL) {
-                const PoseView& pv = s_view[0];
-                lattice_values3(p, pv, pv.kx0 + (int)(h & 0x3FFu), pv.ky0 + (int)((h >> 10) & 0x3FFu),
-                                pv.kz0 + (int)(h >> 20), gr[k], gm[k], cd);
-              } else {
-                const PoseView& pv = s_view[hit_pose(h)];
-                lattice_values<NDIM>(p, pv, hit_kx(h, pv), hit_ky(h, pv), gr[k], gm[k], cd);
-              }
-              if (in_box<NDIM>(bx, cd.q)) spread<NDIM, INTERP, WEIGHTS, G>(br, cd, inv_q, acc);
-            }
-          }
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-          __syncthreads();
-          if (lane == 0) s_red[wave] = amax;
-          __syncthreads();
-          float gmax = s_red[0];
-#pragma unroll
-          for (int w = 1; w < BS / 64; ++w) gmax = fmaxf(gmax, s_red[w]);
-          if (!(gmax > 0.f)) break;  // an all-zero slice adds nothing
-          if (!measure_only && gmax <= m_assume) {
-            // flush the slice into fp32 registers
-#pragma unroll
-            for (int i = 0; i < kPerThread; ++i) {
-              const int v = tid + i * BS;
-              if (v >= kNVox) continue;
-              const int sl = acc_word<NDIM, G>(v % XR, (v / XR) % YR, v / (XR * YR));
-              if (WEIGHTS) {
-                fre[i] = fmaf((float)acc_r[sl], q, fre[i]);
-                acc_r[sl] = 0;
-              } else {
-                int ir, ii;
-                unpack_pair(acc[sl], ir, ii);
-                fre[i] = fmaf((float)ir, q, fre[i]);
-                fim[i] = fmaf((float)ii, q, fim[i]);
-                acc[sl] = 0ull;
-              }
-            }
-            m_prev = gmax;
-            break;
-          }
-          if (!measure_only) {
-#pragma unroll
-            for (int i = 0; i < kPerThread; ++i) {
-              const int v = tid + i * BS;
-              if (v >= kNVox) continue;
-              const int sl = acc_word<NDIM, G>(v % XR, (v / XR) % YR, v / (XR * YR));
-              if (WEIGHTS) acc_r[sl] = 0;
-              else acc[sl] = 0ull;
-            }
-            __syncthreads();
-          }
-          m_assume = gmax;
-          measure_only = false;
+        for (int i = 0; i < kPerThread; ++i) {
+          const int v = tid + i * BS;
+          if (v >= kNVox) continue;
+          const int sl = acc_word<NDIM, G>(v % XR, (v / XR) % YR, v / (XR * YR));
+          if (WEIGHTS) acc_r[sl] = 0;
+          else acc[sl] = 0ull;
         }
         __syncthreads();
       }
+      m_assume = gmax;
+      measure_only = false;
+    }
+  });
+
+  if (brick_bad) {
+    // Some upstream values were not finite.  Walk the slices again and mark
+    // the slots that their taps reach in the accumulator (clear after the
+    // last flush); those voxels become NaN, as a non-finite term makes the
+    // adjoint's sum there.
+    traverse([&](int nh, float) {
+      for (int i = tid; i < nh; i += BS) {
+        const uint32_t h = s_hits[i];
+        float2 gr, gm;
+        load_hit(h, gr, gm);
+        const bool b0 = !finite2(gr), b1 = b0 || !finite2(gm);
+        if (!b1) continue;
+        double qp[3] = {0.0, 0.0, 0.0};
+        if (VOL) {
+          const PoseView& pv = s_view[0];
+          const int kx = pv.kx0 + (int)(h & 0x3FFu), ky = pv.ky0 + (int)((h >> 10) & 0x3FFu), kz = pv.kz0 + (int)(h >> 20);
+          for (int j = 0; j < 3; ++j) qp[j] = (double)kx * pv.u[j] + (double)ky * pv.v[j] + (double)kz * pv.w[j];
+        } else {
+          const PoseView& pv = s_view[hit_pose(h)];
+          const int kx = hit_kx(h, pv), ky = hit_ky(h, pv);
+          for (int j = 0; j < NDIM; ++j) qp[j] = (double)kx * pv.u[j] + (double)ky * pv.v[j];
+        }
+        if (in_box<NDIM>(bx, qp)) mark_taps<NDIM, INTERP, WEIGHTS, G>(br, qp, b0, b1, acc);
+      }
+    });
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int v = tid + i * BS;
+      if (v >= kNVox) continue;
+      const int sl = acc_word<NDIM, G>(v % XR, (v / XR) % YR, v / (XR * YR));
+      if (WEIGHTS ? acc_r[sl] != 0 : acc[sl] != 0ull) fre[i] = fim[i] = __builtin_nanf("");
     }
   }
 

@@ -90,8 +90,15 @@ struct AxisPos {
   float f;    // fraction in [0, 1)
 };
 
-__device__ __forceinline__ AxisPos axis_pos(double q, int off) {
-  const double fl = floor(q);
+// LEFT takes the stencil from ceil(q) - 1 instead of floor(q).  At a
+// non-integer q the two agree; at an integer q the taps move one down and the
+// fraction is 1 instead of 0, with the same weights.  The gradient gathers
+// use it where they evaluate a stencil at the negated sample point -p: the
+// tap set, weights and derivative weights are then exactly the mirror of
+// floor(p)'s, so the linear kernel's one-sided derivative at an integer
+// coordinate is the right derivative in p there as well.
+__device__ __forceinline__ AxisPos axis_pos(double q, int off, bool left = false) {
+  const double fl = left ? ceil(q) - 1.0 : floor(q);
   AxisPos a;
   a.x0 = (int)fl + off;
   a.f = (float)(q - fl);

@@ -80,9 +80,9 @@ __device__ __forceinline__ float2 gather(rsrc_t rs, const RefGeom& g, const doub
 
 template <int NDIM, int INTERP>
 __device__ __forceinline__ void gather_grad(rsrc_t rs, const RefGeom& g, const double* q, int xmin,
-                                            float2* out) {
+                                            float2* out, bool left) {
   static_assert(NDIM == 2, "3D gathers use the lane-pair kernels");
-  gather2_grad<INTERP>(rs, g, q[0], q[1], xmin, out);
+  gather2_grad<INTERP>(rs, g, q[0], q[1], xmin, out, left);
 }
 
 // ------------------------------------------------------------------ forward
@@ -138,10 +138,11 @@ __global__ __launch_bounds__(kBlock) void k_grad_pose(OpParams p) {
     }
     const int xmin1 = c ? 1 : 0, xmin2 = c ? 0 : 1;
     float2 mv[NDIM + 1], sv[NDIM + 1];
-    gather_grad<NDIM, INTERP>(rs, g, m, xmin1, mv);
+    // the stencil at the negated sample point is the mirror of p's (left)
+    gather_grad<NDIM, INTERP>(rs, g, m, xmin1, mv, c);
 #pragma unroll
     for (int j = 0; j <= NDIM; ++j) sv[j] = make_float2(0.f, 0.f);
-    if (needs_secondary<INTERP>(m[0], xmin2)) gather_grad<NDIM, INTERP>(rs, g, mneg, xmin2, sv);
+    if (needs_secondary_grad<INTERP>(m[0], xmin2)) gather_grad<NDIM, INTERP>(rs, g, mneg, xmin2, sv, !c);
     // S and dS/dp (chain rule through m = +-p, see tp_device.h)
     float2 S, dS[NDIM];
     if (c) {
@@ -260,10 +261,12 @@ __device__ __forceinline__ void pair_grad_values(const OpParams& p, const Out& o
     }
     const int xmin1 = c ? 1 : 0, xmin2 = c ? 0 : 1;
     float2 mv[4], sv[4];
-    gather3_grad_half<INTERP>(rs, g, m[0], m[1], m[2], xmin1, h, mv);
+    // the stencil at the negated sample point is the mirror of p's (left)
+    gather3_grad_half<INTERP>(rs, g, m[0], m[1], m[2], xmin1, h, mv, c);
 #pragma unroll
     for (int j = 0; j < 4; ++j) sv[j] = make_float2(0.f, 0.f);
-    if (needs_secondary<INTERP>(m[0], xmin2)) gather3_grad_half<INTERP>(rs, g, mneg[0], mneg[1], mneg[2], xmin2, h, sv);
+    if (needs_secondary_grad<INTERP>(m[0], xmin2))
+      gather3_grad_half<INTERP>(rs, g, mneg[0], mneg[1], mneg[2], xmin2, h, sv, !c);
     // S and dS/dp (chain rule through m = +-p, see tp_device.h); linear in the halves
     if (c) {
       S = make_float2(mv[0].x + sv[0].x, sv[0].y - mv[0].y);

@@ -116,10 +116,12 @@ __device__ __forceinline__ void rpair_grad_values(const OpParams& p, const ROut&
 #pragma unroll
     for (int j = 0; j < 3; ++j) m[j] = c ? -q[j] : q[j];
     float2 mv[4], sv[4];
-    gather3_grad_half<INTERP>(rs, g, m[0], m[1], m[2], c ? 1 : 0, h, mv);
+    // the stencil at the negated sample point is the mirror of p's (left)
+    gather3_grad_half<INTERP>(rs, g, m[0], m[1], m[2], c ? 1 : 0, h, mv, c);
 #pragma unroll
     for (int j = 0; j < 4; ++j) sv[j] = make_float2(0.f, 0.f);
-    if (needs_secondary<INTERP>(m[0], c ? 0 : 1)) gather3_grad_half<INTERP>(rs, g, -m[0], -m[1], -m[2], c ? 0 : 1, h, sv);
+    if (needs_secondary_grad<INTERP>(m[0], c ? 0 : 1))
+      gather3_grad_half<INTERP>(rs, g, -m[0], -m[1], -m[2], c ? 0 : 1, h, sv, !c);
     // S and dS/dp through m = +-p (as the central-slice gradient kernels)
     if (c) {
       S = make_float2(mv[0].x + sv[0].x, sv[0].y - mv[0].y);

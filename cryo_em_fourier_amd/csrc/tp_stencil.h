@@ -22,11 +22,13 @@ __device__ __forceinline__ RefGeom ref_geom(const OpParams& p) {
 
 // x axis: weights (zeroed outside [xmin, xmax]) and the byte offset of the
 // first loaded tap, which is moved to x >= 0 by shifting the weights.
+// (left: see axis_pos; only the linear kernel's derivative depends on it)
 template <int INTERP, bool GRAD>
-__device__ __forceinline__ uint32_t setup_x(const RefGeom& g, double q, int xmin, float* w, float* dw) {
+__device__ __forceinline__ uint32_t setup_x(const RefGeom& g, double q, int xmin, float* w, float* dw,
+                                            bool left = false) {
   using K = Kern<INTERP>;
   constexpr int T = K::T;
-  const AxisPos a = axis_pos(q, K::OFF);
+  const AxisPos a = axis_pos(q, K::OFF, INTERP == 0 && left);
   K::w(a.f, w);
   if (GRAD) K::dw(a.f, dw);
 #pragma unroll
@@ -56,9 +58,9 @@ __device__ __forceinline__ uint32_t setup_x(const RefGeom& g, double q, int xmin
 // range); returns the first tap's coordinate.
 template <int INTERP, bool GRAD>
 __device__ __forceinline__ int setup_yz(const RefGeom& g, double q, uint32_t stride, float* w,
-                                        float* dw, uint32_t* off) {
+                                        float* dw, uint32_t* off, bool left = false) {
   using K = Kern<INTERP>;
-  const AxisPos a = axis_pos(q, K::OFF);
+  const AxisPos a = axis_pos(q, K::OFF, INTERP == 0 && left);
   K::w(a.f, w);
   if (GRAD) K::dw(a.f, dw);
 #pragma unroll
@@ -117,15 +119,15 @@ __device__ __forceinline__ float2 gather2(rsrc_t rs, const RefGeom& g, double qx
 }
 
 // Value and gradient w.r.t. the sample point (2D): out[0] = S, out[1 + j] =
-// dS/dq_j.
+// dS/dq_j.  left: q is the negated sample point (see axis_pos).
 template <int INTERP>
 __device__ __forceinline__ void gather2_grad(rsrc_t rs, const RefGeom& g, double qx, double qy,
-                                             int xmin, float2* out) {
+                                             int xmin, float2* out, bool left) {
   constexpr int T = Kern<INTERP>::T;
   float wx[T], wy[T], dwx[T], dwy[T];
   uint32_t yb[T];
-  const uint32_t xo = setup_x<INTERP, true>(g, qx, xmin, wx, dwx);
-  setup_yz<INTERP, true>(g, qy, g.row, wy, dwy, yb);
+  const uint32_t xo = setup_x<INTERP, true>(g, qx, xmin, wx, dwx, left);
+  setup_yz<INTERP, true>(g, qy, g.row, wy, dwy, yb, left);
   float2 s = make_float2(0.f, 0.f), sx = s, sy = s;
 #pragma unroll
   for (int dy = 0; dy < T; ++dy) {
@@ -228,15 +230,16 @@ __device__ __forceinline__ float2 gather3_half(rsrc_t rs, const RefGeom& g, doub
   return acc;
 }
 
+// (left: q is the negated sample point, see axis_pos)
 template <int INTERP>
 __device__ __forceinline__ void gather3_grad_half(rsrc_t rs, const RefGeom& g, double qx, double qy,
-                                                  double qz, int xmin, int h, float2* out) {
+                                                  double qz, int xmin, int h, float2* out, bool left) {
   constexpr int T = Kern<INTERP>::T, H = T / 2;
   float wx[T], wy[T], wz[T], dwx[T], dwy[T], dwz[T];
   uint32_t yb[T], zb[T];
-  const uint32_t xo = setup_x<INTERP, true>(g, qx, xmin, wx, dwx) + 8u * H * h;
-  const int y0 = setup_yz<INTERP, true>(g, qy, g.row, wy, dwy, yb);
-  const int z0 = setup_yz<INTERP, true>(g, qz, g.plane, wz, dwz, zb);
+  const uint32_t xo = setup_x<INTERP, true>(g, qx, xmin, wx, dwx, left) + 8u * H * h;
+  const int y0 = setup_yz<INTERP, true>(g, qy, g.row, wy, dwy, yb, left);
+  const int z0 = setup_yz<INTERP, true>(g, qz, g.plane, wz, dwz, zb, left);
   by_residue<T>(wy, y0);
   by_residue<T>(dwy, y0);
   by_residue<T>(yb, y0);
@@ -314,6 +317,19 @@ __device__ __forceinline__ bool needs_secondary(double mx, int xmin2) {
   const double q = -mx, fl = floor(q);
   if (INTERP == 0) return (int)fl + 1 >= xmin2 && q > fl;
   return (int)fl + K::OFF + K::T - 1 >= xmin2;
+}
+
+// The same test for the gradient gathers, whose main sum at m = -p (folded
+// samples, xmin2 = 0) uses the mirrored stencil of axis_pos's LEFT form, and
+// whose secondary sum is then taken at p itself with floor(p).  A linear tap
+// of weight 0 still carries derivative +1, so the secondary sum is needed
+// whenever its first tap floor(p_x) + 1 >= 0 (p_x >= -1), integer or not.
+// Unfolded linear samples (xmin2 = 1) have every tap at x >= 0.  Cubic
+// stencils are C1, and the tests of needs_secondary already count every tap.
+template <int INTERP>
+__device__ __forceinline__ bool needs_secondary_grad(double mx, int xmin2) {
+  if (INTERP == 0) return xmin2 == 0 && floor(-mx) >= -1.0;
+  return needs_secondary<INTERP>(mx, xmin2);
 }
 
 }  // namespace tp

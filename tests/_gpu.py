@@ -43,3 +43,27 @@ def assert_parity(got, ref, what: str, rel_tol: float = REL_L2, abs_tol: float =
 
 def complex_normal(rng, shape):
     return (rng.standard_normal(shape) + 1j * rng.standard_normal(shape)).astype(np.complex64) * np.float32(np.sqrt(0.5))
+
+
+def _oracle_backproject_part(args):
+    import oracle
+
+    G, R, s, N, interp, os_, cutoff = args
+    return oracle.backproject(G, R, s, N, interp, os_, cutoff)
+
+
+def oracle_backproject_pooled(G, R, s, N, interp, os_, cutoff, workers=16):
+    """oracle.backproject summed over pose chunks computed by CPU worker
+    processes (spawned: they import numpy and the oracle only, never the
+    GPU).  The adjoint is linear in the poses, so the sum is the oracle's
+    adjoint of all of them, up to the order of fp64 additions."""
+    import multiprocessing as mp
+    import os
+
+    P = G.shape[1]
+    nw = max(1, min(workers, len(os.sched_getaffinity(0)), P))
+    chunks = [c for c in np.array_split(np.arange(P), 2 * nw) if c.size]
+    jobs = [(G[:, c], R[:, c], None if s is None else s[:, c], N, interp, os_, cutoff) for c in chunks]
+    with mp.get_context("spawn").Pool(nw) as pool:
+        parts = pool.map(_oracle_backproject_part, jobs)
+    return np.sum(parts, axis=0)

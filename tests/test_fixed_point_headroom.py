@@ -1,0 +1,112 @@
+"""Headroom of the adjoint's int32 fixed-point sums (host-side check, CPU).
+
+The brick adjoint sums every brick's contributions exactly in int32 fixed
+point.  Its quantum assumes that one pose adds to one voxel at most
+4 * dens * (the largest |value| it carries), where dens is the pose's lattice
+density (max(1, 1 / |u x v|) for a slice with rows u = os R[0, :],
+v = os R[1, :]; max(1, 1 / |det|) for the 3D -> 3D rotation's volume
+lattice): the sum over the lattice points k of |w(p(k) - t)|, the separable
+kernel's weight at voxel t, must stay below 4 * dens.  Nothing on the pages
+fixes this number; it is a property of the kernels (Keys' a = -0.5 cubic and
+the tent) and the lattice geometry, so it is searched here: every cube
+rotation at half-voxel offsets, random orientations, oversampling 0.25 to 2
+and offsets, and a local maximisation from seeded starts.  Largest ratios
+found while writing this: 1.62 (cubic) and 1.32 (linear) for slices, 2.05
+and 1.44 for volume lattices.
+"""
+import itertools
+
+import numpy as np
+import pytest
+from scipy.optimize import minimize
+from scipy.spatial.transform import Rotation
+
+BOUND = 4.0  # the multiple of dens the adjoint's quantum assumes
+
+
+def kern(interp, t):
+    t = np.abs(t)
+    if interp == 0:
+        return np.maximum(0.0, 1.0 - t)
+    return np.where(t <= 1, 1.5 * t ** 3 - 2.5 * t ** 2 + 1,
+                    np.where(t < 2, -0.5 * t ** 3 + 2.5 * t ** 2 - 4 * t + 2, 0.0))
+
+
+def slice_ratio(interp, Rm, os_, t):
+    """sum_k |w(kx u + ky v - t)| / dens for the lattice points near t."""
+    u, v = os_ * Rm[0], os_ * Rm[1]
+    dens = max(1.0, 1.0 / np.linalg.norm(np.cross(u, v)))
+    ab = np.linalg.lstsq(np.stack([u, v], 1), t, rcond=None)[0]
+    span = int(np.ceil(3.0 / os_)) + 2
+    ka = np.arange(np.floor(ab[0]) - span, np.floor(ab[0]) + span + 1)
+    kb = np.arange(np.floor(ab[1]) - span, np.floor(ab[1]) + span + 1)
+    KA, KB = np.meshgrid(ka, kb, indexing="ij")
+    p = KA[..., None] * u + KB[..., None] * v - t
+    return float(np.prod(np.abs(kern(interp, p)), axis=-1).sum()) / dens
+
+
+def volume_ratio(interp, Rm, os_, t):
+    """sum_k |w(os R^T k - t)| / dens over the 3D lattice points near t."""
+    A = os_ * np.asarray(Rm).T          # p = kx u + ky v + kz w = A k
+    dens = max(1.0, 1.0 / abs(np.linalg.det(A)))
+    c = np.linalg.solve(A, t)
+    span = int(np.ceil(3.0 / os_)) + 1
+    r = np.arange(-span, span + 1)
+    k = np.stack(np.meshgrid(r, r, r, indexing="ij"), -1).reshape(-1, 3) + np.floor(c)
+    p = k @ A.T - t
+    return float(np.prod(np.abs(kern(interp, p)), axis=-1).sum()) / dens
+
+
+def cube_rotations():
+    mats = []
+    for perm in itertools.permutations(range(3)):
+        for signs in itertools.product((1, -1), repeat=3):
+            M = np.zeros((3, 3))
+            for i, j in enumerate(perm):
+                M[i, j] = signs[i]
+            if np.isclose(np.linalg.det(M), 1.0):
+                mats.append(M)
+    return mats
+
+
+def search(ratio, interp, seed, n_random, n_local):
+    rng = np.random.default_rng(seed)
+    best = 0.0
+    offsets = [np.array(o) for o in itertools.product((0.0, 0.25, 0.5), repeat=3)]
+    for M in cube_rotations():               # grid-aligned planes, half-voxel offsets
+        for os_ in (0.25, 0.5, 1.0, 1.5, 2.0):
+            for o in offsets:
+                best = max(best, ratio(interp, M, os_, o))
+    structured = best
+    rots = Rotation.random(n_random, random_state=seed).as_matrix()
+    for Rm in rots:                          # random orientations, oversampling, offsets
+        best = max(best, ratio(interp, Rm, rng.uniform(0.25, 2.0), rng.uniform(-1, 1, 3)))
+
+    def neg(x):
+        return -ratio(interp, Rotation.from_rotvec(x[:3]).as_matrix(), float(np.clip(x[3], 0.25, 2.0)), x[4:7])
+
+    for i in range(n_local):                 # local maximisation (some starts at the identity)
+        x0 = np.concatenate([rng.uniform(-np.pi, np.pi, 3) * (i % 3 != 0), [rng.uniform(0.25, 2.0)],
+                             rng.uniform(-1, 1, 3)])
+        best = max(best, -minimize(neg, x0, method="Nelder-Mead", options=dict(maxiter=300)).fun)
+    return structured, best
+
+
+@pytest.mark.parametrize("interp", [0, 1])
+def test_slice_lattice_stays_below_the_assumed_bound(interp):
+    structured, best = search(slice_ratio, interp, seed=10 + interp, n_random=400, n_local=12)
+    print(f"slice interp {interp}: structured {structured:.4f}, searched {best:.4f} (bound {BOUND})")
+    if interp == 1:
+        # an axis-aligned slice half a voxel off the grid in-plane:
+        # (sum_k |K(k + 1/2)|)^2 = 1.25^2, which the search must reach
+        assert structured >= 1.5625 - 1e-9
+    assert best < BOUND
+
+
+@pytest.mark.parametrize("interp", [0, 1])
+def test_volume_lattice_stays_below_the_assumed_bound(interp):
+    structured, best = search(volume_ratio, interp, seed=20 + interp, n_random=150, n_local=8)
+    print(f"volume interp {interp}: structured {structured:.4f}, searched {best:.4f} (bound {BOUND})")
+    if interp == 1:
+        assert structured >= 1.25 ** 3 - 1e-9   # grid-aligned, half a voxel off on every axis
+    assert best < BOUND

@@ -294,3 +294,21 @@ def test_grad_bricks_against_oracle(interp, os_, batch):
     assert_parity(gs[:, idx], ds, f"grad_shift bricks interp={interp} os={os_}")
     rest = np.setdiff1d(np.arange(P), idx)
     assert not gr[:, rest].any() and not gs[:, rest].any()
+
+
+def test_fullsize_c3_adjoint_dense_all_poses():
+    """c3 (box 128, 1024 poses) with a dense upstream gradient on every pose:
+    the adjoint in the benchmark's launch shape, element by element against
+    the oracle's (summed over pose chunks in CPU worker processes).  Every
+    brick near the origin runs dozens of fixed-point groups and pose chunks."""
+    from _gpu import oracle_backproject_pooled
+
+    from cryo_em_fourier_amd import tp_backproject_3d
+
+    w = synth.WORKLOADS["c3"]
+    R, s = synth.make_rotations(w), synth.make_shifts(w)
+    G = synth.make_upstream(w, poses=np.arange(w.P))
+    log(f"[fullsize adjoint dense] c3: {w.P} poses, dense upstream")
+    got = tp_backproject_3d(to_dev(G), to_dev(R), to_dev(s), w.N, w.interp, 1.0, w.cutoff).cpu().numpy()
+    ref = oracle_backproject_pooled(G, R, s, w.N, w.interp, 1.0, w.cutoff)
+    assert_parity(got, ref, "adjoint c3 dense")

@@ -118,16 +118,9 @@ def test_grad_pose_3d_matches_oracle(name):
     V, R, s, G = _dev(c)
     gr, gs = tp_grad_pose(V, G, R, s, c["interp"], float(c["os"]), float(c["cutoff"]))
     dR, ds = oracle.grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
-    if name == "adv-linear":
-        # The linear kernel has kinks at integer coordinates, where the
-        # gradient is a one-sided derivative by convention: the oracle takes
-        # the right derivative in p, the kernels the right derivative in the
-        # evaluation point +-p (folded samples: the left one in p).  Poses
-        # whose samples sit on kinks with p_x < 0 (Rz90, Rx90, the 180 degree
-        # turn) are left out; identity and the x = 0 plane agree.
-        keep = [0, 1, 4, 5, 6]
-        gr, dR = gr[:, keep], dR[:, keep]
-        gs, ds = gs[:, keep], ds[:, keep]
+    # adv-linear: every pose, including those whose samples sit on the linear
+    # kernel's kinks (integer coordinates, folded or not), where both sides
+    # take the right derivative in p
     assert_parity(gr.cpu().numpy(), dR, f"grad_rot {name}")
     assert_parity(gs.cpu().numpy(), ds, f"grad_shift {name}")
 
@@ -148,9 +141,6 @@ def test_project_3d_jac_and_grad_pose_jac_match_oracle(name):
     gr, gs = tp_grad_pose_jac(G, out, jac, c["R"].shape[0], B_shift, float(c["os"]), float(c["cutoff"]))
     dR, ds = oracle.grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
     gr, gs = gr.cpu().numpy(), gs.cpu().numpy()
-    if name == "adv-linear":
-        keep = [0, 1, 4, 5, 6]  # one-sided derivatives at kinks, as in the gradient test above
-        gr, dR, gs, ds = gr[:, keep], dR[:, keep], gs[:, keep], ds[:, keep]
     assert_parity(gr, dR, f"grad_rot (jac) {name}")
     assert_parity(gs, ds, f"grad_shift (jac) {name}")
     assert not gr[:, :, 2].any(), "the last row of dL/dR is 0"
@@ -171,9 +161,6 @@ def test_backward_3d_jac_matches_oracle(name):
     assert_parity(d_vol.cpu().numpy(), ref, f"backward_3d_jac volume {name}")
     dR, ds = oracle.grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
     gr, gs = gr.cpu().numpy(), gs.cpu().numpy()
-    if name == "adv-linear":
-        keep = [0, 1, 4, 5, 6]  # one-sided derivatives at kinks, as in the gradient test above
-        gr, dR, gs, ds = gr[:, keep], dR[:, keep], gs[:, keep], ds[:, keep]
     assert_parity(gr, dR, f"grad_rot (backward_3d_jac) {name}")
     assert_parity(gs, ds, f"grad_shift (backward_3d_jac) {name}")
 
@@ -247,9 +234,6 @@ def test_grad_pose_2d_matches_oracle(name):
     V, R, s, G = _dev(c)
     gr, gs = tp_grad_pose(V, G, R, s, c["interp"], float(c["os"]), float(c["cutoff"]))
     dR, ds = oracle.grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
-    if name == "adv-linear":
-        keep = [4, 5]
-        gr, dR, gs, ds = gr[:, keep], dR[:, keep], gs[:, keep], ds[:, keep]
     assert_parity(gr.cpu().numpy(), dR, f"grad_rot2d {name}")
     assert_parity(gs.cpu().numpy(), ds, f"grad_shift2d {name}")
 
@@ -468,3 +452,106 @@ def test_taps_at_the_end_of_the_reference(N, interp):
     out = tp_project_2d(to_dev(V2), to_dev(R2), None, 4, interp, 1.0, -1.0).cpu().numpy()
     ref = oracle.project(V2, R2, None, 4, interp, 1.0, -1.0)
     assert_parity(out, ref, f"end-of-buffer 2D N={N}")
+
+
+# ------------------------------------------- the adjoint's fixed-point groups
+
+def _ramp_upstream(rng, B, P, n_out, period=60):
+    """Dense complex upstream gradient whose per-pose amplitude climbs from
+    1e-3 to 1 over `period` consecutive poses, then starts again: a brick's
+    group of 16 crossing poses then usually holds more than twice the
+    previous group's largest value (its fixed-point quantum is redone), and
+    after each restart a group is far below its predecessor."""
+    G = complex_normal(rng, (B, P, n_out, n_out // 2 + 1))
+    amp = 10.0 ** (-3.0 + 3.0 * ((np.arange(P) % period) / (period - 1)))
+    return (G * amp[None, :, None, None]).astype(np.complex64)
+
+
+@functools.lru_cache(maxsize=None)
+def dense_case(P):
+    rng = np.random.default_rng(4800 + P)
+    N = 48
+    V = synth.rfft_spectrum(synth.blob_volume(rng, N, 30), 3)[None].astype(np.complex64)
+    R = synth.uniform_rotations(rng, P)[None]
+    s = rng.uniform(-4, 4, (1, P, 2)).astype(np.float32)
+    G = _ramp_upstream(rng, 1, P, N)
+    return dict(V=V, R=R, s=s, G=G, N=N, n_out=N, interp=CUBIC, os=1.0, cutoff=23.0)
+
+
+@pytest.mark.parametrize("P", [240, 600])
+def test_adjoint_many_poses_per_brick_dense(P):
+    """Box 48 with 240 or 600 poses and a dense upstream gradient: every brick
+    near the origin takes 15 to 38 groups of 16 poses (600 poses also split
+    them into pose chunks merged with atomics), carrying the quantum from
+    group to group and redoing groups that exceed it.  Element by element
+    against the oracle, for the adjoint and the fused backward's volume."""
+    from cryo_em_fourier_amd import tp_backproject_3d, tp_backward_3d_jac, tp_project_3d_jac
+
+    c = dense_case(P)
+    log(f"[adjoint dense] N={c['N']} P={P}")
+    V, R, s, G = to_dev(c["V"]), to_dev(c["R"]), to_dev(c["s"]), to_dev(c["G"])
+    got = tp_backproject_3d(G, R, s, c["N"], c["interp"], c["os"], c["cutoff"]).cpu().numpy()
+    ref = oracle.backproject(c["G"], c["R"], c["s"], c["N"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(got, ref, f"backproject_3d dense P={P}")
+    out, jac = tp_project_3d_jac(V, R, s, c["n_out"], c["interp"], c["os"], c["cutoff"])
+    d_vol, gr, gs = tp_backward_3d_jac(G, out, jac, R, s, c["N"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(d_vol.cpu().numpy(), ref, f"backward_3d_jac volume dense P={P}")
+    dR, ds = oracle.grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(gr.cpu().numpy(), dR, f"grad_rot (backward_3d_jac) dense P={P}")
+    assert_parity(gs.cpu().numpy(), ds, f"grad_shift (backward_3d_jac) dense P={P}")
+
+
+# ------------------------------------------------- non-finite upstream values
+
+def _nonfinite_parity(got, ref, what):
+    """Non-finite entries where and only where the oracle has them; the
+    finite rest within the parity bar."""
+    with np.errstate(invalid="ignore"):
+        bad_ref = ~np.isfinite(ref)
+        bad_got = ~np.isfinite(got)
+    log(f"  {what}: {int(bad_ref.sum())} non-finite entries in the oracle, {int(bad_got.sum())} on the GPU")
+    assert bad_ref.any(), "the case must reach the output"
+    assert np.array_equal(bad_ref, bad_got), f"{what}: non-finite entries differ"
+    assert_parity(np.where(bad_got, 0, got), np.where(bad_ref, 0, ref), f"{what} (finite entries)")
+
+
+@pytest.mark.parametrize("ndim", [3, 2])
+def test_adjoint_propagates_nonfinite_upstream(ndim):
+    """A NaN and an Inf in the upstream gradient make the voxels their
+    stencils reach non-finite (the oracle's sums there are NaN or +-Inf; the
+    adjoint writes NaN), in the adjoint and the fused backward; everything
+    else is unaffected."""
+    import warnings
+
+    from cryo_em_fourier_amd import (tp_backproject_2d, tp_backproject_3d, tp_backward_3d_jac,
+                                     tp_project_3d_jac)
+
+    rng = np.random.default_rng(77 + ndim)
+    N, P = 24, 6
+    if ndim == 3:
+        V = complex_normal(rng, (1, N, N, N // 2 + 1))
+        R = synth.uniform_rotations(rng, P)[None]
+    else:
+        V = complex_normal(rng, (1, N, N // 2 + 1))
+        R = synth.inplane_rotations(rng.uniform(0, 2 * math.pi, P)).reshape(1, P, 2, 2)
+    s = rng.uniform(-3, 3, (1, P, 2)).astype(np.float32)
+    G = complex_normal(rng, (1, P, N, N // 2 + 1))
+    G[0, 1, 3, 5] = np.nan                       # kx = 5, ky = 3
+    G[0, 4, N - 7, 0] = np.complex64(np.inf)     # kx = 0 column, ky = -7: real output and its mirror
+    G[0, 5, 10, 2] = np.complex64(complex(1.0, -np.inf))
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore", RuntimeWarning)
+        ref = oracle.backproject(G, R, s, N, CUBIC, 1.0, 11.0)
+    Gd, Rd, sd = to_dev(G), to_dev(R), to_dev(s)
+    if ndim == 3:
+        got = tp_backproject_3d(Gd, Rd, sd, N, CUBIC, 1.0, 11.0).cpu().numpy()
+        _nonfinite_parity(got, ref, "backproject_3d")
+        out, jac = tp_project_3d_jac(to_dev(V), Rd, sd, N, CUBIC, 1.0, 11.0)
+        d_vol, gr, gs = tp_backward_3d_jac(Gd, out, jac, Rd, sd, N, CUBIC, 1.0, 11.0)
+        _nonfinite_parity(d_vol.cpu().numpy(), ref, "backward_3d_jac volume")
+        gr, gs = gr.cpu().numpy(), gs.cpu().numpy()
+        assert not np.isfinite(gr[0, [1, 4, 5]]).all() and np.isfinite(gr[0, [0, 2, 3]]).all()
+        assert not np.isfinite(gs[0, [1, 4, 5]]).all() and np.isfinite(gs[0, [0, 2, 3]]).all()
+    else:
+        got = tp_backproject_2d(Gd, Rd, sd, N, CUBIC, 1.0, 11.0).cpu().numpy()
+        _nonfinite_parity(got, ref, "backproject_2d")
