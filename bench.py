@@ -2,19 +2,21 @@
 
 One step = the whole path on one batch: forward projection, then the
 backward of a loss on its output: the adjoint for the reference gradient
-and the rotation + shift gradients.  By default the forward saves each
-output's Jacobian with respect to its sample point (tp_project_3d_jac) and
-one launch (tp_backward_3d_jac) runs the adjoint and streams the Jacobian
-for the pose gradients; ``--pose-grads recompute`` times tp_project_3d +
-tp_backproject_3d + tp_grad_pose instead, which gathers from the reference a
-second time.  The other kernels' times ride along in ``extras``.  Default workload (``c4``): a 256^3 blob phantom (rfft
-half-spectrum 256x256x129 complex64), 4096 uniform SO(3) poses, shifts
-U[-10,10] px, Catmull-Rom cubic, oversampling 1, cutoff 128.
+and the rotation + shift gradients, with nothing stored between the two
+beyond the forward's output.  By default (``--pose-grads separate``) the
+step is tp_project_3d + tp_backproject_3d + tp_grad_pose.  ``--pose-grads
+jacobian`` times the path that stores each output's Jacobian in the forward
+(tp_project_3d_jac + tp_backward_3d_jac, 24 extra bytes per output); the
+kernels of the other modes ride along in ``extras``.  Default workload
+(``c4``): a 256^3 blob phantom (rfft half-spectrum 256x256x129 complex64),
+4096 uniform SO(3) poses, shifts U[-10,10] px, Catmull-Rom cubic,
+oversampling 1, cutoff 128.
 
 Prints one JSON line:  value = projections/s forward+backward; the forward
-rate, per-kernel times, the roofline of the dominant kernel and the CPU
-baseline (the fp64 oracle on a bounded pose sample, timed on the host before
-the GPU is touched) ride along.
+rate, per-kernel times, the roofline of the dominant kernel (tap bytes
+against the L2 bandwidth from unit counts and clock, with the compulsory
+HBM bytes beside it) and the CPU baseline (the fp64 oracle on a bounded
+pose sample, timed on the host before the GPU is touched) ride along.
 """
 from __future__ import annotations
 
@@ -127,11 +129,8 @@ def _oracle_worker_2d(idx):
 
 def cpu_baseline_2d(V, R, s, G, w: synth.Workload, images_per_worker: int):
     """The oracle's 2D path on a seeded sample of images, in forked workers."""
-    try:
-        ncpu = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncpu = os.cpu_count() or 1
-    workers = max(1, min(16, ncpu))
+    ncpu = host_cores()
+    workers = max(1, min(CPU_SHARE, ncpu))
     rng = np.random.default_rng(12345)
     n_img = min(w.B, max(images_per_worker, 1) * 32)  # all 256 images at the default: a few seconds
     sample = np.sort(rng.choice(w.B, size=n_img, replace=False))
@@ -150,8 +149,10 @@ def cpu_baseline_2d(V, R, s, G, w: synth.Workload, images_per_worker: int):
         "value": n / wall,
         "unit": "images/s fwd+bwd",
         "cores": workers,
+        "host_cores": ncpu,
         "kind": "oracle",
-        "sample": f"{n} of {w.B} images (seeded), {workers} single-threaded workers, fork pool",
+        "sample": f"{n} of {w.B} images (seeded), {workers} single-threaded workers, fork pool "
+                  f"({ncpu} host cores visible)",
         "value_1core": n / (fwd + bwd) if fwd + bwd > 0 else None,
         "wall_s": wall,
     }
@@ -247,13 +248,22 @@ def bench_2d(args, w: synth.Workload):
     print(json.dumps(res), flush=True)
 
 
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+# A GPU machine gives one GPU's process a CPU share of 16 cores, whatever the
+# host shows: the oracle's pool takes at most that many workers.
+CPU_SHARE = 16
+
+
 def cpu_baseline(V, R, s, w: synth.Workload, N: int, os_: float, poses_per_worker: int):
     """Time the oracle on a bounded pose sample with a fork pool (no GPU yet)."""
-    try:
-        ncpu = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncpu = os.cpu_count() or 1
-    workers = max(1, min(16, ncpu))
+    ncpu = host_cores()
+    workers = max(1, min(CPU_SHARE, ncpu))
     rng = np.random.default_rng(12345)
     sample = rng.choice(w.P, size=workers * poses_per_worker, replace=False)
     G = synth.make_upstream(w, poses=sample)
@@ -274,8 +284,10 @@ def cpu_baseline(V, R, s, w: synth.Workload, N: int, os_: float, poses_per_worke
         "value": rate_total,
         "unit": "projections/s fwd+bwd",
         "cores": workers,
+        "host_cores": ncpu,
         "kind": "oracle",
-        "sample": f"{n} of {w.P} poses (seeded), {workers} single-threaded workers, fork pool",
+        "sample": f"{n} of {w.P} poses (seeded), {workers} single-threaded workers, fork pool "
+                  f"({ncpu} host cores visible)",
         "fwd_proj_per_s": n / (fwd / workers) if fwd > 0 else None,
         # one core: poses per second of a single-threaded worker's own time
         "value_1core": n / (fwd + bwd) if fwd + bwd > 0 else None,
@@ -581,9 +593,12 @@ def main():
                     help="c2 runs the 2D -> 2D path (images/s); the others the 3D -> 2D path")
     ap.add_argument("--oversampling", type=int, default=1, choices=[1, 2])
     ap.add_argument("--poses", type=int, default=0, help="override the pose count")
-    ap.add_argument("--pose-grads", choices=["jacobian", "recompute"], default="jacobian",
-                    help="pose gradients from the forward's saved Jacobian, or by a second gather pass")
+    ap.add_argument("--pose-grads", choices=["separate", "jacobian"], default="separate",
+                    help="separate: the adjoint and a second gather pass for the pose gradients, nothing stored; "
+                         "jacobian: the forward saves each output's Jacobian for the backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the step only: no other kernels, no peak probes (for counter runs)")
     ap.add_argument("--cpu-poses-per-worker", type=int, default=10)
     ap.add_argument("--study", choices=["oversampling"], default=None,
                     help="run a study instead of the step benchmark")
@@ -672,12 +687,14 @@ def main():
                                         R.shape[0], sd.data_ptr(), s.shape[0], N, w.interp, os_, w.cutoff,
                                         dV.data_ptr(), dR.data_ptr(), ds.data_ptr(), sh), "tp_backward_3d_jac")
 
-    if args.pose_grads == "jacobian":
-        kernels = [("project_jac", fwd_jac), ("backward_jac", bwd_jac)]
-        other = [("project", fwd), ("backproject", adj), ("grad_pose_jac", grad_jac), ("grad_pose", grad)]
-    else:
-        kernels = [("project", fwd), ("backproject", adj), ("grad_pose", grad)]
-        other = [("project_jac", fwd_jac), ("backward_jac", bwd_jac), ("grad_pose_jac", grad_jac)]
+    modes = {
+        "separate": [("project", fwd), ("backproject", adj), ("grad_pose", grad)],
+        "jacobian": [("project_jac", fwd_jac), ("backward_jac", bwd_jac)],
+    }
+    kernels = modes[args.pose_grads]
+    named = dict(kernels)
+    other = [(n, f) for m in modes.values() for n, f in m if n not in named]
+    other.append(("grad_pose_jac", grad_jac))
 
     # calibration for HBM byte counters: one plain streaming copy (y = x * 1)
     # of known size, outside the timed region.  A counter run of this same
@@ -703,10 +720,15 @@ def main():
             ev[k][j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    avg_names = {name for name, _ in kernels}
     # the widened ops, timed after the step on the same inputs (not part of it)
-    extras = time_extras(L, _lib, torch, stream, Gd, Rd, R, dV, w, N, os_, B, P)
-    for name, f in other:  # the other pose-gradient path, same inputs
-        extras[name + "_ms"] = time_launches(torch, stream, f)
+    extras = {}
+    if not args.no_extras:
+        extras = time_extras(L, _lib, torch, stream, Gd, Rd, R, dV, w, N, os_, B, P)
+        for name, f in other:  # the other pose-gradient paths, same inputs
+            extras[name + "_ms"] = time_launches(torch, stream, f)
+    elif "project" not in avg_names:
+        extras["project_ms"] = time_launches(torch, stream, fwd)
 
     per_kernel = {name: [] for name, _ in kernels}
     step_ms = []
@@ -719,6 +741,9 @@ def main():
     ms_step = float(np.mean(step_ms))
     fwd_bwd_rate = B * P / (ms_step * 1e-3)
     fwd_ms = avg["project"] if "project" in avg else extras["project_ms"]
+    # the step's tap bytes against the unit-count L2 figure (3 B_tap per
+    # forward + backward: the forward's gather, the adjoint's scatter and the
+    # pose gradients' gather)
     fwd_rate = B * P / (fwd_ms * 1e-3)  # the plain forward (no Jacobian saved)
 
     # algorithmic traffic / work per launch
@@ -741,52 +766,61 @@ def main():
     tap_bytes = {"project": units * taps * 8, "project_jac": units * taps * 8, "backproject": units * taps * 8,
                  "grad_pose": units * taps * 8, "grad_pose_jac": 0, "backward_jac": units * taps * 8}
     dom = max(avg, key=avg.get)
-    achieved = hbm[dom] / (avg[dom] * 1e-3) / 1e9
     wl_key = f"{w.name}_os{args.oversampling}" + (f"_p{P}" if args.poses else "")
     traffic = measured_traffic(wl_key, copy_bytes)
+    # The dominant kernel on the bound that applies to a gather or scatter:
+    # its tap bytes (8 B x taps x in-cutoff outputs per pass over the taps)
+    # against the L2 bandwidth derived from unit counts and clock (8 XCDs x
+    # 16 channels x 128 B/clk x 2.4 GHz); the compulsory HBM bytes against
+    # HBM's 8 TB/s beside it.
+    achieved = tap_bytes[dom] / (avg[dom] * 1e-3) / 1e9
+    achieved_hbm = hbm[dom] / (avg[dom] * 1e-3) / 1e9
     roof = {
         "kernel": dom,
-        "bound": "hbm",
+        "bound": "l2",
         "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBS,
+        "peak": L2_PEAK_GBS,
         "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "frac": round(achieved / L2_PEAK_GBS, 4),
         "traffic": traffic.get(dom),
-        "algorithmic_bytes_per_launch": hbm[dom],
+        "algorithmic_bytes_per_launch": tap_bytes[dom],
+        "hbm_compulsory": {"bytes_per_launch": hbm[dom], "achieved": round(achieved_hbm, 1),
+                           "peak": HBM_PEAK_GBS, "frac": round(achieved_hbm / HBM_PEAK_GBS, 4)},
     }
-    # the on-chip term that actually bounds a gather / scatter: tap bytes
-    # (8 B x taps x in-cutoff outputs) against the L2 peak derived from unit
-    # counts and clock (8 XCDs x 16 channels x 128 B/clk x 2.4 GHz)
+    # every kernel's tap bytes against the same L2 figure
     tap_roof = {
         k: {"achieved": round(tap_bytes[k] / (avg[k] * 1e-3) / 1e9, 1),
             "frac": round(tap_bytes[k] / (avg[k] * 1e-3) / 1e9 / L2_PEAK_GBS, 4)}
         for k in avg if tap_bytes[k]
     }
-    roof_tap = {"bound": "l2", "peak": L2_PEAK_GBS, "unit": "GB/s",
-                "tap_bytes_per_launch": tap_bytes[dom], "kernels": tap_roof}
+    roof_tap = {"bound": "l2", "peak": L2_PEAK_GBS, "unit": "GB/s", "kernels": tap_roof}
     # the same fractions against this GPU's measured peaks (probes run after
     # the timed steps); the adjoint's LDS adds against the measured LDS rate
-    peaks = measure_peaks(torch, dev, stream)
+    peaks = {} if args.no_extras else measure_peaks(torch, dev, stream)
     frac_measured = {}
-    for k in avg:
+    for k in (avg if peaks else ()):
         f = {"hbm_compulsory": round(hbm[k] / (avg[k] * 1e-3) / 1e9 / peaks["hbm_read_GBs"], 4)}
         if tap_bytes[k]:
             f["l2_tap"] = round(tap_bytes[k] / (avg[k] * 1e-3) / 1e9 / peaks["l2_read_GBs"], 4)
         if k in ("backproject", "backward_jac"):
             f["lds_tap_adds"] = round(units * taps / (avg[k] * 1e-3) / 1e9 / peaks["lds_add64_Glanes_per_s"], 4)
         frac_measured[k] = f
-    peaks["fractions"] = frac_measured
+    if peaks:
+        peaks["fractions"] = frac_measured
     # the tap-gather roofline of the whole step at the measured L2 peak, with
     # the scope table's accounting: B_tap = 8 B x taps x in-cutoff outputs
     # per call; a forward touches B_tap, a forward + backward 3 B_tap (a
     # gather for the pose gradients and a scatter for the volume)
     b_tap = units * taps * 8
-    roof_fwd = B * P / (b_tap / (peaks["l2_read_GBs"] * 1e9))
-    peaks["l2_tap_roofline"] = {
-        "fwd_proj_per_s": round(roof_fwd, 1), "fwd_frac": round(fwd_rate / roof_fwd, 4),
-        "fwd_bwd_proj_per_s": round(roof_fwd / 3, 1), "fwd_bwd_frac": round(fwd_bwd_rate / (roof_fwd / 3), 4),
-        "b_tap_per_call": b_tap,
-    }
+    if peaks:
+        # (the L2 probe is a measured lower bound of the L2 read rate, about
+        # half the unit-count figure: fractions against it are upper bounds)
+        roof_fwd = B * P / (b_tap / (peaks["l2_read_GBs"] * 1e9))
+        peaks["l2_tap_roofline_at_probe"] = {
+            "fwd_proj_per_s": round(roof_fwd, 1), "fwd_frac": round(fwd_rate / roof_fwd, 4),
+            "fwd_bwd_proj_per_s": round(roof_fwd / 3, 1), "fwd_bwd_frac": round(fwd_bwd_rate / (roof_fwd / 3), 4),
+            "b_tap_per_call": b_tap,
+        }
     res = {
         "metric": METRIC,
         "value": round(fwd_bwd_rate, 1),
@@ -808,6 +842,8 @@ def main():
             "oversampling": args.oversampling, "cutoff": w.cutoff, "in_cutoff_outputs_per_pose": n_c,
         },
         "fwd_proj_per_s": round(fwd_rate, 1),
+        "step_l2_tap_frac": round(3 * units * taps * 8 / (ms_step * 1e-3) / 1e9 / L2_PEAK_GBS, 4),
+        "fwd_l2_tap_frac": round(units * taps * 8 / (fwd_ms * 1e-3) / 1e9 / L2_PEAK_GBS, 4),
         "kernel_ms_mean": {k: round(v, 4) for k, v in avg.items()},
         "kernel_ms_median": {k: round(v, 4) for k, v in med.items()},
         "wall_s_timed": round(wall, 3),

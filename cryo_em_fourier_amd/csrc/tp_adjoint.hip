@@ -57,15 +57,20 @@ struct AdjShape {
   static constexpr int WAVES_PER_EU = BS == 512 ? 4 : 3;
 };
 constexpr int kPrefetch = 2;        // hits whose G values a thread loads at once
-// Fixed point: per group, |sum| < 2^kQuantumBits q at every voxel, with
-// q = 2^e / 2^kQuantumBits >= 8 sum_poses(dens) max|G| / 2^kQuantumBits.
-// A pose's share of a voxel is at most 2 max|G| (a lattice point carries a
-// real and a mirror value) times the sum of |w| over its lattice points,
-// which is about dens times the plane integral of |kernel|: sampled over
-// 20,000 random poses and voxel offsets it stays below 1.6 dens (Catmull-Rom)
-// and 1.25 dens (linear) for oversampling 0.25 to 2.  The bound takes 4 dens,
-// and 29 bits leave another factor 4 of int32 headroom.
-constexpr int kQuantumBits = 29;
+// Fixed point.  A pose adds to a voxel at most 2 m (a lattice point carries
+// a real and a mirror value, m the largest |re| + |im| of G) times W, the sum
+// of |w| over its lattice points.  Searched over orientations, voxel offsets
+// and oversampling 0.25 to 2 (a CPU test), W / dens stays below 1.62 (cubic
+// slices), 1.27 (linear slices), 2.05 (cubic volume lattices) and 1.44
+// (linear volume lattices); nearly degenerate rows cap dens at 0.4 times
+// their rectangle's lattice count + 1, which bounds W by itself (every |w| <=
+// 1).  The quantum assumes W <= kDensBound dens:
+//   q = 2 kDensBound sum_poses(dens) m_assume / 2^kQuantumBits,
+// not rounded to a power of two, with m_assume >= the group's m (checked;
+// else the group is redone).  Every int32 sum then stays below
+// 2.05 / 2.5 * 2^30, under 2^31 / 2.4.
+constexpr float kDensBound = 2.5f;
+constexpr int kQuantumBits = 30;
 
 // kSliceGrad / kVolumeGrad: kSlice / kVolume followed by B * P workgroups
 // (1D grid) that each reduce one pose's gradients from a saved Jacobian (the
@@ -325,7 +330,7 @@ __device__ __forceinline__ PoseView vol_view(const OpParams& p, int b, const Box
   pv.hit = finite3(pv.u) && finite3(pv.v) && finite3(pv.w) && pv.kx0 <= pv.kx1 && pv.ky0 <= pv.ky1 &&
            pv.kz0 <= pv.kz1;
   if (pv.hit)
-    pv.dens = fminf(pv.dens, 0.25f * (float)(pv.kx1 - pv.kx0 + 1) * (float)(pv.ky1 - pv.ky0 + 1) *
+    pv.dens = fminf(pv.dens, 0.4f * (float)(pv.kx1 - pv.kx0 + 1) * (float)(pv.ky1 - pv.ky0 + 1) *
                                  (float)(pv.kz1 - pv.kz0 + 1) + 1.f);
   return pv;
 }
@@ -652,11 +657,10 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
     while (nh > 0) {
       float inv_q = 0.f;
       if (!measure_only) {
-        int e;
-        frexpf(fminf(8.f * dens_sum * m_assume, 3e38f), &e);
-        e = max(e, -90);  // |G| below ~1e-27 gets a coarser quantum than needed
-        inv_q = ldexpf(1.f, kQuantumBits - e);
-        q = ldexpf(1.f, e - kQuantumBits);
+        // (|G| below ~1e-19 gets a coarser quantum than needed)
+        const float x = fminf(fmaxf(2.f * kDensBound * dens_sum * m_assume, 0x1p-60f), 3e38f);
+        q = ldexpf(x, -kQuantumBits);
+        inv_q = 1.f / q;
       }
       float amax = 0.f;
       bool bad = false;

@@ -109,8 +109,9 @@ __device__ __forceinline__ PoseView pose_view(const OpParams& p, int b, const Bo
   if (pv.kx0 > pv.kx1 || pv.ky0 > pv.ky1) pv.hit = 0;
   // every weight is at most 1 in magnitude, so a pose adds at most its
   // rectangle's lattice count of them to a voxel: this caps the density
-  // bound of nearly degenerate rows
-  if (pv.hit) pv.dens = fminf(pv.dens, 0.25f * (float)(pv.kx1 - pv.kx0 + 1) * (float)(pv.ky1 - pv.ky0 + 1) + 1.f);
+  // bound of nearly degenerate rows (the adjoint assumes 2.5 dens per pose,
+  // and 2.5 (0.4 count + 1) exceeds the count)
+  if (pv.hit) pv.dens = fminf(pv.dens, 0.4f * (float)(pv.kx1 - pv.kx0 + 1) * (float)(pv.ky1 - pv.ky0 + 1) + 1.f);
   return pv;
 }
 

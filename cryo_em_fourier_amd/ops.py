@@ -11,12 +11,12 @@ autograd functions wrapping the native ops):
 
 * ``project_3d`` / ``project_2d``: the backward calls the adjoint for the
   reference gradient and ``tp_grad_pose`` for the rotation and shift
-  gradients, each only when needed.  When the 3D op needs pose gradients
-  its forward runs ``tp_project_3d_jac``, which also saves each output's
-  Jacobian with respect to its sample point (3 complex values per output),
-  and the backward takes them from ``tp_grad_pose_jac`` in one streaming
-  pass instead of a second pass of gathers (``save_jacobian=False`` keeps
-  the recomputing path and its smaller memory).
+  gradients, each only when needed; nothing is kept from the forward but
+  its inputs (it page tech. section 3: a single pass without intermediate
+  tensors).  ``project_3d(save_jacobian=True)`` opts into a forward
+  (``tp_project_3d_jac``) that also saves each output's Jacobian with
+  respect to its sample point (3 complex values per output, 24 bytes), which
+  the backward then streams instead of gathering from the reference again.
 * ``backproject_3d`` / ``backproject_2d``: backprojection as an op of its
   own (2D -> 3D; it page tech. section 2, list of operations), optionally
   with the x = 0 plane symmetrised.  Its backward is the forward projection
@@ -301,11 +301,12 @@ class _Project(torch.autograd.Function):
 
 
 def project_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0,
-               save_jacobian=True):
+               save_jacobian=False):
     """Differentiable 3D->2D projection (gradients to vol, rot and shift).
 
-    With pose gradients needed and save_jacobian, the forward keeps 24 bytes
-    per output for a backward without a second gather pass."""
+    By default the forward stores nothing beyond its inputs.  With pose
+    gradients needed and save_jacobian=True, it keeps 24 bytes per output
+    for a backward without a second gather pass."""
     return _Project.apply(vol, rot, shift, 3, n_out, interp, oversampling, cutoff, save_jacobian)
 
 
@@ -637,7 +638,7 @@ class _Rotate(torch.autograd.Function):
         return d_vol, d_rot, d_shift, None, None, None, None, None
 
 
-def rotate_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0, save_jacobian=True):
+def rotate_3d(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0, save_jacobian=False):
     """Differentiable 3D->3D rotation (gradients to vol, rot and shift).
 
     With pose gradients needed and save_jacobian (output boxes up to 1023),

@@ -64,11 +64,12 @@
  * Results.  Forward and pose gradients are deterministic up to the order of
  *   float atomics that merge per-workgroup partial sums of the pose
  *   gradients.  The adjoint sums each brick's contributions exactly in
- *   int32 fixed point, one power-of-two quantum per group of up to 16 poses
- *   (for oversampling >= 1 at most 2^-20 of the largest |proj| read by that
- *   group or the previous one), and merges the pose chunks of bricks near
- *   the origin with float atomics, so its last bits there may differ
- *   between runs.
+ *   int32 fixed point, one quantum per group of up to 16 poses (for
+ *   oversampling >= 1 at most 2^-22 of the largest |re| + |im| of proj read
+ *   by that group or the previous one), and merges the pose chunks of bricks
+ *   near the origin with float atomics, so its last bits there may differ
+ *   between runs.  A non-finite proj value makes the voxels its stencil
+ *   reaches NaN (the rest of the adjoint is unaffected).
  */
 #ifndef TP_H
 #define TP_H

@@ -2,11 +2,12 @@
 
 The brick adjoint sums every brick's contributions exactly in int32 fixed
 point.  Its quantum assumes that one pose adds to one voxel at most
-4 * dens * (the largest |value| it carries), where dens is the pose's lattice
+2.5 * dens * 2 * (the largest |value| a lattice point carries: a real and a
+mirror value), where dens is the pose's lattice
 density (max(1, 1 / |u x v|) for a slice with rows u = os R[0, :],
 v = os R[1, :]; max(1, 1 / |det|) for the 3D -> 3D rotation's volume
 lattice): the sum over the lattice points k of |w(p(k) - t)|, the separable
-kernel's weight at voxel t, must stay below 4 * dens.  Nothing on the pages
+kernel's weight at voxel t, must stay below 2.5 * dens.  Nothing on the pages
 fixes this number; it is a property of the kernels (Keys' a = -0.5 cubic and
 the tent) and the lattice geometry, so it is searched here: every cube
 rotation at half-voxel offsets, random orientations, oversampling 0.25 to 2
@@ -21,7 +22,7 @@ import pytest
 from scipy.optimize import minimize
 from scipy.spatial.transform import Rotation
 
-BOUND = 4.0  # the multiple of dens the adjoint's quantum assumes
+BOUND = 2.5  # the multiple of dens the adjoint's quantum assumes
 
 
 def kern(interp, t):
