@@ -29,6 +29,7 @@ EXPORTS = (
     "tp_rotate_3d",
     "tp_rotate_backproject_3d",
     "tp_rotate_grad_pose",
+    "tp_backward_3d",
     "tp_project_3d_jac",
     "tp_grad_pose_jac",
     "tp_backward_3d_jac",
@@ -68,6 +69,10 @@ _SIGS = {
     # vol, B, N, grad_out, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, grad_rot, grad_shift, stream
     "tp_rotate_grad_pose": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp,
                              _vp], _int),
+    # vol, B, N, grad_out, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, vol_grad,
+    # grad_rot, grad_shift, stream
+    "tp_backward_3d": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp, _vp,
+                        _vp], _int),
     # vol, B, N, rot, B_rot, P, shift, B_shift, N_out, interp, os, cutoff, out, jac, stream
     "tp_project_3d_jac": ([_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _int, _f32, _f32, _vp, _vp, _vp],
                           _int),

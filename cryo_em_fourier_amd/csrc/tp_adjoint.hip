@@ -14,8 +14,8 @@
 // tap contributions to the brick in LDS.  LDS float atomics are slow on this
 // part, integer ones are not: contributions are accumulated as int32 fixed
 // point (exact, order independent; a (re, im) pair packed in one 64-bit
-// word, or one int32 for the real weight volume), with a power-of-two
-// quantum chosen per group of poses from a bound on |G| that is checked
+// word, or one int32 for the real weight volume), with a quantum chosen per
+// group of poses from a bound on |G| that is checked
 // against the values read (a group that exceeds it is redone), so the sums
 // cannot overflow; each group is flushed into fp32 registers.  Bricks are split over pose chunks in
 // proportion to the poses expected to cross them (near the origin: all of
@@ -26,17 +26,15 @@
 // adjoint of the 3D -> 3D rotation (volume lattices), and the fused
 // backwards: the adjoint followed, in the same launch, by workgroups that
 // stream the pose gradients from a saved Jacobian (tp_gradjac.h).
-#include "tp_bricks.h"
+#include "tp_adjoint.h"
 #include "tp_gradjac.h"
-#include "tp_internal.h"
-#include "tp_stencil.h"
 
 namespace tp {
 
 namespace {
 
-constexpr int kVox = 4096;          // voxels per brick
-constexpr int kGroupMax = 16;       // poses per fixed-point group
+using namespace adj;
+
 // Workgroup shapes.  512 threads (8 waves, two workgroups per CU, 4 waves
 // per SIMD) with a hit list that holds a whole pose group, for dense
 // lattices; 256 threads (three workgroups per CU, 3 waves per SIMD) for
@@ -56,184 +54,10 @@ struct AdjShape {
   static constexpr int PER_THREAD = (NVOX + BS - 1) / BS;     // brick voxels per thread
   static constexpr int WAVES_PER_EU = BS == 512 ? 4 : 3;
 };
-constexpr int kPrefetch = 2;        // hits whose G values a thread loads at once
-// Fixed point.  A pose adds to a voxel at most 2 m (a lattice point carries
-// a real and a mirror value, m the largest |re| + |im| of G) times W, the sum
-// of |w| over its lattice points.  Searched over orientations, voxel offsets
-// and oversampling 0.25 to 2 (a CPU test), W / dens stays below 1.62 (cubic
-// slices), 1.27 (linear slices), 2.05 (cubic volume lattices) and 1.44
-// (linear volume lattices); nearly degenerate rows cap dens at 0.4 times
-// their rectangle's lattice count + 1, which bounds W by itself (every |w| <=
-// 1).  The quantum assumes W <= kDensBound dens:
-//   q = 2 kDensBound sum_poses(dens) m_assume / 2^kQuantumBits,
-// not rounded to a power of two, with m_assume >= the group's m (checked;
-// else the group is redone).  Every int32 sum then stays below
-// 2.05 / 2.5 * 2^30, under 2^31 / 2.4.
-constexpr float kDensBound = 2.5f;
-constexpr int kQuantumBits = 30;
-
 // kSliceGrad / kVolumeGrad: kSlice / kVolume followed by B * P workgroups
 // (1D grid) that each reduce one pose's gradients from a saved Jacobian (the
 // fused backwards of the projection and of the rotation)
 constexpr int kSlice = 0, kWeights = 1, kVolume = 2, kSliceGrad = 3, kVolumeGrad = 4;
-
-template <int NDIM> struct Brick;
-template <> struct Brick<3> { static constexpr int X = 16, Y = 16, Z = 16; };
-template <> struct Brick<2> { static constexpr int X = 64, Y = 64, Z = 1; };
-
-// LDS accumulator of a brick: W slots (packed (re, im) pairs, or int32 real
-// parts for the weight volume) holding the brick's (y, z) rows of X voxels
-// at a stride of S = X + kGuard slots, starting kGuard slots in, so the
-// kGuard slots before each row are shared guard slots: a tap up to kGuard
-// voxels beyond the brick in x, on either side, lands in them and they are
-// never read.  A tap's slot is then its row's base plus a compile-time
-// offset, and no x test is needed.  Bank pairs are slot mod 16: the odd row
-// stride and a z-plane stride of 5 mod 16 (padded) keep taps that differ in
-// y or z only off each other's banks.
-constexpr int kGuard = 3;  // the cubic stencil reaches 3 voxels past its first tap
-// G guard rows and planes follow the brick's last row and plane (exclusive
-// y and z ownership).
-template <int NDIM, int G = 0>
-struct AccLayout {
-  static constexpr int S = Brick<NDIM>::X + kGuard;
-  static constexpr int ROWS = Brick<NDIM>::Y + G;
-  static constexpr int PZ = NDIM == 3 ? ROWS * S + ((5 - ROWS * S % 16) + 16) % 16 : 0;
-  static constexpr int W = (NDIM == 3 ? (Brick<NDIM>::Z + G) * PZ : Brick<NDIM>::Y * S) + kGuard;
-};
-template <int NDIM, int G = 0>
-__device__ __forceinline__ int acc_word(int x, int y, int z) {
-  return kGuard + z * AccLayout<NDIM, G>::PZ + y * AccLayout<NDIM, G>::S + x;
-}
-
-// (re, im) int32 pair as one int64, re * 2^32 + im: sums of such values
-// decode uniquely while both component sums stay inside int32.
-__device__ __forceinline__ unsigned long long pack_pair(int re, int im) {
-  const unsigned hi = (unsigned)(re + (im >> 31));
-  return ((unsigned long long)hi << 32) | (unsigned)im;
-}
-__device__ __forceinline__ void unpack_pair(unsigned long long v, int& re, int& im) {
-  im = (int)(unsigned)(v & 0xFFFFFFFFull);
-  re = (int)(long long)((long long)v >> 32) + (im < 0 ? 1 : 0);
-}
-
-// float -> int32, rounding to nearest (ties up): one VALU instruction.
-__device__ __forceinline__ int cvt_rpi(float x) {
-  int r;
-  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
-  return r;
-}
-
-struct BrickPos {
-  int b;            // batch entry
-  int x0, y0, z0;   // first voxel (x from 0, y and z signed)
-  int x1, y1, z1;   // last voxel (inclusive, clipped to the stored range)
-  int xlim, ylim, zlim;  // last x column, y row and z plane that taps are
-                         // spread to (x1, y1 and z1, or with exclusive
-                         // ownership the guards in range)
-  bool xbottom, ybottom, zbottom;  // the lowest brick of the stored x / y / z range
-  int n0, n1;       // pose range of this workgroup
-  bool chunked;     // merged with atomics
-  bool valid;
-};
-
-// Pose chunks of a brick.  A random plane through the origin meets a ball of
-// radius rho centred at distance r with probability about rho / r, so bricks
-// near the origin see every pose and outer ones a fraction; each chunk gets
-// about pmax of the poses expected to reach the brick.
-template <int NDIM>
-__device__ __forceinline__ int brick_chunks(const OpParams& p, const BrickParams& bp, int x0, int y0,
-                                            int z0) {
-  using BR = Brick<NDIM>;
-  double frac = 1.0;
-  if (NDIM == 3) {
-    const double cx = x0 + 0.5 * (BR::X - 1), cy = y0 + 0.5 * (BR::Y - 1), cz = z0 + 0.5 * (BR::Z - 1);
-    const double r = sqrt(cx * cx + cy * cy + cz * cz);
-    const double rho = 0.5 * sqrt(3.0) * (BR::X + 4);
-    frac = r > rho ? rho / r : 1.0;
-  }
-  const double c = ceil((double)p.P * frac / (double)bp.pmax);
-  return (int)fmin(fmax(c, 1.0), (double)bp.cmax);
-}
-
-template <int NDIM, bool VOL>
-__device__ __forceinline__ BrickPos decode(const OpParams& p, const BrickParams& bp, uint32_t lin) {
-  using BR = Brick<NDIM>;
-  BrickPos r;
-  // plain round-robin over the XCDs: consecutive bricks (and the mostly empty
-  // high chunk slots) spread evenly; bricks share little data across XCDs.
-  // High chunk slots go first: only the busiest bricks near the origin have
-  // them, so the long workgroups start early and the short ones fill the end.
-  const int brick = (int)(lin % (uint32_t)bp.nbricks);
-  const int ch = bp.cmax - 1 - (int)((lin / (uint32_t)bp.nbricks) % (uint32_t)bp.cmax);
-  r.b = (int)(lin / ((uint32_t)bp.nbricks * (uint32_t)bp.cmax));
-  const int bi = brick % bp.nb[0], bj = (brick / bp.nb[0]) % bp.nb[1], bk = brick / (bp.nb[0] * bp.nb[1]);
-  const int lo = -(p.N / 2), hi = (p.N + 1) / 2 - 1;
-  r.x0 = bi * BR::X;
-  r.x1 = min(r.x0 + BR::X - 1, p.N / 2);
-  r.y0 = lo + bj * BR::Y;
-  r.y1 = min(r.y0 + BR::Y - 1, hi);
-  if (NDIM == 3) {
-    r.z0 = lo + bk * BR::Z;
-    r.z1 = min(r.z0 + BR::Z - 1, hi);
-  } else {
-    r.z0 = r.z1 = 0;
-  }
-  r.xlim = r.x1;
-  r.ylim = r.y1;
-  r.zlim = r.z1;
-  r.xbottom = r.x0 == 0;
-  r.ybottom = r.y0 == lo;
-  r.zbottom = r.z0 == (NDIM == 3 ? lo : 0);
-  // every pose of a volume lattice reaches every brick inside its sphere
-  const int nch = VOL ? bp.cmax : brick_chunks<NDIM>(p, bp, r.x0, r.y0, r.z0);
-  r.valid = ch < nch && r.b < p.B;
-  r.chunked = nch > 1;
-  r.n0 = (int)((long long)p.P * ch / nch);
-  r.n1 = (int)((long long)p.P * (ch + 1) / nch);
-  return r;
-}
-
-// Sample points whose stencil can reach the brick lie in the brick widened
-// by the stencil reach: [x0 - r, x1 + r) per axis (r = 2 cubic, 1 linear);
-// any point outside has all its taps outside the brick.  With exclusive z
-// ownership the brick takes in z only the points whose first tap lies in
-// [z0, z1], q_z in [z0 - OFF, z1 + r), except the lowest brick, which also
-// takes those whose first tap lies below the stored range.
-template <int NDIM, int INTERP, bool EXCLZ = false>
-__device__ __forceinline__ Box reach_box(const BrickPos& br) {
-  constexpr double reach = INTERP ? 2.0 : 1.0;
-  Box bx = {{br.x0 - reach, br.y0 - reach, br.z0 - reach}, {br.x1 + reach, br.y1 + reach, br.z1 + reach}};
-  if (EXCLZ && !br.zbottom) bx.lo[2] = (double)(br.z0 - Kern<INTERP>::OFF);
-  if (EXCLZ && !br.ybottom) bx.lo[1] = (double)(br.y0 - Kern<INTERP>::OFF);
-  if (EXCLZ && !br.xbottom) bx.lo[0] = (double)(br.x0 - Kern<INTERP>::OFF);
-  if (NDIM == 2) bx.lo[2] = bx.hi[2] = 0.0;
-  return bx;
-}
-
-// A lattice point (kx, ky) of the full plane carries the real output (kx, ky)
-// when kx >= 0 and the mirror of the real output (-kx, -ky) when kx <= 0.
-__device__ __forceinline__ void lattice_parts(const OpParams& p, int kx, int ky, bool& real, bool& mirr) {
-  const int rlo = -(p.No / 2), rhi = (p.No - 1) / 2;
-  real = kx >= 0 && kx <= p.No / 2 && ky >= rlo && ky <= rhi;
-  mirr = kx <= 0 && -kx <= p.No / 2 && -ky >= rlo && -ky <= rhi;
-}
-
-// G entries of a lattice point: the real output (kx, ky) and the real output
-// (-kx, -ky) whose mirror it carries (zero where absent).
-// (WEIGHTS: real weights, as (w, 0).)
-template <bool WEIGHTS>
-__device__ __forceinline__ void lattice_load(const OpParams& p, size_t img, int kx, int ky, float2& gr,
-                                             float2& gm) {
-  bool real, mirr;
-  lattice_parts(p, kx, ky, real, mirr);
-  if (WEIGHTS) {
-    gr = make_float2(real ? p.wimg[out_index(p, img, kx, ky)] : 0.f, 0.f);
-    gm = make_float2(mirr ? p.wimg[out_index(p, img, -kx, -ky)] : 0.f, 0.f);
-  } else {
-    gr = real ? p.img[out_index(p, img, kx, ky)] : make_float2(0.f, 0.f);
-    gm = mirr ? p.img[out_index(p, img, -kx, -ky)] : make_float2(0.f, 0.f);
-  }
-}
 
 // ---- volume lattice (the adjoint of the 3D -> 3D rotation) ----
 // Lattice point k = (kx, ky, kz) of the full output volume carries the real
@@ -398,30 +222,6 @@ __device__ __forceinline__ int list_hits_vol(const OpParams& p, const Box& bx, c
   return carry;
 }
 
-// Phase B: sample point and the values spread by a lattice point that hit.
-struct Cand {
-  double q[3];
-  float2 v0;   // value for taps at x = 0 (real part only)
-  float2 v1;   // value for taps at x >= 1 (real + conj(mirror))
-};
-
-template <int NDIM>
-__device__ __forceinline__ void lattice_values(const OpParams& p, const PoseView& pv, int kx, int ky,
-                                               float2 gr, float2 gm, Cand& cd) {
-#pragma unroll
-  for (int j = 0; j < NDIM; ++j) cd.q[j] = (double)kx * pv.u[j] + (double)ky * pv.v[j];
-  float2 cr = gr, cm = gm;
-  if (p.shift) {
-    // conj(phase(k)) G(k), and for the mirror conj(phase(-k)) G(-k) =
-    // phase(k) G(-k): one phase per lattice point
-    const float2 ph = shift_phase(kx, ky, pv.sx, pv.sy, p.inv_no);
-    cr = cmul(conjf2(ph), gr);
-    cm = cmul(ph, gm);
-  }
-  cd.v0 = cr;
-  cd.v1 = make_float2(cr.x + cm.x, cr.y - cm.y);
-}
-
 __device__ __forceinline__ void lattice_values3(const OpParams& p, const PoseView& pv, int kx, int ky, int kz,
                                                 float2 gr, float2 gm, Cand& cd) {
 #pragma unroll
@@ -439,104 +239,6 @@ __device__ __forceinline__ void lattice_values3(const OpParams& p, const PoseVie
   cd.v0 = cr;
   cd.v1 = make_float2(cr.x + cm.x, cr.y - cm.y);
 }
-
-// Hit of thread tid within a block of workgroup-size consecutive hits: each
-// pair of waves takes alternate hits of its own 128.
-// Consecutive hits are neighbouring lattice points whose sample points can
-// share a voxel, and lanes adding to one LDS address in the same instruction
-// serialise; two lattice steps apart (two voxels at oversampling 1) they
-// cannot.  Measured against strides 1, 4 and 8, which were slower.
-__device__ __forceinline__ int hit_slot(int tid) { return (tid & 63) * 2 + ((tid >> 6) & 1) + (tid >> 7) * 64 * 2; }
-
-// Spread one lattice point over its taps inside the brick (int32 fixed point).
-// The point lies in the brick's reach box, so its first x tap is at most
-// kGuard voxels before the brick and its last at most kGuard after it: taps
-// outside the brick in x fall into guard words.  Rows outside in y or z are
-// skipped.  REAL: int32 real parts only (the weight volume), else packed
-// pairs.
-template <int NDIM, int INTERP, bool REAL, int G = 0>
-__device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float inv_q, unsigned long long* acc) {
-  using BR = Brick<NDIM>;
-  using L = AccLayout<NDIM, G>;
-  using K = Kern<INTERP>;
-  constexpr int T = K::T;
-  static_assert(T - 1 <= kGuard, "guard words must cover the stencil");
-  const AxisPos ax = axis_pos(cd.q[0], K::OFF), ay = axis_pos(cd.q[1], K::OFF);
-  float wx[T], wy[T], wz[T];
-  K::w(ax.f, wx);
-  K::w(ay.f, wy);
-  int z0 = 0;
-  if (NDIM == 3) {
-    const AxisPos az = axis_pos(cd.q[2], K::OFF);
-    K::w(az.f, wz);
-    z0 = az.x0;
-  } else {
-#pragma unroll
-    for (int d = 0; d < T; ++d) wz[d] = d == 0 ? 1.f : 0.f;
-  }
-  // x weights folded with the per-x value (x = 0 takes the real part only)
-  float are[T], aim[T];
-#pragma unroll
-  for (int d = 0; d < T; ++d) {
-    const float2 v = ax.x0 + d >= 1 ? cd.v1 : cd.v0;
-    are[d] = wx[d] * v.x * inv_q;
-    aim[d] = wx[d] * v.y * inv_q;
-    // with guard columns read back, a tap before x = 0 (whose slot is the
-    // previous row's guard column) must add nothing
-    if (G > 0 && ax.x0 + d < 0) are[d] = aim[d] = 0.f;
-  }
-  const int x0w = acc_word<NDIM, G>(ax.x0 - br.x0, 0, 0);
-#pragma unroll
-  for (int dz = 0; dz < (NDIM == 3 ? T : 1); ++dz) {
-    const int tz = z0 + dz;
-    if (NDIM == 3 && (tz < br.z0 || tz > br.zlim)) continue;
-#pragma unroll
-    for (int dy = 0; dy < T; ++dy) {
-      const int ty = ay.x0 + dy;
-      if (ty < br.y0 || ty > br.ylim) continue;
-      const float wyz = wy[dy] * wz[dz];
-      const int w = x0w + (NDIM == 3 ? tz - br.z0 : 0) * L::PZ + (ty - br.y0) * L::S;
-#pragma unroll
-      for (int dx = 0; dx < T; ++dx) {
-        if (REAL) atomicAdd(reinterpret_cast<int*>(acc) + w + dx, cvt_rpi(are[dx] * wyz));
-        else atomicAdd(acc + w + dx, pack_pair(cvt_rpi(are[dx] * wyz), cvt_rpi(aim[dx] * wyz)));
-      }
-    }
-  }
-}
-
-// Mark the accumulator slots (set them to 1) that a lattice point's taps
-// reach inside the brick, where its spread values are not finite: the x = 0
-// taps when v0 is not, the x >= 1 taps when v1 is not (the same taps and row
-// tests as spread(), whatever their weight: the product of a weight of 0 and a
-// non-finite value is not finite either).
-template <int NDIM, int INTERP, bool REAL, int G = 0>
-__device__ __forceinline__ void mark_taps(const BrickPos& br, const double* q, bool bad0, bool bad1,
-                                          unsigned long long* acc) {
-  using L = AccLayout<NDIM, G>;
-  using K = Kern<INTERP>;
-  constexpr int T = K::T;
-  const AxisPos ax = axis_pos(q[0], K::OFF), ay = axis_pos(q[1], K::OFF);
-  const int z0 = NDIM == 3 ? axis_pos(q[2], K::OFF).x0 : 0;
-  const int x0w = acc_word<NDIM, G>(ax.x0 - br.x0, 0, 0);
-  for (int dz = 0; dz < (NDIM == 3 ? T : 1); ++dz) {
-    const int tz = z0 + dz;
-    if (NDIM == 3 && (tz < br.z0 || tz > br.zlim)) continue;
-    for (int dy = 0; dy < T; ++dy) {
-      const int ty = ay.x0 + dy;
-      if (ty < br.y0 || ty > br.ylim) continue;
-      const int w = x0w + (NDIM == 3 ? tz - br.z0 : 0) * L::PZ + (ty - br.y0) * L::S;
-      for (int dx = 0; dx < T; ++dx) {
-        const int tx = ax.x0 + dx;
-        if (tx < 0 || !(tx == 0 ? bad0 : bad1)) continue;
-        if (REAL) reinterpret_cast<int*>(acc)[w + dx] = 1;
-        else acc[w + dx] = 1ull;
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ bool finite2(float2 v) { return isfinite(v.x) && isfinite(v.y); }
 
 // MODE: kSlice (the projector's adjoint), kWeights (real weight volume),
 // kVolume (the adjoint of the 3D -> 3D rotation: volume lattices, one pose
@@ -629,14 +331,14 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
           s_view[tid] = VOL ? vol_view(p, br.b, bx, s_poses[g0 + tid])
                             : pose_view<NDIM>(p, br.b, bx, s_poses[g0 + tid], false);
         __syncthreads();
-        float dens_sum = 0.f;
-        for (int g = 0; g < cnt; ++g)
-          if (s_view[g].hit) dens_sum += s_view[g].dens;
+        float dens_sum;
+        int cum[kGroupMax];
+        group_sums<kGroupMax>(s_view, cnt, dens_sum, cum);
         for (int h0 = 0, hits_total = 1; h0 < hits_total; h0 += kHitCap) {
           // phase A: list the lattice points that can reach the brick (this
           // slice keeps the flat indices [h0, h0 + kHitCap))
           hits_total = VOL ? list_hits_vol<BS>(p, bx, s_view[0], h0, kHitCap, s_hits, s_wcnt)
-                           : list_hits<NDIM, kGroupMax, BS>(p, bx, s_view, cnt, h0, kHitCap, s_hits, s_wcnt);
+                           : list_hits<NDIM, kGroupMax, BS>(p, bx, s_view, cum, h0, kHitCap, s_hits, s_wcnt);
           on_slice(max(0, min(hits_total, h0 + kHitCap) - h0), dens_sum);
           __syncthreads();
         }
@@ -705,13 +407,15 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
         s_bad[wave] = wbad;
       }
       __syncthreads();
-      float gmax = s_red[0];
+      // one read per lane, then readlane: the workgroup's max and flag
+      const float rv = lane < BS / 64 ? s_red[lane] : 0.f;
+      const int bv = lane < BS / 64 ? s_bad[lane] : 0;
+      float gmax = 0.f;
 #pragma unroll
-      for (int w = 1; w < BS / 64; ++w) {
-        gmax = fmaxf(gmax, s_red[w]);
-        brick_bad = brick_bad || s_bad[w] != 0;
+      for (int w = 0; w < BS / 64; ++w) {
+        gmax = fmaxf(gmax, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rv), w)));
+        brick_bad = brick_bad || __builtin_amdgcn_readlane(bv, w) != 0;
       }
-      brick_bad = brick_bad || s_bad[0] != 0;
       if (!(gmax > 0.f)) break;  // an all-zero slice adds nothing
       if (!measure_only && gmax <= m_assume) {
         // flush the slice into fp32 registers

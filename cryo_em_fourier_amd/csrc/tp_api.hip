@@ -305,6 +305,39 @@ tp_status tp_grad_pose(int ndim, const tp_c64* ref, int64_t B, int64_t N, const 
   return hip_status(tp::launch_grad_pose(p, interp, s));
 }
 
+tp_status tp_backward_3d(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* grad_out, const float* rot,
+                         int64_t B_rot, int64_t P, const float* shift, int64_t B_shift, int64_t N_out,
+                         int interp, float oversampling, float cutoff, tp_c64* vol_grad, float* grad_rot,
+                         float* grad_shift, void* stream) {
+  if (!vol || !grad_out || !aligned8(vol) || !aligned8(grad_out)) return TP_EINVAL;
+  if (vol_grad && !aligned8(vol_grad)) return TP_EINVAL;
+  if ((grad_rot && !aligned4(grad_rot)) || (grad_shift && !aligned4(grad_shift))) return TP_EINVAL;
+  if (grad_shift && B_shift != 1 && B_shift != B) return TP_EINVAL;
+  tp::OpParams p;
+  const Common c{B, N, P, N_out, B_rot, B_shift, interp, 3, oversampling, cutoff, rot, shift};
+  const tp_status st = check_and_fill(c, p);
+  if (st != TP_OK) return st;
+  if (vol_grad && (N_out > tp::kMaxBrickOut || B > 65535 || tp::adjoint_blocks(p) > kMaxBlocks ||
+                   tp::backward_blocks(p) > kMaxBlocks))
+    return TP_EUNSUPPORTED;
+  if (!vol_grad && !grad_rot && !grad_shift) return TP_OK;
+  p.ref = reinterpret_cast<const float2*>(vol);
+  p.img = reinterpret_cast<const float2*>(grad_out);
+  p.ref_out = reinterpret_cast<float2*>(vol_grad);
+  p.grad_rot = grad_rot;
+  p.grad_shift = grad_shift;
+  if (!shift) p.B_shift = (int)B_shift;
+  const hipStream_t s = (hipStream_t)stream;
+  if (grad_rot && tp::launch_zero(grad_rot, (size_t)p.B_rot * p.P * 9 * sizeof(float), s) != hipSuccess)
+    return TP_EHIP;
+  if (grad_shift && tp::launch_zero(grad_shift, (size_t)p.B_shift * p.P * 2 * sizeof(float), s) != hipSuccess)
+    return TP_EHIP;
+  if (!vol_grad) return hip_status(tp::launch_grad_pose(p, interp, s));
+  if (tp::launch_zero(p.ref_out, ref_bytes_total(p), s) != hipSuccess) return TP_EHIP;
+  if (!grad_rot && !grad_shift) return hip_status(tp::launch_backproject(p, interp, s));
+  return hip_status(tp::launch_backward(p, interp, s));
+}
+
 tp_status tp_project_3d_jac(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot,
                             int64_t P, const float* shift, int64_t B_shift, int64_t N_out, int interp,
                             float oversampling, float cutoff, tp_c64* out, tp_c64* jac, void* stream) {

@@ -229,11 +229,13 @@ __device__ __forceinline__ int scan_poses_if(Meets meets, int w0, int n1, int* s
   __syncthreads();
   if (lane == 0) s_wcnt[wave] = __popcll(m);
   __syncthreads();
+  const int wc = lane < BS / 64 ? s_wcnt[lane] : 0;  // one read per lane, then readlane
   int off = 0, total = 0;
 #pragma unroll
   for (int w = 0; w < BS / 64; ++w) {
-    off += w < wave ? s_wcnt[w] : 0;
-    total += s_wcnt[w];
+    const int c = __builtin_amdgcn_readlane(wc, w);
+    off += w < wave ? c : 0;
+    total += c;
   }
   if (hit) s_poses[off + __popcll(m & ((1ull << lane) - 1ull))] = n;
   __syncthreads();
@@ -247,25 +249,44 @@ __device__ __forceinline__ int scan_poses(const OpParams& p, int b, const Box& b
   return scan_poses_if<BS>([&](int n) { return plane_meets<NDIM>(p, b, bx, n); }, w0, n1, s_poses, s_wcnt);
 }
 
+// Uniform sums over a group's pose views s_view[0, cnt) (cnt <= MAXG): the
+// lattice density summed over the poses that hit, and cum[g], the candidate
+// rows of poses 0..g.  Each lane below cnt reads one view, and the values go
+// to every lane through readlane (scalar registers), so the group costs one
+// LDS read per lane instead of a loop of reads of every view by every
+// thread.  The density sum is taken in pose order.
+template <int MAXG>
+__device__ __forceinline__ void group_sums(const PoseView* s_view, int cnt, float& dens_sum, int* cum) {
+  const int lane = threadIdx.x & 63;
+  int H = 0;
+  float d = 0.f;
+  if (lane < cnt && s_view[lane].hit) {
+    H = s_view[lane].ky1 - s_view[lane].ky0 + 1;
+    d = s_view[lane].dens;
+  }
+  int run = 0;
+  float ds = 0.f;
+#pragma unroll
+  for (int g = 0; g < MAXG; ++g) {
+    run += __builtin_amdgcn_readlane(H, g);
+    cum[g] = run;
+    ds += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), g));
+  }
+  dens_sum = ds;
+}
+
 // List the lattice points of the poses s_view[0, cnt) (cnt <= MAXG) whose
 // sample points fall in the (widened) box, row by row.  The flat index runs
 // over the rows of pose 0, then pose 1, ...; entries with flat index in
-// [h0, h0 + cap) go to s_hits[flat - h0].  Returns the total count (the same
-// for every h0).  Every thread of the workgroup calls it.
+// [h0, h0 + cap) go to s_hits[flat - h0].  cum: group_sums' row counts.
+// Returns the total count (the same for every h0).
+// Every thread of the workgroup calls it.
 template <int NDIM, int MAXG, int BS = kBlock>
-__device__ __forceinline__ int list_hits(const OpParams& p, const Box& bx, const PoseView* s_view, int cnt,
+__device__ __forceinline__ int list_hits(const OpParams& p, const Box& bx, const PoseView* s_view, const int* cum,
                                          int h0, int cap, uint32_t* s_hits, int* s_wcnt) {
   static_assert(MAXG <= kHitPoses, "pose slot does not fit the hit tag");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int cum[MAXG];  // rows of poses 0..g (uniform)
-  int rows_total = 0;
-#pragma unroll
-  for (int g = 0; g < MAXG; ++g) {
-    int H = 0;
-    if (g < cnt && s_view[g].hit) H = s_view[g].ky1 - s_view[g].ky0 + 1;
-    rows_total += __builtin_amdgcn_readfirstlane(H);
-    cum[g] = rows_total;
-  }
+  const int rows_total = cum[MAXG - 1];
   const int h1 = h0 + cap;
   int carry = 0;
   for (int rw = 0; rw < rows_total; rw += BS) {
@@ -294,11 +315,13 @@ __device__ __forceinline__ int list_hits(const OpParams& p, const Box& bx, const
     }
     if (lane == 63) s_wcnt[wave] = incl;
     __syncthreads();
+    const int wc = lane < BS / 64 ? s_wcnt[lane] : 0;  // one read per lane, then readlane
     int off = carry + incl - cr, tot = 0;
 #pragma unroll
     for (int w = 0; w < BS / 64; ++w) {
-      off += w < wave ? s_wcnt[w] : 0;
-      tot += s_wcnt[w];
+      const int c = __builtin_amdgcn_readlane(wc, w);
+      off += w < wave ? c : 0;
+      tot += c;
     }
     for (int j = max(0, h0 - off); j < cr && off + j < h1; ++j) s_hits[off + j - h0] = hit_tag(g, r - rb, a + j);
     carry += tot;

@@ -9,11 +9,11 @@ outputs with torch and pass raw pointers and the current HIP stream.
 Differentiable forms (torch.autograd.Function; pages, tech. section 2:
 autograd functions wrapping the native ops):
 
-* ``project_3d`` / ``project_2d``: the backward calls the adjoint for the
-  reference gradient and ``tp_grad_pose`` for the rotation and shift
-  gradients, each only when needed; nothing is kept from the forward but
-  its inputs (it page tech. section 3: a single pass without intermediate
-  tensors).  ``project_3d(save_jacobian=True)`` opts into a forward
+* ``project_3d`` / ``project_2d``: the backward computes the reference
+  gradient (the adjoint) and the rotation and shift gradients, each only
+  when needed; in 3D both together come from ``tp_backward_3d`` in one pass.
+  Nothing is kept from the forward but its inputs (it page tech. section 3:
+  a single pass without intermediate tensors).  ``project_3d(save_jacobian=True)`` opts into a forward
   (``tp_project_3d_jac``) that also saves each output's Jacobian with
   respect to its sample point (3 complex values per output, 24 bytes), which
   the backward then streams instead of gathering from the reference again.
@@ -180,6 +180,32 @@ def tp_grad_pose(ref, grad_out, rot, shift=None, interp="cubic", oversampling=1.
     return gr, gs
 
 
+def tp_backward_3d(vol, grad_out, rot, shift=None, interp="cubic", oversampling=1.0, cutoff=-1.0,
+                   want_vol=True, want_rot=True, want_shift=True, B_shift=None):
+    """The backward of tp_project_3d in one pass, storing nothing from the
+    forward: (d_vol [B,N,N,N//2+1] or None, grad_rot [B_rot,P,3,3] or None,
+    grad_shift or None), the values of tp_backproject_3d and tp_grad_pose."""
+    B, N = _ref_dims(vol, 3, "reference")
+    B_rot, P, Bs = _pose_dims(rot, shift, 3, B, vol.device)
+    _need(grad_out, "grad_out", torch.complex64, 4)
+    if grad_out.shape[0] != B or grad_out.shape[1] != P or grad_out.shape[3] != grad_out.shape[2] // 2 + 1:
+        raise ValueError(f"grad_out must be [{B}, {P}, n, n//2+1], got {tuple(grad_out.shape)}")
+    if grad_out.device != vol.device:
+        raise ValueError("grad_out is on another device")
+    n_out = grad_out.shape[2]
+    if shift is None:
+        Bs = 1 if B_shift is None else int(B_shift)
+    dev = vol.device
+    dv = torch.empty_like(vol) if want_vol else None
+    gr = torch.empty_like(rot) if want_rot else None
+    gs = torch.empty((Bs, P, 2), dtype=torch.float32, device=dev) if want_shift else None
+    st = _lib.lib().tp_backward_3d(vol.data_ptr(), B, N, grad_out.data_ptr(), rot.data_ptr(), B_rot, P,
+                                   _ptr(shift), Bs, n_out, _interp(interp), float(oversampling), float(cutoff),
+                                   _ptr(dv), _ptr(gr), _ptr(gs), _stream(dev))
+    _lib.check(st, "tp_backward_3d")
+    return dv, gr, gs
+
+
 def tp_project_3d_jac(vol, rot, shift=None, n_out=None, interp="cubic", oversampling=1.0, cutoff=-1.0):
     """tp_project_3d that also returns the Jacobian of each output w.r.t. its
     sample point: (out [B,P,n,n//2+1], jac [B,P,3,n,n//2+1]) c64."""
@@ -287,6 +313,11 @@ class _Project(torch.autograd.Function):
             # both gradients from one launch
             d_ref, d_rot, d_shift = tp_backward_3d_jac(g, out, jac, rot, shift, ref.shape[1], interp,
                                                        oversampling, cutoff, want_rot, want_shift)
+            return d_ref, d_rot, d_shift, None, None, None, None, None, None
+        if ndim == 3 and ctx.needs_input_grad[0] and (want_rot or want_shift):
+            # both gradients in one pass over the reference
+            d_ref, d_rot, d_shift = tp_backward_3d(ref, g, rot, shift, interp, oversampling, cutoff, True,
+                                                   want_rot, want_shift)
             return d_ref, d_rot, d_shift, None, None, None, None, None, None
         if ctx.needs_input_grad[0]:
             d_ref = _backproject(ndim, g, rot, shift, ref.shape[1], interp, oversampling, cutoff)

@@ -92,7 +92,7 @@ typedef enum {
 } tp_status;
 
 /* ABI version of this header (major * 100 + minor). */
-#define TP_ABI_VERSION 100
+#define TP_ABI_VERSION 101
 int tp_abi_version(void);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -247,6 +247,38 @@ tp_status tp_grad_pose(int ndim, const tp_c64* ref, int64_t B, int64_t N,
                        const float* shift, int64_t B_shift,
                        int64_t N_out, int interp, float oversampling, float cutoff,
                        float* grad_rot, float* grad_shift, void* stream);
+
+/*
+ * The backward of tp_project_3d in one pass, storing nothing between the
+ * forward and the backward (it page tech. section 3: a single pass without
+ * intermediate tensors): for L = Re sum conj(grad_out) * project_3d(vol,
+ * rot, shift),
+ *   vol_grad   = dL/dvol, the adjoint of tp_backproject_3d applied to
+ *                grad_out (ko page tech. section 2: the backward is the
+ *                adjoint; conjugate phase)
+ *   grad_rot, grad_shift = the rotation and shift gradients of tp_grad_pose
+ *                (ar page tech. section 2: chain rule through the
+ *                interpolation kernel's derivative)
+ * For the cubic kernel both come from one walk over the lattice points,
+ * with the reference read from LDS tiles beside the adjoint's accumulator;
+ * the linear kernel runs tp_backproject_3d's and tp_grad_pose's kernels.
+ * Results are those of the two calls (the adjoint's fixed point as
+ * tp_backproject_3d; gradient sums merged with float atomics).
+ *   vol        [B, N, N, N/2+1] complex64, input (the forward's reference)
+ *   grad_out   [B, P, N_out, N_out/2+1] complex64, input
+ *   rot, shift as tp_project_3d
+ *   vol_grad   [B, N, N, N/2+1] complex64, overwritten, or NULL to skip
+ *   grad_rot   [B_rot, P, 3, 3] float32, overwritten (last row 0), or NULL
+ *   grad_shift [B_shift, P, 2] float32, overwritten, or NULL (with shift ==
+ *              NULL the shift is 0 and grad_shift still has B_shift rows)
+ * With vol_grad NULL this is tp_grad_pose (ndim 3), with both gradients
+ * NULL tp_backproject_3d.  Errors as tp_backproject_3d and tp_grad_pose.
+ */
+tp_status tp_backward_3d(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* grad_out,
+                         const float* rot, int64_t B_rot, int64_t P,
+                         const float* shift, int64_t B_shift, int64_t N_out,
+                         int interp, float oversampling, float cutoff,
+                         tp_c64* vol_grad, float* grad_rot, float* grad_shift, void* stream);
 
 /*
  * Forward 3D -> 2D that also saves what the pose gradients need, so that

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(L, name), name
     assert set(declared_functions()) == set(_lib.EXPORTS)
-    assert L.tp_abi_version() == 100
+    assert L.tp_abi_version() == 101
 
 
 def test_status_strings():
@@ -61,6 +61,13 @@ def grad(**kw):
              N_out=32, interp=1, os=1.0, cutoff=16.0, gr=FAKE, gs=None, stream=None)
     a.update(kw)
     return _lib.lib().tp_grad_pose(*a.values())
+
+
+def bwd3(**kw):
+    a = dict(vol=FAKE, B=1, N=32, g=FAKE, rot=FAKE, B_rot=1, P=4, shift=None, B_shift=1, N_out=32,
+             interp=1, os=1.0, cutoff=16.0, vg=FAKE, gr=FAKE, gs=None, stream=None)
+    a.update(kw)
+    return _lib.lib().tp_backward_3d(*a.values())
 
 
 EINVAL, EUNSUP = _lib.TP_EINVAL, _lib.TP_EUNSUPPORTED
@@ -99,6 +106,22 @@ def test_backproject_3d_argument_checks(kw, code):
 ])
 def test_grad_pose_argument_checks(kw, code):
     assert grad(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(vol=None), EINVAL), (dict(g=None), EINVAL), (dict(rot=None), EINVAL),
+    (dict(vol=FAKE_ODD), EINVAL), (dict(vg=FAKE_ODD), EINVAL), (dict(gr=FAKE + 2), EINVAL),
+    (dict(gs=FAKE, B=2, B_rot=2, B_shift=3), EINVAL), (dict(interp=2), EINVAL), (dict(os=0.0), EINVAL),
+    (dict(cutoff=math.nan), EINVAL), (dict(B=3, B_rot=2), EINVAL),
+    (dict(N=2000), EUNSUP), (dict(N_out=16384), EUNSUP), (dict(B=70000, B_rot=1), EUNSUP),
+])
+def test_backward_3d_argument_checks(kw, code):
+    assert bwd3(**kw) == code
+
+
+def test_backward_3d_with_nothing_to_compute_launches_nothing():
+    # no volume gradient and no pose gradients: valid, and no device access
+    assert bwd3(vg=None, gr=None, gs=None) == _lib.TP_OK
 
 
 def test_2d_entry_points_check_arguments():

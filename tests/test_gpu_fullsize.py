@@ -296,19 +296,58 @@ def test_grad_bricks_against_oracle(interp, os_, batch):
     assert not gr[:, rest].any() and not gs[:, rest].any()
 
 
+@pytest.mark.parametrize("key", KEYS)
+def test_fullsize_backward_sampled_poses(key):
+    """tp_backward_3d (the one-pass backward of the benchmark's step) over all
+    poses with the sparse upstream gradient: its volume gradient is the
+    oracle's adjoint of the sampled poses, their pose gradients the oracle's,
+    every other pose's gradients exactly 0."""
+    import torch
+
+    from cryo_em_fourier_amd import tp_backward_3d
+
+    c = workload(key)
+    w = c["w"]
+    log(f"[fullsize backward_3d] {key}: {w.P} poses, upstream nonzero on {c['idx'].tolist()}")
+    dv, gr, gs = tp_backward_3d(to_dev(c["V"]), _sparse_upstream(c), to_dev(c["R"]), to_dev(c["s"]), w.interp,
+                                c["os"], w.cutoff)
+    dv, gr, gs = dv.cpu().numpy(), gr.cpu().numpy(), gs.cpu().numpy()
+    torch.cuda.empty_cache()
+    ref = oracle.backproject(c["G_sub"], c["R"][:, c["idx"]], c["s"][:, c["idx"]], c["N"], w.interp, c["os"],
+                             w.cutoff)
+    assert_parity(dv, ref, f"backward_3d volume {key}")
+    dR, ds = oracle.grad_pose(c["V"], c["G_sub"], c["R"][:, c["idx"]], c["s"][:, c["idx"]], w.N_out, w.interp,
+                              c["os"], w.cutoff)
+    assert_parity(gr[:, c["idx"]], dR, f"backward_3d grad_rot {key}")
+    assert_parity(gs[:, c["idx"]], ds, f"backward_3d grad_shift {key}")
+    rest = np.setdiff1d(np.arange(w.P), c["idx"])
+    assert not gr[:, rest].any() and not gs[:, rest].any(), "poses with zero upstream must get zero gradients"
+
+
 def test_fullsize_c3_adjoint_dense_all_poses():
     """c3 (box 128, 1024 poses) with a dense upstream gradient on every pose:
-    the adjoint in the benchmark's launch shape, element by element against
-    the oracle's (summed over pose chunks in CPU worker processes).  Every
-    brick near the origin runs dozens of fixed-point groups and pose chunks."""
+    the adjoint and the one-pass backward in the benchmark's launch shape.
+    Volumes element by element against the oracle's adjoint (summed over pose
+    chunks in CPU worker processes); the one-pass backward's pose gradients
+    of sampled poses against the oracle's (a pose's gradient depends on its
+    own upstream values only).  Every brick near the origin runs dozens of
+    fixed-point groups and pose chunks."""
     from _gpu import oracle_backproject_pooled
 
-    from cryo_em_fourier_amd import tp_backproject_3d
+    from cryo_em_fourier_amd import tp_backproject_3d, tp_backward_3d
 
     w = synth.WORKLOADS["c3"]
-    R, s = synth.make_rotations(w), synth.make_shifts(w)
+    V, R, s = synth.make_reference(w), synth.make_rotations(w), synth.make_shifts(w)
     G = synth.make_upstream(w, poses=np.arange(w.P))
     log(f"[fullsize adjoint dense] c3: {w.P} poses, dense upstream")
-    got = tp_backproject_3d(to_dev(G), to_dev(R), to_dev(s), w.N, w.interp, 1.0, w.cutoff).cpu().numpy()
+    Gd, Rd, sd = to_dev(G), to_dev(R), to_dev(s)
+    got = tp_backproject_3d(Gd, Rd, sd, w.N, w.interp, 1.0, w.cutoff).cpu().numpy()
+    dv, gr, gs = tp_backward_3d(to_dev(V), Gd, Rd, sd, w.interp, 1.0, w.cutoff)
+    dv, gr, gs = dv.cpu().numpy(), gr.cpu().numpy(), gs.cpu().numpy()
     ref = oracle_backproject_pooled(G, R, s, w.N, w.interp, 1.0, w.cutoff)
     assert_parity(got, ref, "adjoint c3 dense")
+    assert_parity(dv, ref, "backward_3d volume c3 dense")
+    idx = np.sort(np.random.default_rng(31).choice(w.P, size=6, replace=False))
+    dR, ds = oracle.grad_pose(V, G[:, idx], R[:, idx], s[:, idx], w.N_out, w.interp, 1.0, w.cutoff)
+    assert_parity(gr[:, idx], dR, "backward_3d grad_rot c3 dense (sampled poses)")
+    assert_parity(gs[:, idx], ds, "backward_3d grad_shift c3 dense (sampled poses)")

@@ -52,6 +52,8 @@ def case3d(name):
         "ragged":        (40, 37, 1, 4, 1, 1, CUBIC, 40 / 37, 18.0, "cplx", "so3"),
         "mixed-rot":     (24, 24, 2, 4, 2, 1, CUBIC, 1.0, 11.0, "cplx", "so3"),
         "mixed-shift":   (22, 20, 2, 3, 1, 2, LINEAR, 1.1, 9.0, "cplx", "so3"),
+        "bcast-cubic":   (20, 22, 3, 3, 1, 1, CUBIC, 1.0, 10.5, "cplx", "so3"),
+        "adv-cubic-cplx": (32, 32, 1, 8, 1, 1, CUBIC, 1.0, 15.0, "cplx", "adv"),
     }[name]
     N, n_out, B, P, B_rot, B_shift, interp, os_, cutoff, vk, pk = spec
     if vk == "c1":
@@ -75,7 +77,7 @@ def case3d(name):
 
 
 CASES3 = ["c1", "c1-cubic", "odd-nocut", "os2", "os1.5-linear", "batch", "batch-bcast",
-          "adv-cubic", "adv-linear", "ragged", "mixed-rot", "mixed-shift"]
+          "adv-cubic", "adv-linear", "ragged", "mixed-rot", "mixed-shift", "bcast-cubic", "adv-cubic-cplx"]
 
 
 def _dev(c):
