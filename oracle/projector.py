@@ -461,3 +461,27 @@ def rotate_grad_pose(V, G, R, s, n_out: int, interp: int, os: float = 1.0, cutof
                 ds[bs, n, i] += np.sum(np.real(g * (-2j * np.pi * ks[i] / n_out) * S))
     return dR, ds
 
+
+
+# ------------------------------------------------- the caller's spectrum step
+
+def spectrum(real, ndim: int, pad_to: int | None = None):
+    """The reference the projector samples, made from a centred real box
+    (the last ``ndim`` axes; leading axes are a batch): zero-padded to
+    ``pad_to`` (default: no padding) with the box centre N // 2 placed at
+    the padded box's centre M // 2, the centre moved to index 0
+    (ifftshift), then rfftn, complex128.  With pad_to = os * N the
+    projector samples it at oversampling os: the pages' on-the-fly
+    oversampling pays this padding and FFT on every pass (it/de/ja pages,
+    results section on interpolation), and their reference layout is
+    PyTorch's rfftn half-spectrum (tech. section 2 of every page)."""
+    x = np.asarray(real, np.float64)
+    N = x.shape[-1]
+    M = N if pad_to is None else int(pad_to)
+    if M < N or any(d != N for d in x.shape[-ndim:]):
+        raise ValueError("a cube (square) of side N, padded to M >= N")
+    big = np.zeros(x.shape[:-ndim] + (M,) * ndim)
+    off = M // 2 - N // 2
+    big[(Ellipsis,) + (slice(off, off + N),) * ndim] = x
+    axes = tuple(range(-ndim, 0))
+    return np.fft.rfftn(np.fft.ifftshift(big, axes=axes), axes=axes)

@@ -149,3 +149,63 @@ def test_symmetrize_algebra(shape):
     lhs = np.real(np.vdot(Sa, b))
     rhs = np.real(np.vdot(a, oracle.symmetrize_x0(b)))
     assert abs(lhs - rhs) < 1e-10
+
+
+# ------------------------------------------------- the caller's spectrum step
+# A centred delta transforms to 1, an offset delta to a pure phase ramp, and
+# zero-padding to 2N samples the same transform twice as finely (the even
+# indices are the unpadded spectrum): the definition of the DFT with its
+# origin at the box centre, which is what on-the-fly oversampling relies on.
+
+SPECTRUM_CASES = [(3, 8, None), (3, 8, 16), (3, 7, 14), (3, 6, 9), (2, 10, 20), (2, 9, None), (2, 9, 18)]
+
+
+def _spectrum_shape(ndim, M):
+    return (M,) * (ndim - 1) + (M // 2 + 1,)
+
+
+@pytest.mark.parametrize("ndim,N,M", SPECTRUM_CASES)
+def test_spectrum_of_the_centred_delta_is_one(ndim, N, M):
+    x = np.zeros((N,) * ndim)
+    x[(N // 2,) * ndim] = 1.0
+    S = oracle.spectrum(x, ndim, M)
+    assert S.shape == _spectrum_shape(ndim, N if M is None else M)
+    np.testing.assert_allclose(S, 1.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("ndim,N,M", SPECTRUM_CASES)
+def test_spectrum_of_an_offset_delta_is_a_phase_ramp(ndim, N, M):
+    rng = np.random.default_rng(ndim * 100 + N)
+    d = rng.integers(-(N // 2), (N + 1) // 2, ndim)      # offset from the centre, array order
+    x = np.zeros((N,) * ndim)
+    x[tuple(N // 2 + d)] = 1.0
+    Mm = N if M is None else M
+    S = oracle.spectrum(x, ndim, M)
+    grids = np.meshgrid(*[np.arange(n) for n in _spectrum_shape(ndim, Mm)], indexing="ij")
+    expect = np.exp(-2j * np.pi * sum(g * di for g, di in zip(grids, d)) / Mm)
+    np.testing.assert_allclose(S, expect, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("ndim,N", [(3, 8), (3, 7), (2, 12), (2, 11)])
+def test_twice_padded_spectrum_at_even_indices_is_the_unpadded_one(ndim, N):
+    x = np.random.default_rng(N).standard_normal((2,) + (N,) * ndim)   # a batch of two boxes
+    S1 = oracle.spectrum(x, ndim)
+    S2 = oracle.spectrum(x, ndim, 2 * N)
+    assert S2.shape == (2,) + _spectrum_shape(ndim, 2 * N)
+    np.testing.assert_allclose(S2[(Ellipsis,) + (slice(None, None, 2),) * ndim], S1, rtol=0,
+                               atol=1e-10 * np.abs(S1).max())
+
+
+@pytest.mark.parametrize("ndim,N,M", SPECTRUM_CASES)
+def test_spectrum_dc_and_parseval(ndim, N, M):
+    x = np.random.default_rng(7 + N).standard_normal((N,) * ndim)
+    Mm = N if M is None else M
+    S = oracle.spectrum(x, ndim, M)
+    assert abs(S[(0,) * ndim] - x.sum()) < 1e-10
+    # the full spectrum's energy: half-spectrum columns with a mirror that is
+    # not stored count twice
+    w = np.full(S.shape[-1], 2.0)
+    w[0] = 1.0
+    if Mm % 2 == 0:
+        w[-1] = 1.0
+    assert np.isclose(float((np.abs(S) ** 2 * w).sum()), Mm ** ndim * float((x * x).sum()), rtol=1e-12)

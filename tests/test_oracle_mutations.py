@@ -52,6 +52,9 @@ MUTATIONS = [
      "kx[:, None] * Rm[:, 0][None, :] + ky[:, None] * Rm[:, 1][None, :] + kz[:, None] * Rm[:, 2][None, :]"),
     ("rotation drops kz", "+ kz[:, None] * Rm[2][None, :])", ")"),
     ("3D phase drops s_z", "(kx * sv[0] + ky * sv[1] + kz * sv[2]) / n_out", "(kx * sv[0] + ky * sv[1]) / n_out"),
+    ("spectrum pad off centre", "off = M // 2 - N // 2", "off = M // 2 - (N - 1) // 2"),
+    ("spectrum without ifftshift", "np.fft.rfftn(np.fft.ifftshift(big, axes=axes), axes=axes)",
+     "np.fft.rfftn(big, axes=axes)"),
     ("rotation gradient row 2 dropped", "for i in range(3):\n                dR[br, n, i, :]", "for i in range(2):\n                dR[br, n, i, :]"),
 ]
 
