@@ -490,21 +490,96 @@ def shell_stats(got, truth, keep, n_out: int, fracs=(0.1, 0.2, 0.3, 0.4, 0.45, 0
     return res
 
 
+def kernel_ft(interp: int, nu: np.ndarray) -> np.ndarray:
+    """Continuous Fourier transform of the interpolation kernel (tent or
+    Keys' a = -0.5 cubic; both even) at nu cycles per voxel, by quadrature."""
+    t = np.linspace(-2.0, 2.0, 40001)
+    a = np.abs(t)
+    if interp == synth.LINEAR:
+        w = np.maximum(0.0, 1.0 - a)
+    else:
+        w = np.where(a <= 1, 1.5 * a ** 3 - 2.5 * a ** 2 + 1, np.where(a < 2, -0.5 * a ** 3 + 2.5 * a ** 2 - 4 * a + 2, 0.0))
+    nu = np.asarray(nu, np.float64)
+    return np.trapezoid(w[None, :] * np.cos(2 * np.pi * nu.reshape(-1, 1) * t[None, :]), t, axis=1).reshape(nu.shape)
+
+
+def attenuation_study(pipelines, N: int, n_out: int, cutoff: float, poses_per_dir: int = 16, n_dirs: int = 3,
+                      fracs=(0.0, 0.05, 0.1, 0.15, 0.2, 0.25, 0.3, 0.35, 0.4, 0.45), sigma: float = 1.5):
+    """Real-space intensity against radius.  Phantoms of small blobs
+    (sigma 1.5 voxels, amplitude 1) at r = f N from the box centre along a
+    seeded direction, projected by each pipeline along poses that see the
+    direction nearly in plane (in-plane length >= 0.95, so the blobs'
+    images stay apart); each projection goes back to real space (irfft2)
+    and each blob's intensity (the sum over a disc of radius 4 sigma about
+    its projected centre) is divided by the same sum in the analytic
+    projection.  ``predicted``: the product over axes of the kernel's
+    Fourier transform at the blob's position in cycles per voxel of the
+    (padded) reference, the factor by which interpolation in Fourier space
+    scales a point's real-space signal."""
+    import torch
+
+    rng = np.random.default_rng(777)
+    pool = synth.uniform_rotations(rng, 4000).astype(np.float64)
+    fr = np.asarray(fracs)
+    rad = 4.0 * sigma
+    yy, xx = np.mgrid[0:n_out, 0:n_out]
+    acc = {name: [] for name in pipelines}
+    pred = {name: [] for name in pipelines}
+    for _ in range(n_dirs):
+        d = rng.standard_normal(3)
+        d /= np.linalg.norm(d)                              # (z, y, x)
+        c = N // 2 + np.outer(fr * N, d)
+        params = (c, np.full(len(fr), sigma), np.ones(len(fr)))
+        real = synth.render_blobs(params, N)
+        dxyz = d[::-1]
+        inplane = np.hypot(pool[:, 0] @ dxyz, pool[:, 1] @ dxyz)
+        R = pool[inplane >= 0.95][:poses_per_dir]
+        truth, _ = blob_slice_truth(params, R, n_out, N, cutoff)
+        timg = np.fft.fftshift(np.fft.irfft2(truth, s=(n_out, n_out)), axes=(-2, -1))
+        rel = (c - N // 2)[:, ::-1]                         # (x, y, z) from the centre
+        ix = n_out // 2 + rel @ R[:, 0].T                   # [blob, pose]
+        iy = n_out // 2 + rel @ R[:, 1].T
+        masks = [[(yy - iy[j, n]) ** 2 + (xx - ix[j, n]) ** 2 <= rad * rad for n in range(len(R))]
+                 for j in range(len(fr))]
+        t_int = np.array([[timg[n][masks[j][n]].sum() for n in range(len(R))] for j in range(len(fr))])
+        Rd = torch.from_numpy(R.astype(np.float32))[None].cuda()
+        for name, (project, interp, os_) in pipelines.items():
+            out = project(torch.from_numpy(real).cuda(), Rd, interp, os_)
+            img = torch.fft.fftshift(torch.fft.irfft2(out[0], s=(n_out, n_out)), dim=(-2, -1)).double().cpu().numpy()
+            g_int = np.array([[img[n][masks[j][n]].sum() for n in range(len(R))] for j in range(len(fr))])
+            acc[name].append((g_int / t_int).mean(axis=1))
+            nu = np.outer(fr * N, np.abs(d)) / (os_ * N)
+            pred[name].append(np.prod(kernel_ft(interp, nu), axis=1))
+    res = {}
+    for name in pipelines:
+        m = np.mean(acc[name], axis=0)
+        p_ = np.mean(pred[name], axis=0)
+        keep90 = [f for f, v in zip(fr, m) if v >= 0.9]
+        res[name] = {"radius_frac": [round(float(f), 3) for f in fr],
+                     "intensity_ratio": [round(float(v), 4) for v in m],
+                     "predicted": [round(float(v), 4) for v in p_],
+                     "max_radius_frac_ratio_ge_0.9": round(float(max(keep90)), 3) if keep90 else 0.0}
+    return res
+
+
 def oversampling_study(args):
     """Cubic at oversampling 1 against linear at oversampling 2 with the
     padding and FFT done on the fly, on the c4 phantom: wall time of the
-    forward pipeline (FFT of the real volume + projection) and of the
-    training step (+ adjoint, pose gradients, inverse FFT of the volume
-    gradient), and accuracy of the projections against the analytic slices
-    of the blobs.  One JSON line."""
+    forward pipeline (the spectrum step of the real volume + projection)
+    and of the training step (+ the adjoint, the pose gradients and the
+    volume gradient back to real space), accuracy of the projections
+    against the analytic slices of the blobs per Fourier ring, and the
+    real-space intensity against radius (``attenuation_study``).  One JSON
+    line."""
     import torch
 
     from cryo_em_fourier_amd import _lib
+    from cryo_em_fourier_amd.spectrum import real_from_spectrum, rfft_spectrum
 
     w = synth.WORKLOADS["c4"]
     rng = synth.rng_for(w.cfg_id, synth.STREAM_VOLUME)
     params = synth.blob_params(rng, w.N, w.n_blobs)
-    real = synth.blob_volume(synth.rng_for(w.cfg_id, synth.STREAM_VOLUME), w.N, w.n_blobs)
+    real = synth.make_real(w)[0]
     R = synth.make_rotations(w)
     L = _lib.lib()
     dev = torch.device("cuda:0")
@@ -516,42 +591,24 @@ def oversampling_study(args):
     G = torch.randn((1, P, n_out, Wo), dtype=torch.complex64, device=dev,
                     generator=torch.Generator(device=dev).manual_seed(4))
     out = torch.empty((1, P, n_out, Wo), dtype=torch.complex64, device=dev)
-    jac = torch.empty((1, P, 3, n_out, Wo), dtype=torch.complex64, device=dev)
     dR = torch.empty_like(Rd)
 
-    def spectrum(os_):
-        M = w.N * os_
-        x = realt
-        if os_ != 1:
-            big = torch.zeros((M, M, M), dtype=torch.float32, device=dev)
-            off = M // 2 - w.N // 2
-            big[off:off + w.N, off:off + w.N, off:off + w.N] = realt
-            x = big
-        return torch.fft.rfftn(torch.fft.ifftshift(x), dim=(0, 1, 2))[None].contiguous()
-
-    def to_real(dV, os_):
-        M = w.N * os_
-        x = torch.fft.fftshift(torch.fft.irfftn(dV[0], s=(M, M, M), dim=(0, 1, 2)))
-        off = M // 2 - w.N // 2
-        return x[off:off + w.N, off:off + w.N, off:off + w.N]
-
     def pipeline(interp, os_, backward):
-        # forward only: tp_project_3d; training step: the bench step's calls
-        # (Jacobian-saving forward, then the adjoint and the pose gradients
-        # from the Jacobian in one launch)
-        V = spectrum(os_)
+        # forward: the spectrum step + tp_project_3d; training step: + the
+        # adjoint and the pose gradients (nothing stored between forward and
+        # backward), then the volume gradient back to real space
+        V = rfft_spectrum(realt[None], 3, w.N * os_)
         M = V.shape[1]
+        _lib.check(L.tp_project_3d(V.data_ptr(), 1, M, Rd.data_ptr(), 1, P, None, 1, n_out, interp,
+                                   float(os_), w.cutoff, out.data_ptr(), sh), "project")
         if not backward:
-            _lib.check(L.tp_project_3d(V.data_ptr(), 1, M, Rd.data_ptr(), 1, P, None, 1, n_out, interp,
-                                       float(os_), w.cutoff, out.data_ptr(), sh), "project")
             return
-        _lib.check(L.tp_project_3d_jac(V.data_ptr(), 1, M, Rd.data_ptr(), 1, P, None, 1, n_out, interp, float(os_),
-                                       w.cutoff, out.data_ptr(), jac.data_ptr(), sh), "project_jac")
         dV = torch.empty_like(V)
-        _lib.check(L.tp_backward_3d_jac(G.data_ptr(), out.data_ptr(), jac.data_ptr(), 1, P, n_out, Rd.data_ptr(), 1,
-                                        None, 1, M, interp, float(os_), w.cutoff, dV.data_ptr(), dR.data_ptr(), None,
-                                        sh), "backward_jac")
-        to_real(dV, os_)
+        _lib.check(L.tp_backproject_3d(G.data_ptr(), 1, P, n_out, Rd.data_ptr(), 1, None, 1, M, interp, float(os_),
+                                       w.cutoff, dV.data_ptr(), sh), "backproject")
+        _lib.check(L.tp_grad_pose(3, V.data_ptr(), 1, M, G.data_ptr(), Rd.data_ptr(), 1, P, None, 1, n_out, interp,
+                                  float(os_), w.cutoff, dR.data_ptr(), None, sh), "grad_pose")
+        real_from_spectrum(dV, w.N, 3)
 
     def timed(f, reps=5):
         f()
@@ -581,9 +638,18 @@ def oversampling_study(args):
     res["speedup_cubic_os1_over_linear_os2"] = {
         "fwd": round(res["linear_os2"]["fwd_pipeline_ms"] / res["cubic_os1"]["fwd_pipeline_ms"], 3),
         "step": round(res["linear_os2"]["step_pipeline_ms"] / res["cubic_os1"]["step_pipeline_ms"], 3)}
+
+    def project(real_t, Rt, interp, os_):
+        V = rfft_spectrum(real_t[None], 3, w.N * os_)
+        o = torch.empty((1, Rt.shape[1], n_out, Wo), dtype=torch.complex64, device=dev)
+        _lib.check(L.tp_project_3d(V.data_ptr(), 1, V.shape[1], Rt.data_ptr(), 1, Rt.shape[1], None, 1, n_out,
+                                   interp, float(os_), w.cutoff, o.data_ptr(), sh), "project")
+        return o
+
+    att = attenuation_study({k: (project, i, o) for k, (i, o) in cases.items()}, w.N, n_out, w.cutoff)
     print(json.dumps({"study": "oversampling", "workload": "c4 blob phantom, box 256, 4096 poses, cutoff 128, "
                       "no shifts; accuracy on the first %d poses against analytic blob slices" % Ps,
-                      "results": res}), flush=True)
+                      "results": res, "attenuation": att}), flush=True)
 
 
 def main():

@@ -125,9 +125,15 @@ def blob_volume(rng: np.random.Generator, N: int, n_blobs: int,
     Each blob is evaluated on a +-4 sigma window (separable), which is exact
     to ~3e-4 of its peak and keeps generation cheap at N = 256..512.
     """
-    c, s, a = blob_params(rng, N, n_blobs, sigma, amp)
+    return render_blobs(blob_params(rng, N, n_blobs, sigma, amp), N)
+
+
+def render_blobs(params, N: int) -> np.ndarray:
+    """The N^3 volume (z, y, x) of blobs with the given (centres, widths,
+    amplitudes), each evaluated on a +-4 sigma window."""
+    c, s, a = params
     vol = np.zeros((N, N, N), np.float64)
-    for i in range(n_blobs):
+    for i in range(len(s)):
         h = int(math.ceil(4 * s[i]))
         lo = np.maximum(np.floor(c[i]).astype(int) - h, 0)
         hi = np.minimum(np.floor(c[i]).astype(int) + h + 2, N)
@@ -236,19 +242,21 @@ WORKLOADS = {
 }
 
 
-def make_reference(w: Workload, pad_to: int | None = None) -> np.ndarray:
-    """The reference half-spectrum [B, M, M, M//2+1] (3D) or [B, M, M//2+1] (2D)."""
+def make_real(w: Workload) -> np.ndarray:
+    """The real-space reference, centred: [B, N, N, N] (3D) or [B, N, N] (2D), float32."""
     rng = rng_for(w.cfg_id, STREAM_VOLUME)
     if w.vol_kind == "iid":
-        real = rng.standard_normal((w.N,) * 3).astype(np.float32)
-        return rfft_spectrum(real, 3, pad_to)[None]
+        return rng.standard_normal((w.N,) * 3).astype(np.float32)[None]
     if w.vol_kind == "blobs":
-        real = blob_volume(rng, w.N, w.n_blobs)
-        return rfft_spectrum(real, 3, pad_to)[None]
+        return blob_volume(rng, w.N, w.n_blobs)[None]
     if w.vol_kind == "images":
-        real = blob_images(rng, w.B, w.N, w.n_blobs)
-        return rfft_spectrum(real, 2, pad_to)
+        return blob_images(rng, w.B, w.N, w.n_blobs)
     raise ValueError(w.vol_kind)
+
+
+def make_reference(w: Workload, pad_to: int | None = None) -> np.ndarray:
+    """The reference half-spectrum [B, M, M, M//2+1] (3D) or [B, M, M//2+1] (2D)."""
+    return rfft_spectrum(make_real(w), w.ndim, pad_to)
 
 
 def make_rotations(w: Workload) -> np.ndarray:
