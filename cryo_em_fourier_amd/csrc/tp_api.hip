@@ -156,8 +156,8 @@ extern "C" {
 
 int tp_abi_version(void) { return TP_ABI_VERSION; }
 
-const char* tp_status_str(int status) {
-  switch (status) {
+const char* tp_status_str(tp_status status) {
+  switch ((int)status) {
     case TP_OK: return "TP_OK";
     case TP_EINVAL: return "TP_EINVAL: invalid argument";
     case TP_EUNSUPPORTED: return "TP_EUNSUPPORTED: size or shape not supported";
@@ -167,14 +167,14 @@ const char* tp_status_str(int status) {
 }
 
 tp_status tp_project_3d(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot,
-                        int64_t P, const float* shift, int64_t B_shift, int64_t N_out, int interp,
+                        int64_t P, const float* shift, int64_t B_shift, int64_t N_out, tp_interp interp,
                         float oversampling, float cutoff, tp_c64* out, void* stream) {
   return project(3, vol, B, N, rot, B_rot, P, shift, B_shift, N_out, interp, oversampling, cutoff,
                  out, stream);
 }
 
 tp_status tp_project_2d(const tp_c64* img, int64_t B, int64_t N, const float* rot, int64_t B_rot,
-                        int64_t P, const float* shift, int64_t B_shift, int64_t N_out, int interp,
+                        int64_t P, const float* shift, int64_t B_shift, int64_t N_out, tp_interp interp,
                         float oversampling, float cutoff, tp_c64* out, void* stream) {
   return project(2, img, B, N, rot, B_rot, P, shift, B_shift, N_out, interp, oversampling, cutoff,
                  out, stream);
@@ -182,7 +182,7 @@ tp_status tp_project_2d(const tp_c64* img, int64_t B, int64_t N, const float* ro
 
 tp_status tp_backproject_3d(const tp_c64* proj, int64_t B, int64_t P, int64_t N_out,
                             const float* rot, int64_t B_rot, const float* shift, int64_t B_shift,
-                            int64_t N, int interp, float oversampling, float cutoff,
+                            int64_t N, tp_interp interp, float oversampling, float cutoff,
                             tp_c64* vol_out, void* stream) {
   return backproject(3, proj, B, P, N_out, rot, B_rot, shift, B_shift, N, interp, oversampling,
                      cutoff, vol_out, stream);
@@ -190,28 +190,28 @@ tp_status tp_backproject_3d(const tp_c64* proj, int64_t B, int64_t P, int64_t N_
 
 tp_status tp_backproject_2d(const tp_c64* proj, int64_t B, int64_t P, int64_t N_out,
                             const float* rot, int64_t B_rot, const float* shift, int64_t B_shift,
-                            int64_t N, int interp, float oversampling, float cutoff,
+                            int64_t N, tp_interp interp, float oversampling, float cutoff,
                             tp_c64* img_out, void* stream) {
   return backproject(2, proj, B, P, N_out, rot, B_rot, shift, B_shift, N, interp, oversampling,
                      cutoff, img_out, stream);
 }
 
 tp_status tp_backproject_weights_3d(const float* weights, int64_t B, int64_t P, int64_t N_out,
-                                    const float* rot, int64_t B_rot, int64_t N, int interp,
+                                    const float* rot, int64_t B_rot, int64_t N, tp_interp interp,
                                     float oversampling, float cutoff, float* wvol_out, void* stream) {
   return backproject_weights(3, weights, B, P, N_out, rot, B_rot, N, interp, oversampling, cutoff, wvol_out,
                              stream);
 }
 
 tp_status tp_backproject_weights_2d(const float* weights, int64_t B, int64_t P, int64_t N_out,
-                                    const float* rot, int64_t B_rot, int64_t N, int interp,
+                                    const float* rot, int64_t B_rot, int64_t N, tp_interp interp,
                                     float oversampling, float cutoff, float* wimg_out, void* stream) {
   return backproject_weights(2, weights, B, P, N_out, rot, B_rot, N, interp, oversampling, cutoff, wimg_out,
                              stream);
 }
 
 tp_status tp_rotate_3d(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot, int64_t P,
-                       const float* shift, int64_t B_shift, int64_t N_out, int interp, float oversampling,
+                       const float* shift, int64_t B_shift, int64_t N_out, tp_interp interp, float oversampling,
                        float cutoff, tp_c64* out, void* stream) {
   if (!vol || !out || !aligned8(vol) || !aligned8(out)) return TP_EINVAL;
   tp::OpParams p;
@@ -224,7 +224,7 @@ tp_status tp_rotate_3d(const tp_c64* vol, int64_t B, int64_t N, const float* rot
 }
 
 tp_status tp_rotate_backproject_3d(const tp_c64* grad_out, int64_t B, int64_t P, int64_t N_out, const float* rot,
-                                   int64_t B_rot, const float* shift, int64_t B_shift, int64_t N, int interp,
+                                   int64_t B_rot, const float* shift, int64_t B_shift, int64_t N, tp_interp interp,
                                    float oversampling, float cutoff, tp_c64* vol_out, void* stream) {
   if (!grad_out || !vol_out || !aligned8(grad_out) || !aligned8(vol_out)) return TP_EINVAL;
   tp::OpParams p;
@@ -242,7 +242,7 @@ tp_status tp_rotate_backproject_3d(const tp_c64* grad_out, int64_t B, int64_t P,
 
 tp_status tp_rotate_grad_pose(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* grad_out, const float* rot,
                               int64_t B_rot, int64_t P, const float* shift, int64_t B_shift, int64_t N_out,
-                              int interp, float oversampling, float cutoff, float* grad_rot, float* grad_shift,
+                              tp_interp interp, float oversampling, float cutoff, float* grad_rot, float* grad_shift,
                               void* stream) {
   if (!vol || !grad_out || !aligned8(vol) || !aligned8(grad_out)) return TP_EINVAL;
   if ((grad_rot && !aligned4(grad_rot)) || (grad_shift && !aligned4(grad_shift))) return TP_EINVAL;
@@ -277,7 +277,7 @@ tp_status tp_symmetrize_x0(int ndim, tp_c64* ref, int64_t B, int64_t N, void* st
 
 tp_status tp_grad_pose(int ndim, const tp_c64* ref, int64_t B, int64_t N, const tp_c64* grad_out,
                        const float* rot, int64_t B_rot, int64_t P, const float* shift,
-                       int64_t B_shift, int64_t N_out, int interp, float oversampling,
+                       int64_t B_shift, int64_t N_out, tp_interp interp, float oversampling,
                        float cutoff, float* grad_rot, float* grad_shift, void* stream) {
   if (!ref || !grad_out || !aligned8(ref) || !aligned8(grad_out)) return TP_EINVAL;
   if ((grad_rot && !aligned4(grad_rot)) || (grad_shift && !aligned4(grad_shift))) return TP_EINVAL;
@@ -307,7 +307,7 @@ tp_status tp_grad_pose(int ndim, const tp_c64* ref, int64_t B, int64_t N, const 
 
 tp_status tp_backward_3d(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* grad_out, const float* rot,
                          int64_t B_rot, int64_t P, const float* shift, int64_t B_shift, int64_t N_out,
-                         int interp, float oversampling, float cutoff, tp_c64* vol_grad, float* grad_rot,
+                         tp_interp interp, float oversampling, float cutoff, tp_c64* vol_grad, float* grad_rot,
                          float* grad_shift, void* stream) {
   if (!vol || !grad_out || !aligned8(vol) || !aligned8(grad_out)) return TP_EINVAL;
   if (vol_grad && !aligned8(vol_grad)) return TP_EINVAL;
@@ -339,7 +339,7 @@ tp_status tp_backward_3d(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* 
 }
 
 tp_status tp_project_3d_jac(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot,
-                            int64_t P, const float* shift, int64_t B_shift, int64_t N_out, int interp,
+                            int64_t P, const float* shift, int64_t B_shift, int64_t N_out, tp_interp interp,
                             float oversampling, float cutoff, tp_c64* out, tp_c64* jac, void* stream) {
   if (!vol || !out || !jac || !aligned8(vol) || !aligned8(out) || !aligned8(jac)) return TP_EINVAL;
   tp::OpParams p;
@@ -394,7 +394,7 @@ tp_status tp_grad_pose_jac(const tp_c64* grad_out, const tp_c64* proj, const tp_
 
 tp_status tp_backward_3d_jac(const tp_c64* grad_out, const tp_c64* proj, const tp_c64* jac, int64_t B, int64_t P,
                             int64_t N_out, const float* rot, int64_t B_rot, const float* shift, int64_t B_shift,
-                            int64_t N, int interp, float oversampling, float cutoff, tp_c64* vol_out,
+                            int64_t N, tp_interp interp, float oversampling, float cutoff, tp_c64* vol_out,
                             float* grad_rot, float* grad_shift, void* stream) {
   if (!grad_out || !proj || !jac || !vol_out) return TP_EINVAL;
   if (!aligned8(grad_out) || !aligned8(proj) || !aligned8(jac) || !aligned8(vol_out)) return TP_EINVAL;
@@ -425,7 +425,7 @@ tp_status tp_backward_3d_jac(const tp_c64* grad_out, const tp_c64* proj, const t
 
 tp_status tp_rotate_backward_3d_jac(const tp_c64* grad_out, const tp_c64* out, const tp_c64* jac, int64_t B,
                                    int64_t P, int64_t N_out, const float* rot, int64_t B_rot, const float* shift,
-                                   int64_t B_shift, int64_t N, int interp, float oversampling, float cutoff,
+                                   int64_t B_shift, int64_t N, tp_interp interp, float oversampling, float cutoff,
                                    tp_c64* vol_out, float* grad_rot, float* grad_shift, void* stream) {
   if (!grad_out || !out || !jac || !vol_out) return TP_EINVAL;
   if (!aligned8(grad_out) || !aligned8(out) || !aligned8(jac) || !aligned8(vol_out)) return TP_EINVAL;
@@ -456,7 +456,7 @@ tp_status tp_rotate_backward_3d_jac(const tp_c64* grad_out, const tp_c64* out, c
 }
 
 tp_status tp_rotate_3d_jac(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot, int64_t P,
-                           const float* shift, int64_t B_shift, int64_t N_out, int interp, float oversampling,
+                           const float* shift, int64_t B_shift, int64_t N_out, tp_interp interp, float oversampling,
                            float cutoff, tp_c64* out, tp_c64* jac, void* stream) {
   if (!vol || !out || !jac || !aligned8(vol) || !aligned8(out) || !aligned8(jac)) return TP_EINVAL;
   tp::OpParams p;

@@ -96,10 +96,13 @@ typedef enum {
 int tp_abi_version(void);
 
 /* Human-readable name of a status code (static string, never NULL). */
-const char* tp_status_str(int status);
+const char* tp_status_str(tp_status status);
 
 /*
- * Forward 3D -> 2D (central slice).
+ * Forward 3D -> 2D (central slice): the projection of the rotated, shifted
+ * reference is its central slice in Fourier space (Fourier slice theorem,
+ * it/de pages tech. section 1; rotation, Friedel fold, interpolation and
+ * shift phase as in tech. section 2 of every page).
  *   vol    [B, N, N, N/2+1] complex64, input
  *   rot    [B_rot, P, 3, 3] float32, input
  *   shift  [B_shift, P, 2] float32 or NULL, input
@@ -108,12 +111,14 @@ const char* tp_status_str(int status);
 tp_status tp_project_3d(const tp_c64* vol, int64_t B, int64_t N,
                         const float* rot, int64_t B_rot, int64_t P,
                         const float* shift, int64_t B_shift,
-                        int64_t N_out, int interp, float oversampling, float cutoff,
+                        int64_t N_out, tp_interp interp, float oversampling, float cutoff,
                         tp_c64* out, void* stream);
 
 /*
  * Adjoint of tp_project_3d for the real inner product Re sum conj(a) b
- * (2D -> 3D backprojection): every kept output c = conj(phase) * proj is
+ * (2D -> 3D backprojection; ko page tech. section 2: the backward pass is the
+ * adjoint, accumulated with the conjugate phase; it page results: scatter
+ * with atomic adds, the slow direction): every kept output c = conj(phase) * proj is
  * spread with the forward's interpolation weights onto the taps it was read
  * from; a folded tap (x < 0) receives conj(w c) at -t.
  *   proj     [B, P, N_out, N_out/2+1] complex64, input
@@ -122,11 +127,12 @@ tp_status tp_project_3d(const tp_c64* vol, int64_t B, int64_t N,
 tp_status tp_backproject_3d(const tp_c64* proj, int64_t B, int64_t P, int64_t N_out,
                             const float* rot, int64_t B_rot,
                             const float* shift, int64_t B_shift,
-                            int64_t N, int interp, float oversampling, float cutoff,
+                            int64_t N, tp_interp interp, float oversampling, float cutoff,
                             tp_c64* vol_out, void* stream);
 
 /*
- * Forward 2D -> 2D (rotated, shifted copy of a 2D reference).
+ * Forward 2D -> 2D (rotated, shifted copy of a 2D reference; the 2D variant
+ * of the operations list, it/ko pages tech. section 2).
  *   img    [B, N, N/2+1] complex64, input
  *   rot    [B_rot, P, 2, 2] float32, input
  *   out    [B, P, N_out, N_out/2+1] complex64, overwritten
@@ -134,14 +140,15 @@ tp_status tp_backproject_3d(const tp_c64* proj, int64_t B, int64_t P, int64_t N_
 tp_status tp_project_2d(const tp_c64* img, int64_t B, int64_t N,
                         const float* rot, int64_t B_rot, int64_t P,
                         const float* shift, int64_t B_shift,
-                        int64_t N_out, int interp, float oversampling, float cutoff,
+                        int64_t N_out, tp_interp interp, float oversampling, float cutoff,
                         tp_c64* out, void* stream);
 
-/* Adjoint of tp_project_2d; img_out [B, N, N/2+1] is overwritten. */
+/* Adjoint of tp_project_2d (ko page tech. section 2, as tp_backproject_3d);
+ * img_out [B, N, N/2+1] is overwritten. */
 tp_status tp_backproject_2d(const tp_c64* proj, int64_t B, int64_t P, int64_t N_out,
                             const float* rot, int64_t B_rot,
                             const float* shift, int64_t B_shift,
-                            int64_t N, int interp, float oversampling, float cutoff,
+                            int64_t N, tp_interp interp, float oversampling, float cutoff,
                             tp_c64* img_out, void* stream);
 
 /*
@@ -159,10 +166,10 @@ tp_status tp_backproject_2d(const tp_c64* proj, int64_t B, int64_t P, int64_t N_
  * Limits and errors as tp_backproject_3d; pointers need 4-byte alignment.
  */
 tp_status tp_backproject_weights_3d(const float* weights, int64_t B, int64_t P, int64_t N_out,
-                                    const float* rot, int64_t B_rot, int64_t N, int interp,
+                                    const float* rot, int64_t B_rot, int64_t N, tp_interp interp,
                                     float oversampling, float cutoff, float* wvol_out, void* stream);
 tp_status tp_backproject_weights_2d(const float* weights, int64_t B, int64_t P, int64_t N_out,
-                                    const float* rot, int64_t B_rot, int64_t N, int interp,
+                                    const float* rot, int64_t B_rot, int64_t N, tp_interp interp,
                                     float oversampling, float cutoff, float* wimg_out, void* stream);
 
 /*
@@ -197,7 +204,7 @@ tp_status tp_symmetrize_x0(int ndim, tp_c64* ref, int64_t B, int64_t N, void* st
  * N_out^2 (kz, ky) rows).
  */
 tp_status tp_rotate_3d(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot, int64_t P,
-                       const float* shift, int64_t B_shift, int64_t N_out, int interp, float oversampling,
+                       const float* shift, int64_t B_shift, int64_t N_out, tp_interp interp, float oversampling,
                        float cutoff, tp_c64* out, void* stream);
 
 /*
@@ -210,7 +217,7 @@ tp_status tp_rotate_3d(const tp_c64* vol, int64_t B, int64_t N, const float* rot
  * Errors as tp_backproject_3d, with N_out limited to 1023.
  */
 tp_status tp_rotate_backproject_3d(const tp_c64* grad_out, int64_t B, int64_t P, int64_t N_out, const float* rot,
-                                   int64_t B_rot, const float* shift, int64_t B_shift, int64_t N, int interp,
+                                   int64_t B_rot, const float* shift, int64_t B_shift, int64_t N, tp_interp interp,
                                    float oversampling, float cutoff, tp_c64* vol_out, void* stream);
 
 /*
@@ -223,7 +230,7 @@ tp_status tp_rotate_backproject_3d(const tp_c64* grad_out, int64_t B, int64_t P,
  */
 tp_status tp_rotate_grad_pose(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* grad_out, const float* rot,
                               int64_t B_rot, int64_t P, const float* shift, int64_t B_shift, int64_t N_out,
-                              int interp, float oversampling, float cutoff, float* grad_rot, float* grad_shift,
+                              tp_interp interp, float oversampling, float cutoff, float* grad_rot, float* grad_shift,
                               void* stream);
 
 /*
@@ -245,7 +252,7 @@ tp_status tp_rotate_grad_pose(const tp_c64* vol, int64_t B, int64_t N, const tp_
 tp_status tp_grad_pose(int ndim, const tp_c64* ref, int64_t B, int64_t N,
                        const tp_c64* grad_out, const float* rot, int64_t B_rot, int64_t P,
                        const float* shift, int64_t B_shift,
-                       int64_t N_out, int interp, float oversampling, float cutoff,
+                       int64_t N_out, tp_interp interp, float oversampling, float cutoff,
                        float* grad_rot, float* grad_shift, void* stream);
 
 /*
@@ -277,7 +284,7 @@ tp_status tp_grad_pose(int ndim, const tp_c64* ref, int64_t B, int64_t N,
 tp_status tp_backward_3d(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* grad_out,
                          const float* rot, int64_t B_rot, int64_t P,
                          const float* shift, int64_t B_shift, int64_t N_out,
-                         int interp, float oversampling, float cutoff,
+                         tp_interp interp, float oversampling, float cutoff,
                          tp_c64* vol_grad, float* grad_rot, float* grad_shift, void* stream);
 
 /*
@@ -297,7 +304,7 @@ tp_status tp_backward_3d(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* 
 tp_status tp_project_3d_jac(const tp_c64* vol, int64_t B, int64_t N,
                             const float* rot, int64_t B_rot, int64_t P,
                             const float* shift, int64_t B_shift,
-                            int64_t N_out, int interp, float oversampling, float cutoff,
+                            int64_t N_out, tp_interp interp, float oversampling, float cutoff,
                             tp_c64* out, tp_c64* jac, void* stream);
 
 /*
@@ -340,7 +347,7 @@ tp_status tp_grad_pose_jac(const tp_c64* grad_out, const tp_c64* proj, const tp_
 tp_status tp_backward_3d_jac(const tp_c64* grad_out, const tp_c64* proj, const tp_c64* jac,
                              int64_t B, int64_t P, int64_t N_out,
                              const float* rot, int64_t B_rot, const float* shift, int64_t B_shift,
-                             int64_t N, int interp, float oversampling, float cutoff,
+                             int64_t N, tp_interp interp, float oversampling, float cutoff,
                              tp_c64* vol_out, float* grad_rot, float* grad_shift, void* stream);
 
 /*
@@ -356,7 +363,7 @@ tp_status tp_backward_3d_jac(const tp_c64* grad_out, const tp_c64* proj, const t
  * TP_EUNSUPPORTED.
  */
 tp_status tp_rotate_3d_jac(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot, int64_t P,
-                           const float* shift, int64_t B_shift, int64_t N_out, int interp, float oversampling,
+                           const float* shift, int64_t B_shift, int64_t N_out, tp_interp interp, float oversampling,
                            float cutoff, tp_c64* out, tp_c64* jac, void* stream);
 
 /*
@@ -393,7 +400,7 @@ tp_status tp_rotate_grad_pose_jac(const tp_c64* grad_out, const tp_c64* out, con
 tp_status tp_rotate_backward_3d_jac(const tp_c64* grad_out, const tp_c64* out, const tp_c64* jac,
                                     int64_t B, int64_t P, int64_t N_out,
                                     const float* rot, int64_t B_rot, const float* shift, int64_t B_shift,
-                                    int64_t N, int interp, float oversampling, float cutoff,
+                                    int64_t N, tp_interp interp, float oversampling, float cutoff,
                                     tp_c64* vol_out, float* grad_rot, float* grad_shift, void* stream);
 
 #ifdef __cplusplus
