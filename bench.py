@@ -4,11 +4,10 @@ One step = the whole path on one batch: forward projection, then the
 backward of a loss on its output: the adjoint for the reference gradient
 and the rotation + shift gradients, with nothing stored between the two
 beyond the forward's output.  By default (``--pose-grads separate``) the
-step is tp_project_3d + tp_backproject_3d + tp_grad_pose (the fastest form
-measured); ``--pose-grads fused`` times tp_project_3d + tp_backward_3d (the
-backward in one pass), and ``--pose-grads jacobian`` the path that stores each
-output's Jacobian in the forward (tp_project_3d_jac + tp_backward_3d_jac,
-24 extra bytes per output).  The kernels of the other modes ride along in
+step is tp_project_3d + tp_backproject_3d + tp_grad_pose (the kernels that
+tp_backward_3d runs); ``--pose-grads jacobian`` times the path that stores
+each output's Jacobian in the forward (tp_project_3d_jac +
+tp_backward_3d_jac, 24 extra bytes per output).  The kernels of the other modes ride along in
 ``extras``.  Default workload
 (``c4``): a 256^3 blob phantom (rfft half-spectrum 256x256x129 complex64),
 4096 uniform SO(3) poses, shifts U[-10,10] px, Catmull-Rom cubic,
@@ -661,10 +660,10 @@ def main():
                     help="c2 runs the 2D -> 2D path (images/s); the others the 3D -> 2D path")
     ap.add_argument("--oversampling", type=int, default=1, choices=[1, 2])
     ap.add_argument("--poses", type=int, default=0, help="override the pose count")
-    ap.add_argument("--pose-grads", choices=["fused", "separate", "jacobian"], default="separate",
-                    help="fused: the backward in one pass (tp_backward_3d), nothing stored; separate: the adjoint "
-                         "and a second gather pass for the pose gradients; jacobian: the forward saves each "
-                         "output's Jacobian for the backward")
+    ap.add_argument("--pose-grads", choices=["separate", "jacobian"], default="separate",
+                    help="separate: the adjoint and a second gather pass for the pose gradients, nothing stored "
+                         "(tp_backward_3d's kernels); jacobian: the forward saves each output's Jacobian for the "
+                         "backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the step only: no other kernels, no peak probes (for counter runs)")
@@ -756,13 +755,7 @@ def main():
                                         R.shape[0], sd.data_ptr(), s.shape[0], N, w.interp, os_, w.cutoff,
                                         dV.data_ptr(), dR.data_ptr(), ds.data_ptr(), sh), "tp_backward_3d_jac")
 
-    def bwd():
-        _lib.check(L.tp_backward_3d(Vd.data_ptr(), B, N, Gd.data_ptr(), Rd.data_ptr(), R.shape[0], P,
-                                    sd.data_ptr(), s.shape[0], w.N_out, w.interp, os_, w.cutoff, dV.data_ptr(),
-                                    dR.data_ptr(), ds.data_ptr(), sh), "tp_backward_3d")
-
     modes = {
-        "fused": [("project", fwd), ("backward", bwd)],
         "separate": [("project", fwd), ("backproject", adj), ("grad_pose", grad)],
         "jacobian": [("project_jac", fwd_jac), ("backward_jac", bwd_jac)],
     }
@@ -837,15 +830,10 @@ def main():
         "grad_pose_jac": units * 40 + grad_bytes,                # G, out and jac inside the cutoff
         # both: G, out and jac inside the cutoff, the volume (fill + write)
         "backward_jac": units * 40 + 2 * ref_bytes + pose_bytes + grad_bytes,
-        # one pass: G inside the cutoff, the reference read, the volume gradient (fill + write)
-        "backward": units * 8 + 3 * ref_bytes + pose_bytes + grad_bytes,
     }
-    # tap bytes per launch: 8 B x taps x in-cutoff outputs per pass over the
-    # taps; the one-pass backward makes two (the adjoint's scatter and the
-    # pose gradients' gather)
+    # tap bytes per launch: 8 B x taps x in-cutoff outputs per pass over the taps
     tap_bytes = {"project": units * taps * 8, "project_jac": units * taps * 8, "backproject": units * taps * 8,
-                 "grad_pose": units * taps * 8, "grad_pose_jac": 0, "backward_jac": units * taps * 8,
-                 "backward": 2 * units * taps * 8}
+                 "grad_pose": units * taps * 8, "grad_pose_jac": 0, "backward_jac": units * taps * 8}
     dom = max(avg, key=avg.get)
     wl_key = f"{w.name}_os{args.oversampling}" + (f"_p{P}" if args.poses else "")
     traffic = measured_traffic(wl_key, copy_bytes)
@@ -883,7 +871,7 @@ def main():
         f = {"hbm_compulsory": round(hbm[k] / (avg[k] * 1e-3) / 1e9 / peaks["hbm_read_GBs"], 4)}
         if tap_bytes[k]:
             f["l2_tap"] = round(tap_bytes[k] / (avg[k] * 1e-3) / 1e9 / peaks["l2_read_GBs"], 4)
-        if k in ("backproject", "backward_jac", "backward"):
+        if k in ("backproject", "backward_jac"):
             f["lds_tap_adds"] = round(units * taps / (avg[k] * 1e-3) / 1e9 / peaks["lds_add64_Glanes_per_s"], 4)
         frac_measured[k] = f
     if peaks:

@@ -1,6 +1,5 @@
-// Building blocks of the brick-owned adjoint kernels (tp_adjoint.hip: the
-// adjoint and its modes; tp_backward.hip: the adjoint with the pose
-// gradients in one pass): brick decomposition, the LDS accumulator layout and
+// Building blocks of the brick-owned adjoint kernels of tp_adjoint.hip (the
+// adjoint and its modes): brick decomposition, the LDS accumulator layout and
 // its int32 fixed point, lattice points and their values, the spread of one
 // lattice point over its taps.
 //

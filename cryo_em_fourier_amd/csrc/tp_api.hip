@@ -317,8 +317,7 @@ tp_status tp_backward_3d(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* 
   const Common c{B, N, P, N_out, B_rot, B_shift, interp, 3, oversampling, cutoff, rot, shift};
   const tp_status st = check_and_fill(c, p);
   if (st != TP_OK) return st;
-  if (vol_grad && (N_out > tp::kMaxBrickOut || B > 65535 || tp::adjoint_blocks(p) > kMaxBlocks ||
-                   tp::backward_blocks(p) > kMaxBlocks))
+  if (vol_grad && (N_out > tp::kMaxBrickOut || B > 65535 || tp::adjoint_blocks(p) > kMaxBlocks))
     return TP_EUNSUPPORTED;
   if (!vol_grad && !grad_rot && !grad_shift) return TP_OK;
   p.ref = reinterpret_cast<const float2*>(vol);
@@ -334,8 +333,9 @@ tp_status tp_backward_3d(const tp_c64* vol, int64_t B, int64_t N, const tp_c64* 
     return TP_EHIP;
   if (!vol_grad) return hip_status(tp::launch_grad_pose(p, interp, s));
   if (tp::launch_zero(p.ref_out, ref_bytes_total(p), s) != hipSuccess) return TP_EHIP;
-  if (!grad_rot && !grad_shift) return hip_status(tp::launch_backproject(p, interp, s));
-  return hip_status(tp::launch_backward(p, interp, s));
+  const hipError_t e = tp::launch_backproject(p, interp, s);
+  if (e != hipSuccess || (!grad_rot && !grad_shift)) return hip_status(e);
+  return hip_status(tp::launch_grad_pose(p, interp, s));
 }
 
 tp_status tp_project_3d_jac(const tp_c64* vol, int64_t B, int64_t N, const float* rot, int64_t B_rot,

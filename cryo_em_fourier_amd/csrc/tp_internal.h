@@ -73,10 +73,6 @@ hipError_t launch_grad_jac(const OpParams& p, hipStream_t s);
 // the adjoint with the pose gradients from a saved Jacobian in the same launch
 hipError_t launch_backward_jac(const OpParams& p, int interp, hipStream_t s);
 uint64_t backward_jac_blocks(const OpParams& p);
-// the backward of the 3D projection in one pass (tp_backward.hip): the
-// adjoint into ref_out and the pose gradients, reading the reference
-hipError_t launch_backward(const OpParams& p, int interp, hipStream_t s);
-uint64_t backward_blocks(const OpParams& p);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
 uint64_t adjoint_blocks(const OpParams& p);
 

@@ -11,9 +11,9 @@ autograd functions wrapping the native ops):
 
 * ``project_3d`` / ``project_2d``: the backward computes the reference
   gradient (the adjoint) and the rotation and shift gradients, each only
-  when needed; in 3D both together come from ``tp_backward_3d`` in one pass.
+  when needed; in 3D both together come from one ``tp_backward_3d`` call.
   Nothing is kept from the forward but its inputs (it page tech. section 3:
-  a single pass without intermediate tensors).  ``project_3d(save_jacobian=True)`` opts into a forward
+  no intermediate tensors).  ``project_3d(save_jacobian=True)`` opts into a forward
   (``tp_project_3d_jac``) that also saves each output's Jacobian with
   respect to its sample point (3 complex values per output, 24 bytes), which
   the backward then streams instead of gathering from the reference again.
@@ -182,7 +182,7 @@ def tp_grad_pose(ref, grad_out, rot, shift=None, interp="cubic", oversampling=1.
 
 def tp_backward_3d(vol, grad_out, rot, shift=None, interp="cubic", oversampling=1.0, cutoff=-1.0,
                    want_vol=True, want_rot=True, want_shift=True, B_shift=None):
-    """The backward of tp_project_3d in one pass, storing nothing from the
+    """The backward of tp_project_3d in one call, storing nothing from the
     forward: (d_vol [B,N,N,N//2+1] or None, grad_rot [B_rot,P,3,3] or None,
     grad_shift or None), the values of tp_backproject_3d and tp_grad_pose."""
     B, N = _ref_dims(vol, 3, "reference")
@@ -315,7 +315,7 @@ class _Project(torch.autograd.Function):
                                                        oversampling, cutoff, want_rot, want_shift)
             return d_ref, d_rot, d_shift, None, None, None, None, None, None
         if ndim == 3 and ctx.needs_input_grad[0] and (want_rot or want_shift):
-            # both gradients in one pass over the reference
+            # both gradients in one call (the adjoint, then the pose-gradient gather)
             d_ref, d_rot, d_shift = tp_backward_3d(ref, g, rot, shift, interp, oversampling, cutoff, True,
                                                    want_rot, want_shift)
             return d_ref, d_rot, d_shift, None, None, None, None, None, None

@@ -256,21 +256,19 @@ tp_status tp_grad_pose(int ndim, const tp_c64* ref, int64_t B, int64_t N,
                        float* grad_rot, float* grad_shift, void* stream);
 
 /*
- * The backward of tp_project_3d in one pass, storing nothing between the
- * forward and the backward (it page tech. section 3: a single pass without
- * intermediate tensors): for L = Re sum conj(grad_out) * project_3d(vol,
- * rot, shift),
+ * The backward of tp_project_3d in one call, storing nothing between the
+ * forward and the backward (it page tech. section 3: no intermediate
+ * tensors): for L = Re sum conj(grad_out) * project_3d(vol, rot, shift),
  *   vol_grad   = dL/dvol, the adjoint of tp_backproject_3d applied to
  *                grad_out (ko page tech. section 2: the backward is the
  *                adjoint; conjugate phase)
  *   grad_rot, grad_shift = the rotation and shift gradients of tp_grad_pose
  *                (ar page tech. section 2: chain rule through the
  *                interpolation kernel's derivative)
- * For the cubic kernel both come from one walk over the lattice points,
- * with the reference read from LDS tiles beside the adjoint's accumulator;
- * the linear kernel runs tp_backproject_3d's and tp_grad_pose's kernels.
- * Results are those of the two calls (the adjoint's fixed point as
- * tp_backproject_3d; gradient sums merged with float atomics).
+ * It runs tp_backproject_3d's and tp_grad_pose's kernels on the stream,
+ * one after the other, and its results are those of the two calls (the
+ * adjoint's fixed point as tp_backproject_3d; gradient sums merged with
+ * float atomics).
  *   vol        [B, N, N, N/2+1] complex64, input (the forward's reference)
  *   grad_out   [B, P, N_out, N_out/2+1] complex64, input
  *   rot, shift as tp_project_3d
