@@ -667,7 +667,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the step only: no other kernels, no peak probes (for counter runs)")
-    ap.add_argument("--cpu-poses-per-worker", type=int, default=10)
+    ap.add_argument("--cpu-poses-per-worker", type=int, default=40,
+                    help="oracle poses per CPU worker (about 13 s of host time with 16 workers at c4)")
     ap.add_argument("--study", choices=["oversampling"], default=None,
                     help="run a study instead of the step benchmark")
     ap.add_argument("--study-poses", type=int, default=64, help="poses scored against the analytic slice")
