@@ -298,7 +298,7 @@ def test_grad_bricks_against_oracle(interp, os_, batch):
 
 @pytest.mark.parametrize("key", KEYS)
 def test_fullsize_backward_sampled_poses(key):
-    """tp_backward_3d (the one-pass backward of the benchmark's step) over all
+    """tp_backward_3d (the backward of the benchmark's step in one call) over all
     poses with the sparse upstream gradient: its volume gradient is the
     oracle's adjoint of the sampled poses, their pose gradients the oracle's,
     every other pose's gradients exactly 0."""
@@ -326,9 +326,9 @@ def test_fullsize_backward_sampled_poses(key):
 
 def test_fullsize_c3_adjoint_dense_all_poses():
     """c3 (box 128, 1024 poses) with a dense upstream gradient on every pose:
-    the adjoint and the one-pass backward in the benchmark's launch shape.
+    the adjoint and tp_backward_3d in the benchmark's launch shape.
     Volumes element by element against the oracle's adjoint (summed over pose
-    chunks in CPU worker processes); the one-pass backward's pose gradients
+    chunks in CPU worker processes); tp_backward_3d's pose gradients
     of sampled poses against the oracle's (a pose's gradient depends on its
     own upstream values only).  Every brick near the origin runs dozens of
     fixed-point groups and pose chunks."""
