@@ -226,7 +226,10 @@ __global__ __launch_bounds__(kBlock) void k_project3p(OpParams p) {
       mneg[j] = -m[j];
     }
     const int xmin1 = c ? 1 : 0, xmin2 = c ? 0 : 1;
-    const float2 mv = gather3_half<INTERP>(rs, g, m[0], m[1], m[2], xmin1, h);
+    float2 mv = gather3_half<INTERP>(rs, g, m[0], m[1], m[2], xmin1, h);
+    // finish the main sum before the secondary gather: its loads then find
+    // the main gather's registers free and go out together
+    asm volatile("" : "+v"(mv.x), "+v"(mv.y));
     float2 sv = make_float2(0.f, 0.f);
     if (needs_secondary<INTERP>(m[0], xmin2)) sv = gather3_half<INTERP>(rs, g, mneg[0], mneg[1], mneg[2], xmin2, h);
     res = c ? make_float2(mv.x + sv.x, sv.y - mv.y) : make_float2(mv.x + sv.x, mv.y - sv.y);
@@ -243,7 +246,9 @@ __global__ __launch_bounds__(kBlock) void k_project3p(OpParams p) {
 // S and dS/dp at an output's sample point from the value and derivative
 // gathers, summed over the lane pair (both lanes hold the totals; zero where
 // the output is not active).
-template <int INTERP>
+// MAIN_FIRST: finish the main sums before the secondary gather (faster for
+// k_grad3p; the Jacobian forward measured slower with it).
+template <int INTERP, bool MAIN_FIRST>
 __device__ __forceinline__ void pair_grad_values(const OpParams& p, const Out& o, int h, bool active,
                                                  const double* q, float2& S, float2* dS) {
   S = make_float2(0.f, 0.f);
@@ -263,6 +268,10 @@ __device__ __forceinline__ void pair_grad_values(const OpParams& p, const Out& o
     float2 mv[4], sv[4];
     // the stencil at the negated sample point is the mirror of p's (left)
     gather3_grad_half<INTERP>(rs, g, m[0], m[1], m[2], xmin1, h, mv, c);
+    if (MAIN_FIRST) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(mv[j].x), "+v"(mv[j].y));
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) sv[j] = make_float2(0.f, 0.f);
     if (needs_secondary_grad<INTERP>(m[0], xmin2))
@@ -294,7 +303,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   double q[3] = {0.0, 0.0, 0.0};
   const bool active = o.keep && sample_point<3>(p, o, q);
   float2 S, dS[3];
-  pair_grad_values<INTERP>(p, o, h, active, q, S, dS);
+  pair_grad_values<INTERP, true>(p, o, h, active, q, S, dS);
   double acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.0;
@@ -357,7 +366,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   double q[3] = {0.0, 0.0, 0.0};
   const bool active = o.keep && sample_point<3>(p, o, q);
   float2 S, dS[3];
-  pair_grad_values<INTERP>(p, o, h, active, q, S, dS);
+  pair_grad_values<INTERP, false>(p, o, h, active, q, S, dS);
   // lane 0 of a pair stores the output and jac_x, lane 1 jac_y and jac_z
   float2 a = h ? dS[1] : S, c = h ? dS[2] : dS[0];
   if (active && p.shift) {
