@@ -66,8 +66,11 @@ __device__ __forceinline__ float2 pose_shift(const OpParams& p, const Out& o) {
   return make_float2(s[0], s[1]);
 }
 
+// (the pose's offset is uniform over the workgroup; the in-image offset is
+// below No * Wo < 2^32 for boxes up to 65535)
 __device__ __forceinline__ size_t img_index(const OpParams& p, const Out& o) {
-  return ((size_t)((size_t)o.b * p.P + o.n) * p.No + o.iy) * p.Wo + o.kx;
+  const size_t pose = (size_t)o.b * p.P + o.n;
+  return pose * ((size_t)p.No * p.Wo) + ((uint32_t)o.iy * (uint32_t)p.Wo + (uint32_t)o.kx);
 }
 
 // The one-lane-per-output kernels below run the 2D path only (the 3D
@@ -104,7 +107,8 @@ __global__ __launch_bounds__(kBlock) void k_project(OpParams p) {
       mneg[j] = -m[j];
     }
     const int xmin1 = c ? 1 : 0, xmin2 = c ? 0 : 1;
-    const float2 mv = gather<NDIM, INTERP>(rs, g, m, xmin1);
+    float2 mv = gather<NDIM, INTERP>(rs, g, m, xmin1);
+    asm volatile("" : "+v"(mv.x), "+v"(mv.y));  // main sum first (see k_project3p)
     float2 sv = make_float2(0.f, 0.f);
     if (needs_secondary<INTERP>(m[0], xmin2)) sv = gather<NDIM, INTERP>(rs, g, mneg, xmin2);
     res = c ? make_float2(mv.x + sv.x, sv.y - mv.y) : make_float2(mv.x + sv.x, mv.y - sv.y);
@@ -140,6 +144,8 @@ __global__ __launch_bounds__(kBlock) void k_grad_pose(OpParams p) {
     float2 mv[NDIM + 1], sv[NDIM + 1];
     // the stencil at the negated sample point is the mirror of p's (left)
     gather_grad<NDIM, INTERP>(rs, g, m, xmin1, mv, c);
+#pragma unroll
+    for (int j = 0; j <= NDIM; ++j) asm volatile("" : "+v"(mv[j].x), "+v"(mv[j].y));  // main sums first
 #pragma unroll
     for (int j = 0; j <= NDIM; ++j) sv[j] = make_float2(0.f, 0.f);
     if (needs_secondary_grad<INTERP>(m[0], xmin2)) gather_grad<NDIM, INTERP>(rs, g, mneg, xmin2, sv, !c);
@@ -212,6 +218,7 @@ template <int INTERP>
 __global__ __launch_bounds__(kBlock) void k_project3p(OpParams p) {
   const Out o = locate<true>(p);
   const int h = threadIdx.x & 1;
+  const float2 sh = pose_shift(p, o);  // read before any store: a scalar load
   double q[3] = {0.0, 0.0, 0.0};
   const bool active = o.keep && sample_point<3>(p, o, q);
   float2 res = make_float2(0.f, 0.f);
@@ -236,10 +243,7 @@ __global__ __launch_bounds__(kBlock) void k_project3p(OpParams p) {
   }
   res = pair_sum(res);  // both lanes of a pair share `active`
   if (!o.in || h) return;
-  if (active && p.shift) {
-    const float2 s = pose_shift(p, o);
-    res = cmul(shift_phase(o.kx, o.ky, s.x, s.y, p.inv_no), res);
-  }
+  if (active && p.shift) res = cmul(shift_phase(o.kx, o.ky, sh.x, sh.y, p.inv_no), res);
   p.img_out[img_index(p, o)] = res;
 }
 
@@ -300,6 +304,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   __shared__ double red[kBlock / 64][NV];
   const Out o = locate<true>(p);
   const int h = threadIdx.x & 1;
+  const float2 sh = pose_shift(p, o);  // read before any store: a scalar load
   double q[3] = {0.0, 0.0, 0.0};
   const bool active = o.keep && sample_point<3>(p, o, q);
   float2 S, dS[3];
@@ -308,12 +313,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.0;
   if (active && h == 0) {
-    const float2 G = p.img[img_index(p, o)];
-    float2 gph = conjf2(G);
-    if (p.shift) {
-      const float2 s = pose_shift(p, o);
-      gph = cmul(gph, shift_phase(o.kx, o.ky, s.x, s.y, p.inv_no));
-    }
+    // (G read here: reading it before the gathers raised the registers to
+    // 117 and measured slower)
+    float2 gph = conjf2(p.img[img_index(p, o)]);
+    if (p.shift) gph = cmul(gph, shift_phase(o.kx, o.ky, sh.x, sh.y, p.inv_no));
     const double os = (double)p.os;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {

@@ -88,7 +88,10 @@ __global__ __launch_bounds__(kBlock) void k_rotate(OpParams p) {
     double m[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) m[j] = c ? -q[j] : q[j];
-    const float2 mv = gather3_half<INTERP>(rs, g, m[0], m[1], m[2], c ? 1 : 0, h);
+    float2 mv = gather3_half<INTERP>(rs, g, m[0], m[1], m[2], c ? 1 : 0, h);
+    // finish the main sum before the secondary gather, whose loads then go
+    // out together instead of one round trip each
+    asm volatile("" : "+v"(mv.x), "+v"(mv.y));
     float2 sv = make_float2(0.f, 0.f);
     if (needs_secondary<INTERP>(m[0], c ? 0 : 1)) sv = gather3_half<INTERP>(rs, g, -m[0], -m[1], -m[2], c ? 0 : 1, h);
     res = c ? make_float2(mv.x + sv.x, sv.y - mv.y) : make_float2(mv.x + sv.x, mv.y - sv.y);
@@ -118,6 +121,8 @@ __device__ __forceinline__ void rpair_grad_values(const OpParams& p, const ROut&
     float2 mv[4], sv[4];
     // the stencil at the negated sample point is the mirror of p's (left)
     gather3_grad_half<INTERP>(rs, g, m[0], m[1], m[2], c ? 1 : 0, h, mv, c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(mv[j].x), "+v"(mv[j].y));  // main sums first
 #pragma unroll
     for (int j = 0; j < 4; ++j) sv[j] = make_float2(0.f, 0.f);
     if (needs_secondary_grad<INTERP>(m[0], c ? 0 : 1))
