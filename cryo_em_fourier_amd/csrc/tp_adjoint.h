@@ -19,7 +19,7 @@ namespace tp {
 namespace adj {
 constexpr int kVox = 4096;          // voxels per brick
 constexpr int kGroupMax = 16;       // poses per fixed-point group
-constexpr int kPrefetch = 2;        // hits whose G values a thread loads at once
+constexpr int kPrefetch = 1;        // hits whose G values a thread loads at once (2: more spills, 1.3 % slower at c4)
 // Fixed point.  A pose adds to a voxel at most 2 m (a lattice point carries
 // a real and a mirror value, m the largest |re| + |im| of G) times W, the sum
 // of |w| over its lattice points.  Searched over orientations, voxel offsets
@@ -183,17 +183,25 @@ __device__ __forceinline__ void lattice_parts(const OpParams& p, int kx, int ky,
 // G entries of a lattice point: the real output (kx, ky) and the real output
 // (-kx, -ky) whose mirror it carries (zero where absent).
 // (WEIGHTS: real weights, as (w, 0).)
+// (the image's offset is taken once; the in-image offsets are 32-bit, below
+// No * Wo < 2^32)
 template <bool WEIGHTS>
 __device__ __forceinline__ void lattice_load(const OpParams& p, size_t img, int kx, int ky, float2& gr,
                                              float2& gm) {
   bool real, mirr;
   lattice_parts(p, kx, ky, real, mirr);
+  const size_t base = img * ((size_t)p.No * p.Wo);
+  const uint32_t wo = (uint32_t)p.Wo;
+  const uint32_t or_ = (uint32_t)(ky < 0 ? ky + p.No : ky) * wo + (uint32_t)kx;
+  const uint32_t om = (uint32_t)(-ky < 0 ? -ky + p.No : -ky) * wo + (uint32_t)(-kx);
   if (WEIGHTS) {
-    gr = make_float2(real ? p.wimg[out_index(p, img, kx, ky)] : 0.f, 0.f);
-    gm = make_float2(mirr ? p.wimg[out_index(p, img, -kx, -ky)] : 0.f, 0.f);
+    const float* w = p.wimg + base;
+    gr = make_float2(real ? w[or_] : 0.f, 0.f);
+    gm = make_float2(mirr ? w[om] : 0.f, 0.f);
   } else {
-    gr = real ? p.img[out_index(p, img, kx, ky)] : make_float2(0.f, 0.f);
-    gm = mirr ? p.img[out_index(p, img, -kx, -ky)] : make_float2(0.f, 0.f);
+    const float2* g = p.img + base;
+    gr = real ? g[or_] : make_float2(0.f, 0.f);
+    gm = mirr ? g[om] : make_float2(0.f, 0.f);
   }
 }
 
