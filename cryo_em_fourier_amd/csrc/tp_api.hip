@@ -75,6 +75,7 @@ tp_status check_and_fill(const Common& c, tp::OpParams& p) {
   p.tiles_per_pose = (int)(tx * ty);
   p.tile_y = (int)tile_y;
   p.nblocks = (uint32_t)blocks;
+  p.nblocks2 = (uint32_t)((uint64_t)c.B * (uint64_t)c.P * (uint64_t)(tx * ((ty + 1) / 2)));
   return TP_OK;
 }
 

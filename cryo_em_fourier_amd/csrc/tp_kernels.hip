@@ -45,6 +45,29 @@ __device__ __forceinline__ Out locate(const OpParams& p) {
   return o;
 }
 
+// The two-tile 3D kernel (k_grad3p): a workgroup takes two vertically adjacent tiles
+// of one pose (tile rows 2r and 2r + 1), batch t the tile row 2r + t, two
+// lanes per output in both.
+__device__ __forceinline__ void locate2(const OpParams& p, Out* o) {
+  const uint32_t per = (uint32_t)p.tiles_x * (((uint32_t)p.tiles_y + 1u) >> 1);
+  const uint32_t g = xcd_remap(blockIdx.x, gridDim.x);
+  const uint32_t tile = g % per, bn = g / per;
+  const int oi = (int)(threadIdx.x >> 1);
+  const int kx = (int)(tile % (uint32_t)p.tiles_x) * kTileXPairs + oi % kTileXPairs;
+  const int row0 = (int)(tile / (uint32_t)p.tiles_x) * 2 * p.tile_y + oi / kTileXPairs;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    o[t].n = (int)(bn % (uint32_t)p.P);
+    o[t].b = (int)(bn / (uint32_t)p.P);
+    o[t].kx = kx;
+    o[t].iy = row0 + t * p.tile_y;
+    o[t].in = o[t].kx < p.Wo && o[t].iy < p.No;
+    o[t].ky = signed_row(o[t].iy, p.No);
+    const long long k2 = (long long)o[t].kx * o[t].kx + (long long)o[t].ky * o[t].ky;
+    o[t].keep = o[t].in && (p.cut2 < 0 || k2 <= p.cut2);
+  }
+}
+
 // p = os * (kx R[0,:] + ky R[1,:]) in fp64; false if a component is not finite
 // or beyond +-2^30 (such samples read 0).
 template <int NDIM>
@@ -296,35 +319,55 @@ __device__ __forceinline__ void pair_grad_values(const OpParams& p, const Out& o
   for (int j = 0; j < 3; ++j) dS[j] = pair_sum(dS[j]);
 }
 
+// Two tiles per workgroup (locate2): the lane pairs gather S and dS for one
+// output of each tile, then every lane forms the gradient terms of its own
+// output and the wave reduces 64 outputs at once, so the G read, the phase
+// and the fp64 terms run on every lane (3.92 against 4.22 ms at box 256,
+// 4096 poses).  The forward keeps one tile: its two-tile form needs 93
+// registers, and the lost occupancy cost more than the shared tail saved.
 // (4 waves per SIMD: capping registers at 128 measured 12 % faster at box
 // 256 than the 155 the compiler picks on its own, with no spills)
 template <int INTERP>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_grad3p(OpParams p) {
   constexpr int NV = 8;  // dR rows 0 and 1, then ds_x, ds_y
   __shared__ double red[kBlock / 64][NV];
-  const Out o = locate<true>(p);
+  Out ob[2];
+  locate2(p, ob);
   const int h = threadIdx.x & 1;
-  const float2 sh = pose_shift(p, o);  // read before any store: a scalar load
-  double q[3] = {0.0, 0.0, 0.0};
-  const bool active = o.keep && sample_point<3>(p, o, q);
-  float2 S, dS[3];
-  pair_grad_values<INTERP, true>(p, o, h, active, q, S, dS);
+  const float2 sh = pose_shift(p, ob[0]);  // one pose, read before any store: a scalar load
+  float2 S[2], dS[2][3];
+  bool act[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    double q[3] = {0.0, 0.0, 0.0};
+    act[t] = ob[t].keep && sample_point<3>(p, ob[t], q);
+    pair_grad_values<INTERP, true>(p, ob[t], h, act[t], q, S[t], dS[t]);
+    // the first tile's sums are finished before the second tile's gathers
+    asm volatile("" : "+v"(S[t].x), "+v"(S[t].y));
+#pragma unroll
+    for (int j = 0; j < 3; ++j) asm volatile("" : "+v"(dS[t][j].x), "+v"(dS[t][j].y));
+  }
+  // lane h takes the pair's output in tile h
+  const Out& o = h ? ob[1] : ob[0];
+  const bool active = h ? act[1] : act[0];
+  const float2 Sh = h ? S[1] : S[0];
   double acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.0;
-  if (active && h == 0) {
-    // (G read here: reading it before the gathers raised the registers to
-    // 117 and measured slower)
+  if (active) {
+    // (G read here: reading it before the gathers raised the registers and
+    // measured slower)
     float2 gph = conjf2(p.img[img_index(p, o)]);
     if (p.shift) gph = cmul(gph, shift_phase(o.kx, o.ky, sh.x, sh.y, p.inv_no));
     const double os = (double)p.os;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      const double dldp = (double)gph.x * dS[j].x - (double)gph.y * dS[j].y;
+      const float2 d = h ? dS[1][j] : dS[0][j];
+      const double dldp = (double)gph.x * d.x - (double)gph.y * d.y;
       acc[j] = os * o.kx * dldp;
       acc[3 + j] = os * o.ky * dldp;
     }
-    const double im_gs = (double)gph.x * S.y + (double)gph.y * S.x;
+    const double im_gs = (double)gph.x * Sh.y + (double)gph.y * Sh.x;
     const double two_pi_over_n = 6.283185307179586476925 * p.inv_no;
     acc[6] = two_pi_over_n * o.kx * im_gs;
     acc[7] = two_pi_over_n * o.ky * im_gs;
@@ -343,14 +386,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 #pragma unroll
     for (int w = 0; w < kBlock / 64; ++w) v += red[w][i];
     if (v == 0.0) return;
+    const int b = ob[0].b, n = ob[0].n;
     if (i < 6) {
       if (p.grad_rot) {
-        const size_t br = p.B_rot == 1 ? 0 : (size_t)o.b;
-        unsafeAtomicAdd(p.grad_rot + ((br * p.P + o.n) * 3 + i / 3) * 3 + i % 3, (float)v);
+        const size_t br = p.B_rot == 1 ? 0 : (size_t)b;
+        unsafeAtomicAdd(p.grad_rot + ((br * p.P + n) * 3 + i / 3) * 3 + i % 3, (float)v);
       }
     } else if (p.grad_shift) {
-      const size_t bs = p.B_shift == 1 ? 0 : (size_t)o.b;
-      unsafeAtomicAdd(p.grad_shift + (bs * p.P + o.n) * 2 + (i - 6), (float)v);
+      const size_t bs = p.B_shift == 1 ? 0 : (size_t)b;
+      unsafeAtomicAdd(p.grad_shift + (bs * p.P + n) * 2 + (i - 6), (float)v);
     }
   }
 }
@@ -441,8 +485,8 @@ hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s) {
   const dim3 grid(p.nblocks), block(kBlock);
   if (p.ndim == 3) {
     if (use_grad_bricks(p, interp)) return launch_grad_bricks(p, interp, s);
-    if (interp) hipLaunchKernelGGL((k_grad3p<1>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_grad3p<0>), grid, block, 0, s, p);
+    if (interp) hipLaunchKernelGGL((k_grad3p<1>), dim3(p.nblocks2), block, 0, s, p);
+    else hipLaunchKernelGGL((k_grad3p<0>), dim3(p.nblocks2), block, 0, s, p);
   } else {
     if (interp) hipLaunchKernelGGL((k_grad_pose<2, 1>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((k_grad_pose<2, 0>), grid, block, 0, s, p);
