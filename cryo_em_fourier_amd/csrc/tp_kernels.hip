@@ -325,10 +325,10 @@ __device__ __forceinline__ void pair_grad_values(const OpParams& p, const Out& o
 // and the fp64 terms run on every lane (3.92 against 4.22 ms at box 256,
 // 4096 poses).  The forward keeps one tile: its two-tile form needs 93
 // registers, and the lost occupancy cost more than the shared tail saved.
-// (4 waves per SIMD: capping registers at 128 measured 12 % faster at box
-// 256 than the 155 the compiler picks on its own, with no spills)
+// (5 waves per SIMD: the compiler fits the kernel in 91 registers with no
+// spills, 3.70 against 3.95 ms at 4 waves (116 registers))
 template <int INTERP>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_grad3p(OpParams p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) void k_grad3p(OpParams p) {
   constexpr int NV = 8;  // dR rows 0 and 1, then ds_x, ds_y
   __shared__ double red[kBlock / 64][NV];
   Out ob[2];
