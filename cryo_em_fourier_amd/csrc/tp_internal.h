@@ -30,7 +30,7 @@ struct OpParams {
   int tiles_x, tiles_y, tiles_per_pose;
   int tile_y;             // ky-rows per tile (kTileY, or kTileYPairs for the paired 3D kernels)
   uint32_t nblocks;
-  uint32_t nblocks2;      // workgroups of the two-tile 3D gradient kernel (tile rows taken in pairs)
+  uint32_t nblocks2;      // workgroups of the two-tile pose-gradient kernel (tile rows taken in pairs)
 };
 
 // Brick decomposition of the adjoint (tp_adjoint.hip).

@@ -237,7 +237,9 @@ __global__ __launch_bounds__(kBlock) void k_grad_pose(OpParams p) {
 
 // ------------------------------------------------- 3D with two lanes per output
 
-template <int INTERP>
+// MAIN_FIRST: finish the main sum before the secondary gather (the reference
+// is in the Infinity Cache; see ref_cached)
+template <int INTERP, bool MAIN_FIRST>
 __global__ __launch_bounds__(kBlock) void k_project3p(OpParams p) {
   const Out o = locate<true>(p);
   const int h = threadIdx.x & 1;
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kBlock) void k_project3p(OpParams p) {
     float2 mv = gather3_half<INTERP>(rs, g, m[0], m[1], m[2], xmin1, h);
     // finish the main sum before the secondary gather: its loads then find
     // the main gather's registers free and go out together
-    asm volatile("" : "+v"(mv.x), "+v"(mv.y));
+    if (MAIN_FIRST) asm volatile("" : "+v"(mv.x), "+v"(mv.y));
     float2 sv = make_float2(0.f, 0.f);
     if (needs_secondary<INTERP>(m[0], xmin2)) sv = gather3_half<INTERP>(rs, g, mneg[0], mneg[1], mneg[2], xmin2, h);
     res = c ? make_float2(mv.x + sv.x, sv.y - mv.y) : make_float2(mv.x + sv.x, mv.y - sv.y);
@@ -319,26 +321,29 @@ __device__ __forceinline__ void pair_grad_values(const OpParams& p, const Out& o
   for (int j = 0; j < 3; ++j) dS[j] = pair_sum(dS[j]);
 }
 
-// Two tiles per workgroup (locate2): the lane pairs gather S and dS for one
-// output of each tile, then every lane forms the gradient terms of its own
-// output and the wave reduces 64 outputs at once, so the G read, the phase
-// and the fp64 terms run on every lane (3.92 against 4.22 ms at box 256,
-// 4096 poses).  The forward keeps one tile: its two-tile form needs 93
-// registers, and the lost occupancy cost more than the shared tail saved.
-// (5 waves per SIMD: the compiler fits the kernel in 91 registers with no
-// spills, 3.70 against 3.95 ms at 4 waves (116 registers))
+// Two tiles per workgroup (locate2): the lane pairs gather S and dS for
+// one output of each tile, then every lane forms the gradient terms of
+// its own output and the wave reduces 64 outputs at once, so the G read, the
+// phase and the fp64 terms run on every lane (3.70 against 4.22 ms for one
+// tile at box 256, 4096 poses, 5 waves per SIMD in 91 registers).  With the
+// reference streamed from HBM one tile per workgroup (k_grad3p_1) measured
+// faster (6.29 against 6.78 ms at box 256, oversampling 2).  The forward
+// keeps one tile:
+// its two-tile form needs 93 registers, and the lost occupancy cost more
+// than the shared tail saved.
 template <int INTERP>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) void k_grad3p(OpParams p) {
   constexpr int NV = 8;  // dR rows 0 and 1, then ds_x, ds_y
+  constexpr int NT = 2;
   __shared__ double red[kBlock / 64][NV];
-  Out ob[2];
+  Out ob[NT];
   locate2(p, ob);
   const int h = threadIdx.x & 1;
   const float2 sh = pose_shift(p, ob[0]);  // one pose, read before any store: a scalar load
-  float2 S[2], dS[2][3];
-  bool act[2];
+  float2 S[NT], dS[NT][3];
+  bool act[NT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NT; ++t) {
     double q[3] = {0.0, 0.0, 0.0};
     act[t] = ob[t].keep && sample_point<3>(p, ob[t], q);
     pair_grad_values<INTERP, true>(p, ob[t], h, act[t], q, S[t], dS[t]);
@@ -395,6 +400,67 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     } else if (p.grad_shift) {
       const size_t bs = p.B_shift == 1 ? 0 : (size_t)b;
       unsafeAtomicAdd(p.grad_shift + (bs * p.P + n) * 2 + (i - 6), (float)v);
+    }
+  }
+}
+
+// One tile per workgroup: lane 0 of each pair forms its output's gradient
+// terms.  Taken when the reference streams from HBM (see ref_cached).
+// (4 waves per SIMD: capping registers at 128 measured 12 % faster at box
+// 256 than the 155 the compiler picks on its own, with no spills)
+template <int INTERP>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_grad3p_1(OpParams p) {
+  constexpr int NV = 8;  // dR rows 0 and 1, then ds_x, ds_y
+  __shared__ double red[kBlock / 64][NV];
+  const Out o = locate<true>(p);
+  const int h = threadIdx.x & 1;
+  const float2 sh = pose_shift(p, o);  // read before any store: a scalar load
+  double q[3] = {0.0, 0.0, 0.0};
+  const bool active = o.keep && sample_point<3>(p, o, q);
+  float2 S, dS[3];
+  pair_grad_values<INTERP, true>(p, o, h, active, q, S, dS);
+  double acc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = 0.0;
+  if (active && h == 0) {
+    // (G read here: reading it before the gathers raised the registers to
+    // 117 and measured slower)
+    float2 gph = conjf2(p.img[img_index(p, o)]);
+    if (p.shift) gph = cmul(gph, shift_phase(o.kx, o.ky, sh.x, sh.y, p.inv_no));
+    const double os = (double)p.os;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const double dldp = (double)gph.x * dS[j].x - (double)gph.y * dS[j].y;
+      acc[j] = os * o.kx * dldp;
+      acc[3 + j] = os * o.ky * dldp;
+    }
+    const double im_gs = (double)gph.x * S.y + (double)gph.y * S.x;
+    const double two_pi_over_n = 6.283185307179586476925 * p.inv_no;
+    acc[6] = two_pi_over_n * o.kx * im_gs;
+    acc[7] = two_pi_over_n * o.ky * im_gs;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (__ballot(active) != 0ull) {
+    const double d = wave_sum8(acc);
+    if ((lane & 7) == 0) red[wave][lane >> 3] = d;
+  } else if (lane < NV) {
+    red[wave][lane] = 0.0;
+  }
+  __syncthreads();
+  if (threadIdx.x < NV) {
+    const int i = threadIdx.x;
+    double v = 0.0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) v += red[w][i];
+    if (v == 0.0) return;
+    if (i < 6) {
+      if (p.grad_rot) {
+        const size_t br = p.B_rot == 1 ? 0 : (size_t)o.b;
+        unsafeAtomicAdd(p.grad_rot + ((br * p.P + o.n) * 3 + i / 3) * 3 + i % 3, (float)v);
+      }
+    } else if (p.grad_shift) {
+      const size_t bs = p.B_shift == 1 ? 0 : (size_t)o.b;
+      unsafeAtomicAdd(p.grad_shift + (bs * p.P + o.n) * 2 + (i - 6), (float)v);
     }
   }
 }
@@ -469,11 +535,24 @@ __global__ __launch_bounds__(kBlock) void k_zero(uint32_t* ptr, size_t words) {
 
 }  // namespace
 
+// One batch entry's reference fits the 256 MB Infinity Cache (box 256 at
+// oversampling 1: 67.6 MB; box 320: 132 MB; box 256 at oversampling 2:
+// 539 MB streams from HBM).  The gathers' scheduling choices (main sum
+// first, two-tile pose gradients) were measured faster there and slower
+// when the taps come from HBM, where more loads in flight per wave pay.
+static bool ref_cached(const OpParams& p) { return (uint64_t)p.ref_elems * 8u <= (256ull << 20); }
+
 hipError_t launch_project(const OpParams& p, int interp, hipStream_t s) {
   const dim3 grid(p.nblocks), block(kBlock);
   if (p.ndim == 3) {
-    if (interp) hipLaunchKernelGGL((k_project3p<1>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_project3p<0>), grid, block, 0, s, p);
+    const bool c = ref_cached(p);
+    if (interp) {
+      if (c) hipLaunchKernelGGL((k_project3p<1, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((k_project3p<1, false>), grid, block, 0, s, p);
+    } else {
+      if (c) hipLaunchKernelGGL((k_project3p<0, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((k_project3p<0, false>), grid, block, 0, s, p);
+    }
   } else {
     if (interp) hipLaunchKernelGGL((k_project<2, 1>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((k_project<2, 0>), grid, block, 0, s, p);
@@ -485,8 +564,13 @@ hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s) {
   const dim3 grid(p.nblocks), block(kBlock);
   if (p.ndim == 3) {
     if (use_grad_bricks(p, interp)) return launch_grad_bricks(p, interp, s);
-    if (interp) hipLaunchKernelGGL((k_grad3p<1>), dim3(p.nblocks2), block, 0, s, p);
-    else hipLaunchKernelGGL((k_grad3p<0>), dim3(p.nblocks2), block, 0, s, p);
+    if (ref_cached(p)) {
+      if (interp) hipLaunchKernelGGL((k_grad3p<1>), dim3(p.nblocks2), block, 0, s, p);
+      else hipLaunchKernelGGL((k_grad3p<0>), dim3(p.nblocks2), block, 0, s, p);
+    } else {
+      if (interp) hipLaunchKernelGGL((k_grad3p_1<1>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((k_grad3p_1<0>), grid, block, 0, s, p);
+    }
   } else {
     if (interp) hipLaunchKernelGGL((k_grad_pose<2, 1>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((k_grad_pose<2, 0>), grid, block, 0, s, p);
