@@ -106,6 +106,31 @@ def test_fullsize_grad_pose_sampled_poses(key):
     assert not gr[:, rest].any() and not gs[:, rest].any(), "poses with zero upstream must get zero gradients"
 
 
+def test_streamed_reference_linear_sampled_poses():
+    """A reference above the Infinity Cache's 256 MB (box 256 padded to 512:
+    539 MB) takes the gathers' other scheduling (the forward without the
+    main-first order, the one-tile pose-gradient kernel); the cubic cases
+    above cover it for the cubic kernel, this one for the linear kernel:
+    forward and pose gradients of the sampled poses against the oracle."""
+    from cryo_em_fourier_amd import tp_grad_pose, tp_project_3d
+
+    c = workload("c4-os2")
+    w = c["w"]
+    assert c["V"][0].nbytes > 256 << 20
+    log(f"[streamed reference, linear] c4-os2: ref {c['V'].shape}, sampled {c['idx'].tolist()}")
+    lin = oracle.LINEAR
+    out = tp_project_3d(to_dev(c["V"]), to_dev(c["R"]), to_dev(c["s"]), w.N_out, lin, c["os"], w.cutoff)
+    ref = oracle.project(c["V"], c["R"][:, c["idx"]], c["s"][:, c["idx"]], w.N_out, lin, c["os"], w.cutoff)
+    assert_parity(out[:, c["idx"]].cpu().numpy(), ref, "forward c4-os2 linear")
+    del out
+    gr, gs = tp_grad_pose(to_dev(c["V"]), _sparse_upstream(c), to_dev(c["R"]), to_dev(c["s"]), lin, c["os"],
+                          w.cutoff)
+    dR, ds = oracle.grad_pose(c["V"], c["G_sub"], c["R"][:, c["idx"]], c["s"][:, c["idx"]], w.N_out, lin, c["os"],
+                              w.cutoff)
+    assert_parity(gr.cpu().numpy()[:, c["idx"]], dR, "grad_rot c4-os2 linear")
+    assert_parity(gs.cpu().numpy()[:, c["idx"]], ds, "grad_shift c4-os2 linear")
+
+
 @pytest.mark.parametrize("key", KEYS)
 def test_fullsize_grad_pose_jac_sampled_poses(key):
     """The Jacobian-saving forward over all poses, then the pose gradients
