@@ -17,7 +17,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtp.so")
-SOURCES = ["tp_api.hip", "tp_kernels.hip", "tp_adjoint.hip", "tp_gather.hip", "tp_rotate.hip"]
+SOURCES = ["tp_api.hip", "tp_kernels.hip", "tp_adjoint.hip", "tp_rotate.hip"]
 PEAKS_LIB = os.path.join(HERE, "libtp_peaks.so")
 PEAKS_SOURCES = ["peaks.hip"]
 ARCH = os.environ.get("TP_OFFLOAD_ARCH", "gfx950")

@@ -77,11 +77,6 @@ uint64_t backward_jac_blocks(const OpParams& p);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
 uint64_t adjoint_blocks(const OpParams& p);
 
-// Brick gather of the 3D pose gradients (tp_gather.hip), chosen by
-// use_grad_bricks() over the per-output kernel where it is faster and fits.
-bool use_grad_bricks(const OpParams& p, int interp);
-hipError_t launch_grad_bricks(const OpParams& p, int interp, hipStream_t s);
-
 // Largest output box of the brick kernels (14-bit lattice offsets).
 constexpr int64_t kMaxBrickOut = (1 << 14) - 1;
 

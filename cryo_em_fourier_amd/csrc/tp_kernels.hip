@@ -1,6 +1,5 @@
 // Projector kernels for gfx950: forward gather and pose gradients (the
-// adjoint lives in tp_adjoint.hip, the brick gradient gather in
-// tp_gather.hip); 2D and 3D references; linear and Catmull-Rom
+// adjoint lives in tp_adjoint.hip); 2D and 3D references; linear and Catmull-Rom
 // interpolation; the forward that saves each output's Jacobian and the pose
 // gradients taken from it.
 //
@@ -563,7 +562,6 @@ hipError_t launch_project(const OpParams& p, int interp, hipStream_t s) {
 hipError_t launch_grad_pose(const OpParams& p, int interp, hipStream_t s) {
   const dim3 grid(p.nblocks), block(kBlock);
   if (p.ndim == 3) {
-    if (use_grad_bricks(p, interp)) return launch_grad_bricks(p, interp, s);
     if (ref_cached(p)) {
       if (interp) hipLaunchKernelGGL((k_grad3p<1>), dim3(p.nblocks2), block, 0, s, p);
       else hipLaunchKernelGGL((k_grad3p<0>), dim3(p.nblocks2), block, 0, s, p);
