@@ -165,8 +165,11 @@ __device__ __forceinline__ void gather2_grad(rsrc_t rs, const RefGeom& g, double
 // are always active.  (The gradient gathers keep a full setup per lane: with
 // the derivative weights the exchange spills at 128 registers.)
 
-__device__ __forceinline__ int from_even_lane(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xA0, 0xF, 0xF, false); }
-__device__ __forceinline__ int from_odd_lane(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xF5, 0xF, 0xF, false); }
+// (quad permutes read within the lane pair, whose two lanes are always
+// active together, so no lane reads a disabled one and no old value is
+// needed: a single v_mov_b32_dpp each)
+__device__ __forceinline__ int from_even_lane(int v) { return __builtin_amdgcn_mov_dpp(v, 0xA0, 0xF, 0xF, true); }
+__device__ __forceinline__ int from_odd_lane(int v) { return __builtin_amdgcn_mov_dpp(v, 0xF5, 0xF, 0xF, true); }
 
 // The pair's y and z weights and row offsets (in residue order, see
 // by_residue): each lane sets up one axis.
@@ -301,7 +304,7 @@ __device__ __forceinline__ void gather3_grad_half(rsrc_t rs, const RefGeom& g, d
 // 1, 0, 3, 2) feeds the add, with no LDS round trip.  Every lane of the wave
 // must be active.
 __device__ __forceinline__ float pair_sum1(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float2 pair_sum(float2 v) { return make_float2(pair_sum1(v.x), pair_sum1(v.y)); }
 
