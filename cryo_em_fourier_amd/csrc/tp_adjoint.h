@@ -19,7 +19,7 @@ namespace tp {
 namespace adj {
 constexpr int kVox = 4096;          // voxels per brick
 constexpr int kGroupMax = 16;       // poses per fixed-point group
-constexpr int kPrefetch = 1;        // hits whose G values a thread loads at once (2: more spills, 1.3 % slower at c4)
+constexpr int kPrefetch = 1;        // hits whose G values a thread loads at once (2: more spills, 1.3 % slower at box 256)
 // Fixed point.  A pose adds to a voxel at most 2 m (a lattice point carries
 // a real and a mirror value, m the largest |re| + |im| of G) times W, the sum
 // of |w| over its lattice points.  Searched over orientations, voxel offsets

@@ -551,8 +551,9 @@ uint64_t adjoint_blocks(const OpParams& p) {
 }
 
 // Dense lattices (oversampling up to 1.25) fill a brick with hits and run
-// faster on 512-thread workgroups; sparse ones on 256 (measured at c4: 5.9
-// against 6.4 ms at oversampling 1, 8.9 against 9.8 ms at oversampling 2).
+// faster on 512-thread workgroups; sparse ones on 256 (measured at box 256
+// with 4096 poses: 5.9 against 6.4 ms at oversampling 1, 8.9 against 9.8 ms
+// at oversampling 2).
 static bool wide_adjoint(const OpParams& p) { return p.os <= 1.25f; }
 
 template <int MODE, int BS>
@@ -583,14 +584,15 @@ hipError_t launch_backproject(const OpParams& p, int interp, hipStream_t s) {
 }
 
 // The adjoint and the pose gradients from a saved Jacobian in one launch:
-// measured at c4, 6.0 ms against 6.65 ms for the two launches (the gradient
+// measured at box 256 with 4096 poses, 6.0 ms against 6.65 ms for the two launches (the gradient
 // workgroups fill the adjoint's tail).  Spreading them among the bricks
 // instead was slower (7.2 to 8.8 ms): they take the LDS-bound bricks' slots.
 hipError_t launch_backward_jac(const OpParams& p, int interp, hipStream_t s) {
   // with many bricks (boxes from 256), larger pose chunks than the plain
   // adjoint's: fewer, longer brick workgroups, whose uneven end the gradient
-  // workgroups fill (c4: 6.01 ms with 512 poses per chunk, 6.10 with 256,
-  // 6.2 with 768; c5 16.35 against 16.66; a box of 128 has 320 bricks and
+  // workgroups fill (box 256, 4096 poses: 6.01 ms with 512 poses per chunk,
+  // 6.10 with 256, 6.2 with 768; box 320, 8192 poses: 16.35 against 16.66;
+  // a box of 128 has 320 bricks and
   // needs the smaller chunks to fill the GPU: 1.23 against 0.80 ms)
   const BrickParams bp = brick_params<3>(p);
   return launch_adjoint<kSliceGrad>(p, bp.nbricks >= 2048 ? brick_params<3>(p, false, 512) : bp, 3, interp, s);

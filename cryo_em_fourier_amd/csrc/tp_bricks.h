@@ -1,4 +1,4 @@
-// Brick-owned kernels (the adjoint, the brick gathers): which poses' sample
+// Brick-owned kernels (the adjoints): which poses' sample
 // planes meet a box of sample positions, and which lattice points of a pose
 // fall in it, enumerated row by row.
 //
