@@ -228,11 +228,7 @@ __device__ __forceinline__ void lattice_values3(const OpParams& p, const PoseVie
   for (int j = 0; j < 3; ++j) cd.q[j] = (double)kx * pv.u[j] + (double)ky * pv.v[j] + (double)kz * pv.w[j];
   float2 cr = gr, cm = gm;
   if (p.shift) {
-    double t = ((double)kx * pv.sx + (double)ky * pv.sy + (double)kz * pv.sz) * p.inv_no;
-    t -= rint(t);
-    float sn, cs;
-    sincospif((float)(-2.0 * t), &sn, &cs);
-    const float2 ph = make_float2(cs, sn);
+    const float2 ph = phase_of_turns(((double)kx * pv.sx + (double)ky * pv.sy + (double)kz * pv.sz) * p.inv_no);
     cr = cmul(conjf2(ph), gr);
     cm = cmul(ph, gm);
   }

@@ -140,14 +140,12 @@ __device__ __forceinline__ uint32_t axis_off(int t, const RefGeom& g, uint32_t s
   return ok ? __umul24((uint32_t)w, stride) : kBig;
 }
 
-// exp(-2 pi i (kx sx + ky sy) / n_out).  The turns t are reduced in fp64
-// (so that large kx*s products keep full fp32 accuracy) to a quarter-turn
-// count q in [-2, 2] and a rest r = t - q/4 in [-1/8, 1/8]; sin and cos of
-// 2 pi r come from polynomials in r^2 fitted by least squares on that
-// interval at Chebyshev nodes (largest error 9e-8 evaluated in fp32), then
-// turn by q quarter turns.
-__device__ __forceinline__ float2 shift_phase(int kx, int ky, float sx, float sy, double inv_n) {
-  double t = ((double)kx * (double)sx + (double)ky * (double)sy) * inv_n;
+// exp(-2 pi i t) for t in turns.  t is reduced in fp64 (so that large k*s
+// products keep full fp32 accuracy) to a quarter-turn count q in [-2, 2] and
+// a rest r = t - q/4 in [-1/8, 1/8]; sin and cos of 2 pi r come from
+// polynomials in r^2 fitted by least squares on that interval at Chebyshev
+// nodes (largest error 9e-8 evaluated in fp32), then turn by q quarter turns.
+__device__ __forceinline__ float2 phase_of_turns(double t) {
   t -= rint(t);
   const double q = rint(4.0 * t);
   const float r = (float)(t - 0.25 * q), u = r * r;
@@ -158,6 +156,11 @@ __device__ __forceinline__ float2 shift_phase(int kx, int ky, float sx, float sy
   const int k = (int)q & 3;
   const float ca = (k & 1) ? sn : cs, sa = (k & 1) ? cs : sn;
   return make_float2(((k + 1) & 2) ? -ca : ca, (k & 2) ? sa : -sa);
+}
+
+// exp(-2 pi i (kx sx + ky sy) / n_out)
+__device__ __forceinline__ float2 shift_phase(int kx, int ky, float sx, float sy, double inv_n) {
+  return phase_of_turns(((double)kx * (double)sx + (double)ky * (double)sy) * inv_n);
 }
 
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {

@@ -66,11 +66,7 @@ __device__ __forceinline__ bool rsample(const OpParams& p, const ROut& o, double
 __device__ __forceinline__ float2 rphase(const OpParams& p, const ROut& o) {
   if (!p.shift) return make_float2(1.f, 0.f);
   const float* s = p.shift + ((size_t)(p.B_shift == 1 ? 0 : o.b) * p.P + o.n) * 3;
-  double t = ((double)o.kx * s[0] + (double)o.ky * s[1] + (double)o.kz * s[2]) * p.inv_no;
-  t -= rint(t);
-  float sn, cs;
-  sincospif((float)(-2.0 * t), &sn, &cs);
-  return make_float2(cs, sn);
+  return phase_of_turns(((double)o.kx * s[0] + (double)o.ky * s[1] + (double)o.kz * s[2]) * p.inv_no);
 }
 
 template <int INTERP>
