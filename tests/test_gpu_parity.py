@@ -54,6 +54,11 @@ def case3d(name):
         "mixed-shift":   (22, 20, 2, 3, 1, 2, LINEAR, 1.1, 9.0, "cplx", "so3"),
         "bcast-cubic":   (20, 22, 3, 3, 1, 1, CUBIC, 1.0, 10.5, "cplx", "so3"),
         "adv-cubic-cplx": (32, 32, 1, 8, 1, 1, CUBIC, 1.0, 15.0, "cplx", "adv"),
+        # the shift phase's fp64 turn reduction: shifts of thousands of pixels,
+        # and shifts in multiples of N_out / 8 that put the rest r exactly on
+        # the ends of its [-1/8, 1/8] interval
+        "big-shift":     (32, 32, 1, 6, 1, 1, CUBIC, 1.0, 15.0, "cplx", "so3"),
+        "eighth-shift":  (32, 32, 1, 6, 1, 1, LINEAR, 1.0, 15.0, "cplx", "so3"),
     }[name]
     N, n_out, B, P, B_rot, B_shift, interp, os_, cutoff, vk, pk = spec
     if vk == "c1":
@@ -71,13 +76,18 @@ def case3d(name):
     else:
         R = np.stack([synth.uniform_rotations(rng, P) for _ in range(B_rot)])
     s = None if B_shift == 0 else rng.uniform(-4, 4, (B_shift, P, 2)).astype(np.float32)
+    if name == "big-shift":
+        s = rng.uniform(-3000, 3000, (B_shift, P, 2)).astype(np.float32)
+    elif name == "eighth-shift":
+        s = (rng.integers(-40, 41, (B_shift, P, 2)) * (n_out / 8)).astype(np.float32)
     G = complex_normal(rng, (B, P, n_out, n_out // 2 + 1))
     return dict(V=V.astype(np.complex64), R=R.astype(np.float32), s=s, G=G, N=N, n_out=n_out,
                 interp=interp, os=np.float32(os_), cutoff=np.float32(cutoff))
 
 
 CASES3 = ["c1", "c1-cubic", "odd-nocut", "os2", "os1.5-linear", "batch", "batch-bcast",
-          "adv-cubic", "adv-linear", "ragged", "mixed-rot", "mixed-shift", "bcast-cubic", "adv-cubic-cplx"]
+          "adv-cubic", "adv-linear", "ragged", "mixed-rot", "mixed-shift", "bcast-cubic", "adv-cubic-cplx",
+          "big-shift", "eighth-shift"]
 
 
 def _dev(c):
