@@ -136,6 +136,8 @@ ROT_CASES = {
     "batch": (16, 18, 2, 2, 2, True, CUBIC, 16 / 18, 8.5, "so3"),
     "cube": (20, 20, 24, 1, 1, True, CUBIC, 1.0, 9.0, "cube"),
     "chunked-os1.5": (48, 32, 40, 1, 1, True, CUBIC, 1.5, 15.0, "so3"),
+    # shifts of thousands of voxels: the phase's fp64 turn reduction
+    "big-shift": (16, 16, 3, 1, 1, True, CUBIC, 1.0, 7.0, "so3"),
 }
 
 
@@ -159,6 +161,8 @@ def rot_case(name):
     else:
         R = np.stack([synth.uniform_rotations(rng, P) for _ in range(B_rot)]).astype(np.float32)
     s = rng.uniform(-3, 3, (B_rot, P, 3)).astype(np.float32) if shifted else None
+    if name == "big-shift":
+        s = rng.uniform(-2500, 2500, (B_rot, P, 3)).astype(np.float32)
     G = complex_normal(rng, (B, P, n_out, n_out, n_out // 2 + 1))
     return dict(V=V, R=R, s=s, G=G, N=N, n_out=n_out, interp=interp, os=np.float32(os_), cutoff=np.float32(cutoff))
 
@@ -187,6 +191,23 @@ def test_rotate_backproject_3d_matches_oracle(name):
                                    float(c["cutoff"])).cpu().numpy()
     ref = oracle.rotate_backproject_3d(c["G"], c["R"], c["s"], c["N"], c["interp"], c["os"], c["cutoff"])
     assert_parity(got, ref, f"rotate_backproject_3d {name}")
+
+
+@pytest.mark.parametrize("name", list(ROT_CASES))
+def test_rotate_grad_pose_matches_oracle(name):
+    """The rotation's pose gradients gathered again from the reference
+    (nothing saved by the forward) against the oracle's."""
+    from cryo_em_fourier_amd import tp_rotate_grad_pose
+
+    c = rot_case(name)
+    log(f"[rotate_grad_pose] {name}")
+    s = None if c["s"] is None else to_dev(c["s"])
+    gr, gs = tp_rotate_grad_pose(to_dev(c["V"]), to_dev(c["G"]), to_dev(c["R"]), s, c["interp"], float(c["os"]),
+                                 float(c["cutoff"]))
+    dR, ds = oracle.rotate_grad_pose(c["V"], c["G"], c["R"], c["s"], c["n_out"], c["interp"], c["os"], c["cutoff"])
+    assert_parity(gr.cpu().numpy(), dR, f"rotate grad_rot {name}")
+    if c["s"] is not None:
+        assert_parity(gs.cpu().numpy(), ds, f"rotate grad_shift {name}")
 
 
 @pytest.mark.parametrize("name", list(ROT_CASES))
