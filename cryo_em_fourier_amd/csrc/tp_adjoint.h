@@ -19,7 +19,7 @@ namespace tp {
 namespace adj {
 constexpr int kVox = 4096;          // voxels per brick
 constexpr int kGroupMax = 16;       // poses per fixed-point group
-constexpr int kPrefetch = 1;        // hits whose G values a thread loads at once (2: more spills, 1.3 % slower at box 256)
+
 // Fixed point.  A pose adds to a voxel at most 2 m (a lattice point carries
 // a real and a mirror value, m the largest |re| + |im| of G) times W, the sum
 // of |w| over its lattice points.  Searched over orientations, voxel offsets
@@ -181,27 +181,34 @@ __device__ __forceinline__ void lattice_parts(const OpParams& p, int kx, int ky,
 }
 
 // G entries of a lattice point: the real output (kx, ky) and the real output
-// (-kx, -ky) whose mirror it carries (zero where absent).
-// (WEIGHTS: real weights, as (w, 0).)
+// (-kx, -ky) whose mirror it carries (zero where absent, or where valid is
+// false).  (WEIGHTS: real weights, as (w, 0).)  Both loads are issued
+// unconditionally, an absent entry reading the image's first entry instead,
+// so that a caller can keep the loads in flight across other work (no
+// branch between the loads and their use).
 // (the image's offset is taken once; the in-image offsets are 32-bit, below
 // No * Wo < 2^32)
 template <bool WEIGHTS>
-__device__ __forceinline__ void lattice_load(const OpParams& p, size_t img, int kx, int ky, float2& gr,
+__device__ __forceinline__ void lattice_load(const OpParams& p, size_t img, int kx, int ky, bool valid, float2& gr,
                                              float2& gm) {
   bool real, mirr;
   lattice_parts(p, kx, ky, real, mirr);
+  real = real && valid;
+  mirr = mirr && valid;
   const size_t base = img * ((size_t)p.No * p.Wo);
   const uint32_t wo = (uint32_t)p.Wo;
-  const uint32_t or_ = (uint32_t)(ky < 0 ? ky + p.No : ky) * wo + (uint32_t)kx;
-  const uint32_t om = (uint32_t)(-ky < 0 ? -ky + p.No : -ky) * wo + (uint32_t)(-kx);
+  const uint32_t or_ = real ? (uint32_t)(ky < 0 ? ky + p.No : ky) * wo + (uint32_t)kx : 0u;
+  const uint32_t om = mirr ? (uint32_t)(-ky < 0 ? -ky + p.No : -ky) * wo + (uint32_t)(-kx) : 0u;
   if (WEIGHTS) {
     const float* w = p.wimg + base;
-    gr = make_float2(real ? w[or_] : 0.f, 0.f);
-    gm = make_float2(mirr ? w[om] : 0.f, 0.f);
+    const float a = w[or_], b = w[om];
+    gr = make_float2(real ? a : 0.f, 0.f);
+    gm = make_float2(mirr ? b : 0.f, 0.f);
   } else {
     const float2* g = p.img + base;
-    gr = real ? g[or_] : make_float2(0.f, 0.f);
-    gm = mirr ? g[om] : make_float2(0.f, 0.f);
+    const float2 a = g[or_], b = g[om];
+    gr = real ? a : make_float2(0.f, 0.f);
+    gm = mirr ? b : make_float2(0.f, 0.f);
   }
 }
 
@@ -288,6 +295,107 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
       for (int dx = 0; dx < T; ++dx) {
         if (REAL) atomicAdd(reinterpret_cast<int*>(acc) + w + dx, cvt_rpi(are[dx] * wyz));
         else atomicAdd(acc + w + dx, pack_pair(cvt_rpi(are[dx] * wyz), cvt_rpi(aim[dx] * wyz)));
+      }
+    }
+  }
+}
+
+// Whether a 3D brick with guard columns, rows and planes (G = kGuard) is
+// interior: not the lowest brick in x, y or z, and its guards lie inside the
+// stored range.  Then every tap of a lattice point in the reach box lands in
+// the accumulator (its first tap lies in the brick on every axis), every x
+// tap is at x >= 1, and spread_interior() applies.
+template <int NDIM, int G, int BZ = 16>
+__device__ __forceinline__ bool brick_interior(const BrickPos& br) {
+  using BR = Brick<NDIM, BZ>;
+  if (NDIM != 3 || G < kGuard) return false;
+  return !br.xbottom && !br.ybottom && !br.zbottom && br.ylim == br.y0 + BR::Y + G - 1 &&
+         br.zlim == br.z0 + BR::Z + G - 1;
+}
+
+// Spread of an interior brick (brick_interior), with the lanes of a wave
+// reassigned so that the lanes of each LDS pass add to distinct banks.
+//
+// A wave's 64-bit LDS add is served 16 lanes at a time (lanes 16j .. 16j +
+// 15), and lanes of one pass whose slots share a bank pair (slot mod 16)
+// are served one after the other.  Every tap of a lattice point sits at a
+// compile-time offset from its first tap's slot, so the bank pairs of all 64
+// tap adds of a lane follow from that base slot.  The wave ranks its lattice
+// points by base mod 16 (a counting sort over ballots) and deals them out
+// round-robin over the four passes: with four points per bank pair every
+// pass gets one of each.  The lattice points themselves (their G loads, the
+// phase, the sample point) stay in the lanes that read them, which keeps the
+// loads coalesced; only the spread's inputs move, through ds_permute.
+
+// The rank of each lane's key (0..16) in the wave's stable ascending order.
+// Every lane of the wave must be active.
+__device__ __forceinline__ int wave_rank(int key) {
+  int rank = 0, pre = 0;
+#pragma unroll
+  for (int b = 0; b <= 16; ++b) {
+    const unsigned long long m = __ballot(key == b);
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+    if (key == b) rank = pre + below;
+    pre += __popcll(m);
+  }
+  return rank;
+}
+
+// Sends v to lane dest (a permutation of the wave's lanes).
+__device__ __forceinline__ float permute_f(int dest, float v) {
+  return __int_as_float(__builtin_amdgcn_ds_permute(dest << 2, __float_as_int(v)));
+}
+
+// Every lane of the wave calls it; act: the lane holds a lattice point in the
+// reach box (cd valid).
+template <int INTERP, bool REAL, int G, int BZ = 16>
+__device__ __forceinline__ void spread_interior(const BrickPos& br, const Cand& cd, bool act, float inv_q,
+                                                unsigned long long* acc) {
+  using L = AccLayout<3, G, BZ>;
+  using K = Kern<INTERP>;
+  constexpr int T = K::T;
+  uint32_t base = ~0u;
+  float fx = 0.f, fy = 0.f, fz = 0.f, vr = 0.f, vi = 0.f;
+  if (act) {
+    const AxisPos ax = axis_pos(cd.q[0], K::OFF), ay = axis_pos(cd.q[1], K::OFF), az = axis_pos(cd.q[2], K::OFF);
+    base = (uint32_t)acc_word<3, G, BZ>(ax.x0 - br.x0, ay.x0 - br.y0, az.x0 - br.z0);
+    fx = ax.f;
+    fy = ay.f;
+    fz = az.f;
+    vr = cd.v1.x * inv_q;
+    vi = cd.v1.y * inv_q;
+  }
+  const int rank = wave_rank(act ? (int)(base & 15u) : 16);
+  const int dest = ((rank & 3) << 4) | (rank >> 2);
+  base = (uint32_t)__builtin_amdgcn_ds_permute(dest << 2, (int)base);
+  fx = permute_f(dest, fx);
+  fy = permute_f(dest, fy);
+  fz = permute_f(dest, fz);
+  vr = permute_f(dest, vr);
+  if (!REAL) vi = permute_f(dest, vi);
+  if (base == ~0u) return;
+  float wx[T], wy[T], wz[T];
+  K::w(fx, wx);
+  K::w(fy, wy);
+  K::w(fz, wz);
+  float are[T], aim[T];
+#pragma unroll
+  for (int d = 0; d < T; ++d) {
+    are[d] = wx[d] * vr;
+    aim[d] = wx[d] * vi;
+  }
+  unsigned long long* a = acc + base;
+  int* ar = reinterpret_cast<int*>(acc) + base;
+#pragma unroll
+  for (int dz = 0; dz < T; ++dz) {
+#pragma unroll
+    for (int dy = 0; dy < T; ++dy) {
+      const float wyz = wy[dy] * wz[dz];
+#pragma unroll
+      for (int dx = 0; dx < T; ++dx) {
+        const int o = dz * L::PZ + dy * L::S + dx;
+        if (REAL) atomicAdd(ar + o, cvt_rpi(are[dx] * wyz));
+        else atomicAdd(a + o, pack_pair(cvt_rpi(are[dx] * wyz), cvt_rpi(aim[dx] * wyz)));
       }
     }
   }

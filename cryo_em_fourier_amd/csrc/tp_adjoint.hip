@@ -293,21 +293,23 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   __syncthreads();
 
   const Box bx = reach_box<NDIM, INTERP, EXCLZ>(br);
+  const bool interior = brick_interior<NDIM, G>(br);
   int g0 = 0;  // first pose of the current group in s_poses
 
   // G entries of hit h of the current group
-  auto load_hit = [&](uint32_t h, float2& gr, float2& gm) {
+  auto load_hit = [&](uint32_t h, float2& gr, float2& gm, bool valid = true) {
     if (VOL) {
       const PoseView& pv = s_view[0];
       const int kx = pv.kx0 + (int)(h & 0x3FFu), ky = pv.ky0 + (int)((h >> 10) & 0x3FFu), kz = pv.kz0 + (int)(h >> 20);
       const size_t img = (size_t)br.b * p.P + s_poses[g0];
       bool real, mirr;
       lattice_parts3(p, kx, ky, kz, real, mirr);
-      gr = real ? p.img[out_index3(p, img, kx, ky, kz)] : make_float2(0.f, 0.f);
-      gm = mirr ? p.img[out_index3(p, img, -kx, -ky, -kz)] : make_float2(0.f, 0.f);
+      gr = real && valid ? p.img[out_index3(p, img, kx, ky, kz)] : make_float2(0.f, 0.f);
+      gm = mirr && valid ? p.img[out_index3(p, img, -kx, -ky, -kz)] : make_float2(0.f, 0.f);
     } else {
       const PoseView& pv = s_view[hit_pose(h)];
-      lattice_load<WEIGHTS>(p, (size_t)br.b * p.P + s_poses[g0 + hit_pose(h)], hit_kx(h, pv), hit_ky(h, pv), gr, gm);
+      lattice_load<WEIGHTS>(p, (size_t)br.b * p.P + s_poses[g0 + hit_pose(h)], hit_kx(h, pv), hit_ky(h, pv), valid, gr,
+                            gm);
     }
   };
 
@@ -362,36 +364,40 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
       }
       float amax = 0.f;
       bool bad = false;
-      for (int i0 = 0; i0 < nh; i0 += kPrefetch * BS) {
-        float2 gr[kPrefetch], gm[kPrefetch];
-#pragma unroll
-        for (int k = 0; k < kPrefetch; ++k) {
-          const int i = i0 + hit_slot(tid) + k * BS;
-          gr[k] = gm[k] = make_float2(0.f, 0.f);
-          if (i < nh) load_hit(s_hits[i], gr[k], gm[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < kPrefetch; ++k) {
-          if (!finite2(gr[k])) { gr[k] = make_float2(0.f, 0.f); bad = true; }
-          if (!finite2(gm[k])) { gm[k] = make_float2(0.f, 0.f); bad = true; }
-          amax = fmaxf(amax, fmaxf(fabsf(gr[k].x) + fabsf(gr[k].y), fabsf(gm[k].x) + fabsf(gm[k].y)));
-        }
+      // software pipeline: the G values of a thread's next hit are loaded
+      // while its current hit is spread
+      float2 ngr, ngm;
+      uint32_t nh_tag = s_hits[min(hit_slot(tid), nh - 1)];
+      load_hit(nh_tag, ngr, ngm, hit_slot(tid) < nh);
+      for (int i0 = 0; i0 < nh; i0 += BS) {
+        const int i = i0 + hit_slot(tid);
+        const uint32_t h = nh_tag;
+        float2 gr = ngr, gm = ngm;
+        nh_tag = s_hits[min(i + BS, nh - 1)];
+        load_hit(nh_tag, ngr, ngm, i + BS < nh);
+        if (!finite2(gr)) { gr = make_float2(0.f, 0.f); bad = true; }
+        if (!finite2(gm)) { gm = make_float2(0.f, 0.f); bad = true; }
+        amax = fmaxf(amax, fmaxf(fabsf(gr.x) + fabsf(gr.y), fabsf(gm.x) + fabsf(gm.y)));
         if (measure_only) continue;
-#pragma unroll
-        for (int k = 0; k < kPrefetch; ++k) {
-          const int i = i0 + hit_slot(tid) + k * BS;
-          if (i >= nh) continue;
-          const uint32_t h = s_hits[i];
-          Cand cd;
+        // (interior bricks: every lane of the wave takes part in the spread)
+        if (i >= nh && !interior) continue;
+        Cand cd;
+        bool act = i < nh;
+        if (act) {
           if (VOL) {
             const PoseView& pv = s_view[0];
             lattice_values3(p, pv, pv.kx0 + (int)(h & 0x3FFu), pv.ky0 + (int)((h >> 10) & 0x3FFu),
-                            pv.kz0 + (int)(h >> 20), gr[k], gm[k], cd);
+                            pv.kz0 + (int)(h >> 20), gr, gm, cd);
           } else {
             const PoseView& pv = s_view[hit_pose(h)];
-            lattice_values<NDIM>(p, pv, hit_kx(h, pv), hit_ky(h, pv), gr[k], gm[k], cd);
+            lattice_values<NDIM>(p, pv, hit_kx(h, pv), hit_ky(h, pv), gr, gm, cd);
           }
-          if (in_box<NDIM>(bx, cd.q)) spread<NDIM, INTERP, WEIGHTS, G>(br, cd, inv_q, acc);
+          act = in_box<NDIM>(bx, cd.q);
+        }
+        if (NDIM == 3 && G > 0 && interior) {
+          if constexpr (NDIM == 3 && G > 0) spread_interior<INTERP, WEIGHTS, G>(br, cd, act, inv_q, acc);
+        } else if (act) {
+          spread<NDIM, INTERP, WEIGHTS, G>(br, cd, inv_q, acc);
         }
       }
 #pragma unroll
