@@ -300,20 +300,23 @@ __device__ __forceinline__ void spread(const BrickPos& br, const Cand& cd, float
   }
 }
 
-// Whether a 3D brick with guard columns, rows and planes (G = kGuard) is
-// interior: not the lowest brick in x, y or z, and its guards lie inside the
-// stored range.  Then every tap of a lattice point in the reach box lands in
-// the accumulator (its first tap lies in the brick on every axis), every x
-// tap is at x >= 1, and spread_interior() applies.
+// Which spread a 3D brick with guard columns, rows and planes (G = kGuard)
+// takes: 0 the general one (spread()); 1 or 2 spread_interior(), for bricks
+// that are not the lowest in y or z and whose guard rows and planes lie
+// inside the stored range, so that every tap of a lattice point in the reach
+// box lands in the accumulator (its first tap lies in the brick on every
+// axis).  2: not the lowest brick in x either, so every x tap is at x >= 1;
+// 1: the lowest, whose taps at x = 0 take the real part only and whose taps
+// at x < 0 add nothing.
 template <int NDIM, int G, int BZ = 16>
-__device__ __forceinline__ bool brick_interior(const BrickPos& br) {
+__device__ __forceinline__ int brick_kind(const BrickPos& br) {
   using BR = Brick<NDIM, BZ>;
-  if (NDIM != 3 || G < kGuard) return false;
-  return !br.xbottom && !br.ybottom && !br.zbottom && br.ylim == br.y0 + BR::Y + G - 1 &&
-         br.zlim == br.z0 + BR::Z + G - 1;
+  if (NDIM != 3 || G < kGuard) return 0;
+  const bool yz = !br.ybottom && !br.zbottom && br.ylim == br.y0 + BR::Y + G - 1 && br.zlim == br.z0 + BR::Z + G - 1;
+  return yz ? (br.xbottom ? 1 : 2) : 0;
 }
 
-// Spread of an interior brick (brick_interior), with the lanes of a wave
+// Spread of an interior brick (brick_kind 1 or 2), with the lanes of a wave
 // reassigned so that the lanes of each LDS pass add to distinct banks.
 //
 // A wave's 64-bit LDS add is served 16 lanes at a time (lanes 16j .. 16j +
@@ -347,15 +350,15 @@ __device__ __forceinline__ float permute_f(int dest, float v) {
 }
 
 // Every lane of the wave calls it; act: the lane holds a lattice point in the
-// reach box (cd valid).
-template <int INTERP, bool REAL, int G, int BZ = 16>
+// reach box (cd valid).  XB: the lowest brick in x (brick_kind 1).
+template <int INTERP, bool REAL, int G, bool XB, int BZ = 16>
 __device__ __forceinline__ void spread_interior(const BrickPos& br, const Cand& cd, bool act, float inv_q,
                                                 unsigned long long* acc) {
   using L = AccLayout<3, G, BZ>;
   using K = Kern<INTERP>;
   constexpr int T = K::T;
-  uint32_t base = ~0u;
-  float fx = 0.f, fy = 0.f, fz = 0.f, vr = 0.f, vi = 0.f;
+  uint32_t base = ~0u;  // XB: the first x tap + 8 in bits 16 and up
+  float fx = 0.f, fy = 0.f, fz = 0.f, vr = 0.f, vi = 0.f, vr0 = 0.f, vi0 = 0.f;
   if (act) {
     const AxisPos ax = axis_pos(cd.q[0], K::OFF), ay = axis_pos(cd.q[1], K::OFF), az = axis_pos(cd.q[2], K::OFF);
     base = (uint32_t)acc_word<3, G, BZ>(ax.x0 - br.x0, ay.x0 - br.y0, az.x0 - br.z0);
@@ -364,25 +367,39 @@ __device__ __forceinline__ void spread_interior(const BrickPos& br, const Cand& 
     fz = az.f;
     vr = cd.v1.x * inv_q;
     vi = cd.v1.y * inv_q;
+    if (XB) {
+      vr0 = cd.v0.x * inv_q;
+      vi0 = cd.v0.y * inv_q;
+    }
   }
   const int rank = wave_rank(act ? (int)(base & 15u) : 16);
   const int dest = ((rank & 3) << 4) | (rank >> 2);
+  if (XB && act) base |= (uint32_t)(axis_pos(cd.q[0], K::OFF).x0 + 8) << 16;
   base = (uint32_t)__builtin_amdgcn_ds_permute(dest << 2, (int)base);
   fx = permute_f(dest, fx);
   fy = permute_f(dest, fy);
   fz = permute_f(dest, fz);
   vr = permute_f(dest, vr);
   if (!REAL) vi = permute_f(dest, vi);
+  if (XB) {
+    vr0 = permute_f(dest, vr0);
+    if (!REAL) vi0 = permute_f(dest, vi0);
+  }
   if (base == ~0u) return;
   float wx[T], wy[T], wz[T];
   K::w(fx, wx);
   K::w(fy, wy);
   K::w(fz, wz);
   float are[T], aim[T];
+  const int x0 = XB ? (int)(base >> 16) - 8 : 1;
+  if (XB) base &= 0xFFFFu;
 #pragma unroll
   for (int d = 0; d < T; ++d) {
-    are[d] = wx[d] * vr;
-    aim[d] = wx[d] * vi;
+    // (XB: a tap at x < 0, whose slot is the previous row's guard column,
+    // adds nothing; a tap at x = 0 takes the real output's value only)
+    const int xt = x0 + d;
+    are[d] = wx[d] * (!XB || xt >= 1 ? vr : (xt == 0 ? vr0 : 0.f));
+    aim[d] = wx[d] * (!XB || xt >= 1 ? vi : (xt == 0 ? vi0 : 0.f));
   }
   unsigned long long* a = acc + base;
   int* ar = reinterpret_cast<int*>(acc) + base;

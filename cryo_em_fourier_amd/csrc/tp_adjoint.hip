@@ -293,7 +293,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   __syncthreads();
 
   const Box bx = reach_box<NDIM, INTERP, EXCLZ>(br);
-  const bool interior = brick_interior<NDIM, G>(br);
+  const int kind = brick_kind<NDIM, G>(br);
   int g0 = 0;  // first pose of the current group in s_poses
 
   // G entries of hit h of the current group
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
         amax = fmaxf(amax, fmaxf(fabsf(gr.x) + fabsf(gr.y), fabsf(gm.x) + fabsf(gm.y)));
         if (measure_only) continue;
         // (interior bricks: every lane of the wave takes part in the spread)
-        if (i >= nh && !interior) continue;
+        if (i >= nh && kind == 0) continue;
         Cand cd;
         bool act = i < nh;
         if (act) {
@@ -394,8 +394,10 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
           }
           act = in_box<NDIM>(bx, cd.q);
         }
-        if (NDIM == 3 && G > 0 && interior) {
-          if constexpr (NDIM == 3 && G > 0) spread_interior<INTERP, WEIGHTS, G>(br, cd, act, inv_q, acc);
+        if (NDIM == 3 && G > 0 && kind == 2) {
+          if constexpr (NDIM == 3 && G > 0) spread_interior<INTERP, WEIGHTS, G, false>(br, cd, act, inv_q, acc);
+        } else if (NDIM == 3 && G > 0 && kind == 1) {
+          if constexpr (NDIM == 3 && G > 0) spread_interior<INTERP, WEIGHTS, G, true>(br, cd, act, inv_q, acc);
         } else if (act) {
           spread<NDIM, INTERP, WEIGHTS, G>(br, cd, inv_q, acc);
         }
