@@ -255,8 +255,20 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   constexpr int kHitCap = SH::HIT_CAP;
   constexpr int kPerThread = SH::PER_THREAD;
   constexpr int kNVox = SH::NVOX;
+  // RAW (exclusive ownership): thread tid keeps the accumulator slots tid +
+  // i BS (one base address, immediate offsets in the flushes); the write-out
+  // maps a slot back to its voxel.  Otherwise it keeps voxels tid + i BS.
+  constexpr bool RAW = SH::EXCLZ;
   constexpr int G = EXCLZ ? kGuard : 0;
   constexpr int XR = BR::X + G, YR = BR::Y + G;  // x columns and y rows of the accumulator
+  static_assert(!RAW || ((AL::W + BS - 1) / BS <= kPerThread && AL::S == XR && AL::ROWS == YR),
+                "raw accumulator slots must fit the per-thread registers");
+  // accumulator slot of entry i of this thread (-1: none)
+  auto slot_of = [&](int i) -> int {
+    const int v = threadIdx.x + i * BS;
+    if (RAW) return v < AL::W ? v : -1;
+    return v < kNVox ? acc_word<NDIM, G>(v % XR, (v / XR) % YR, v / (XR * YR)) : -1;
+  };
   __shared__ uint32_t s_hits[kHitCap];
   __shared__ int s_poses[BS];
   __shared__ PoseView s_view[kGroupMax];
@@ -425,9 +437,8 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
         // flush the slice into fp32 registers
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i) {
-          const int v = tid + i * BS;
-          if (v >= kNVox) continue;
-          const int sl = acc_word<NDIM, G>(v % XR, (v / XR) % YR, v / (XR * YR));
+          const int sl = slot_of(i);
+          if (sl < 0) continue;
           if (WEIGHTS) {
             fre[i] = fmaf((float)acc_r[sl], q, fre[i]);
             acc_r[sl] = 0;
@@ -445,9 +456,8 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
       if (!measure_only) {
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i) {
-          const int v = tid + i * BS;
-          if (v >= kNVox) continue;
-          const int sl = acc_word<NDIM, G>(v % XR, (v / XR) % YR, v / (XR * YR));
+          const int sl = slot_of(i);
+          if (sl < 0) continue;
           if (WEIGHTS) acc_r[sl] = 0;
           else acc[sl] = 0ull;
         }
@@ -485,9 +495,8 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
     });
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int v = tid + i * BS;
-      if (v >= kNVox) continue;
-      const int sl = acc_word<NDIM, G>(v % XR, (v / XR) % YR, v / (XR * YR));
+      const int sl = slot_of(i);
+      if (sl < 0) continue;
       if (WEIGHTS ? acc_r[sl] != 0 : acc[sl] != 0ull) fre[i] = fim[i] = __builtin_nanf("");
     }
   }
@@ -500,9 +509,22 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   const int wh = p.N / 2 + 1;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const int v = tid + i * BS;
-    if (v >= kNVox) continue;
-    const int xr = v % XR, yr = (v / XR) % YR, zr = v / (XR * YR);
+    int xr, yr, zr;
+    if (RAW) {
+      const int t = tid + i * BS - kGuard;  // (the leading guard slots hold no voxel)
+      if (t < 0 || t >= AL::W - kGuard) continue;
+      zr = t / AL::PZ;
+      const int r = t - zr * AL::PZ;
+      if (r >= AL::ROWS * AL::S) continue;  // plane padding
+      yr = r / AL::S;
+      xr = r - yr * AL::S;
+    } else {
+      const int v = tid + i * BS;
+      if (v >= kNVox) continue;
+      xr = v % XR;
+      yr = (v / XR) % YR;
+      zr = v / (XR * YR);
+    }
     const int x = br.x0 + xr;
     const int y = br.y0 + yr;
     const int z = br.z0 + zr;
