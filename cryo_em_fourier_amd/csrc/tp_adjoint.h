@@ -324,24 +324,52 @@ __device__ __forceinline__ int brick_kind(const BrickPos& br) {
 // are served one after the other.  Every tap of a lattice point sits at a
 // compile-time offset from its first tap's slot, so the bank pairs of all 64
 // tap adds of a lane follow from that base slot.  The wave ranks its lattice
-// points by base mod 16 (a counting sort over ballots) and deals them out
+// points by base mod 16 (a counting sort, wave_rank) and deals them out
 // round-robin over the four passes: with four points per bank pair every
 // pass gets one of each.  The lattice points themselves (their G loads, the
 // phase, the sample point) stay in the lanes that read them, which keeps the
 // loads coalesced; only the spread's inputs move, through ds_permute.
 
-// The rank of each lane's key (0..16) in the wave's stable ascending order.
-// Every lane of the wave must be active.
+// Inclusive prefix sum over the wave's 64 lanes (DPP row shifts within each
+// row of 16 lanes, then the row broadcasts of lanes 15 and 31).  Every lane
+// of the wave must be active.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// The rank of each lane's key in the wave's stable ascending order of keys,
+// for keys 0..15, with the lanes of key 16 (no point) after all others.  A
+// counting sort: 16 counters of 8 bits in four words, one-hot per lane,
+// prefix-summed over the lanes (counts stay below 65, so bytes never carry);
+// the totals of the last lane, prefix-summed over the keys bytewise (a
+// multiply by 0x01010101), give each key's first rank.  Every lane of the
+// wave must be active.
 __device__ __forceinline__ int wave_rank(int key) {
-  int rank = 0, pre = 0;
+  const bool act = key < 16;
+  const int wsel = key >> 2, sh = (key & 3) * 8;
+  const uint32_t bit = act ? (1u << sh) : 0u;
+  uint32_t c[4];
 #pragma unroll
-  for (int b = 0; b <= 16; ++b) {
-    const unsigned long long m = __ballot(key == b);
-    const int below = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-    if (key == b) rank = pre + below;
-    pre += __popcll(m);
+  for (int w = 0; w < 4; ++w) c[w] = wave_prefix_sum(wsel == w ? bit : 0u);
+  uint32_t first[4];  // byte b of word w: the first rank of key 4 w + b
+  uint32_t below = 0;  // points with keys of the earlier words
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t inc = (uint32_t)__builtin_amdgcn_readlane((int)c[w], 63) * 0x01010101u;
+    first[w] = (inc << 8) + below * 0x01010101u;
+    below += inc >> 24;
   }
-  return rank;
+  const uint32_t fw = wsel == 0 ? first[0] : wsel == 1 ? first[1] : wsel == 2 ? first[2] : first[3];
+  const uint32_t cw = wsel == 0 ? c[0] : wsel == 1 ? c[1] : wsel == 2 ? c[2] : c[3];
+  const unsigned long long none = __ballot(!act);
+  const int before = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(none >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)none, 0u));
+  return act ? (int)(((fw >> sh) & 0xFFu) + ((cw >> sh) & 0xFFu) - 1u) : (int)below + before;
 }
 
 // Sends v to lane dest (a permutation of the wave's lanes).
