@@ -576,11 +576,15 @@ uint64_t adjoint_blocks(const OpParams& p) {
   return (uint64_t)p.B * (uint64_t)bp.nbricks * (uint64_t)bp.cmax;
 }
 
-// Dense lattices (oversampling up to 1.25) fill a brick with hits and run
-// faster on 512-thread workgroups; sparse ones on 256 (measured at box 256
-// with 4096 poses: 5.9 against 6.4 ms at oversampling 1, 8.9 against 9.8 ms
-// at oversampling 2).
-static bool wide_adjoint(const OpParams& p) { return p.os <= 1.25f; }
+// Dense lattices fill a brick with hits and run faster on 512-thread
+// workgroups (in 3D with exclusive ownership); sparse ones on 256.  Measured
+// at box 256 with 4096 poses: 5.9 against 6.4 ms at oversampling 1 (up to
+// 1.25 for every kernel); with the bank-ranked spread and raw flush slots,
+// the 3D cubic adjoint at oversampling 2 takes 7.84 against 8.16 ms on 512
+// threads (cubic 3D: up to 2), the linear one 6.33 against 4.62 ms.
+static bool wide_adjoint(const OpParams& p, int interp) {
+  return p.os <= (p.ndim == 3 && interp == 1 ? 2.f : 1.25f);  // 1: cubic
+}
 
 template <int MODE, int BS>
 static void launch_modes(const OpParams& p, const BrickParams& bp, int ndim, int interp, hipStream_t s) {
@@ -599,7 +603,7 @@ static void launch_modes(const OpParams& p, const BrickParams& bp, int ndim, int
 
 template <int MODE>
 static hipError_t launch_adjoint(const OpParams& p, const BrickParams& bp, int ndim, int interp, hipStream_t s) {
-  if (wide_adjoint(p)) launch_modes<MODE, 512>(p, bp, ndim, interp, s);
+  if (wide_adjoint(p, interp)) launch_modes<MODE, 512>(p, bp, ndim, interp, s);
   else launch_modes<MODE, 256>(p, bp, ndim, interp, s);
   return hipGetLastError();
 }

@@ -1,7 +1,7 @@
 """GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
 
 Small cases that span several 16x16 output tiles with ragged edges, odd and
-even boxes, oversampling 1 / 1.5 / 2, batches with per-entry and broadcast
+even boxes, oversampling 1 / 1.5 / 2 / 2.5, batches with per-entry and broadcast
 poses, no cutoff (taps reach the Nyquist planes), and adversarial poses: the
 identity, cube rotations (on-grid samples), the slice plane on the x = 0 plane
 (every stencil straddles the Friedel fold), near it, and +-60 degree tilts.
@@ -45,6 +45,9 @@ def case3d(name):
         "odd-nocut":     (33, 33, 1, 6, 1, 1, CUBIC, 1.0, -1.0, "cplx", "so3"),
         "os2":           (40, 20, 1, 6, 1, 1, CUBIC, 2.0, 9.0, "pad2", "so3"),
         "os1.5-linear":  (36, 24, 1, 5, 1, 1, LINEAR, 1.5, 11.0, "cplx", "so3"),
+        # above oversampling 2 the cubic 3D adjoint takes the 256-thread
+        # bricks (os2 runs the 512-thread ones)
+        "os2.5":         (40, 16, 1, 6, 1, 1, CUBIC, 2.5, 7.0, "cplx", "so3"),
         "batch":         (24, 24, 2, 4, 2, 2, CUBIC, 1.0, 11.0, "cplx", "so3"),
         "batch-bcast":   (20, 22, 3, 3, 1, 1, LINEAR, 1.0, 10.5, "cplx", "so3"),
         "adv-cubic":     (32, 32, 1, 8, 1, 1, CUBIC, 1.0, -1.0, "real", "adv"),
@@ -85,7 +88,7 @@ def case3d(name):
                 interp=interp, os=np.float32(os_), cutoff=np.float32(cutoff))
 
 
-CASES3 = ["c1", "c1-cubic", "odd-nocut", "os2", "os1.5-linear", "batch", "batch-bcast",
+CASES3 = ["c1", "c1-cubic", "odd-nocut", "os2", "os1.5-linear", "os2.5", "batch", "batch-bcast",
           "adv-cubic", "adv-linear", "ragged", "mixed-rot", "mixed-shift", "bcast-cubic", "adv-cubic-cplx",
           "big-shift", "eighth-shift"]
 
