@@ -305,7 +305,11 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
   __syncthreads();
 
   const Box bx = reach_box<NDIM, INTERP, EXCLZ>(br);
-  const int kind = brick_kind<NDIM, G>(br);
+  // (the linear kernel's 8 taps per point do not pay for the wave's ranking:
+  // 2.39 against 2.10 ms at box 256, 4096 poses, so it keeps the general
+  // spread; so does the weight volume, whose 32-bit adds are served 32 lanes
+  // at a time over 32 banks: 3.11 against 3.08 ms)
+  const int kind = INTERP && !WEIGHTS ? brick_kind<NDIM, G>(br) : 0;
   int g0 = 0;  // first pose of the current group in s_poses
 
   // G entries of hit h of the current group
