@@ -103,15 +103,17 @@ def test_backward_3d_many_poses_per_brick_dense(P):
     assert_parity(gs.cpu().numpy(), ds, f"backward_3d grad_shift dense P={P}")
 
 
-def test_backward_3d_propagates_nonfinite_upstream():
+@pytest.mark.parametrize("N", [24, 48])
+def test_backward_3d_propagates_nonfinite_upstream(N):
     """A NaN and an Inf upstream: the voxels their stencils reach and the
-    gradients of their poses are not finite; everything else matches."""
+    gradients of their poses are not finite; everything else matches.  (At
+    N = 48 the central bricks take the bank-ranked spread.)"""
     import math
 
     from cryo_em_fourier_amd import tp_backward_3d
 
-    rng = np.random.default_rng(91)
-    N, P = 24, 6
+    rng = np.random.default_rng(91 + N)
+    P = 6
     V = complex_normal(rng, (1, N, N, N // 2 + 1))
     R = synth.uniform_rotations(rng, P)[None]
     s = rng.uniform(-3, 3, (1, P, 2)).astype(np.float32)
