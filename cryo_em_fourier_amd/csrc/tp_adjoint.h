@@ -378,8 +378,9 @@ __device__ __forceinline__ float permute_f(int dest, float v) {
 }
 
 // Every lane of the wave calls it; act: the lane holds a lattice point in the
-// reach box (cd valid).  XB: the lowest brick in x (brick_kind 1).
-template <int INTERP, bool REAL, int G, bool XB, int BZ = 16>
+// reach box (cd valid).  XB: the lowest brick in x (brick_kind 1).  Packed
+// (re, im) adds only: the weight volume keeps the general spread.
+template <int INTERP, int G, bool XB, int BZ = 16>
 __device__ __forceinline__ void spread_interior(const BrickPos& br, const Cand& cd, bool act, float inv_q,
                                                 unsigned long long* acc) {
   using L = AccLayout<3, G, BZ>;
@@ -408,10 +409,10 @@ __device__ __forceinline__ void spread_interior(const BrickPos& br, const Cand& 
   fy = permute_f(dest, fy);
   fz = permute_f(dest, fz);
   vr = permute_f(dest, vr);
-  if (!REAL) vi = permute_f(dest, vi);
+  vi = permute_f(dest, vi);
   if (XB) {
     vr0 = permute_f(dest, vr0);
-    if (!REAL) vi0 = permute_f(dest, vi0);
+    vi0 = permute_f(dest, vi0);
   }
   if (base == ~0u) return;
   float wx[T], wy[T], wz[T];
@@ -430,7 +431,6 @@ __device__ __forceinline__ void spread_interior(const BrickPos& br, const Cand& 
     aim[d] = wx[d] * (!XB || xt >= 1 ? vi : (xt == 0 ? vi0 : 0.f));
   }
   unsigned long long* a = acc + base;
-  int* ar = reinterpret_cast<int*>(acc) + base;
 #pragma unroll
   for (int dz = 0; dz < T; ++dz) {
 #pragma unroll
@@ -439,8 +439,7 @@ __device__ __forceinline__ void spread_interior(const BrickPos& br, const Cand& 
 #pragma unroll
       for (int dx = 0; dx < T; ++dx) {
         const int o = dz * L::PZ + dy * L::S + dx;
-        if (REAL) atomicAdd(ar + o, cvt_rpi(are[dx] * wyz));
-        else atomicAdd(a + o, pack_pair(cvt_rpi(are[dx] * wyz), cvt_rpi(aim[dx] * wyz)));
+        atomicAdd(a + o, pack_pair(cvt_rpi(are[dx] * wyz), cvt_rpi(aim[dx] * wyz)));
       }
     }
   }

@@ -411,9 +411,9 @@ __global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(AdjShape<NDI
           act = in_box<NDIM>(bx, cd.q);
         }
         if (NDIM == 3 && G > 0 && kind == 2) {
-          if constexpr (NDIM == 3 && G > 0) spread_interior<INTERP, WEIGHTS, G, false>(br, cd, act, inv_q, acc);
+          if constexpr (NDIM == 3 && G > 0 && !WEIGHTS) spread_interior<INTERP, G, false>(br, cd, act, inv_q, acc);
         } else if (NDIM == 3 && G > 0 && kind == 1) {
-          if constexpr (NDIM == 3 && G > 0) spread_interior<INTERP, WEIGHTS, G, true>(br, cd, act, inv_q, acc);
+          if constexpr (NDIM == 3 && G > 0 && !WEIGHTS) spread_interior<INTERP, G, true>(br, cd, act, inv_q, acc);
         } else if (act) {
           spread<NDIM, INTERP, WEIGHTS, G>(br, cd, inv_q, acc);
         }
